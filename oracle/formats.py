@@ -1,0 +1,40 @@
+"""Storage-format decoding, written from the format definitions.
+
+fp8 e4m3fn (OCP 8-bit floating point, "FN" variant): 1 sign bit, 4 exponent
+bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+m * 2^-9; no infinities; only S.1111.111 is NaN.  The index cache and the
+index queries are stored in this format (the pages keep the index cache
+resident in device memory and leave its element type open; the reading taken
+is fp8 with integer values, which it represents exactly).
+
+bf16: the upper 16 bits of an IEEE binary32.
+"""
+import numpy as np
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one fp8 e4m3fn byte."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * man * 2.0 ** -9
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)],
+                        dtype=np.float64)
+
+
+def decode_e4m3fn(b: np.ndarray) -> np.ndarray:
+    """uint8 array of fp8 e4m3fn codes -> float64 array."""
+    return E4M3FN_TABLE[np.asarray(b, dtype=np.uint8)]
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """uint16 array of bf16 bit patterns -> float64 array."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
