@@ -1,0 +1,408 @@
+// C ABI of the sparse-decode library: host-side checks, launch dispatch and
+// the whole-step orchestration.  Every check happens before anything is
+// enqueued, so a nonzero status means the stream is untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ess_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ess_status fail(ess_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ess_status hip_fail(hipError_t e, const char* what) {
+  return fail(ESS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define ESS_NONNULL(p) \
+  if (!(p)) return fail(ESS_ERR_INVALID, "%s: %s is NULL", fn, #p)
+
+ess_status check_dims(const ess_dims* d, const char* fn) {
+  if (!d) return fail(ESS_ERR_INVALID, "%s: dims is NULL", fn);
+  if (d->batch < 1 || d->mtp < 1 || d->ctx_len < 1 || d->idx_heads < 1 ||
+      d->idx_dim < 1 || d->mla_heads < 1 || d->topk < 1 || d->pool_slots < 1)
+    return fail(ESS_ERR_INVALID, "%s: every size in dims must be >= 1", fn);
+  if (d->lat_dim != ess::kLat || d->v_dim != ess::kVal)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: lat_dim must be 576 and v_dim 512",
+                fn);
+  if (d->mtp > 4)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: mtp above 4", fn);
+  if (!std::isfinite(d->softmax_scale))
+    return fail(ESS_ERR_INVALID, "%s: softmax_scale is not finite", fn);
+  if (d->ctx_len > (1 << 28))
+    return fail(ESS_ERR_UNSUPPORTED, "%s: ctx_len above 2^28", fn);
+  return ESS_OK;
+}
+
+ess_status check_indexer(const ess_dims* d, const char* fn) {
+  if (d->idx_dim != 64 && d->idx_dim != 128)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: idx_dim must be 64 or 128", fn);
+  if (d->idx_heads % 16 != 0 || d->mtp * d->idx_heads > 128)
+    return fail(ESS_ERR_UNSUPPORTED,
+                "%s: idx_heads must be a multiple of 16 with mtp*idx_heads <= 128",
+                fn);
+  return ESS_OK;
+}
+
+ess_status check_topk(const ess_dims* d, int k, int n_tok, const char* fn) {
+  if (k < 1 || k > ess::kMaxTopk)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: k must be in [1, %d]", fn,
+                ess::kMaxTopk);
+  if (n_tok < 1 || n_tok > d->mtp)
+    return fail(ESS_ERR_INVALID, "%s: n_tok must be in [1, mtp]", fn);
+  return ESS_OK;
+}
+
+ess_status check_update(const ess_dims* d, int k, int n_tok, const char* fn) {
+  ess_status s = check_topk(d, k, n_tok, fn);
+  if (s != ESS_OK) return s;
+  if ((int64_t)n_tok * k > d->pool_slots)
+    return fail(ESS_ERR_CAPACITY,
+                "%s: n_tok*k = %lld exceeds pool_slots = %d", fn,
+                (long long)n_tok * k, d->pool_slots);
+  if ((int64_t)n_tok * k > ess::kMaxTopk)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: n_tok*k above %d", fn,
+                ess::kMaxTopk);
+  return ESS_OK;
+}
+
+ess_status check_mla(const ess_dims* d, const char* fn) {
+  if (d->mla_heads % 16 != 0)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: mla_heads must be a multiple of 16",
+                fn);
+  if (d->topk > ess::kMaxTopk)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: topk above %d", fn, ess::kMaxTopk);
+  return ESS_OK;
+}
+
+// Events for ordering the prefetch stream against the main stream.
+std::mutex g_ev_mu;
+std::vector<hipEvent_t> g_events;
+
+ess_status get_events(size_t n, hipEvent_t** out) {
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  while (g_events.size() < n) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) return hip_fail(r, "hipEventCreateWithFlags");
+    g_events.push_back(e);
+  }
+  *out = g_events.data();
+  return ESS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ess_workspace_bytes(const ess_dims* d) {
+  if (check_dims(d, "ess_workspace_bytes") != ESS_OK) return 0;
+  return ess::sparse_mla_ws_bytes(*d);
+}
+
+size_t ess_lru_state_bytes(const ess_dims* d) {
+  if (check_dims(d, "ess_lru_state_bytes") != ESS_OK) return 0;
+  return ess::lru_bytes_per_req(d->pool_slots) * (size_t)d->batch;
+}
+
+ess_status ess_pool_reset(const ess_dims* d, int32_t* cache_slots,
+                          int32_t* slot_pos, void* lru_state,
+                          hipStream_t stream) {
+  const char* fn = "ess_pool_reset";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  ESS_NONNULL(cache_slots);
+  ESS_NONNULL(slot_pos);
+  ESS_NONNULL(lru_state);
+  hipError_t e = ess::launch_pool_reset(*d, cache_slots, slot_pos, lru_state,
+                                        stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
+                            const float* w, const uint8_t* k_fp8,
+                            const int32_t* n_vis, float* scores,
+                            hipStream_t stream) {
+  const char* fn = "ess_index_scores";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_indexer(d, fn)) != ESS_OK) return s;
+  ESS_NONNULL(q_fp8);
+  ESS_NONNULL(w);
+  ESS_NONNULL(k_fp8);
+  ESS_NONNULL(n_vis);
+  ESS_NONNULL(scores);
+  hipError_t e = ess::launch_index_scores(*d, q_fp8, w, k_fp8, n_vis, scores,
+                                          stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
+                           const float* scores, const int32_t* n_vis,
+                           const int32_t* cache_slots, int32_t* sel_pos,
+                           int32_t* sel_slot, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const char* fn = "ess_topk_lookup";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_topk(d, k, n_tok, fn)) != ESS_OK) return s;
+  ESS_NONNULL(scores);
+  ESS_NONNULL(n_vis);
+  ESS_NONNULL(cache_slots);
+  ESS_NONNULL(sel_pos);
+  ESS_NONNULL(sel_slot);
+  ESS_NONNULL(n_sel);
+  hipError_t e = ess::launch_topk(*d, k, n_tok, scores, n_vis, cache_slots,
+                                  sel_pos, sel_slot, n_sel, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
+                           const int32_t* sel_pos, const int32_t* n_sel,
+                           int32_t* cache_slots, int32_t* slot_pos,
+                           void* lru_state, int32_t* miss_pos,
+                           int32_t* miss_slot, int32_t* n_miss,
+                           int32_t* n_evict, int32_t* row_dst,
+                           int32_t* sel_slot_post, hipStream_t stream) {
+  const char* fn = "ess_pool_update";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_update(d, k, n_tok, fn)) != ESS_OK) return s;
+  ESS_NONNULL(sel_pos);
+  ESS_NONNULL(n_sel);
+  ESS_NONNULL(cache_slots);
+  ESS_NONNULL(slot_pos);
+  ESS_NONNULL(lru_state);
+  ESS_NONNULL(miss_pos);
+  ESS_NONNULL(miss_slot);
+  ESS_NONNULL(n_miss);
+  ESS_NONNULL(n_evict);
+  ESS_NONNULL(row_dst);
+  ESS_NONNULL(sel_slot_post);
+  hipError_t e = ess::launch_pool_update(*d, k, n_tok, sel_pos, n_sel,
+                                         cache_slots, slot_pos, lru_state,
+                                         miss_pos, miss_slot, n_miss, n_evict,
+                                         row_dst, sel_slot_post, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
+                                 const int32_t* sel_pos,
+                                 const int32_t* sel_src,
+                                 const int32_t* row_dst, const int32_t* n_sel,
+                                 uint16_t* pool, const uint16_t* host_view,
+                                 float* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "ess_sparse_mla_decode";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_mla(d, fn)) != ESS_OK) return s;
+  ESS_NONNULL(q_abs);
+  ESS_NONNULL(sel_pos);
+  ESS_NONNULL(sel_src);
+  ESS_NONNULL(n_sel);
+  ESS_NONNULL(pool);
+  ESS_NONNULL(host_view);
+  ESS_NONNULL(out);
+  ESS_NONNULL(ws);
+  const size_t need = ess::sparse_mla_ws_bytes(*d);
+  if (ws_bytes < need)
+    return fail(ESS_ERR_NOMEM, "%s: workspace of %zu bytes, need %zu", fn,
+                ws_bytes, need);
+  hipError_t e = ess::launch_sparse_mla(*d, q_abs, sel_pos, sel_src, row_dst,
+                                        n_sel, pool, host_view, out, lse, ws,
+                                        stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
+                         const int32_t* miss_pos, const int32_t* miss_slot,
+                         const int32_t* n_miss, const uint16_t* host_view,
+                         uint16_t* pool, hipStream_t stream) {
+  const char* fn = "ess_miss_copy";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if (list_stride < 1)
+    return fail(ESS_ERR_INVALID, "%s: list_stride must be >= 1", fn);
+  ESS_NONNULL(miss_pos);
+  ESS_NONNULL(miss_slot);
+  ESS_NONNULL(n_miss);
+  ESS_NONNULL(host_view);
+  ESS_NONNULL(pool);
+  hipError_t e = ess::launch_miss_copy(*d, list_stride, miss_pos, miss_slot,
+                                       n_miss, host_view, pool, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
+  const char* fn = "ess_decode_step";
+  if (!io.q_idx || !io.w_idx || !io.k_idx || !io.host_view || !io.pool ||
+      !io.cache_slots || !io.slot_pos || !io.lru_state || !io.scores ||
+      !io.sel_pos || !io.sel_slot || !io.n_sel || !io.row_dst ||
+      !io.sel_slot_post || !io.miss_pos || !io.miss_slot || !io.n_miss ||
+      !io.n_evict)
+    return fail(ESS_ERR_INVALID, "%s: layer %d has a NULL buffer", fn, l);
+  if (mode != ESS_MODE_FILL && (!io.q_abs || !io.out || !io.ws))
+    return fail(ESS_ERR_INVALID, "%s: layer %d has a NULL attention buffer",
+                fn, l);
+  return ESS_OK;
+}
+
+// Scores, top-k and pool update of one layer on one stream.
+static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
+                                 const int32_t* n_vis, int k, int n_tok,
+                                 hipStream_t st) {
+  hipError_t e = ess::launch_index_scores(d, io.q_idx, io.w_idx, io.k_idx,
+                                          n_vis, io.scores, st);
+  if (e != hipSuccess) return e;
+  e = ess::launch_topk(d, k, n_tok, io.scores, n_vis, io.cache_slots,
+                       io.sel_pos, io.sel_slot, io.n_sel, st);
+  if (e != hipSuccess) return e;
+  return ess::launch_pool_update(d, k, n_tok, io.sel_pos, io.n_sel,
+                                 io.cache_slots, io.slot_pos, io.lru_state,
+                                 io.miss_pos, io.miss_slot, io.n_miss,
+                                 io.n_evict, io.row_dst, io.sel_slot_post, st);
+}
+
+ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
+                           const ess_layer_io* layers, const int32_t* n_vis,
+                           int32_t mode, hipStream_t stream,
+                           hipStream_t side) {
+  const char* fn = "ess_decode_step";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if (n_layers < 1) return fail(ESS_ERR_INVALID, "%s: n_layers < 1", fn);
+  ESS_NONNULL(layers);
+  ESS_NONNULL(n_vis);
+  if (mode != ESS_MODE_FILL && mode != ESS_MODE_INLINE &&
+      mode != ESS_MODE_PREFETCH)
+    return fail(ESS_ERR_INVALID, "%s: unknown mode %d", fn, mode);
+  if ((s = check_indexer(d, fn)) != ESS_OK) return s;
+  if (mode == ESS_MODE_FILL) {
+    if ((s = check_update(d, d->pool_slots, 1, fn)) != ESS_OK) return s;
+  } else {
+    if ((s = check_update(d, d->topk, d->mtp, fn)) != ESS_OK) return s;
+    if ((s = check_mla(d, fn)) != ESS_OK) return s;
+  }
+  if (mode == ESS_MODE_PREFETCH && (side == stream))
+    return fail(ESS_ERR_INVALID, "%s: prefetch needs a second stream", fn);
+  const size_t ws_need = ess::sparse_mla_ws_bytes(*d);
+  for (int l = 0; l < n_layers; ++l) {
+    if ((s = check_layer(layers[l], mode, l)) != ESS_OK) return s;
+    if (mode != ESS_MODE_FILL && layers[l].ws_bytes < ws_need)
+      return fail(ESS_ERR_NOMEM, "%s: layer %d workspace of %zu bytes, need %zu",
+                  fn, l, layers[l].ws_bytes, ws_need);
+  }
+
+  hipError_t e = hipSuccess;
+  if (mode == ESS_MODE_FILL) {
+    const int C = d->pool_slots;
+    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+      const ess_layer_io& io = layers[l];
+      e = enqueue_select(*d, io, n_vis, C, 1, stream);
+      if (e == hipSuccess)
+        e = ess::launch_miss_copy(*d, C, io.miss_pos, io.miss_slot, io.n_miss,
+                                  io.host_view, io.pool, stream);
+    }
+    return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+  }
+  if (mode == ESS_MODE_INLINE) {
+    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+      const ess_layer_io& io = layers[l];
+      e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, stream);
+      if (e == hipSuccess)
+        e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot,
+                                   io.row_dst, io.n_sel, io.pool,
+                                   io.host_view, io.out, io.lse, io.ws,
+                                   stream);
+    }
+    return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+  }
+
+  // Prefetch: the side stream selects every layer and copies its misses into
+  // the pool, running ahead; the main stream runs layer l's attention once
+  // layer l's copy is done, so layer l+1's selection and copy overlap layer
+  // l's attention.
+  hipEvent_t* ev;
+  if ((s = get_events((size_t)n_layers + 1, &ev)) != ESS_OK) return s;
+  e = hipEventRecord(ev[n_layers], stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[n_layers], 0);
+  const int lstride = d->mtp * d->topk;
+  for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+    const ess_layer_io& io = layers[l];
+    e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, side);
+    if (e == hipSuccess)
+      e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
+                                io.n_miss, io.host_view, io.pool, side);
+    if (e == hipSuccess) e = hipEventRecord(ev[l], side);
+  }
+  for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+    const ess_layer_io& io = layers[l];
+    e = hipStreamWaitEvent(stream, ev[l], 0);
+    if (e == hipSuccess)
+      e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot_post,
+                                 nullptr, io.n_sel, io.pool, io.host_view,
+                                 io.out, io.lse, io.ws, stream);
+  }
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view) {
+  const char* fn = "ess_host_alloc";
+  ESS_NONNULL(host_ptr);
+  ESS_NONNULL(dev_view);
+  if (bytes == 0) return fail(ESS_ERR_INVALID, "%s: zero bytes", fn);
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes,
+                               hipHostMallocMapped | hipHostMallocNonCoherent);
+  if (e != hipSuccess || !p)
+    return fail(ESS_ERR_NOMEM, "%s: hipHostMalloc(%zu): %s", fn, bytes,
+                hipGetErrorString(e));
+  void* dv = nullptr;
+  e = hipHostGetDevicePointer(&dv, p, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(p);
+    return hip_fail(e, "hipHostGetDevicePointer");
+  }
+  *host_ptr = p;
+  *dev_view = dv;
+  return ESS_OK;
+}
+
+ess_status ess_host_free(void* host_ptr) {
+  if (!host_ptr) return ESS_OK;
+  hipError_t e = hipHostFree(host_ptr);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, "hipHostFree");
+}
+
+const char* ess_status_string(ess_status s) {
+  switch (s) {
+    case ESS_OK: return "ok";
+    case ESS_ERR_INVALID: return "invalid argument";
+    case ESS_ERR_UNSUPPORTED: return "unsupported shape";
+    case ESS_ERR_CAPACITY: return "pool capacity exceeded";
+    case ESS_ERR_HIP: return "HIP runtime error";
+    case ESS_ERR_NOMEM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+const char* ess_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

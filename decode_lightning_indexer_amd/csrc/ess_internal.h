@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ess.h"
+
+namespace ess {
+
+// Largest k the top-k and pool-update kernels hold on chip (LDS sort buffer
+// of 8-byte keys: 16384 * 8 = 128 KiB of the 160 KiB per CU).
+constexpr int kMaxTopk = 16384;
+constexpr int kLat = 576;   // latent width: c_KV[512] + k_R[64]
+constexpr int kVal = 512;   // value width
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ---- indexer ------------------------------------------------------------
+hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
+                               const float* w, const uint8_t* k,
+                               const int32_t* n_vis, float* scores,
+                               hipStream_t s);
+
+// ---- top-k --------------------------------------------------------------
+hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
+                       const float* scores, const int32_t* n_vis,
+                       const int32_t* cache_slots, int32_t* sel_pos,
+                       int32_t* sel_slot, int32_t* n_sel, hipStream_t s);
+
+// ---- pool ---------------------------------------------------------------
+// Per-request LRU state: header, slot stamps [C], ring of (slot, stamp).
+struct LruHeader {
+  int32_t head;       // first unread ring entry
+  int32_t tail;       // one past the last ring entry
+  int32_t free_head;  // slots [free_head, C) have never been used
+  int32_t epoch;      // stamp of the next update
+  int32_t cap;        // ring capacity in entries
+  int32_t err;        // nonzero: victim scan ran dry (state inconsistent)
+  int32_t pad[2];
+};
+__host__ __device__ inline int lru_ring_cap(int C) { return 4 * C; }
+inline size_t lru_bytes_per_req(int C) {
+  return align_up(sizeof(LruHeader) + sizeof(int32_t) * (size_t)C +
+                      2 * sizeof(int32_t) * (size_t)lru_ring_cap(C),
+                  256);
+}
+
+hipError_t launch_pool_reset(const ess_dims& d, int32_t* cache_slots,
+                             int32_t* slot_pos, void* lru, hipStream_t s);
+hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
+                              const int32_t* sel_pos, const int32_t* n_sel,
+                              int32_t* cache_slots, int32_t* slot_pos,
+                              void* lru, int32_t* miss_pos,
+                              int32_t* miss_slot, int32_t* n_miss,
+                              int32_t* n_evict, int32_t* row_dst,
+                              int32_t* sel_slot_post, hipStream_t s);
+
+// ---- attention ----------------------------------------------------------
+struct MlaPlan {
+  int heads_per_wg;   // 16 * waves
+  int head_groups;    // H / heads_per_wg
+  int rows_per_chunk; // multiple of 32
+  int nchunk;         // chunks of rows per (request, token)
+};
+MlaPlan plan_sparse_mla(const ess_dims& d);
+size_t sparse_mla_ws_bytes(const ess_dims& d);
+hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
+                             const int32_t* sel_pos, const int32_t* sel_src,
+                             const int32_t* row_dst, const int32_t* n_sel,
+                             uint16_t* pool, const uint16_t* host,
+                             float* out, float* lse, void* ws,
+                             hipStream_t s);
+
+// ---- miss copy ----------------------------------------------------------
+hipError_t launch_miss_copy(const ess_dims& d, int list_stride,
+                            const int32_t* miss_pos, const int32_t* miss_slot,
+                            const int32_t* n_miss, const uint16_t* host,
+                            uint16_t* pool, hipStream_t s);
+
+}  // namespace ess

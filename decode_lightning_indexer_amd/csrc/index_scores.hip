@@ -1,0 +1,169 @@
+// Lightning-indexer scores over every cached position, fp8 MFMA on gfx950.
+//
+// The indexer cache is the part of the DSA cache that stays in device memory
+// and is scanned in full every step (ESS concept page, "dual cache" table);
+// it is what grows with context in device memory (FlashOffloading analysis,
+// section "how 95.23 kB per token comes about").  The scan is therefore
+// bandwidth-bound: 2 * m * H_I flops per key byte is far below the fp8
+// MFMA ridge.  MFMA keeps the arithmetic off the critical path.
+//
+// Mapping onto v_mfma_f32_16x16x128_f8f6f4 (A: 16x128, B: 128x16, D: 16x16):
+//   A = 16 query heads x 128 dims (held in registers for the whole kernel),
+//   B = 128 dims x 16 positions (one 32-byte piece of a key row per lane,
+//       two coalesced 16-byte loads),
+//   D[head][pos] -> each lane holds 4 heads of one position; it applies the
+//   ReLU and head weight to its 4 heads, and two lane exchanges finish the
+//   head sum.  Lane group g (lanes 16g..16g+15) feeds dims [32g, 32g+32) of
+//   both operands, so A and B agree on the reduction index.
+// Inputs with integer values in [-7, 7] and integer weights keep every
+// partial sum an integer below 2^24, so the fp32 result is exact.
+#include "ess_internal.h"
+
+namespace ess {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;     // 4 waves
+constexpr int kGroups = 4;        // 16-position groups per wave iteration
+constexpr int kSpan = 1024;       // positions per workgroup
+
+// 32 bytes of a row for lane group g (zeros past a 64-wide row).  Key rows
+// are streamed once per step, so they are loaded non-temporally.
+template <int DI, bool STREAM>
+__device__ __forceinline__ v8i load_piece(const uint8_t* row, int g) {
+  if (DI == 128 || g < 2) {
+    const v4u* p = reinterpret_cast<const v4u*>(row + g * 32);
+    v4u a, b;
+    if (STREAM) {
+      a = __builtin_nontemporal_load(p);
+      b = __builtin_nontemporal_load(p + 1);
+    } else {
+      a = p[0];
+      b = p[1];
+    }
+    v8i v = {(int)a.x, (int)a.y, (int)a.z, (int)a.w,
+             (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    return v;
+  }
+  v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+  return z;
+}
+
+// NT: 16-row tiles of the [m * H_I][DI] query matrix; MT: query tokens m.
+template <int DI, int NT, int MT>
+__global__ __launch_bounds__(kThreads) void index_scores_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ keys, const int32_t* __restrict__ n_vis,
+    float* __restrict__ scores, int L, int HI) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;   // lane group: reduction slice / output rows
+  const int c = lane & 15;   // position within a 16-group / head row
+  const int b = blockIdx.y;
+
+  // Query tiles and head weights for this lane, resident in registers.
+  constexpr int kTilesPerTok = NT / MT;   // a 16-row tile never straddles tokens
+  v8i qa[NT];
+  float wv[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = t * 16 + c;                      // flattened (j, h)
+    qa[t] = load_piece<DI, false>(q + ((size_t)b * MT * HI + row) * DI, g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      wv[t][r] = w[(size_t)b * MT * HI + t * 16 + g * 4 + r];
+  }
+  int nv[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) nv[j] = n_vis[b * MT + j];
+
+  const uint8_t* kb = keys + (size_t)b * L * DI;
+  const int span0 = blockIdx.x * kSpan;
+  const int span1 = min(L, span0 + kSpan);
+
+  for (int p0 = span0 + wave * kGroups * 16; p0 < span1;
+       p0 += (kThreads / 64) * kGroups * 16) {
+    v8i kv[kGroups];
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      const int pos = min(p0 + u * 16 + c, L - 1);
+      kv[u] = load_piece<DI, true>(kb + (size_t)pos * DI, g);
+    }
+    float mine[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) mine[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      float part[MT];
+#pragma unroll
+      for (int j = 0; j < MT; ++j) part[j] = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qa[t], kv[u], acc, 0, 0, 0, 0, 0, 0);
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += wv[t][r] * fmaxf(acc[r], 0.f);
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+          if (t / kTilesPerTok == j) part[j] += s;
+      }
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        float v = part[j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g == u) mine[j] = v;   // lane group u stores group u
+      }
+    }
+    const int pos = p0 + g * 16 + c;
+    if (pos < span1) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        scores[((size_t)b * MT + j) * L + pos] =
+            pos < nv[j] ? mine[j] : -__builtin_inff();
+    }
+  }
+}
+
+template <int DI, int NT, int MT>
+hipError_t launch_t(const ess_dims& d, const uint8_t* q, const float* w,
+                    const uint8_t* k, const int32_t* n_vis, float* scores,
+                    hipStream_t s) {
+  dim3 grid((d.ctx_len + kSpan - 1) / kSpan, d.batch);
+  hipLaunchKernelGGL((index_scores_kernel<DI, NT, MT>), grid, dim3(kThreads),
+                     0, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
+                               const float* w, const uint8_t* k,
+                               const int32_t* n_vis, float* scores,
+                               hipStream_t s) {
+  // Shapes checked by the caller: DI in {64, 128}, H_I % 16 == 0,
+  // m * H_I <= 128.
+  const int rows = d.mtp * d.idx_heads;
+#define ESS_IDX_CASE(DI_, NT_, MT_)                                          \
+  if (d.idx_dim == DI_ && rows == NT_ * 16 && d.mtp == MT_)                 \
+    return launch_t<DI_, NT_, MT_>(d, q, w, k, n_vis, scores, s);
+#define ESS_IDX_ROWS(DI_)                                                    \
+  ESS_IDX_CASE(DI_, 1, 1) ESS_IDX_CASE(DI_, 2, 1) ESS_IDX_CASE(DI_, 3, 1)    \
+  ESS_IDX_CASE(DI_, 4, 1) ESS_IDX_CASE(DI_, 5, 1) ESS_IDX_CASE(DI_, 6, 1)    \
+  ESS_IDX_CASE(DI_, 7, 1) ESS_IDX_CASE(DI_, 8, 1) ESS_IDX_CASE(DI_, 2, 2)    \
+  ESS_IDX_CASE(DI_, 4, 2) ESS_IDX_CASE(DI_, 6, 2) ESS_IDX_CASE(DI_, 8, 2)    \
+  ESS_IDX_CASE(DI_, 3, 3) ESS_IDX_CASE(DI_, 6, 3) ESS_IDX_CASE(DI_, 4, 4)    \
+  ESS_IDX_CASE(DI_, 8, 4)
+  ESS_IDX_ROWS(64)
+  ESS_IDX_ROWS(128)
+#undef ESS_IDX_ROWS
+#undef ESS_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ess

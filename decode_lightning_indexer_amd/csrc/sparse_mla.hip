@@ -1,0 +1,281 @@
+// Gather of the selected latents + absorbed-MLA attention over them.
+//
+// Pages: the main attention reads only the top-k latent entries (c_KV[512]
+// + k^R each) and runs the core MLA on them (ESS concept page, "dual cache"
+// table).  The fused gather forks per row between a hit, read from the pool
+// in device memory, and a miss, read straight from pinned host memory; a
+// miss is written to its pool slot and to the on-chip tile together, three
+// memory accesses instead of four (FlashOffloading analysis, section
+// "forking inside KVgather").  Here the on-chip tile is LDS, so a miss costs
+// one host read plus one pool write and a hit one device read.
+//
+// Result independence from placement: the reduction runs over the selected
+// rows in rank order, in fixed chunks of rows combined in fixed order; no
+// atomics.  Which rows came from host memory changes no arithmetic.
+//
+// Per workgroup: one (request, token), 16 * NW heads (16 per wave), one
+// chunk of rows, walked in 32-row tiles staged in LDS twice - row-major for
+// the QK^T operand and transposed for the PV operand.
+//   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
+//                                           from LDS, B = Q from registers
+//   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T from LDS,
+//                                           B = P straight from registers
+// The S^T accumulator leaves each lane holding one head and 8 tokens; those
+// 8 tokens are exactly the lane's reduction slice of the PV operand, so P
+// never leaves registers (the V^T reads use the same token order).
+// Softmax runs in the log2 domain with a running max and sum per head.
+#include "ess_internal.h"
+
+#include <cstdlib>
+
+namespace ess {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 32;            // tokens per LDS tile
+constexpr int kKStride = kLat + 8;   // bf16 per row-major row (1168 B)
+constexpr int kVtStride = kTile + 4; // bf16 per transposed row (72 B)
+constexpr int kChunks16 = kLat / 8;  // 16-byte pieces per latent row (72)
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
+    const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
+    const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
+    const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ host, float* __restrict__ part_acc,
+    float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
+    int rows_per_chunk, int nchunk, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kVal * kVtStride];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int chunk = blockIdx.x, bj = blockIdx.z;
+  const int b = bj / m;
+  const int r0 = chunk * rows_per_chunk;
+  const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
+  const int h0 = blockIdx.y * (NW * 16) + wave * 16;
+
+  // Q fragments: lane holds Q[h0 + c][32 kk + 8 g .. + 8].
+  bf16x8 qf[kLat / 32];
+  {
+    const uint16_t* qrow = q_abs + ((size_t)bj * H + h0 + c) * kLat + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < kLat / 32; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32);
+  }
+
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  v4f oacc[kVal / 16];
+#pragma unroll
+  for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* rpos = sel_pos + (size_t)bj * k;
+  const int32_t* rsrc = sel_src + (size_t)bj * k;
+  const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
+  const uint16_t* pool_b = pool + (size_t)b * C * kLat;
+  const uint16_t* host_b = host + (size_t)b * L * kLat;
+  uint16_t* pool_w = pool + (size_t)b * C * kLat;
+
+  for (int t0 = r0; t0 < r1; t0 += kTile) {
+    __syncthreads();   // previous tile fully consumed
+    // Stage: each thread moves 16-byte pieces; consecutive threads take
+    // consecutive pieces of a row so global reads are contiguous.
+    for (int q = threadIdx.x; q < kTile * kChunks16; q += NW * 64) {
+      const int r = q / kChunks16, ch = q - r * kChunks16;
+      const int i = t0 + r;
+      v4u data = {0u, 0u, 0u, 0u};
+      if (i < r1) {
+        // Out-of-range slots or positions read as zeros (caller error).
+        const int src = rsrc[i];
+        const int pos = rpos[i];
+        const uint16_t* rowp = nullptr;
+        if (src >= 0) {
+          if (src < C) rowp = pool_b + (size_t)src * kLat;
+        } else if (pos >= 0 && pos < L) {
+          rowp = host_b + (size_t)pos * kLat;
+        }
+        if (rowp) data = *reinterpret_cast<const v4u*>(rowp + ch * 8);
+        if (rdst) {
+          const int dst = rdst[i];
+          if (dst >= 0 && dst < C)
+            *reinterpret_cast<v4u*>(pool_w + (size_t)dst * kLat + ch * 8) = data;
+        }
+      }
+      *reinterpret_cast<v4u*>(&krow[r * kKStride + ch * 8]) = data;
+      if (ch < kVal / 8) {
+        uint16_t* col = &vt[(ch * 8) * kVtStride + r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          col[e * kVtStride] = (uint16_t)(data[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+    __syncthreads();
+
+    // S^T for two 16-token halves of the tile.
+    v4f s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* arow = &krow[(mt * 16 + c) * kKStride + g * 8];
+#pragma unroll
+      for (int kk = 0; kk < kLat / 32; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + kk * 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc, 0, 0, 0);
+      }
+      s[mt] = acc;
+    }
+
+    // Online softmax for head h0 + c over this tile's tokens
+    // t0 + 16 mt + 4 g + r.
+    float z[8];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = t0 + (e >> 2) * 16 + g * 4 + (e & 3);
+      z[e] = tok < r1 ? s[e >> 2][e & 3] * scale_log2 : -__builtin_inff();
+      mx = fmaxf(mx, z[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = exp2f(z[e] - m_new);
+      psum += p;
+      pb[e] = (__bf16)p;
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // O^T += V^T P^T over the tile; V^T read in the lane's token order.
+#pragma unroll
+    for (int nt = 0; nt < kVal / 16; ++nt) {
+      const uint16_t* vr = &vt[(nt * 16 + c) * kVtStride];
+      const v2u lo = *reinterpret_cast<const v2u*>(vr + g * 4);
+      const v2u hi = *reinterpret_cast<const v2u*>(vr + 16 + g * 4);
+      const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt] * alpha,
+                                                         0, 0, 0);
+    }
+  }
+
+  // Unnormalised partial: O^T rows 16 nt + 4 g + r of head h0 + c.
+  float* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal;
+#pragma unroll
+  for (int nt = 0; nt < kVal / 16; ++nt)
+    *reinterpret_cast<v4f*>(pa + nt * 16 + g * 4) = oacc[nt];
+  if (g == 0)
+    part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(m_run, l_run);
+}
+
+// Merge the chunk partials of one (request, token, head) in chunk order.
+__global__ __launch_bounds__(128) void mla_combine_kernel(
+    const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
+    float* __restrict__ out, float* __restrict__ lse, int H, int nchunk) {
+  const int h = blockIdx.x, bj = blockIdx.y, t = threadIdx.x;
+  const float2* ml = part_ml + (size_t)bj * nchunk * H + h;
+  float M = -__builtin_inff();
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const float2 v = ml[(size_t)ci * H];
+    if (v.y > 0.f) M = fmaxf(M, v.x);
+  }
+  float den = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const float2 v = ml[(size_t)ci * H];
+    if (!(v.y > 0.f)) continue;
+    const float w = exp2f(v.x - M);
+    den += w * v.y;
+    const v4f a = *reinterpret_cast<const v4f*>(
+        part_acc + (((size_t)bj * nchunk + ci) * H + h) * kVal + t * 4);
+    acc += w * a;
+  }
+  const float inv = 1.f / den;
+  *reinterpret_cast<v4f*>(out + ((size_t)bj * H + h) * kVal + t * 4) = acc * inv;
+  if (lse && t == 0) lse[(size_t)bj * H + h] = (M + log2f(den)) * 0.69314718055994531f;
+}
+
+template <int NW>
+hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
+                    const int32_t* sel_pos, const int32_t* sel_src,
+                    const int32_t* row_dst, const int32_t* n_sel,
+                    uint16_t* pool, const uint16_t* host, float* part_acc,
+                    float2* part_ml, hipStream_t s) {
+  const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  dim3 grid(p.nchunk, p.head_groups, d.batch * d.mtp);
+  hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), 0, s, q,
+                     sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
+                     part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
+                     d.topk, p.rows_per_chunk, p.nchunk, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+MlaPlan plan_sparse_mla(const ess_dims& d) {
+  MlaPlan p;
+  const int H = d.mla_heads;
+  p.heads_per_wg = (H % 64 == 0) ? 64 : (H % 48 == 0) ? 48 : (H % 32 == 0) ? 32 : 16;
+  p.head_groups = H / p.heads_per_wg;
+  // Enough workgroups to cover the chip about twice; more chunks also mean
+  // more partial traffic, so stop there.
+  int target = 512;
+  if (const char* env = std::getenv("ESS_MLA_TARGET_WGS")) {
+    const int v = std::atoi(env);
+    if (v > 0) target = v;
+  }
+  const int base = d.batch * d.mtp * p.head_groups;
+  const int max_chunks = (d.topk + kTile - 1) / kTile;
+  int nchunk = (target + base - 1) / base;
+  if (nchunk < 1) nchunk = 1;
+  if (nchunk > max_chunks) nchunk = max_chunks;
+  const int per = (d.topk + nchunk - 1) / nchunk;
+  p.rows_per_chunk = (per + kTile - 1) / kTile * kTile;
+  p.nchunk = (d.topk + p.rows_per_chunk - 1) / p.rows_per_chunk;
+  return p;
+}
+
+size_t sparse_mla_ws_bytes(const ess_dims& d) {
+  const MlaPlan p = plan_sparse_mla(d);
+  const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
+  return align_up(parts * kVal * sizeof(float), 256) +
+         align_up(parts * sizeof(float2), 256);
+}
+
+hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
+                             const int32_t* sel_pos, const int32_t* sel_src,
+                             const int32_t* row_dst, const int32_t* n_sel,
+                             uint16_t* pool, const uint16_t* host,
+                             float* out, float* lse, void* ws,
+                             hipStream_t s) {
+  const MlaPlan p = plan_sparse_mla(d);
+  const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
+  float* part_acc = static_cast<float*>(ws);
+  float2* part_ml = reinterpret_cast<float2*>(
+      static_cast<char*>(ws) + align_up(parts * kVal * sizeof(float), 256));
+  hipError_t e;
+  switch (p.heads_per_wg / 16) {
+    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(d.mla_heads, d.batch * d.mtp),
+                     dim3(kVal / 4), 0, s, part_acc, part_ml, out, lse,
+                     d.mla_heads, p.nchunk);
+  return hipGetLastError();
+}
+
+}  // namespace ess

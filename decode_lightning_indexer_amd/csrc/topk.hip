@@ -1,0 +1,242 @@
+// Top-k selection per (request, query token) with the residency lookup read
+// off the winners.
+//
+// The pages fold the cache_slots lookup into the top-k itself by packing the
+// candidate's index and slot with its score into one int32 selection key
+// (FlashOffloading analysis, section "LIM: packing the index into the
+// score") and note that this caps sequence length and pool size.  At 1M
+// positions and 16K slots the pieces do not fit in 32 bits, so here the key
+// is 64 bits - the order-preserving score bits above the complemented
+// position (equal scores: lower position wins) - and the slot of each winner
+// is gathered in the same final pass that writes the winners.
+//
+// One 1024-thread workgroup per row (the rows are few: B * m):
+//   1. min and max of the order-preserving keys of the visible positions;
+//   2. radix passes of up to 11 bits starting at the highest bit where min
+//      and max differ, each narrowing the bin that holds the k-th key, until
+//      that bin holds at most `cap` keys (usually after one pass);
+//   3. one collect pass: keys above the bin are winners, keys in the bin are
+//      candidates; the candidates are sorted in LDS on the full 64-bit key
+//      and the best `need` of them join the winners.  If the bin is still
+//      too large after all 32 bits (a run of equal scores), the equal keys
+//      are taken in position order with a workgroup scan;
+//   4. bitonic sort of the k winners (rank order) and the emit pass.
+#include "block_util.h"
+#include "ess_internal.h"
+
+namespace ess {
+namespace {
+
+constexpr int NT = 1024;
+constexpr int kBins = 2048;
+constexpr size_t kLdsBudget = 160 * 1024 - 16 * 1024;  // leave static LDS room
+
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;          // -0 ranks as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t full_key(uint32_t ok, int pos) {
+  return ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)pos);
+}
+
+__device__ __forceinline__ bool above_fixed(uint32_t key, uint32_t prefix,
+                                            int lo_fixed) {
+  return ((uint64_t)key >> lo_fixed) > ((uint64_t)prefix >> lo_fixed);
+}
+__device__ __forceinline__ bool in_fixed(uint32_t key, uint32_t prefix,
+                                         int lo_fixed) {
+  return ((uint64_t)key >> lo_fixed) == ((uint64_t)prefix >> lo_fixed);
+}
+
+__global__ __launch_bounds__(NT) void topk_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
+    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
+    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
+    int n_tok, int k, int kpow2, int cap) {
+  extern __shared__ uint64_t smem[];
+  uint64_t* win = smem;              // kpow2 winners
+  uint64_t* cand = smem + kpow2;     // cap candidates
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t tmp[2 * (NT / 64) + 1];
+  __shared__ uint32_t s_nwin, s_ncand, s_bin_need, s_bin_cnt;
+  __shared__ int s_bin;
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / n_tok, j = row % n_tok;
+  const float* srow = scores + ((size_t)b * m + j) * L;
+  int n = n_vis[b * m + j];
+  n = n < 0 ? 0 : (n > L ? L : n);
+  const int keff = min(k, n);
+
+  if (tid == 0) {
+    s_nwin = 0;
+    s_ncand = 0;
+  }
+  if (keff == n) {
+    // Every visible position is selected.
+    for (int i = tid; i < kpow2; i += NT)
+      win[i] = i < n ? full_key(ord_key(srow[i]), i) : 0ull;
+    __syncthreads();
+  } else {
+    // 1. Range of the keys.
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = ord_key(srow[i]);
+      mn = min(mn, key);
+      mx = max(mx, key);
+    }
+    block_minmax<NT>(mn, mx, tmp);
+    // Bits at and above lo_fixed are common to every key in the bin that
+    // holds the k-th key; `prefix` carries them.
+    int lo_fixed = (mn == mx) ? 0 : 32 - __clz(mn ^ mx);
+    uint32_t prefix = mn;
+    uint32_t need = keff;      // keys still to take from the current bin
+    uint32_t cnt = n;          // keys in the current bin
+
+    // 2. Radix passes until the bin is small or the bits run out.
+    while (cnt > (uint32_t)cap && lo_fixed > 0) {
+      const int hi = lo_fixed - 1;
+      const int lo = hi >= 10 ? hi - 10 : 0;
+      const int nb = 1 << (hi - lo + 1);
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t key = ord_key(srow[i]);
+        if (in_fixed(key, prefix, lo_fixed))
+          atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      // Bins in descending order: thread t owns bins nb-1-2t and nb-2-2t.
+      uint32_t h0 = 0, h1 = 0;
+      const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
+      if (b0 >= 0) h0 = hist[b0];
+      if (b1 >= 0) h1 = hist[b1];
+      uint32_t tot;
+      const uint32_t above = block_exscan<NT>(h0 + h1, tmp, &tot);
+      if (b0 >= 0 && above < need && need <= above + h0) {
+        s_bin = b0;
+        s_bin_need = need - above;
+        s_bin_cnt = h0;
+      }
+      if (b1 >= 0 && above + h0 < need && need <= above + h0 + h1) {
+        s_bin = b1;
+        s_bin_need = need - above - h0;
+        s_bin_cnt = h1;
+      }
+      __syncthreads();
+      prefix = (prefix & ~(uint32_t)(((1ull << (hi + 1)) - 1))) |
+               ((uint32_t)s_bin << lo);
+      need = s_bin_need;
+      cnt = s_bin_cnt;
+      lo_fixed = lo;
+      __syncthreads();
+    }
+
+    // 3. Collect winners above the bin and the bin's candidates.
+    const bool sort_cands = cnt <= (uint32_t)cap;
+    uint32_t eq_taken = 0;  // ordered path: equal keys taken so far
+    for (int base = 0; base < n; base += NT * 4) {
+      uint32_t keys[4];
+      int n_eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = base + tid * 4 + e;
+        keys[e] = 0;
+        if (p < n) {
+          const uint32_t key = ord_key(srow[p]);
+          keys[e] = key;
+          // The counts guarantee at < kpow2 and at < cap; the checks only
+          // keep LDS writes in bounds if that ever failed.
+          if (above_fixed(key, prefix, lo_fixed)) {
+            const uint32_t at = atomicAdd(&s_nwin, 1u);
+            if (at < (uint32_t)kpow2) win[at] = full_key(key, p);
+          } else if (in_fixed(key, prefix, lo_fixed)) {
+            if (sort_cands) {
+              const uint32_t at = atomicAdd(&s_ncand, 1u);
+              if (at < (uint32_t)cap) cand[at] = full_key(key, p);
+            } else {
+              ++n_eq;
+            }
+          }
+        }
+      }
+      if (!sort_cands) {
+        // All keys in the bin are equal: take them in position order.
+        if (__syncthreads_count(n_eq) > 0) {
+          uint32_t tot;
+          uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &tot);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int p = base + tid * 4 + e;
+            if (p < n && in_fixed(keys[e], prefix, lo_fixed)) {
+              if (rank < need) {
+                const uint32_t at = atomicAdd(&s_nwin, 1u);
+                if (at < (uint32_t)kpow2) win[at] = full_key(keys[e], p);
+              }
+              ++rank;
+            }
+          }
+          eq_taken += tot;
+        }
+      }
+    }
+    __syncthreads();
+    if (sort_cands) {
+      const uint32_t nc = min(s_ncand, (uint32_t)cap);
+      const int cp = pow2_at_least_dev(nc);
+      for (int i = nc + tid; i < cp; i += NT) cand[i] = 0ull;
+      __syncthreads();
+      bitonic_sort_u64<NT, true>(cand, cp);
+      const uint32_t w0 = s_nwin;
+      for (uint32_t i = tid; i < need && i < nc && w0 + i < (uint32_t)kpow2; i += NT)
+        win[w0 + i] = cand[i];
+      __syncthreads();
+    }
+    for (int i = keff + tid; i < kpow2; i += NT) win[i] = 0ull;
+    __syncthreads();
+  }
+
+  // 4. Rank order and emit with the slot lookup.
+  bitonic_sort_u64<NT, true>(win, kpow2);
+  int32_t* op = sel_pos + ((size_t)b * n_tok + j) * k;
+  int32_t* os = sel_slot + ((size_t)b * n_tok + j) * k;
+  const int32_t* cs = cache_slots + (size_t)b * L;
+  for (int i = tid; i < k; i += NT) {
+    if (i < keff) {
+      const int pos = (int)(~(uint32_t)win[i]);
+      op[i] = pos;
+      os[i] = cs[pos];
+    } else {
+      op[i] = -1;
+      os[i] = -1;
+    }
+  }
+  if (tid == 0) n_sel[b * n_tok + j] = keff;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
+                       const float* scores, const int32_t* n_vis,
+                       const int32_t* cache_slots, int32_t* sel_pos,
+                       int32_t* sel_slot, int32_t* n_sel, hipStream_t s) {
+  const int kpow2 = pow2_at_least(k);
+  size_t cap = (kLdsBudget - (size_t)kpow2 * 8) / 8;
+  if (cap > 4096) cap = 4096;
+  int capp = 1;
+  while ((size_t)capp * 2 <= cap) capp <<= 1;
+  const size_t lds = ((size_t)kpow2 + capp) * sizeof(uint64_t);
+  hipError_t e = hipFuncSetAttribute((const void*)topk_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kLdsBudget);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_kernel, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                     scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
+                     d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
+  return hipGetLastError();
+}
+
+}  // namespace ess

@@ -1,0 +1,201 @@
+"""ctypes binding of libess.so: the C ABI declared in include/ess.h, one
+Python function per entry point with the same name.  Argument marshalling
+only: tensors pass their device addresses, streams their HIP handles; every
+step of the path runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or fails to load, every call raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libess.so")
+
+ESS_OK = 0
+ESS_ERR_INVALID = -1
+ESS_ERR_UNSUPPORTED = -2
+ESS_ERR_CAPACITY = -3
+ESS_ERR_HIP = -4
+ESS_ERR_NOMEM = -5
+
+ESS_MODE_FILL = 0
+ESS_MODE_INLINE = 1
+ESS_MODE_PREFETCH = 2
+
+EXPORTED = (
+    "ess_workspace_bytes", "ess_lru_state_bytes", "ess_pool_reset",
+    "ess_index_scores", "ess_topk_lookup", "ess_pool_update",
+    "ess_sparse_mla_decode", "ess_miss_copy", "ess_decode_step",
+    "ess_host_alloc", "ess_host_free", "ess_status_string", "ess_last_error",
+)
+
+
+class EssError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} -> {status}: {msg}")
+        self.status = status
+
+
+class ess_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("mtp", ctypes.c_int32),
+                ("ctx_len", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+                ("idx_dim", ctypes.c_int32), ("mla_heads", ctypes.c_int32),
+                ("lat_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("pool_slots", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+
+
+class ess_layer_io(ctypes.Structure):
+    _fields_ = [(n, _P) for n in (
+        "q_idx", "w_idx", "k_idx", "q_abs", "host_view", "pool",
+        "cache_slots", "slot_pos", "lru_state", "scores", "sel_pos",
+        "sel_slot", "n_sel", "row_dst", "sel_slot_post", "miss_pos",
+        "miss_slot", "n_miss", "n_evict", "out", "lse", "ws")] + [
+        ("ws_bytes", _S)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "or python decode_lightning_indexer_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(ess_dims)
+        sig = {
+            "ess_workspace_bytes": (_S, [D]),
+            "ess_lru_state_bytes": (_S, [D]),
+            "ess_pool_reset": (_I, [D, _P, _P, _P, _P]),
+            "ess_index_scores": (_I, [D, _P, _P, _P, _P, _P, _P]),
+            "ess_topk_lookup": (_I, [D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+            "ess_pool_update": (_I, [D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _P, _P]),
+            "ess_sparse_mla_decode": (_I, [D, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _S, _P]),
+            "ess_miss_copy": (_I, [D, _I, _P, _P, _P, _P, _P, _P]),
+            "ess_decode_step": (_I, [D, _I, ctypes.POINTER(ess_layer_io), _P,
+                                     _I, _P, _P]),
+            "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+            "ess_host_free": (_I, [_P]),
+            "ess_status_string": (ctypes.c_char_p, [_I]),
+            "ess_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn, st):
+    if st != ESS_OK:
+        L = lib()
+        raise EssError(fn, L.ess_status_string(st).decode(),
+                       L.ess_last_error().decode())
+
+
+def make_dims(batch, mtp, ctx_len, idx_heads, idx_dim, mla_heads, topk,
+              pool_slots, softmax_scale, lat_dim=576, v_dim=512) -> ess_dims:
+    return ess_dims(batch, mtp, ctx_len, idx_heads, idx_dim, mla_heads,
+                    lat_dim, v_dim, topk, pool_slots, softmax_scale)
+
+
+def ess_workspace_bytes(d: ess_dims) -> int:
+    return lib().ess_workspace_bytes(ctypes.byref(d))
+
+
+def ess_lru_state_bytes(d: ess_dims) -> int:
+    return lib().ess_lru_state_bytes(ctypes.byref(d))
+
+
+def ess_pool_reset(d, cache_slots, slot_pos, lru_state, stream=None):
+    _check("ess_pool_reset", lib().ess_pool_reset(
+        ctypes.byref(d), _ptr(cache_slots), _ptr(slot_pos), _ptr(lru_state),
+        _stream(stream)))
+
+
+def ess_index_scores(d, q_fp8, w, k_fp8, n_vis, scores, stream=None):
+    _check("ess_index_scores", lib().ess_index_scores(
+        ctypes.byref(d), _ptr(q_fp8), _ptr(w), _ptr(k_fp8), _ptr(n_vis),
+        _ptr(scores), _stream(stream)))
+
+
+def ess_topk_lookup(d, k, n_tok, scores, n_vis, cache_slots, sel_pos,
+                    sel_slot, n_sel, ws=None, ws_bytes=0, stream=None):
+    _check("ess_topk_lookup", lib().ess_topk_lookup(
+        ctypes.byref(d), k, n_tok, _ptr(scores), _ptr(n_vis),
+        _ptr(cache_slots), _ptr(sel_pos), _ptr(sel_slot), _ptr(n_sel),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ess_pool_update(d, k, n_tok, sel_pos, n_sel, cache_slots, slot_pos,
+                    lru_state, miss_pos, miss_slot, n_miss, n_evict, row_dst,
+                    sel_slot_post, stream=None):
+    _check("ess_pool_update", lib().ess_pool_update(
+        ctypes.byref(d), k, n_tok, _ptr(sel_pos), _ptr(n_sel),
+        _ptr(cache_slots), _ptr(slot_pos), _ptr(lru_state), _ptr(miss_pos),
+        _ptr(miss_slot), _ptr(n_miss), _ptr(n_evict), _ptr(row_dst),
+        _ptr(sel_slot_post), _stream(stream)))
+
+
+def ess_sparse_mla_decode(d, q_abs, sel_pos, sel_src, row_dst, n_sel, pool,
+                          host_view, out, lse, ws, ws_bytes, stream=None):
+    _check("ess_sparse_mla_decode", lib().ess_sparse_mla_decode(
+        ctypes.byref(d), _ptr(q_abs), _ptr(sel_pos), _ptr(sel_src),
+        _ptr(row_dst), _ptr(n_sel), _ptr(pool), _ptr(host_view), _ptr(out),
+        _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ess_miss_copy(d, list_stride, miss_pos, miss_slot, n_miss, host_view,
+                  pool, stream=None):
+    _check("ess_miss_copy", lib().ess_miss_copy(
+        ctypes.byref(d), list_stride, _ptr(miss_pos), _ptr(miss_slot),
+        _ptr(n_miss), _ptr(host_view), _ptr(pool), _stream(stream)))
+
+
+def ess_decode_step(d, layers, n_vis, mode, stream=None, side=None):
+    """layers: a sequence of ess_layer_io."""
+    arr = (ess_layer_io * len(layers))(*layers)
+    _check("ess_decode_step", lib().ess_decode_step(
+        ctypes.byref(d), len(layers), arr, _ptr(n_vis), mode,
+        _stream(stream), _stream(side) if side is not None else None))
+
+
+def ess_host_alloc(nbytes: int):
+    """Pinned, mapped host memory: returns (host address, device view)."""
+    h, dv = _P(), _P()
+    _check("ess_host_alloc", lib().ess_host_alloc(nbytes, ctypes.byref(h),
+                                                  ctypes.byref(dv)))
+    return h.value, dv.value
+
+
+def ess_host_free(host_ptr: int):
+    _check("ess_host_free", lib().ess_host_free(host_ptr))

@@ -1,0 +1,35 @@
+"""Drive whole decode steps over several layers through ess_decode_step.
+
+Holds one LayerBuffers per layer, the shared n_vis tensor and the streams
+(the caller's current stream, plus a second stream at default priority for
+the prefetch mode).  Plumbing only: each step is one ess_decode_step call.
+"""
+import torch
+
+from . import ess
+from .session import LayerBuffers
+
+
+class DecodeRunner:
+    def __init__(self, d: ess.ess_dims, hosts, device="cuda"):
+        self.d = d
+        self.layers = [LayerBuffers(d, h, device) for h in hosts]
+        self.n_vis = torch.empty((d.batch, d.mtp), dtype=torch.int32,
+                                 device=device)
+        self.side = torch.cuda.Stream(device=device)
+        self._ios = [lb.io() for lb in self.layers]
+
+    def set_n_vis(self, n_vis):
+        self.n_vis.copy_(torch.as_tensor(n_vis, dtype=torch.int32))
+
+    def reset(self):
+        for lb in self.layers:
+            lb.reset()
+
+    def fill(self, stream=None):
+        ess.ess_decode_step(self.d, self._ios, self.n_vis, ess.ESS_MODE_FILL,
+                            stream)
+
+    def step(self, mode=ess.ESS_MODE_INLINE, stream=None):
+        ess.ess_decode_step(self.d, self._ios, self.n_vis, mode, stream,
+                            self.side)

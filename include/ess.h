@@ -1,0 +1,254 @@
+/*
+ * ess.h - C ABI of the MI355X (gfx950) sparse-decode library.
+ *
+ * One decode step of DSA-style sparse attention over a latent cache whose
+ * authoritative copy lives in pinned host memory.  Per layer and per query
+ * token the step runs:
+ *   1. lightning-indexer scores over every cached position  (ess_index_scores)
+ *   2. top-k selection with the cache_slots lookup fused    (ess_topk_lookup)
+ *   3. residency update of the hot pool (union, victims,
+ *      pairing, cache_slots rewrite, copy list)              (ess_pool_update)
+ *   4+5. gather of the selected latents - hits from the pool
+ *      in device memory, misses straight from mapped host
+ *      memory - and absorbed-MLA attention over them         (ess_sparse_mla_decode)
+ * plus a standalone host->pool copy of a miss list (ess_miss_copy) and a
+ * whole-step entry point over several layers with side-stream prefetch
+ * (ess_decode_step).
+ *
+ * Sources: the ESS concept page ("ESS: Latent-Cache Offload", tables "dual
+ * cache" and "core mechanism") and the FlashOffloading analysis
+ * (hwcomputing.csdn.net; sections "cache_slots", "five steps and the MTP
+ * union", "LIM: packing the index into the score", "forking inside
+ * KVgather", Figs. 4-6).  Each call below names the passage it follows.
+ *
+ * Conventions for every call:
+ *   - All array arguments are device pointers (or, for host_view, the device
+ *     view of mapped pinned host memory from ess_host_alloc), owned by the
+ *     caller.  The library keeps no pointer after the call returns and
+ *     allocates no device memory in these calls; scratch space is a caller
+ *     workspace sized by ess_workspace_bytes.
+ *   - Arguments are checked on the host before anything is enqueued.  A
+ *     nonzero status means nothing was enqueued; ess_last_error() holds a
+ *     message.  The contents of the arrays are not checked (positions must be
+ *     < ctx_len, n_vis in [1, ctx_len]); a launch failure reported by the HIP
+ *     runtime returns ESS_ERR_HIP.
+ *   - Every call is asynchronous on the given stream; counts such as n_sel
+ *     and n_miss stay in device memory.
+ *   - Layouts are row-major with the listed shapes; "bf16" arrays are passed
+ *     as uint16_t bit patterns; fp8 arrays are OCP e4m3fn bytes.
+ */
+#ifndef ESS_H
+#define ESS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem shape of one layer.
+ *   batch      B  requests
+ *   mtp        m  query tokens per step per request (MTP ways sharing a pool)
+ *   ctx_len    L  cached positions per request
+ *   idx_heads  H_I indexer heads (multiple of 16; mtp*idx_heads <= 128)
+ *   idx_dim    d_I indexer dimension (64 or 128)
+ *   mla_heads  H  absorbed-MLA query heads (16, 32, 48, ... 128)
+ *   lat_dim    576 = c_KV[512] + k_R[64]
+ *   v_dim      512
+ *   topk       k  (1 .. 16384)
+ *   pool_slots C  hot-pool slots per request (mtp*topk <= C)
+ *   softmax_scale  multiplies the latent dot products before the softmax */
+typedef struct ess_dims {
+  int32_t batch, mtp, ctx_len, idx_heads, idx_dim, mla_heads;
+  int32_t lat_dim, v_dim, topk, pool_slots;
+  float softmax_scale;
+} ess_dims;
+
+typedef enum ess_status {
+  ESS_OK = 0,
+  ESS_ERR_INVALID = -1,      /* null pointer, bad size or count            */
+  ESS_ERR_UNSUPPORTED = -2,  /* shape outside what the kernels implement   */
+  ESS_ERR_CAPACITY = -3,     /* union of the ways could exceed the pool    */
+  ESS_ERR_HIP = -4,          /* HIP runtime error (launch or earlier fault) */
+  ESS_ERR_NOMEM = -5         /* host allocation failed / workspace too small */
+} ess_status;
+
+/* Bytes of workspace the calls below need for these dims (top-k scratch and
+ * the attention's split-row partials).  One workspace serves one stream at a
+ * time. */
+size_t ess_workspace_bytes(const ess_dims* d);
+
+/* Bytes of the opaque per-layer LRU state (B requests): per request a header,
+ * one recency stamp per slot and a ring of (slot, stamp) entries. */
+size_t ess_lru_state_bytes(const ess_dims* d);
+
+/* Empty pool: cache_slots[B][L] = -1, slot_pos[B][C] = -1, every slot free,
+ * recency ring empty.  Call before the first fill of a request batch. */
+ess_status ess_pool_reset(const ess_dims* d, int32_t* cache_slots,
+                          int32_t* slot_pos, void* lru_state,
+                          hipStream_t stream);
+
+/* Indexer scores (the indexer scores all L positions every step: ESS concept
+ * page, "dual cache" table; score form: the DSA lightning indexer):
+ *   scores[b][j][s] = sum_h w[b][j][h] * max(0, sum_d q[b][j][h][d] * k[b][s][d])
+ * for s < n_vis[b][j], and -inf for n_vis[b][j] <= s < L.
+ *   q_fp8   [B][m][H_I][d_I]  fp8 e4m3fn
+ *   w       [B][m][H_I]       float
+ *   k_fp8   [B][L][d_I]       fp8 e4m3fn (the resident index cache)
+ *   n_vis   [B][m]            int32 in [1, L]
+ *   scores  [B][m][L]         float (output)
+ * Accumulation is fp32 via fp8 MFMA; integer-valued inputs whose partial
+ * sums stay below 2^24 give exact integer scores. */
+ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
+                            const float* w, const uint8_t* k_fp8,
+                            const int32_t* n_vis, float* scores,
+                            hipStream_t stream);
+
+/* Top-k of each of the first n_tok query tokens of every request, with the
+ * residency lookup read off the winners (FlashOffloading analysis, section
+ * "LIM: packing the index into the score", 20-candidate example).
+ *   n_sel[b][j]    = min(k, n_vis[b][j])
+ *   sel_pos[b][j][i], i < n_sel: positions of the n_sel largest scores in
+ *                  rank order (score descending; equal scores: lower
+ *                  position first); -1 beyond n_sel
+ *   sel_slot[b][j][i] = cache_slots[b][sel_pos] before this step's update
+ *                  (-1: not resident); -1 beyond n_sel
+ * Inputs scores [B][m][L], n_vis [B][m], cache_slots [B][L]; outputs
+ * sel_pos, sel_slot [B][n_tok][k] and n_sel [B][n_tok].  1 <= n_tok <= m,
+ * 1 <= k <= 16384.  Scores must not be NaN.  ws: ess_workspace_bytes. */
+ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
+                           const float* scores, const int32_t* n_vis,
+                           const int32_t* cache_slots, int32_t* sel_pos,
+                           int32_t* sel_slot, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Residency update of the hot pool for one step (FlashOffloading analysis,
+ * section "five steps and the MTP union": lookup per way, union of the
+ * misses, as many victims as misses from the pool minus the union, one-to-one
+ * pairing and cache_slots rewrite; ESS concept page: LRU hot pool).  Per
+ * request b, with U = the union of sel_pos[b][j][0..n_sel) over j < n_tok:
+ *   misses M = positions of U not resident, ascending;
+ *   victims  = free slots in ascending order, then resident positions outside
+ *              U from the least-recently-used end (recency: the last update
+ *              whose union held the position; within one update, ascending
+ *              position order);
+ *   M[i] is paired with victim i: cache_slots[M[i]] = slot,
+ *   slot_pos[slot] = M[i]; evicted positions get cache_slots = -1.
+ * Outputs per request: miss_pos[b][i], miss_slot[b][i] for i < n_miss[b]
+ * (capacity n_tok*k entries per request, the copy list host -> pool),
+ * n_evict[b] (victims taken from resident positions), and per row
+ * [B][n_tok][k]: row_dst = the paired slot on the one row (smallest j, then
+ * its row) that is the designated writer of a miss, else -1;
+ * sel_slot_post = cache_slots after the update (-1 beyond n_sel).
+ * The first fill is this call with n_tok = 1, k = C on an empty pool: slot i
+ * receives the i-th smallest selected position.  Requires n_tok*k <= C
+ * (else ESS_ERR_CAPACITY).  Calls on one lru_state must be ordered. */
+ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
+                           const int32_t* sel_pos, const int32_t* n_sel,
+                           int32_t* cache_slots, int32_t* slot_pos,
+                           void* lru_state, int32_t* miss_pos,
+                           int32_t* miss_slot, int32_t* n_miss,
+                           int32_t* n_evict, int32_t* row_dst,
+                           int32_t* sel_slot_post, hipStream_t stream);
+
+/* Gather + absorbed-MLA attention over the selected latents (ESS concept
+ * page, "dual cache" table: only the top-k latents are read; FlashOffloading
+ * analysis, section "forking inside KVgather": hits from device memory, misses
+ * straight from pinned host memory, a miss written to its slot and the
+ * on-chip tile together).  For each b, j < m, h < H, over i < n_sel[b][j]:
+ *   row_i = pool[b][sel_src[i]] if sel_src[i] >= 0
+ *           else host_view[b][sel_pos[i]]            (576 bf16)
+ *   z_i   = softmax_scale * <q_abs[b][j][h], row_i>
+ *   out[b][j][h][:] = sum_i softmax(z)_i * row_i[0:512]
+ *   lse[b][j][h]    = log sum_i exp(z_i)                 (lse may be NULL)
+ * If row_dst is not NULL, a row with row_dst[i] >= 0 is also written to
+ * pool[b][row_dst[i]] (it must be a slot no selected row reads, as the slots
+ * from ess_pool_update are).  The reduction order is the rank order in fixed
+ * chunks combined in fixed order, so the result does not depend on which
+ * rows came from host memory.
+ *   q_abs [B][m][H][576] bf16; sel_pos, sel_src, row_dst [B][m][k];
+ *   n_sel [B][m]; pool [B][C][576] bf16; host_view [B][L][576] bf16;
+ *   out [B][m][H][512] float; lse [B][m][H] float. */
+ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
+                                 const int32_t* sel_pos,
+                                 const int32_t* sel_src,
+                                 const int32_t* row_dst, const int32_t* n_sel,
+                                 uint16_t* pool, const uint16_t* host_view,
+                                 float* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Copy a miss list from host memory into the pool (the pages' step 5, the
+ * H2D load of the copy triples; ESS concept page: small-block transfers of
+ * latent entries).  For each b and i < n_miss[b]:
+ *   pool[b][miss_slot[b*list_stride + i]] = host_view[b][miss_pos[b*list_stride + i]]
+ * Used for the first fill and for side-stream prefetch. */
+ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
+                         const int32_t* miss_pos, const int32_t* miss_slot,
+                         const int32_t* n_miss, const uint16_t* host_view,
+                         uint16_t* pool, hipStream_t stream);
+
+/* One layer's buffers for ess_decode_step.  Shapes as in the calls above;
+ * miss_pos/miss_slot hold max(m*k, C) entries per request (the fill needs C);
+ * sel_* and row_dst hold max(m*k, C) entries per request too. */
+typedef struct ess_layer_io {
+  const uint8_t* q_idx;       /* [B][m][H_I][d_I] fp8 */
+  const float* w_idx;         /* [B][m][H_I] */
+  const uint8_t* k_idx;       /* [B][L][d_I] fp8 */
+  const uint16_t* q_abs;      /* [B][m][H][576] bf16 */
+  const uint16_t* host_view;  /* [B][L][576] bf16, mapped pinned host */
+  uint16_t* pool;             /* [B][C][576] bf16 */
+  int32_t* cache_slots;       /* [B][L] */
+  int32_t* slot_pos;          /* [B][C] */
+  void* lru_state;            /* ess_lru_state_bytes */
+  float* scores;              /* [B][m][L] */
+  int32_t* sel_pos;           /* [B][m][k] (fill: [B][C]) */
+  int32_t* sel_slot;
+  int32_t* n_sel;             /* [B][m] */
+  int32_t* row_dst;           /* [B][m][k] (fill: [B][C]) */
+  int32_t* sel_slot_post;
+  int32_t* miss_pos;          /* [B][max(m*k, C)] */
+  int32_t* miss_slot;
+  int32_t* n_miss;            /* [B] */
+  int32_t* n_evict;           /* [B] */
+  float* out;                 /* [B][m][H][512] */
+  float* lse;                 /* [B][m][H] or NULL */
+  void* ws;                   /* ess_workspace_bytes, one per layer */
+  size_t ws_bytes;
+} ess_layer_io;
+
+enum {
+  ESS_MODE_FILL = 0,     /* first fill: top-C of token 0, empty-pool update,
+                            host -> pool copy; no attention                  */
+  ESS_MODE_INLINE = 1,   /* per layer on `stream`: scores, top-k, pool update,
+                            attention reading misses from host in-kernel     */
+  ESS_MODE_PREFETCH = 2  /* layer l+1's scores, top-k, update and miss copy
+                            run on `side` while layer l's attention runs on
+                            `stream`; attention then reads only the pool     */
+};
+
+/* A whole decode step over n_layers layers (ESS concept page: layer-wise
+ * compute/transfer overlap; the FlashOffloading analysis's decode layer
+ * order LIM -> CopySFA, Fig. 5).  n_vis [B][m] is shared by all layers.
+ * In ESS_MODE_PREFETCH, `side` must be a different stream from `stream`;
+ * on return all work is ordered before later work on `stream`. */
+ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
+                           const ess_layer_io* layers, const int32_t* n_vis,
+                           int32_t mode, hipStream_t stream,
+                           hipStream_t side);
+
+/* Pinned host memory mapped into the device address space (write-combined
+ * off; coarse-grained).  *host_ptr is the CPU address, *dev_view the address
+ * kernels use.  ESS_ERR_NOMEM on failure. */
+ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view);
+ess_status ess_host_free(void* host_ptr);
+
+const char* ess_status_string(ess_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* ess_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ESS_H */

@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports every entry point include/ess.h declares,
+and rejects bad arguments on the host before touching any GPU.  Runs
+without a GPU: every call here fails validation before its first HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_lightning_indexer_amd import ess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ess.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ess_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ess.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ess.EXPORTED)
+
+
+def _d(**kw):
+    base = dict(batch=2, mtp=1, ctx_len=4096, idx_heads=16, idx_dim=64,
+                mla_heads=16, topk=256, pool_slots=1024, softmax_scale=1 / 24)
+    base.update(kw)
+    return ess.make_dims(**base)
+
+
+P = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def _status(call):
+    with pytest.raises(ess.EssError) as e:
+        call()
+    return e.value.status
+
+
+def test_sizes(L):
+    d = _d()
+    assert ess.ess_workspace_bytes(d) > 0
+    lru = ess.ess_lru_state_bytes(d)
+    assert lru >= 2 * (32 + 4 * 1024 + 8 * 4 * 1024)
+    assert ess.ess_workspace_bytes(_d(lat_dim=512)) == 0
+
+
+def test_null_and_bad_sizes(L):
+    d = _d()
+    assert _status(lambda: ess.ess_index_scores(d, 0, P, P, P, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_pool_reset(d, P, 0, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_index_scores(_d(batch=0), P, P, P, P, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_miss_copy(d, 0, P, P, P, P, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_topk_lookup(d, 8, 2, P, P, P, P, P, P, stream=0)) == "invalid argument"
+    nan = _d(softmax_scale=float("nan"))
+    assert _status(lambda: ess.ess_miss_copy(nan, 8, P, P, P, P, P, stream=0)) == "invalid argument"
+
+
+def test_unsupported_shapes(L):
+    assert _status(lambda: ess.ess_index_scores(_d(idx_dim=96), P, P, P, P, P, stream=0)) == "unsupported shape"
+    assert _status(lambda: ess.ess_index_scores(_d(idx_heads=24), P, P, P, P, P, stream=0)) == "unsupported shape"
+    assert _status(lambda: ess.ess_index_scores(_d(mtp=2, idx_heads=128), P, P, P, P, P, stream=0)) == "unsupported shape"
+    assert _status(lambda: ess.ess_topk_lookup(_d(), 16385, 1, P, P, P, P, P, P, stream=0)) == "unsupported shape"
+    assert _status(lambda: ess.ess_sparse_mla_decode(_d(mla_heads=24), P, P, P, P, P, P, P, P, P, P, 1 << 30, stream=0)) == "unsupported shape"
+    assert _status(lambda: ess.ess_miss_copy(_d(lat_dim=512), 8, P, P, P, P, P, stream=0)) == "unsupported shape"
+
+
+def test_capacity(L):
+    d = _d(mtp=2, topk=600, pool_slots=1000)
+    st = _status(lambda: ess.ess_pool_update(d, 600, 2, P, P, P, P, P, P, P, P, P, P, P, stream=0))
+    assert st == "pool capacity exceeded"
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30)
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE, stream=0, side=1)) == "pool capacity exceeded"
+
+
+def test_workspace_too_small(L):
+    d = _d()
+    need = ess.ess_workspace_bytes(d)
+    st = _status(lambda: ess.ess_sparse_mla_decode(d, P, P, P, P, P, P, P, P, P, P, need - 1, stream=0))
+    assert st == "out of memory"
+    assert "workspace" in L.ess_last_error().decode()
+
+
+def test_decode_step_argument_checks(L):
+    d = _d()
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30)
+    bad = ess.ess_layer_io(*([P] * 5 + [0] + [P] * 16), 1 << 30)
+    assert _status(lambda: ess.ess_decode_step(d, [bad], P, ess.ESS_MODE_INLINE, stream=0, side=1)) == "invalid argument"
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, 7, stream=0, side=1)) == "invalid argument"
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_PREFETCH, stream=5, side=5)) == "invalid argument"
+    assert _status(lambda: ess.ess_decode_step(_d(pool_slots=20000, topk=256), [io], P, ess.ESS_MODE_FILL, stream=0, side=1)) == "unsupported shape"
+
+
+def test_status_strings(L):
+    for code, text in ((0, "ok"), (-3, "pool capacity exceeded"), (-4, "HIP runtime error")):
+        assert L.ess_status_string(code).decode() == text

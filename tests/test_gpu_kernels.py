@@ -1,0 +1,288 @@
+"""Per-call GPU parity against the CPU oracle: indexer scores and top-k
+bit-exact, pool updates bit-exact over step sequences, attention within the
+stated tolerance with miss write-back and placement invariance."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from decode_lightning_indexer_amd import ess
+from decode_lightning_indexer_amd.session import HostStore
+from oracle.attention import attend
+from oracle.indexer import index_scores
+from oracle.pool import HotPool
+from oracle.topk import topk_lookup
+from synth import gen
+from tests.gpu_util import assert_attn_close, dims, h, lse_close, sync, t
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------- indexer --
+
+@pytest.mark.parametrize("B,m,L,HI,dI,ragged", [
+    (1, 1, 4096, 16, 64, False),
+    (2, 1, 5000, 64, 128, False),
+    (2, 2, 3001, 64, 128, False),
+    (3, 1, 17, 16, 64, True),
+    (2, 1, 1500, 32, 128, True),
+    (1, 4, 777, 32, 64, True),
+])
+def test_index_scores_bit_exact(B, m, L, HI, dI, ragged):
+    rng = np.random.default_rng(L + B + m)
+    qi = rng.integers(-7, 8, (B, m, HI, dI))
+    ki = rng.integers(-7, 8, (B, L, dI))
+    w = rng.integers(1, 5, (B, m, HI)).astype(np.float32)
+    if ragged:
+        n_vis = rng.integers(1, L + 1, (B, m)).astype(np.int32)
+    else:
+        n_vis = np.array([[L - m + 1 + j for j in range(m)]] * B, np.int32)
+    q8, k8 = gen.encode_e4m3_int(qi), gen.encode_e4m3_int(ki)
+    d = dims(batch=B, mtp=m, ctx_len=L, idx_heads=HI, idx_dim=dI)
+    scores = torch.empty((B, m, L), dtype=torch.float32, device="cuda")
+    ess.ess_index_scores(d, t(q8), t(w), t(k8), t(n_vis), scores)
+    sync()
+    got = h(scores)
+    for b in range(B):
+        ref = index_scores(q8[b], w[b], k8[b], n_vis[b])
+        assert np.array_equal(got[b].astype(np.float64), ref), b
+
+
+# --------------------------------------------------------------- top-k --
+
+def _scores(kind, rng, shape):
+    if kind == "int_ties":
+        return rng.integers(0, 40, shape).astype(np.float32)
+    if kind == "indexer_like":
+        return np.rint(rng.normal(13000, 2500, shape)).clip(0).astype(np.float32)
+    if kind == "float":
+        return rng.standard_normal(shape).astype(np.float32)
+    if kind == "wide":
+        return (rng.lognormal(0, 8, shape) * rng.choice([-1, 1], shape)).astype(np.float32)
+    if kind == "equal":
+        return np.full(shape, 3.5, np.float32)
+    if kind == "zeros":
+        a = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), shape)
+        return a.astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind,B,m,n_tok,L,k,ragged", [
+    ("int_ties", 2, 1, 1, 5000, 256, False),
+    ("indexer_like", 4, 1, 1, 32768, 2048, False),
+    ("indexer_like", 2, 2, 2, 40000, 2048, True),
+    ("float", 2, 1, 1, 3000, 100, True),
+    ("wide", 2, 1, 1, 20000, 1000, False),
+    ("equal", 1, 1, 1, 10000, 300, False),
+    ("equal", 1, 1, 1, 3000, 2500, False),
+    ("zeros", 2, 1, 1, 7000, 512, False),
+    ("int_ties", 2, 1, 1, 100, 2048, True),       # k >= n_vis
+    ("indexer_like", 1, 2, 1, 30000, 16384, False),  # fill-size k, token 0 only
+    ("int_ties", 3, 1, 1, 1, 1, False),
+    ("float", 1, 3, 3, 2049, 7, True),
+])
+def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
+    rng = np.random.default_rng(zlib.crc32(f"{kind}-{L}-{k}".encode()))
+    s = _scores(kind, rng, (B, m, L))
+    if ragged:
+        n_vis = rng.integers(1, L + 1, (B, m)).astype(np.int32)
+    else:
+        n_vis = np.full((B, m), L, np.int32)
+    cs = np.where(rng.random((B, L)) < 0.5, rng.integers(0, 1 << 20, (B, L)), -1).astype(np.int32)
+    d = dims(batch=B, mtp=m, ctx_len=L, topk=min(k, 16384), pool_slots=16384)
+    sp = torch.empty((B, n_tok, k), dtype=torch.int32, device="cuda")
+    ss = torch.empty_like(sp)
+    ns = torch.empty((B, n_tok), dtype=torch.int32, device="cuda")
+    ess.ess_topk_lookup(d, k, n_tok, t(s), t(n_vis), t(cs), sp, ss, ns)
+    sync()
+    for b in range(B):
+        rp, rs, rn = topk_lookup(s[b, :n_tok].astype(np.float64), n_vis[b, :n_tok], k, cs[b])
+        assert np.array_equal(h(ns)[b], rn), b
+        assert np.array_equal(h(sp)[b], rp), b
+        assert np.array_equal(h(ss)[b], rs), b
+
+
+# ---------------------------------------------------------------- pool --
+
+def _ways(rng, L, m, k, prev, keep=0.85):
+    ways = []
+    for j in range(m):
+        kp = [p for p in prev[j] if rng.random() < keep] if prev else []
+        s = set(kp)
+        fresh = [p for p in rng.permutation(L)[:2 * k + 8].tolist() if p not in s]
+        w = (kp + fresh)[:k]
+        rng.shuffle(w)
+        ways.append(w)
+    return ways
+
+
+@pytest.mark.parametrize("B,m,L,C,k,steps,ragged", [
+    (2, 1, 3000, 256, 64, 30, False),
+    (2, 2, 5000, 512, 100, 25, True),
+    (1, 1, 500, 64, 16, 60, False),        # many steps: ring compaction
+    (3, 2, 4000, 300, 150, 12, False),     # union near capacity
+    (1, 1, 200, 400, 50, 10, False),       # pool larger than the context
+])
+def test_pool_update_bit_exact(B, m, L, C, k, steps, ragged):
+    rng = np.random.default_rng(B * 1000 + C)
+    d = dims(batch=B, mtp=m, ctx_len=L, topk=k, pool_slots=C)
+    cs = torch.empty((B, L), dtype=torch.int32, device="cuda")
+    sp = torch.empty((B, C), dtype=torch.int32, device="cuda")
+    lru = torch.empty(ess.ess_lru_state_bytes(d), dtype=torch.uint8, device="cuda")
+    ess.ess_pool_reset(d, cs, sp, lru)
+    lists = max(m * k, C)
+    mp = torch.empty(B * lists, dtype=torch.int32, device="cuda")
+    ms, rd, post = torch.empty_like(mp), torch.empty_like(mp), torch.empty_like(mp)
+    nm = torch.empty(B, dtype=torch.int32, device="cuda")
+    ne = torch.empty_like(nm)
+    pools = [HotPool(L, C) for _ in range(B)]
+
+    def run(kk, n_tok, sel, nsel):
+        ess.ess_pool_update(d, kk, n_tok, t(sel), t(nsel), cs, sp, lru, mp, ms,
+                            nm, ne, rd, post)
+        sync()
+        gm, gs = h(mp)[:B * n_tok * kk].reshape(B, -1), h(ms)[:B * n_tok * kk].reshape(B, -1)
+        grd = h(rd)[:B * n_tok * kk].reshape(B, n_tok, kk)
+        gpost = h(post)[:B * n_tok * kk].reshape(B, n_tok, kk)
+        for b in range(B):
+            r = pools[b].update(sel[b], nsel[b])
+            n = int(h(nm)[b])
+            assert n == r["n_miss"] and int(h(ne)[b]) == r["n_evict"], b
+            assert np.array_equal(gm[b, :n], r["miss_pos"]), b
+            assert np.array_equal(gs[b, :n], r["miss_slot"]), b
+            assert np.array_equal(grd[b], r["row_dst"]), b
+            assert np.array_equal(gpost[b], r["sel_slot_post"]), b
+            assert np.array_equal(h(cs)[b], pools[b].cache_slots), b
+            assert np.array_equal(h(sp)[b], pools[b].slot_pos), b
+
+    # Fill: one way of min(C, L) positions into the empty pool.
+    kf = min(C, L)
+    fill = np.stack([rng.permutation(L)[:kf] for _ in range(B)])[:, None, :].astype(np.int32)
+    run(kf, 1, fill, np.full((B, 1), kf, np.int32))
+    prev = [None] * B
+    for step in range(steps):
+        sel = np.full((B, m, k), -1, np.int32)
+        nsel = np.zeros((B, m), np.int32)
+        for b in range(B):
+            ways = _ways(rng, L, m, k, prev[b])
+            prev[b] = ways
+            for j in range(m):
+                n = int(rng.integers(1, k + 1)) if ragged else k
+                sel[b, j, :n] = ways[j][:n]
+                nsel[b, j] = n
+        run(k, m, sel, nsel)
+
+
+def test_pool_update_rejects_capacity():
+    d = dims(batch=1, mtp=2, ctx_len=100, topk=64, pool_slots=100)
+    z = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    with pytest.raises(ess.EssError) as e:
+        ess.ess_pool_update(d, 64, 2, z, z, z, z, z, z, z, z, z, z, z)
+    assert "capacity" in str(e.value)
+
+
+# ----------------------------------------------------------- attention --
+
+def _bf16(rng, shape, std):
+    return gen.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
+
+
+@pytest.mark.parametrize("B,m,H,L,k,C,ragged,p_hit", [
+    (1, 1, 16, 4096, 256, 1024, False, 0.8),
+    (2, 1, 64, 3000, 300, 1024, True, 0.5),
+    (2, 2, 128, 2000, 2048 // 4, 1200, True, 0.7),
+    (1, 1, 32, 500, 45, 100, False, 0.0),     # all misses
+    (1, 1, 48, 500, 33, 100, False, 1.0),     # all hits
+    (1, 2, 16, 100, 200, 400, True, 0.6),     # k > L: n_sel ragged below k
+])
+def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
+    rng = np.random.default_rng(H * 7 + k)
+    host = HostStore((B, L, 576))
+    host.array[:] = _bf16(rng, (B, L, 576), 0.5)
+    qa = _bf16(rng, (B, m, H, 576), 0.1)
+    n_sel = np.zeros((B, m), np.int32)
+    sel = np.full((B, m, k), -1, np.int32)
+    src = np.full((B, m, k), -1, np.int32)
+    dst = np.full((B, m, k), -1, np.int32)
+    pool = np.zeros((B, C, 576), np.uint16)
+    for b in range(B):
+        slot_of = {}
+        free = list(rng.permutation(C))
+        for j in range(m):
+            n = int(rng.integers(1, min(k, L) + 1)) if ragged else min(k, L)
+            n_sel[b, j] = n
+            pos = rng.permutation(L)[:n]
+            sel[b, j, :n] = pos
+            for i, p in enumerate(pos.tolist()):
+                if p not in slot_of:
+                    hit = rng.random() < p_hit
+                    s = free.pop()
+                    slot_of[p] = (s, hit)
+                    if hit:
+                        pool[b, s] = host.array[b, p]
+                    else:
+                        dst[b, j, i] = s       # designated writer
+                s, hit = slot_of[p]
+                src[b, j, i] = s if hit else -1
+    d = dims(batch=B, mtp=m, ctx_len=L, mla_heads=H, topk=k, pool_slots=C)
+    ws_bytes = ess.ess_workspace_bytes(d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    pool_t = t(pool)
+    out = torch.empty((B, m, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, m, H), dtype=torch.float32, device="cuda")
+    ess.ess_sparse_mla_decode(d, t(qa), t(sel), t(src), t(dst), t(n_sel),
+                              pool_t, host.dev, out, lse, ws, ws_bytes)
+    sync()
+    got, glse = h(out), h(lse)
+    for b in range(B):
+        for j in range(m):
+            n = n_sel[b, j]
+            ref, rlse = attend(qa[b, j], host.array[b, sel[b, j, :n]], 1 / 24)
+            assert_attn_close(got[b, j], ref, (b, j))
+            lse_close(glse[b, j], rlse, (b, j))
+    # Misses landed in their slots, bit for bit.
+    gp = h(pool_t)
+    for b in range(B):
+        for j in range(m):
+            for i in np.nonzero(dst[b, j] >= 0)[0]:
+                assert np.array_equal(gp[b, dst[b, j, i]], host.array[b, sel[b, j, i]])
+    # Placement invariance: every row now read from the pool.
+    src2 = src.copy()
+    for b in range(B):
+        slot_of = {}
+        for j in range(m):
+            for i in range(n_sel[b, j]):
+                if dst[b, j, i] >= 0:
+                    slot_of[sel[b, j, i]] = dst[b, j, i]
+        for j in range(m):
+            for i in range(n_sel[b, j]):
+                if src2[b, j, i] < 0:
+                    src2[b, j, i] = slot_of[sel[b, j, i]]
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    ess.ess_sparse_mla_decode(d, t(qa), t(sel), t(src2), None, t(n_sel),
+                              pool_t, host.dev, out2, lse2, ws, ws_bytes)
+    sync()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    host.free()
+
+
+def test_miss_copy():
+    rng = np.random.default_rng(3)
+    B, L, C, n = 2, 1000, 300, 77
+    host = HostStore((B, L, 576))
+    host.array[:] = _bf16(rng, (B, L, 576), 0.5)
+    d = dims(batch=B, ctx_len=L, pool_slots=C)
+    mp = np.stack([rng.permutation(L)[:n] for _ in range(B)]).astype(np.int32)
+    ms = np.stack([rng.permutation(C)[:n] for _ in range(B)]).astype(np.int32)
+    nm = np.array([n, n // 2], np.int32)
+    pool = torch.zeros((B, C, 576), dtype=torch.int16, device="cuda")
+    ess.ess_miss_copy(d, n, t(mp), t(ms), t(nm), host.dev, pool)
+    sync()
+    gp = h(pool)
+    for b in range(B):
+        assert np.array_equal(gp[b, ms[b, :nm[b]]], host.array[b, mp[b, :nm[b]]])
+        untouched = np.setdiff1d(np.arange(C), ms[b, :nm[b]])
+        assert not gp[b, untouched].any()
+    host.free()
