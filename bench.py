@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of one sparse decode step over a host-offloaded latent cache.
+
+Workload: 32K context, 16 requests, one query token per step, 64x128 fp8
+indexer, top-2048, 128-head absorbed MLA over 576-wide bf16 latents, a hot
+pool of 8192 slots per request, latents in pinned host memory, misses read
+inside the attention kernel.  One step = indexer scores -> top-k with the
+slot lookup -> pool update -> fused hit/miss gather + attention (+ combine),
+for all 16 requests.  All per-step inputs (the drifting indexer queries and
+the absorbed queries) are staged in device memory before the timed region;
+the pool's first fill runs before the warm-up steps.
+
+Prints one JSON line.  Per-stage times come from HIP events recorded on the
+launch stream between the stages of every timed step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=32)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--workload", default="32k-b16")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget for the oracle CPU baseline (0 = skip)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle, as is, on request 0 of the same workload for as many
+    steps as fit in about `seconds` (at least one)."""
+    import numpy as np
+    from oracle import decode as odecode
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    it = odecode.run_workload_request(wl, 0, 0, check_pool=False)
+    next(it)                                  # the fill (untimed)
+    n, t0 = 0, time.perf_counter()
+    for rec in it:
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * wl.mtp / dt, "unit": "query-tok/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"request 0 of {wl.name}, {n} steady-state steps "
+                      f"(fill excluded), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (requests shard across GPUs with no exchange; see "
+              "the design notes)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
+    from synth import gen, get_workload
+
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    base = get_workload(args.workload)
+    wl = base.with_(steps=W + K)
+    B, m, L, k, C, H = wl.batch, wl.mtp, wl.ctx_len, wl.topk, wl.pool_slots, wl.mla_heads
+    d = dims_of(wl)
+    dev = "cuda"
+
+    t_gen = time.perf_counter()
+    host = HostStore((B, L, 576))
+    gen.fill_latents(wl, 0, host.array)
+    lb = LayerBuffers(d, host)
+    kb = np.empty((B, L, wl.idx_dim), np.uint8)
+    gen.fill_index_keys(wl, 0, kb)
+    lb.k_idx.copy_(torch.from_numpy(kb))
+    del kb
+    q_all, w, n_vis_np = gen.index_inputs(wl, 0)
+    lb.w_idx.copy_(torch.from_numpy(w))
+    q_idx = torch.from_numpy(q_all).to(dev)                     # [T][B][m][HI][dI]
+    q_abs = torch.empty((W + K, B, m, H, 576), dtype=torch.int16, device=dev)
+    for t in range(W + K):
+        q_abs[t].copy_(torch.from_numpy(gen.abs_query(wl, 0, t).view(np.int16)))
+    n_vis = torch.from_numpy(n_vis_np).to(dev)
+    torch.cuda.synchronize()
+    log(args, f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    lists = m * k
+    sel_pos = lb.rows(lb.sel_pos, k, m)
+    sel_slot = lb.rows(lb.sel_slot, k, m)
+    row_dst = lb.rows(lb.row_dst, k, m)
+    post = lb.rows(lb.sel_slot_post, k, m)
+
+    n_miss_all = torch.zeros((W + K, B), dtype=torch.int32, device=dev)
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ess.ess_index_scores(d, q_idx[t], lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos,
+                            sel_slot, lb.n_sel, None, 0, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos,
+                            lb.lru, lb.miss_pos, lb.miss_slot, n_miss_all[t], lb.n_evict,
+                            row_dst, post, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
+                                  lb.pool, host.dev, lb.out, lb.lse, lb.ws,
+                                  lb.ws_bytes, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # First fill (top-C of token 0 at step 0 into the empty pool), untimed.
+    lb.reset(stream)
+    lb.q_idx.copy_(q_idx[0])
+    ess.ess_decode_step(d, [lb.io()], n_vis, ess.ESS_MODE_FILL, stream)
+    torch.cuda.synchronize()
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = np.zeros(4)
+    for e in evs:
+        for s in range(4):
+            stage_ms[s] += e[s].elapsed_time(e[s + 1])
+    stage_us = stage_ms / K * 1e3
+    n_miss_tot = int(n_miss_all[W:].sum())
+
+    # The same steps without the per-stage events, as one call per step.
+    lb.reset(stream)
+    lb.q_idx.copy_(q_idx[0])
+    ess.ess_decode_step(d, [lb.io()], n_vis, ess.ESS_MODE_FILL, stream)
+    ios = []
+    for t in range(W + K):
+        io = lb.io()
+        io.q_idx = q_idx[t].data_ptr()
+        io.q_abs = q_abs[t].data_ptr()
+        ios.append([io])
+    for t in range(W):
+        ess.ess_decode_step(d, ios[t], n_vis, ess.ESS_MODE_INLINE, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        ess.ess_decode_step(d, ios[W + i], n_vis, ess.ESS_MODE_INLINE, stream)
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t1
+
+    # Algorithmic bytes / flops per launch.
+    idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
+    idx_flop = 2 * B * m * wl.idx_heads * wl.idx_dim * L
+    sel_bytes = B * m * k * 1152
+    attn_flop = 2 * B * m * H * k * (576 + 512)
+    attn_bytes = sel_bytes + B * m * H * (576 * 2 + 512 * 4)
+    names = ["index_scores", "topk_lookup", "pool_update", "sparse_mla_decode"]
+    dom = int(np.argmax(stage_us))
+    if dom == 0:
+        roof = {"kernel": names[0], "bound": "hbm",
+                "achieved": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None}
+    elif dom == 3:
+        roof = {"kernel": names[3], "bound": "hbm",
+                "achieved": attn_bytes / (stage_us[3] * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None}
+    else:
+        roof = {"kernel": names[dom], "bound": "alu",
+                "achieved": None, "peak": None, "unit": "us", "traffic": None}
+    if roof.get("achieved") is not None:
+        roof["frac"] = roof["achieved"] / roof["peak"]
+
+    steps_per_s = K / wall
+    res = {
+        "metric": "sparse decode steps/s & query-tok/s at 32K/128K; indexer HBM GB/s; miss-fetch GB/s",
+        "value": B * m * K / wall,
+        "unit": "query-tok/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": base.name,
+                   "batch": B, "mtp": m, "ctx_len": L, "idx_heads": wl.idx_heads,
+                   "idx_dim": wl.idx_dim, "topk": k, "mla_heads": H,
+                   "pool_slots": C, "rho": wl.rho, "miss_mode": "inline"},
+        "steps_per_s": steps_per_s,
+        "steps_per_s_one_call": K / wall_plain,
+        "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
+        "indexer_gbps": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
+        "attention_tflops": attn_flop / (stage_us[3] * 1e-6) / 1e12,
+        "misses_per_step": n_miss_tot / K,
+        "miss_rate": n_miss_tot / (K * B * m * k),
+        "miss_fetch_gbps": n_miss_tot * 1152 / K / (stage_us[3] * 1e-6) / 1e9,
+        "roofline": roof,
+    }
+    if args.cpu_seconds > 0:
+        log(args, "timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+    host.free()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
