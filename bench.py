@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+PCIE5_X16_GBPS = 64.0          # published host-link rate per direction
 
 
 def parse():
@@ -45,27 +46,34 @@ def log(args, *a):
 
 
 def cpu_baseline(wl, seconds):
-    """The oracle, as is, on request 0 of the same workload for as many
-    steps as fit in about `seconds` (at least one)."""
-    import numpy as np
+    """The oracle, as is, on the same workload: requests 0, 1, ... each run
+    from its fill through its steps, until about `seconds` of step time
+    (fill and input generation excluded) have been spent."""
     from oracle import decode as odecode
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    it = odecode.run_workload_request(wl, 0, 0, check_pool=False)
-    next(it)                                  # the fill (untimed)
-    n, t0 = 0, time.perf_counter()
-    for rec in it:
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
+    n, spent, reqs = 0, 0.0, 0
+    for b in range(wl.batch):
+        it = odecode.run_workload_request(wl, 0, b, check_pool=False)
+        next(it)                                  # the fill (untimed)
+        reqs += 1
+        while spent < seconds:
+            t0 = time.perf_counter()
+            try:
+                next(it)
+            except StopIteration:
+                break
+            spent += time.perf_counter() - t0
+            n += 1
+        if spent >= seconds:
             break
-    dt = time.perf_counter() - t0
-    return {"value": n * wl.mtp / dt, "unit": "query-tok/s", "cores": int(cores),
+    return {"value": n * wl.mtp / spent, "unit": "query-tok/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"request 0 of {wl.name}, {n} steady-state steps "
-                      f"(fill excluded), {dt:.1f} s"}
+            "sample": f"{n} request-steps of {wl.name} (requests 0..{reqs - 1}, "
+                      f"fill excluded), {spent:.1f} s of step time"}
 
 
 def main():
@@ -84,8 +92,9 @@ def main():
 
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
+    n_ov = min(8, K)                       # extra steps for the overlap split
     base = get_workload(args.workload)
-    wl = base.with_(steps=W + K)
+    wl = base.with_(steps=W + K + n_ov)
     B, m, L, k, C, H = wl.batch, wl.mtp, wl.ctx_len, wl.topk, wl.pool_slots, wl.mla_heads
     d = dims_of(wl)
     dev = "cuda"
@@ -101,8 +110,8 @@ def main():
     q_all, w, n_vis_np = gen.index_inputs(wl, 0)
     lb.w_idx.copy_(torch.from_numpy(w))
     q_idx = torch.from_numpy(q_all).to(dev)                     # [T][B][m][HI][dI]
-    q_abs = torch.empty((W + K, B, m, H, 576), dtype=torch.int16, device=dev)
-    for t in range(W + K):
+    q_abs = torch.empty((wl.steps, B, m, H, 576), dtype=torch.int16, device=dev)
+    for t in range(wl.steps):
         q_abs[t].copy_(torch.from_numpy(gen.abs_query(wl, 0, t).view(np.int16)))
     n_vis = torch.from_numpy(n_vis_np).to(dev)
     torch.cuda.synchronize()
@@ -115,7 +124,7 @@ def main():
     row_dst = lb.rows(lb.row_dst, k, m)
     post = lb.rows(lb.sel_slot_post, k, m)
 
-    n_miss_all = torch.zeros((W + K, B), dtype=torch.int32, device=dev)
+    n_miss_all = torch.zeros((wl.steps, B), dtype=torch.int32, device=dev)
 
     def step(t, ev=None):
         if ev is not None:
@@ -182,6 +191,52 @@ def main():
     torch.cuda.synchronize()
     wall_plain = time.perf_counter() - t1
 
+    # Overlap on the same steps' miss lists (the pages' OverlapRatio):
+    # T_fused = attention reading misses from host inside the kernel,
+    # T_copy  = the miss list copied host -> pool alone,
+    # T_attn  = attention with every row read from the pool.
+    ev_ov = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ov)]
+    t_ov = np.zeros(3)
+    miss_ov = 0
+    for i in range(n_ov):
+        t = W + K + i
+        ess.ess_index_scores(d, q_idx[t], lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
+        ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos,
+                            sel_slot, lb.n_sel, None, 0, stream)
+        ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos,
+                            lb.lru, lb.miss_pos, lb.miss_slot, lb.n_miss, lb.n_evict,
+                            row_dst, post, stream)
+        e = ev_ov[i]
+        e[0].record(stream)
+        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
+                                  lb.pool, host.dev, lb.out, lb.lse, lb.ws,
+                                  lb.ws_bytes, stream)
+        e[1].record(stream)
+        ess.ess_miss_copy(d, lists, lb.miss_pos, lb.miss_slot, lb.n_miss, host.dev,
+                          lb.pool, stream)
+        e[2].record(stream)
+        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, post, None, lb.n_sel,
+                                  lb.pool, host.dev, lb.out, lb.lse, lb.ws,
+                                  lb.ws_bytes, stream)
+        e[3].record(stream)
+        miss_ov += int(lb.n_miss.sum())
+    torch.cuda.synchronize()
+    for e in ev_ov:
+        t_ov += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+    t_fused, t_copy, t_attn = t_ov / n_ov * 1e3          # us
+    overlap = (t_copy + t_attn - t_fused) / t_copy if t_copy > 0 else None
+    overlap_bound = min(1.0, t_attn / t_copy) if t_copy > 0 else None
+
+    # Host-link ceiling: the copy kernel over every row of the pool.
+    ev_h = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    all_pos = torch.arange(C, dtype=torch.int32, device=dev).repeat(B)
+    all_n = torch.full((B,), C, dtype=torch.int32, device=dev)
+    ev_h[0].record(stream)
+    ess.ess_miss_copy(d, C, all_pos, all_pos, all_n, host.dev, lb.pool, stream)
+    ev_h[1].record(stream)
+    torch.cuda.synchronize()
+    host_gbps = B * C * 1152 / (ev_h[0].elapsed_time(ev_h[1]) * 1e-3) / 1e9
+
     # Algorithmic bytes / flops per launch.
     idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
     idx_flop = 2 * B * m * wl.idx_heads * wl.idx_dim * L
@@ -189,20 +244,27 @@ def main():
     attn_flop = 2 * B * m * H * k * (576 + 512)
     attn_bytes = sel_bytes + B * m * H * (576 * 2 + 512 * 4)
     names = ["index_scores", "topk_lookup", "pool_update", "sparse_mla_decode"]
+    miss_bytes = n_miss_tot * 1152 / K
+    t_attn_bound = max(sel_bytes / (HBM_PEAK_GBPS * 1e3), miss_bytes / (host_gbps * 1e3),
+                       attn_flop / (BF16_PEAK_TFLOPS * 1e6))            # us
+    roofs = {
+        "index_scores": {"bound": "hbm", "achieved": idx_bytes / (stage_us[0] * 1e3),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "bytes_per_launch": idx_bytes},
+        "sparse_mla_decode": {"bound": "host-link" if miss_bytes / (host_gbps * 1e3) >= sel_bytes / (HBM_PEAK_GBPS * 1e3) else "hbm",
+                              "achieved": miss_bytes / (stage_us[3] * 1e3),
+                              "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                              "bytes_per_launch": miss_bytes,
+                              "measured_ceiling": host_gbps,
+                              "frac_of_bound": t_attn_bound / stage_us[3]},
+    }
+    for r in roofs.values():
+        r["frac"] = r["achieved"] / r["peak"]
     dom = int(np.argmax(stage_us))
-    if dom == 0:
-        roof = {"kernel": names[0], "bound": "hbm",
-                "achieved": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None}
-    elif dom == 3:
-        roof = {"kernel": names[3], "bound": "hbm",
-                "achieved": attn_bytes / (stage_us[3] * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None}
-    else:
-        roof = {"kernel": names[dom], "bound": "alu",
-                "achieved": None, "peak": None, "unit": "us", "traffic": None}
-    if roof.get("achieved") is not None:
-        roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = dict(roofs.get(names[dom], {"bound": "alu", "achieved": None, "peak": None,
+                                        "unit": "us", "frac": None}))
+    roof["kernel"] = names[dom]
+    roof["traffic"] = None
 
     steps_per_s = K / wall
     res = {
@@ -225,7 +287,12 @@ def main():
         "misses_per_step": n_miss_tot / K,
         "miss_rate": n_miss_tot / (K * B * m * k),
         "miss_fetch_gbps": n_miss_tot * 1152 / K / (stage_us[3] * 1e-6) / 1e9,
+        "host_link_gbps_measured": host_gbps,
+        "overlap": {"t_copy_us": t_copy, "t_attn_us": t_attn, "t_fused_us": t_fused,
+                    "ratio": overlap, "bound": overlap_bound,
+                    "misses_per_step": miss_ov / n_ov},
         "roofline": roof,
+        "rooflines": roofs,
     }
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")

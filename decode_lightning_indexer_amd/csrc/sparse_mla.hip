@@ -13,6 +13,21 @@
 // rows in rank order, in fixed chunks of rows combined in fixed order; no
 // atomics.  Which rows came from host memory changes no arithmetic.
 //
+// Miss handling on MI355X: a miss costs a host-link read (~55 GB/s) against
+// an HBM read for a hit (8 TB/s), so the host link sets the pace.  The pages
+// put the misses at the head of the selection so that one tile in four
+// touches host memory (same section).  Here the same idea works at two
+// levels, neither of which changes the arithmetic:
+//   * chunks are dispatched from the lowest ranks up - new entries enter the
+//     top-k near the cut, so the low-rank chunks hold most misses and start
+//     their host reads first;
+//   * a workgroup first streams every designated-writer miss row of its chunk
+//     from host memory into its pool slot, all rows in flight at once, then
+//     walks its tiles reading every row from device memory.  A miss row that
+//     another token's workgroup writes (MTP ways sharing a miss) is read from
+//     host memory in the tile loop instead, so no workgroup waits on another.
+// Two workgroups per CU keep the MFMA busy while the other waits on the link.
+//
 // Per workgroup: one (request, token), 16 * NW heads (16 per wave), one
 // chunk of rows, walked in 32-row tiles staged in LDS twice - row-major for
 // the QK^T operand and transposed for the PV operand.
@@ -41,8 +56,11 @@ constexpr int kKStride = kLat + 8;   // bf16 per row-major row (1168 B)
 constexpr int kVtStride = kTile + 4; // bf16 per transposed row (72 B)
 constexpr int kChunks16 = kLat / 8;  // 16-byte pieces per latent row (72)
 
+constexpr int kMaxChunkRows = 512;   // miss-row list capacity per chunk
+constexpr int kPrefetchBatch = 8;    // 16-byte host loads in flight per thread
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
+__global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
@@ -52,13 +70,57 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVal * kVtStride];
 
+  __shared__ int mrow[kMaxChunkRows];
+  __shared__ int s_nmiss;
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int chunk = blockIdx.x, bj = blockIdx.z;
+  const int chunk = nchunk - 1 - (int)blockIdx.z;   // lowest ranks first
+  const int bj = blockIdx.y;
   const int b = bj / m;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
-  const int h0 = blockIdx.y * (NW * 16) + wave * 16;
+  const int h0 = blockIdx.x * (NW * 16) + wave * 16;
+
+  const int32_t* rpos = sel_pos + (size_t)bj * k;
+  const int32_t* rsrc = sel_src + (size_t)bj * k;
+  const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
+  const uint16_t* pool_b = pool + (size_t)b * C * kLat;
+  const uint16_t* host_b = host + (size_t)b * L * kLat;
+  uint16_t* pool_w = pool + (size_t)b * C * kLat;
+
+  // Miss prefetch: this chunk's designated-writer miss rows, host -> slot.
+  if (rdst) {
+    if (threadIdx.x == 0) s_nmiss = 0;
+    __syncthreads();
+    for (int i = r0 + threadIdx.x; i < r1; i += NW * 64) {
+      const int dst = rdst[i], pos = rpos[i];
+      if (rsrc[i] < 0 && dst >= 0 && dst < C && pos >= 0 && pos < L)
+        mrow[atomicAdd(&s_nmiss, 1)] = i;
+    }
+    __syncthreads();
+    const int npieces = s_nmiss * kChunks16;
+    for (int q0 = threadIdx.x; q0 < npieces; q0 += NW * 64 * kPrefetchBatch) {
+      v4u buf[kPrefetchBatch];
+#pragma unroll
+      for (int u = 0; u < kPrefetchBatch; ++u) {
+        const int q = q0 + u * NW * 64;
+        if (q < npieces) {
+          const int i = mrow[q / kChunks16], ch = q % kChunks16;
+          buf[u] = *reinterpret_cast<const v4u*>(host_b + (size_t)rpos[i] * kLat + ch * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPrefetchBatch; ++u) {
+        const int q = q0 + u * NW * 64;
+        if (q < npieces) {
+          const int i = mrow[q / kChunks16], ch = q % kChunks16;
+          *reinterpret_cast<v4u*>(pool_w + (size_t)rdst[i] * kLat + ch * 8) = buf[u];
+        }
+      }
+    }
+    __threadfence_block();
+  }
 
   // Q fragments: lane holds Q[h0 + c][32 kk + 8 g .. + 8].
   bf16x8 qf[kLat / 32];
@@ -74,13 +136,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
   for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* rpos = sel_pos + (size_t)bj * k;
-  const int32_t* rsrc = sel_src + (size_t)bj * k;
-  const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
-  const uint16_t* pool_b = pool + (size_t)b * C * kLat;
-  const uint16_t* host_b = host + (size_t)b * L * kLat;
-  uint16_t* pool_w = pool + (size_t)b * C * kLat;
-
   for (int t0 = r0; t0 < r1; t0 += kTile) {
     __syncthreads();   // previous tile fully consumed
     // Stage: each thread moves 16-byte pieces; consecutive threads take
@@ -90,9 +145,15 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
       const int i = t0 + r;
       v4u data = {0u, 0u, 0u, 0u};
       if (i < r1) {
-        // Out-of-range slots or positions read as zeros (caller error).
-        const int src = rsrc[i];
+        // Hits from their slot, prefetched misses from their new slot, other
+        // misses from host.  Out-of-range slots or positions read as zeros
+        // (caller error).
+        int src = rsrc[i];
         const int pos = rpos[i];
+        if (src < 0 && rdst) {
+          const int dst = rdst[i];
+          if (dst >= 0 && dst < C && pos >= 0 && pos < L) src = dst;
+        }
         const uint16_t* rowp = nullptr;
         if (src >= 0) {
           if (src < C) rowp = pool_b + (size_t)src * kLat;
@@ -100,11 +161,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
           rowp = host_b + (size_t)pos * kLat;
         }
         if (rowp) data = *reinterpret_cast<const v4u*>(rowp + ch * 8);
-        if (rdst) {
-          const int dst = rdst[i];
-          if (dst >= 0 && dst < C)
-            *reinterpret_cast<v4u*>(pool_w + (size_t)dst * kLat + ch * 8) = data;
-        }
       }
       *reinterpret_cast<v4u*>(&krow[r * kKStride + ch * 8]) = data;
       if (ch < kVal / 8) {
@@ -213,7 +269,9 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     uint16_t* pool, const uint16_t* host, float* part_acc,
                     float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  dim3 grid(p.nchunk, p.head_groups, d.batch * d.mtp);
+  // Chunk index slowest, so every (request, token)'s lowest-rank chunk is
+  // dispatched before any higher-rank chunk.
+  dim3 grid(p.head_groups, d.batch * d.mtp, p.nchunk);
   hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), 0, s, q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
@@ -238,6 +296,8 @@ MlaPlan plan_sparse_mla(const ess_dims& d) {
   const int base = d.batch * d.mtp * p.head_groups;
   const int max_chunks = (d.topk + kTile - 1) / kTile;
   int nchunk = (target + base - 1) / base;
+  const int min_chunks = (d.topk + kMaxChunkRows - 1) / kMaxChunkRows;
+  if (nchunk < min_chunks) nchunk = min_chunks;   // miss list fits in LDS
   if (nchunk < 1) nchunk = 1;
   if (nchunk > max_chunks) nchunk = max_chunks;
   const int per = (d.topk + nchunk - 1) / nchunk;
