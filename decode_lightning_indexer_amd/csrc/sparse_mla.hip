@@ -29,15 +29,17 @@
 // Two workgroups per CU keep the MFMA busy while the other waits on the link.
 //
 // Per workgroup: one (request, token), 16 * NW heads (16 per wave), one
-// chunk of rows, walked in 32-row tiles staged in LDS twice - row-major for
-// the QK^T operand and transposed for the PV operand.
+// chunk of rows, walked in 32-row tiles staged once in LDS, row-major.
 //   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
-//                                           from LDS, B = Q from registers
-//   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T from LDS,
-//                                           B = P straight from registers
-// The S^T accumulator leaves each lane holding one head and 8 tokens; those
-// 8 tokens are exactly the lane's reduction slice of the PV operand, so P
-// never leaves registers (the V^T reads use the same token order).
+//                                           rows from LDS, B = Q in registers
+//   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T, B = P in registers
+// The V^T operand comes from the same row-major tile through gfx950's
+// transposing LDS read (ds_read_b64_tr_b16): within a 16-lane group, lane i
+// receives element i mod 4 of the 8 bytes addressed by lanes 4e + i/4, so
+// pointing lane r at token 4g + r/4, columns 4(r mod 4).. gives lane i the
+// column i of four tokens.  The S^T accumulator leaves each lane holding one
+// head and 8 tokens; those 8 tokens are exactly the lane's reduction slice
+// of the PV operand, so P never leaves registers.
 // Softmax runs in the log2 domain with a running max and sum per head.
 #include "ess_internal.h"
 
@@ -50,26 +52,33 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int kTile = 32;            // tokens per LDS tile
 constexpr int kKStride = kLat + 8;   // bf16 per row-major row (1168 B)
-constexpr int kVtStride = kTile + 4; // bf16 per transposed row (72 B)
 constexpr int kChunks16 = kLat / 8;  // 16-byte pieces per latent row (72)
-
-constexpr int kMaxChunkRows = 512;   // miss-row list capacity per chunk
+constexpr int kMaxChunkRows = 512;   // rows per chunk held in LDS tables
 constexpr int kPrefetchBatch = 8;    // 16-byte host loads in flight per thread
+constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
+
+__device__ __forceinline__ v2u tr_read(const uint16_t* p) {
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4s*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(v2u, v);
+}
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
+__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ host, float* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, float scale_log2) {
+  constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kVal * kVtStride];
-
+  __shared__ int code[kMaxChunkRows];   // >= 0: pool slot; < 0: ~host position
   __shared__ int mrow[kMaxChunkRows];
   __shared__ int s_nmiss;
 
@@ -89,22 +98,36 @@ __global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
   const uint16_t* host_b = host + (size_t)b * L * kLat;
   uint16_t* pool_w = pool + (size_t)b * C * kLat;
 
-  // Miss prefetch: this chunk's designated-writer miss rows, host -> slot.
-  if (rdst) {
-    if (threadIdx.x == 0) s_nmiss = 0;
-    __syncthreads();
-    for (int i = r0 + threadIdx.x; i < r1; i += NW * 64) {
-      const int dst = rdst[i], pos = rpos[i];
-      if (rsrc[i] < 0 && dst >= 0 && dst < C && pos >= 0 && pos < L)
+  // Row sources of the chunk, once.  Hits read their slot; a designated
+  // writer miss is copied host -> its new slot first and then read from
+  // there; other misses read host memory.  Out-of-range values (caller
+  // error) give zero rows.
+  if (threadIdx.x == 0) s_nmiss = 0;
+  __syncthreads();
+  for (int i = r0 + threadIdx.x; i < r1; i += NT) {
+    const int src = rsrc[i], pos = rpos[i];
+    const int dst = rdst ? rdst[i] : -1;
+    int cd = kNoRow;
+    if (src >= 0) {
+      if (src < C) cd = src;
+    } else if (pos >= 0 && pos < L) {
+      if (dst >= 0 && dst < C) {
+        cd = dst;
         mrow[atomicAdd(&s_nmiss, 1)] = i;
+      } else {
+        cd = ~pos;
+      }
     }
-    __syncthreads();
+    code[i - r0] = cd;
+  }
+  __syncthreads();
+  {
     const int npieces = s_nmiss * kChunks16;
-    for (int q0 = threadIdx.x; q0 < npieces; q0 += NW * 64 * kPrefetchBatch) {
+    for (int q0 = threadIdx.x; q0 < npieces; q0 += NT * kPrefetchBatch) {
       v4u buf[kPrefetchBatch];
 #pragma unroll
       for (int u = 0; u < kPrefetchBatch; ++u) {
-        const int q = q0 + u * NW * 64;
+        const int q = q0 + u * NT;
         if (q < npieces) {
           const int i = mrow[q / kChunks16], ch = q % kChunks16;
           buf[u] = *reinterpret_cast<const v4u*>(host_b + (size_t)rpos[i] * kLat + ch * 8);
@@ -112,10 +135,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
       }
 #pragma unroll
       for (int u = 0; u < kPrefetchBatch; ++u) {
-        const int q = q0 + u * NW * 64;
+        const int q = q0 + u * NT;
         if (q < npieces) {
           const int i = mrow[q / kChunks16], ch = q % kChunks16;
-          *reinterpret_cast<v4u*>(pool_w + (size_t)rdst[i] * kLat + ch * 8) = buf[u];
+          *reinterpret_cast<v4u*>(pool_w + (size_t)code[i - r0] * kLat + ch * 8) = buf[u];
         }
       }
     }
@@ -136,41 +159,49 @@ __global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
 #pragma unroll
   for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int kPer = (kTile * kChunks16 + NT - 1) / NT;   // pieces per thread
+  // Transposed-read address of this lane within a tile half: token
+  // 4 g + (c / 4), columns 4 (c % 4) .. of each 16-column group.
+  const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4;
+
+  // Tile loads go to registers one tile ahead: tile t+1's loads are in
+  // flight while tile t is computed.  Consecutive threads take consecutive
+  // 16-byte pieces of a row.
+  v4u data[kPer];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int q = threadIdx.x + u * NT;
+      data[u] = v4u{0u, 0u, 0u, 0u};
+      if (q < kTile * kChunks16) {
+        const int r = q / kChunks16, ch = q - r * kChunks16;
+        const int i = t0 + r;
+        if (i < r1) {
+          const int cd = code[i - r0];
+          if (cd != kNoRow) {
+            const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
+                                           : host_b + (size_t)(~cd) * kLat;
+            data[u] = *reinterpret_cast<const v4u*>(rowp + ch * 8);
+          }
+        }
+      }
+    }
+  };
+  __syncthreads();            // prefetched miss rows visible to every wave
+  if (r0 < r1) load_tile(r0);
+
   for (int t0 = r0; t0 < r1; t0 += kTile) {
     __syncthreads();   // previous tile fully consumed
-    // Stage: each thread moves 16-byte pieces; consecutive threads take
-    // consecutive pieces of a row so global reads are contiguous.
-    for (int q = threadIdx.x; q < kTile * kChunks16; q += NW * 64) {
-      const int r = q / kChunks16, ch = q - r * kChunks16;
-      const int i = t0 + r;
-      v4u data = {0u, 0u, 0u, 0u};
-      if (i < r1) {
-        // Hits from their slot, prefetched misses from their new slot, other
-        // misses from host.  Out-of-range slots or positions read as zeros
-        // (caller error).
-        int src = rsrc[i];
-        const int pos = rpos[i];
-        if (src < 0 && rdst) {
-          const int dst = rdst[i];
-          if (dst >= 0 && dst < C && pos >= 0 && pos < L) src = dst;
-        }
-        const uint16_t* rowp = nullptr;
-        if (src >= 0) {
-          if (src < C) rowp = pool_b + (size_t)src * kLat;
-        } else if (pos >= 0 && pos < L) {
-          rowp = host_b + (size_t)pos * kLat;
-        }
-        if (rowp) data = *reinterpret_cast<const v4u*>(rowp + ch * 8);
-      }
-      *reinterpret_cast<v4u*>(&krow[r * kKStride + ch * 8]) = data;
-      if (ch < kVal / 8) {
-        uint16_t* col = &vt[(ch * 8) * kVtStride + r];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          col[e * kVtStride] = (uint16_t)(data[e >> 1] >> ((e & 1) * 16));
+    for (int u = 0; u < kPer; ++u) {
+      const int q = threadIdx.x + u * NT;
+      if (q < kTile * kChunks16) {
+        const int r = q / kChunks16, ch = q - r * kChunks16;
+        *reinterpret_cast<v4u*>(&krow[r * kKStride + ch * 8]) = data[u];
       }
     }
     __syncthreads();
+    if (t0 + kTile < r1) load_tile(t0 + kTile);
 
     // S^T for two 16-token halves of the tile.
     v4f s[2];
@@ -213,12 +244,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 3 ? 2 : 1) void sparse_mla_kernel(
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
-    // O^T += V^T P^T over the tile; V^T read in the lane's token order.
+    // O^T += V^T P^T over the tile; V^T read transposed from the tile rows:
+    // tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, column nt*16 + c.
 #pragma unroll
     for (int nt = 0; nt < kVal / 16; ++nt) {
-      const uint16_t* vr = &vt[(nt * 16 + c) * kVtStride];
-      const v2u lo = *reinterpret_cast<const v2u*>(vr + g * 4);
-      const v2u hi = *reinterpret_cast<const v2u*>(vr + 16 + g * 4);
+      const uint16_t* base = &krow[tr_off + nt * 16];
+      const v2u lo = tr_read(base);
+      const v2u hi = tr_read(base + 16 * kKStride);
       const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
       const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
       oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt] * alpha,
