@@ -13,20 +13,19 @@
 // rows in rank order, in fixed chunks of rows combined in fixed order; no
 // atomics.  Which rows came from host memory changes no arithmetic.
 //
-// Miss handling on MI355X: a miss costs a host-link read (~55 GB/s) against
-// an HBM read for a hit (8 TB/s), so the host link sets the pace.  The pages
-// put the misses at the head of the selection so that one tile in four
-// touches host memory (same section).  Here the same idea works at two
-// levels, neither of which changes the arithmetic:
-//   * chunks are dispatched from the lowest ranks up - new entries enter the
-//     top-k near the cut, so the low-rank chunks hold most misses and start
-//     their host reads first;
-//   * a workgroup first streams every designated-writer miss row of its chunk
-//     from host memory into its pool slot, all rows in flight at once, then
-//     walks its tiles reading every row from device memory.  A miss row that
-//     another token's workgroup writes (MTP ways sharing a miss) is read from
-//     host memory in the tile loop instead, so no workgroup waits on another.
-// Two workgroups per CU keep the MFMA busy while the other waits on the link.
+// Miss handling on MI355X: a miss costs a host-link read (~54 GB/s
+// measured) against an HBM read for a hit (8 TB/s), so the host link sets
+// the pace.  The pages fuse the copy into the attention so the copy hides
+// under it and put the misses at the head of the selection (same section).
+// Here the misses go first in time instead: one copy kernel spreads every
+// designated-writer miss row of the call evenly over the whole chip (rows
+// near the top-k cut miss most, so per-chunk copying leaves a few
+// workgroups with most of the rows), then the attention kernel reads those
+// rows from their new slots.  Measured on MI355X, the copy runs at the
+// link's rate only when nothing else is in flight: overlapping it with the
+// HBM-bound attention made both slower than running them back to back.
+// A miss row that another token's row writes (MTP ways sharing a miss)
+// is read straight from host memory inside the attention kernel.
 //
 // Per workgroup: one (request, token), 16 * NW heads (16 per wave), one
 // chunk of rows, walked in 32-row tiles staged once in LDS, row-major.
@@ -59,7 +58,8 @@ constexpr int kTile = 32;            // tokens per LDS tile
 constexpr int kKStride = kLat + 8;   // bf16 per row-major row (1168 B)
 constexpr int kChunks16 = kLat / 8;  // 16-byte pieces per latent row (72)
 constexpr int kMaxChunkRows = 512;   // rows per chunk held in LDS tables
-constexpr int kPrefetchBatch = 8;    // 16-byte host loads in flight per thread
+constexpr int kCopyRows = 32;        // rows scanned per copy workgroup
+constexpr int kCopyThreads = 256;
 constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
 
 __device__ __forceinline__ v2u tr_read(const uint16_t* p) {
@@ -79,8 +79,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
   __shared__ int code[kMaxChunkRows];   // >= 0: pool slot; < 0: ~host position
-  __shared__ int mrow[kMaxChunkRows];
-  __shared__ int s_nmiss;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -98,12 +96,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
   const uint16_t* host_b = host + (size_t)b * L * kLat;
   uint16_t* pool_w = pool + (size_t)b * C * kLat;
 
-  // Row sources of the chunk, once.  Hits read their slot; a designated
-  // writer miss is copied host -> its new slot first and then read from
-  // there; other misses read host memory.  Out-of-range values (caller
-  // error) give zero rows.
-  if (threadIdx.x == 0) s_nmiss = 0;
-  __syncthreads();
+  // Row sources of the chunk, once: hits read their slot, designated-writer
+  // misses their new slot (filled by the copy kernel that runs first), other
+  // misses host memory.  Out-of-range values (caller error) give zero rows.
   for (int i = r0 + threadIdx.x; i < r1; i += NT) {
     const int src = rsrc[i], pos = rpos[i];
     const int dst = rdst ? rdst[i] : -1;
@@ -111,38 +106,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     if (src >= 0) {
       if (src < C) cd = src;
     } else if (pos >= 0 && pos < L) {
-      if (dst >= 0 && dst < C) {
-        cd = dst;
-        mrow[atomicAdd(&s_nmiss, 1)] = i;
-      } else {
-        cd = ~pos;
-      }
+      cd = (dst >= 0 && dst < C) ? dst : ~pos;
     }
     code[i - r0] = cd;
-  }
-  __syncthreads();
-  {
-    const int npieces = s_nmiss * kChunks16;
-    for (int q0 = threadIdx.x; q0 < npieces; q0 += NT * kPrefetchBatch) {
-      v4u buf[kPrefetchBatch];
-#pragma unroll
-      for (int u = 0; u < kPrefetchBatch; ++u) {
-        const int q = q0 + u * NT;
-        if (q < npieces) {
-          const int i = mrow[q / kChunks16], ch = q % kChunks16;
-          buf[u] = *reinterpret_cast<const v4u*>(host_b + (size_t)rpos[i] * kLat + ch * 8);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kPrefetchBatch; ++u) {
-        const int q = q0 + u * NT;
-        if (q < npieces) {
-          const int i = mrow[q / kChunks16], ch = q % kChunks16;
-          *reinterpret_cast<v4u*>(pool_w + (size_t)code[i - r0] * kLat + ch * 8) = buf[u];
-        }
-      }
-    }
-    __threadfence_block();
   }
 
   // Q fragments: lane holds Q[h0 + c][32 kk + 8 g .. + 8].
@@ -187,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
       }
     }
   };
-  __syncthreads();            // prefetched miss rows visible to every wave
+  __syncthreads();            // row table visible to every wave
   if (r0 < r1) load_tile(r0);
 
   for (int t0 = r0; t0 < r1; t0 += kTile) {
@@ -265,6 +231,58 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     *reinterpret_cast<v4f*>(pa + nt * 16 + g * 4) = oacc[nt];
   if (g == 0)
     part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(m_run, l_run);
+}
+
+// Designated-writer miss rows host -> their slot, spread over the chip: each
+// workgroup scans kCopyRows rows of one (request, token), lists its misses in
+// LDS, then copies them with all threads, every host read of a thread in
+// flight together.
+__global__ __launch_bounds__(kCopyThreads) void miss_rows_copy_kernel(
+    const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ sel_src,
+    const int32_t* __restrict__ row_dst, const int32_t* __restrict__ n_sel,
+    uint16_t* __restrict__ pool, const uint16_t* __restrict__ host, int L,
+    int C, int m, int k) {
+  __shared__ int mpos[kCopyRows], mdst[kCopyRows];
+  __shared__ int s_n;
+  const int bj = blockIdx.y, b = bj / m;
+  const int r0 = blockIdx.x * kCopyRows;
+  const int r1 = min(min(n_sel[bj], k), r0 + kCopyRows);
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  if (threadIdx.x < kCopyRows) {
+    const int i = r0 + threadIdx.x;
+    if (i < r1) {
+      const size_t o = (size_t)bj * k + i;
+      const int src = sel_src[o], dst = row_dst[o], pos = sel_pos[o];
+      if (src < 0 && dst >= 0 && dst < C && pos >= 0 && pos < L) {
+        const int at = atomicAdd(&s_n, 1);
+        mpos[at] = pos;
+        mdst[at] = dst;
+      }
+    }
+  }
+  __syncthreads();
+  const int npieces = s_n * kChunks16;
+  const uint16_t* hb = host + (size_t)b * L * kLat;
+  uint16_t* pb = pool + (size_t)b * C * kLat;
+  constexpr int kBatch = (kCopyRows * kChunks16 + kCopyThreads - 1) / kCopyThreads;
+  v4u buf[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int q = threadIdx.x + u * kCopyThreads;
+    if (q < npieces) {
+      const int j = q / kChunks16, ch = q - j * kChunks16;
+      buf[u] = *reinterpret_cast<const v4u*>(hb + (size_t)mpos[j] * kLat + ch * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int q = threadIdx.x + u * kCopyThreads;
+    if (q < npieces) {
+      const int j = q / kChunks16, ch = q - j * kChunks16;
+      *reinterpret_cast<v4u*>(pb + (size_t)mdst[j] * kLat + ch * 8) = buf[u];
+    }
+  }
 }
 
 // Merge the chunk partials of one (request, token, head) in chunk order.
@@ -352,6 +370,16 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              float* out, float* lse, void* ws,
                              hipStream_t s) {
   const MlaPlan p = plan_sparse_mla(d);
+  if (row_dst) {
+    // Misses first: every designated-writer miss row lands in its slot
+    // before the attention reads it there.
+    dim3 cg((d.topk + kCopyRows - 1) / kCopyRows, d.batch * d.mtp);
+    hipLaunchKernelGGL(miss_rows_copy_kernel, cg, dim3(kCopyThreads), 0, s,
+                       sel_pos, sel_src, row_dst, n_sel, pool, host,
+                       d.ctx_len, d.pool_slots, d.mtp, d.topk);
+    hipError_t ce = hipGetLastError();
+    if (ce != hipSuccess) return ce;
+  }
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   float* part_acc = static_cast<float*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(

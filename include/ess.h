@@ -163,11 +163,13 @@ ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
  *   z_i   = softmax_scale * <q_abs[b][j][h], row_i>
  *   out[b][j][h][:] = sum_i softmax(z)_i * row_i[0:512]
  *   lse[b][j][h]    = log sum_i exp(z_i)                 (lse may be NULL)
- * If row_dst is not NULL, a row with row_dst[i] >= 0 is also written to
- * pool[b][row_dst[i]] (it must be a slot no selected row reads, as the slots
- * from ess_pool_update are).  The reduction order is the rank order in fixed
- * chunks combined in fixed order, so the result does not depend on which
- * rows came from host memory.
+ * If row_dst is not NULL, every miss row (sel_src[i] < 0) with
+ * row_dst[i] >= 0 is copied from host memory to pool[b][row_dst[i]] before
+ * the attention reads it from there (that slot must be one no other
+ * selected row reads, as the slots from ess_pool_update are); other miss
+ * rows are read from host memory inside the attention kernel.  The
+ * reduction order is the rank order in fixed chunks combined in fixed order,
+ * so the result does not depend on which rows came from host memory.
  *   q_abs [B][m][H][576] bf16; sel_pos, sel_src, row_dst [B][m][k];
  *   n_sel [B][m]; pool [B][C][576] bf16; host_view [B][L][576] bf16;
  *   out [B][m][H][512] float; lse [B][m][H] float. */
