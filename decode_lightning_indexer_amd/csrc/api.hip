@@ -77,6 +77,9 @@ ess_status check_update(const ess_dims* d, int k, int n_tok, const char* fn) {
   if ((int64_t)n_tok * k > ess::kMaxTopk)
     return fail(ESS_ERR_UNSUPPORTED, "%s: n_tok*k above %d", fn,
                 ess::kMaxTopk);
+  if (d->pool_slots > ess::kMaxPoolSlots)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: pool_slots above %d", fn,
+                ess::kMaxPoolSlots);
   return ESS_OK;
 }
 

@@ -93,4 +93,162 @@ __device__ void bitonic_sort_u64(uint64_t* a, int n) {
   }
 }
 
+// Bitonic sort of n = NT * E 64-bit keys (n a power of two) held in LDS,
+// done mostly in registers: thread t keeps elements r * NT + t (r < E).
+// Compare-exchange partners at stride < 64 are in the same wave (lane
+// shuffles), at stride >= NT in the same thread, and only strides 64..NT/2
+// go through LDS.  DESC: largest first.  Ends with the sorted keys back in
+// `a` and a barrier.
+template <int NT, bool DESC, int E>
+__device__ void block_sort_u64(uint64_t* a) {
+  constexpr int n = NT * E;
+  const int t = threadIdx.x;
+  uint64_t v[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = a[r * NT + t];
+  // Keep the larger of a pair at its lower index in blocks that sort
+  // downward (DESC: the blocks with bit `size` clear).
+  auto want_max = [](int i, int p, int size) {
+    const bool lower = i < p;
+    const bool down = ((i & size) == 0) == DESC;
+    return lower == down;
+  };
+#pragma unroll 1
+  for (int size = 2; size <= n; size <<= 1) {
+#pragma unroll 1
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= NT) {
+        const int rs = stride / NT;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (r & rs) continue;
+          const int i = r * NT + t;
+          const uint64_t x = v[r], y = v[r ^ rs];
+          const bool wm = want_max(i, i ^ stride, size);
+          v[r] = wm ? (x > y ? x : y) : (x < y ? x : y);
+          v[r ^ rs] = wm ? (x > y ? y : x) : (x < y ? y : x);
+        }
+      } else if (stride >= 64) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) a[r * NT + t] = v[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int i = r * NT + t;
+          const uint64_t y = a[i ^ stride];
+          const uint64_t x = v[r];
+          v[r] = want_max(i, i ^ stride, size) ? (x > y ? x : y) : (x < y ? x : y);
+        }
+        __syncthreads();
+      } else {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int i = r * NT + t;
+          const uint32_t lo = (uint32_t)v[r], hi = (uint32_t)(v[r] >> 32);
+          const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)hi, stride) << 32) |
+                             (uint32_t)__shfl_xor((int)lo, stride);
+          const uint64_t x = v[r];
+          v[r] = want_max(i, i ^ stride, size) ? (x > y ? x : y) : (x < y ? x : y);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < E; ++r) a[r * NT + t] = v[r];
+  __syncthreads();
+}
+
+// block_sort_u64 for any power-of-two n in [NT, 16 NT].
+template <int NT, bool DESC>
+__device__ void block_sort_u64_n(uint64_t* a, int n) {
+  switch (n / NT) {
+    case 1: block_sort_u64<NT, DESC, 1>(a); break;
+    case 2: block_sort_u64<NT, DESC, 2>(a); break;
+    case 4: block_sort_u64<NT, DESC, 4>(a); break;
+    case 8: block_sort_u64<NT, DESC, 8>(a); break;
+    default: block_sort_u64<NT, DESC, 16>(a); break;
+  }
+}
+
+// Bucket sort of n 64-bit keys from src into dst (both LDS, not aliased):
+// histogram over nb buckets (a multiple of NT), exclusive scan, scatter,
+// then one thread insertion-sorts each bucket.  bucket(key) must be
+// monotone in the output order (DESC: larger keys never in a later bucket).
+// Returns false - leaving dst undefined - when a bucket holds more than
+// max_bucket keys; the caller then sorts another way.  cnt: nb words of LDS;
+// tmp: NT/64 + 1 words.  Ends with a barrier.
+template <int NT, bool DESC, typename BucketFn>
+__device__ bool bucket_sort_u64(const uint64_t* src, uint64_t* dst, int n,
+                                int nb, BucketFn bucket, uint32_t* cnt,
+                                uint32_t* tmp, int max_bucket) {
+  const int t = threadIdx.x;
+  const int bpt = nb / NT;   // buckets per thread
+  for (int i = t; i < nb; i += NT) cnt[i] = 0;
+  __syncthreads();
+  for (int i = t; i < n; i += NT) atomicAdd(&cnt[bucket(src[i])], 1u);
+  __syncthreads();
+  uint32_t mine = 0, big = 0;
+  for (int q = 0; q < bpt; ++q) {
+    const uint32_t c = cnt[t * bpt + q];
+    mine += c;
+    big = max(big, c);
+  }
+  uint32_t tot;
+  uint32_t off = block_exscan<NT>(mine, tmp, &tot);
+  const bool too_big = __syncthreads_or(big > (uint32_t)max_bucket);
+  if (too_big) return false;
+  for (int q = 0; q < bpt; ++q) {
+    const uint32_t c = cnt[t * bpt + q];
+    cnt[t * bpt + q] = off;      // fill cursor = bucket start
+    off += c;
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += NT) {
+    const uint64_t x = src[i];
+    dst[atomicAdd(&cnt[bucket(x)], 1u)] = x;
+  }
+  __syncthreads();
+  // cnt[b] is now the end of bucket b, so bucket b spans [cnt[b-1], cnt[b]).
+  for (int q = 0; q < bpt; ++q) {
+    const int b = t * bpt + q;
+    const int lo = b == 0 ? 0 : (int)cnt[b - 1], hi = (int)cnt[b];
+    for (int i = lo + 1; i < hi; ++i) {
+      const uint64_t x = dst[i];
+      int j = i - 1;
+      while (j >= lo && (DESC ? dst[j] < x : dst[j] > x)) {
+        dst[j + 1] = dst[j];
+        --j;
+      }
+      dst[j + 1] = x;
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+// Bitonic sort of up to 64 keys by one wave (wave 0), one key per lane;
+// lanes past n hold `pad`, which must sort after every real key.  Other
+// waves just wait at the closing barrier.
+template <bool DESC>
+__device__ void wave_sort_u64(uint64_t* a, int n, uint64_t pad) {
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x;
+    uint64_t x = i < n ? a[i] : pad;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+        const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)hi, stride) << 32) |
+                           (uint32_t)__shfl_xor((int)lo, stride);
+        const bool lower = (i & stride) == 0;
+        const bool down = ((i & size) == 0) == DESC;
+        x = (lower == down) ? (x > y ? x : y) : (x < y ? x : y);
+      }
+    }
+    if (i < n) a[i] = x;
+  }
+  __syncthreads();
+}
+
 }  // namespace ess

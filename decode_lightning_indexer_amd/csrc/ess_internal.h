@@ -12,6 +12,8 @@ namespace ess {
 // Largest k the top-k and pool-update kernels hold on chip (LDS sort buffer
 // of 8-byte keys: 16384 * 8 = 128 KiB of the 160 KiB per CU).
 constexpr int kMaxTopk = 16384;
+// The pool update packs a slot + 1 into 20 bits of its sort entries.
+constexpr int kMaxPoolSlots = (1 << 20) - 2;
 constexpr int kLat = 576;   // latent width: c_KV[512] + k_R[64]
 constexpr int kVal = 512;   // value width
 

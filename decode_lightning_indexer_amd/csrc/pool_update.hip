@@ -28,6 +28,8 @@ namespace ess {
 namespace {
 
 constexpr int NT = 1024;
+constexpr int kSortBuckets = 2048;
+constexpr int kTwoBufferMax = 4096;   // entries sorted out of place up to this
 
 struct Ring {
   int32_t slot;
@@ -60,8 +62,23 @@ __global__ __launch_bounds__(NT) void pool_reset_kernel(
   }
 }
 
-// Entry key: (position * n_tok + token) << 32 | row; ascending order gives
-// positions ascending and, for a repeated position, the smallest token first.
+// Entry layout (64 bits, sorted ascending): position (28 bits) | token (2) |
+// row (14) | slot + 1 (20; 0 until known).  Sorting on the whole value
+// orders positions ascending and, for a repeated position, the smallest
+// token first; the slot field is filled in place once a position's slot
+// after the update is known, so every row's outputs come from LDS.
+__device__ __forceinline__ uint64_t make_entry(int pos, int j, int i) {
+  return ((uint64_t)(uint32_t)pos << 36) | ((uint64_t)j << 34) | ((uint64_t)i << 20);
+}
+__device__ __forceinline__ int ent_pos(uint64_t e) { return (int)(e >> 36); }
+__device__ __forceinline__ int ent_tok(uint64_t e) { return (int)((e >> 34) & 3); }
+__device__ __forceinline__ int ent_row(uint64_t e) { return (int)((e >> 20) & 0x3FFF); }
+__device__ __forceinline__ int ent_slot(uint64_t e) { return (int)(e & 0xFFFFF) - 1; }
+__device__ __forceinline__ uint64_t with_slot(uint64_t e, int slot) {
+  return (e & ~0xFFFFFull) | (uint64_t)(slot + 1);
+}
+constexpr uint64_t kNoEntry = ~0ull;
+
 __global__ __launch_bounds__(NT) void pool_update_kernel(
     const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ n_sel,
     int32_t* __restrict__ cache_slots, int32_t* __restrict__ slot_pos,
@@ -69,10 +86,12 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
     int32_t* __restrict__ miss_slot, int32_t* __restrict__ n_miss_out,
     int32_t* __restrict__ n_evict_out, int32_t* __restrict__ row_dst,
     int32_t* __restrict__ sel_slot_post, int L, int C, int k, int n_tok,
-    int epow2) {
-  extern __shared__ uint64_t ent[];            // epow2 entries
+    int epow2, int two_buffers, int pos_shift) {
+  extern __shared__ uint64_t smem_ent[];       // epow2 entries (x2: sort target)
   __shared__ uint32_t tmp[NT / 64 + 1];
+  __shared__ uint32_t bcnt[kSortBuckets];
   __shared__ int s_head_new;
+  uint64_t* ent = smem_ent;
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -98,42 +117,61 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
     row_dst[rows0 + i] = -1;
     sel_slot_post[rows0 + i] = -1;
   }
-  // 1. Entries of every way, then sort.
+  // 1. Entries of every way, then sort.  Out-of-range positions are dropped
+  // (they sort last and end the scan).
   for (int e = tid; e < epow2; e += NT) {
-    uint64_t key = ~0ull;
+    uint64_t key = kNoEntry;
     if (e < n_e) {
       int j = 0;
       while (e >= off[j + 1]) ++j;
       const int i = e - off[j];
       const int pos = sel_pos[rows0 + (size_t)j * k + i];
-      if (pos >= 0 && pos < L)   // out-of-range positions are dropped
-        key = ((uint64_t)((uint32_t)pos * (uint32_t)n_tok + j) << 32) | (uint32_t)i;
-      else
-        h->err = 2;
+      if (pos >= 0 && pos < L) key = make_entry(pos, j, i);
+      else h->err = 2;
     }
     ent[e] = key;
   }
   __syncthreads();
-  bitonic_sort_u64<NT, false>(ent, epow2);
+  // Sort by position: buckets of the position's top 11 bits (selections are
+  // spread over the context, so buckets hold a few entries each), each then
+  // insertion-sorted on the whole entry; a full sort if the buckets come out
+  // uneven or there is no room for a second buffer.
+  {
+    bool done = false;
+    if (two_buffers) {
+      const int shift = pos_shift;
+      auto bucket = [&](uint64_t x) {
+        const int bk = ent_pos(x) >> shift;
+        return bk < kSortBuckets ? bk : kSortBuckets - 1;   // dropped entries last
+      };
+      done = bucket_sort_u64<NT, false>(smem_ent, smem_ent + epow2, n_e, kSortBuckets,
+                                        bucket, bcnt, tmp, 64);
+      if (done) ent = smem_ent + epow2;
+    }
+    if (!done) block_sort_u64_n<NT, false>(smem_ent, epow2);
+  }
 
-  // 2. Unique positions (first entry of each run) and their lookup.  Dropped
-  // entries sort last (key ~0) and end the run.
+  // 2. Unique positions (first entry of each run) and their lookup; a hit's
+  // slot goes into its entry and its stamp moves to this update (its old
+  // ring entry dies).
   const int per = (epow2 + NT - 1) / NT;       // entries per thread, contiguous
   const int e0 = tid * per;
-  auto first_of_run = [&](int e, uint32_t pk) {
-    return e == 0 || (uint32_t)(ent[e - 1] >> 32) / n_tok != pk / n_tok;
+  auto head_of_run = [&](int e) {
+    return e == 0 || ent_pos(ent[e - 1]) != ent_pos(ent[e]);
   };
   uint32_t n_u_mine = 0, n_m_mine = 0;
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
-    if (e >= n_e) break;
-    if (ent[e] == ~0ull) break;
-    const uint32_t pk = (uint32_t)(ent[e] >> 32);
-    if (first_of_run(e, pk)) {
+    if (e >= n_e || ent[e] == kNoEntry) break;
+    if (head_of_run(e)) {
       ++n_u_mine;
-      const int slot = cs[pk / n_tok];
-      if (slot < 0 || slot >= C) ++n_m_mine;
-      else stamp[slot] = epoch;                // touched: old ring entry dies
+      const int slot = cs[ent_pos(ent[e])];
+      if (slot >= 0 && slot < C) {
+        stamp[slot] = epoch;
+        ent[e] = with_slot(ent[e], slot);
+      } else {
+        ++n_m_mine;
+      }
     }
   }
   uint32_t n_u, n_miss;
@@ -190,14 +228,9 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
     uint32_t mi = m_base;
     for (int q = 0; q < per; ++q) {
       const int e = e0 + q;
-      if (e >= n_e) break;
-      const uint64_t key = ent[e];
-      if (key == ~0ull) break;
-      const uint32_t pk = (uint32_t)(key >> 32);
-      if (!first_of_run(e, pk)) continue;
-      const int pos = (int)(pk / n_tok);
-      const int cur = cs[pos];
-      if (cur >= 0 && cur < C) continue;       // hit (evictions never hit U)
+      if (e >= n_e || ent[e] == kNoEntry) break;
+      if (!head_of_run(e) || ent_slot(ent[e]) >= 0) continue;   // hit
+      const int pos = ent_pos(ent[e]);
       const int v = (int)mi < use_free ? free_head + (int)mi
                                        : miss_slot[list0 + mi];
       if ((int)mi < paired && v >= 0 && v < C) {
@@ -206,9 +239,8 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
         stamp[v] = epoch;
         miss_pos[list0 + mi] = pos;
         miss_slot[list0 + mi] = v;
-        const int j = (int)(pk % n_tok);
-        const int i = (int)(uint32_t)key;
-        row_dst[rows0 + (size_t)j * k + i] = v;  // smallest token's row
+        row_dst[rows0 + (size_t)ent_tok(ent[e]) * k + ent_row(ent[e])] = v;
+        ent[e] = with_slot(ent[e], v);
       }
       ++mi;
     }
@@ -237,27 +269,23 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
     tail = dst;
   }
 
-  // 6. Push the union in ascending position order with current slots.
+  // 6. Push the union in ascending position order with current slots, and
+  // every row's slot after the update (from its run's first entry, at most
+  // n_tok - 1 entries back).
   for (int q = 0, u = (int)u_base; q < per; ++q) {
     const int e = e0 + q;
-    if (e >= n_e) break;
-    if (ent[e] == ~0ull) break;
-    const uint32_t pk = (uint32_t)(ent[e] >> 32);
-    if (!first_of_run(e, pk)) continue;
-    Ring r;
-    r.slot = cs[pk / n_tok];
-    r.stamp = epoch;
-    ring[tail + u] = r;
-    ++u;
-  }
-  __syncthreads();
-
-  // 7. Slots after the update for every selected row.
-  for (int i = tid; i < n_tok * k; i += NT) {
-    const int j = i / k, r = i % k;
-    if (r < min(n_sel[b * n_tok + j], k)) {
-      const int pos = sel_pos[rows0 + i];
-      if (pos >= 0 && pos < L) sel_slot_post[rows0 + i] = cs[pos];
+    if (e >= n_e || ent[e] == kNoEntry) break;
+    const uint64_t x = ent[e];
+    int hd = e;
+    while (hd > 0 && ent_pos(ent[hd - 1]) == ent_pos(x)) --hd;
+    const int slot = ent_slot(ent[hd]);
+    sel_slot_post[rows0 + (size_t)ent_tok(x) * k + ent_row(x)] = slot;
+    if (hd == e) {
+      Ring r;
+      r.slot = slot;
+      r.stamp = epoch;
+      ring[tail + u] = r;
+      ++u;
     }
   }
   if (tid == 0) {
@@ -292,8 +320,13 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               int32_t* n_evict, int32_t* row_dst,
                               int32_t* sel_slot_post, hipStream_t s) {
   const size_t stride = lru_bytes_per_req(d.pool_slots);
-  const int epow2 = pow2_at_least(n_tok * k);
-  const size_t lds = (size_t)epow2 * sizeof(uint64_t);
+  // The sort buffer holds at least one entry per thread.
+  const int epow2 = pow2_at_least(n_tok * k) < NT ? NT : pow2_at_least(n_tok * k);
+  const int two = epow2 <= kTwoBufferMax ? 1 : 0;
+  const size_t lds = (size_t)epow2 * sizeof(uint64_t) * (two ? 2 : 1);
+  int bits = 0;
+  while ((1 << bits) < d.ctx_len) ++bits;
+  const int pos_shift = bits > 11 ? bits - 11 : 0;
   hipError_t e = hipFuncSetAttribute((const void*)pool_update_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)(kMaxTopk * sizeof(uint64_t)));
@@ -301,7 +334,8 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
   hipLaunchKernelGGL(pool_update_kernel, dim3(d.batch), dim3(NT), lds, s,
                      sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
                      miss_pos, miss_slot, n_miss, n_evict, row_dst,
-                     sel_slot_post, d.ctx_len, d.pool_slots, k, n_tok, epow2);
+                     sel_slot_post, d.ctx_len, d.pool_slots, k, n_tok, epow2,
+                     two, pos_shift);
   return hipGetLastError();
 }
 

@@ -10,7 +10,9 @@
 // position (equal scores: lower position wins) - and the slot of each winner
 // is gathered in the same final pass that writes the winners.
 //
-// One 1024-thread workgroup per row (the rows are few: B * m):
+// One 1024-thread workgroup per row (the rows are few: B * m); scores are
+// read with 16-byte loads, all of a thread's loads for a chunk in flight
+// together:
 //   1. min and max of the order-preserving keys of the visible positions;
 //   2. radix passes of up to 11 bits starting at the highest bit where min
 //      and max differ, each narrowing the bin that holds the k-th key, until
@@ -50,6 +52,15 @@ __device__ __forceinline__ bool in_fixed(uint32_t key, uint32_t prefix,
   return ((uint64_t)key >> lo_fixed) == ((uint64_t)prefix >> lo_fixed);
 }
 
+// Keys are read in chunks of NT * 32: thread t holds positions
+// base + (v * NT + t) * 4 + e for v < 8, e < 4, loaded as eight 16-byte
+// loads issued together.  A row of at most one chunk is loaded once and kept
+// in registers for every pass (RES); longer rows are streamed per pass.
+constexpr int VPT = 8;                 // 16-byte loads per thread per chunk
+constexpr int KPT = VPT * 4;           // keys per thread per chunk
+constexpr int CHUNK = NT * KPT;        // 32768 keys
+
+template <bool RES>
 __global__ __launch_bounds__(NT) void topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
@@ -60,7 +71,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   uint64_t* cand = smem + kpow2;     // cap candidates
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
-  __shared__ uint32_t s_nwin, s_ncand, s_bin_need, s_bin_cnt;
+  __shared__ uint32_t s_bin_need, s_bin_cnt;
   __shared__ int s_bin;
 
   const int tid = threadIdx.x;
@@ -70,23 +81,49 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   int n = n_vis[b * m + j];
   n = n < 0 ? 0 : (n > L ? L : n);
   const int keff = min(k, n);
+  const bool vec = (L & 3) == 0;     // rows start 16-byte aligned
 
-  if (tid == 0) {
-    s_nwin = 0;
-    s_ncand = 0;
-  }
+  uint32_t kr[KPT];
+  auto load = [&](int base) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int p0 = base + (v * NT + tid) * 4;
+      if (vec && p0 + 3 < n) {
+        const float4 f = *reinterpret_cast<const float4*>(srow + p0);
+        kr[4 * v + 0] = ord_key(f.x);
+        kr[4 * v + 1] = ord_key(f.y);
+        kr[4 * v + 2] = ord_key(f.z);
+        kr[4 * v + 3] = ord_key(f.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kr[4 * v + e] = (p0 + e < n) ? ord_key(srow[p0 + e]) : 0u;
+      }
+    }
+  };
+  auto pos_of = [&](int base, int v, int e) { return base + (v * NT + tid) * 4 + e; };
+  const int nchunks = (n + CHUNK - 1) / CHUNK;
+
   if (keff == n) {
     // Every visible position is selected.
     for (int i = tid; i < kpow2; i += NT)
       win[i] = i < n ? full_key(ord_key(srow[i]), i) : 0ull;
     __syncthreads();
   } else {
+    if (RES) load(0);
     // 1. Range of the keys.
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t key = ord_key(srow[i]);
-      mn = min(mn, key);
-      mx = max(mx, key);
+    for (int c = 0; c < nchunks; ++c) {
+      const int base = c * CHUNK;
+      if (!RES) load(base);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pos_of(base, v, e) < n) {
+            mn = min(mn, kr[4 * v + e]);
+            mx = max(mx, kr[4 * v + e]);
+          }
     }
     block_minmax<NT>(mn, mx, tmp);
     // Bits at and above lo_fixed are common to every key in the bin that
@@ -103,10 +140,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       const int nb = 1 << (hi - lo + 1);
       for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t key = ord_key(srow[i]);
-        if (in_fixed(key, prefix, lo_fixed))
-          atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
+      for (int c = 0; c < nchunks; ++c) {
+        const int base = c * CHUNK;
+        if (!RES) load(base);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = kr[4 * v + e];
+            if (pos_of(base, v, e) < n && in_fixed(key, prefix, lo_fixed))
+              atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
+          }
       }
       __syncthreads();
       // Bins in descending order: thread t owns bins nb-1-2t and nb-2-2t.
@@ -135,78 +179,131 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       __syncthreads();
     }
 
-    // 3. Collect winners above the bin and the bin's candidates.
+    // 3. Collect winners above the bin and the bin's candidates, compacted
+    // with workgroup scans (winner and candidate counts packed in one word:
+    // winners <= kpow2 <= 16384 and candidates <= cap fit 16 bits each).
     const bool sort_cands = cnt <= (uint32_t)cap;
     uint32_t eq_taken = 0;  // ordered path: equal keys taken so far
-    for (int base = 0; base < n; base += NT * 4) {
-      uint32_t keys[4];
-      int n_eq = 0;
+    uint32_t nwin = 0, ncand = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int base = c * CHUNK;
+      if (!RES) load(base);
+      uint32_t mine = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = base + tid * 4 + e;
-        keys[e] = 0;
-        if (p < n) {
-          const uint32_t key = ord_key(srow[p]);
-          keys[e] = key;
-          // The counts guarantee at < kpow2 and at < cap; the checks only
-          // keep LDS writes in bounds if that ever failed.
-          if (above_fixed(key, prefix, lo_fixed)) {
-            const uint32_t at = atomicAdd(&s_nwin, 1u);
-            if (at < (uint32_t)kpow2) win[at] = full_key(key, p);
-          } else if (in_fixed(key, prefix, lo_fixed)) {
-            if (sort_cands) {
-              const uint32_t at = atomicAdd(&s_ncand, 1u);
-              if (at < (uint32_t)cap) cand[at] = full_key(key, p);
-            } else {
-              ++n_eq;
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = kr[4 * v + e];
+          if (pos_of(base, v, e) < n) {
+            if (above_fixed(key, prefix, lo_fixed)) mine += 1u << 16;
+            else if (sort_cands && in_fixed(key, prefix, lo_fixed)) mine += 1u;
+          }
+        }
+      uint32_t tot;
+      const uint32_t ex = block_exscan<NT>(mine, tmp, &tot);
+      uint32_t wat = nwin + (ex >> 16), cat = ncand + (ex & 0xFFFFu);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = pos_of(base, v, e);
+          const uint32_t key = kr[4 * v + e];
+          if (p < n) {
+            // The counts guarantee wat < kpow2 and cat < cap; the checks
+            // only keep LDS writes in bounds if that ever failed.
+            if (above_fixed(key, prefix, lo_fixed)) {
+              if (wat < (uint32_t)kpow2) win[wat] = full_key(key, p);
+              ++wat;
+            } else if (sort_cands && in_fixed(key, prefix, lo_fixed)) {
+              if (cat < (uint32_t)cap) cand[cat] = full_key(key, p);
+              ++cat;
             }
           }
         }
-      }
+      nwin += tot >> 16;
+      ncand += tot & 0xFFFFu;
       if (!sort_cands) {
-        // All keys in the bin are equal: take them in position order.
-        if (__syncthreads_count(n_eq) > 0) {
-          uint32_t tot;
-          uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &tot);
+        // All keys in the bin are equal: take them in position order.  The
+        // positions of slice v are contiguous per thread and ordered by
+        // thread, so a workgroup scan gives each its rank.
+#pragma unroll 1
+        for (int v = 0; v < VPT; ++v) {
+          int n_eq = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int p = base + tid * 4 + e;
-            if (p < n && in_fixed(keys[e], prefix, lo_fixed)) {
-              if (rank < need) {
-                const uint32_t at = atomicAdd(&s_nwin, 1u);
-                if (at < (uint32_t)kpow2) win[at] = full_key(keys[e], p);
+          for (int e = 0; e < 4; ++e)
+            if (pos_of(base, v, e) < n && in_fixed(kr[4 * v + e], prefix, lo_fixed)) ++n_eq;
+          if (__syncthreads_count(n_eq) > 0) {
+            uint32_t t2;
+            uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
+            uint32_t taken_before = min(eq_taken, need);
+            uint32_t at = nwin + (min(rank, need) - taken_before);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int p = pos_of(base, v, e);
+              if (p < n && in_fixed(kr[4 * v + e], prefix, lo_fixed)) {
+                if (rank < need) {
+                  if (at < (uint32_t)kpow2) win[at] = full_key(kr[4 * v + e], p);
+                  ++at;
+                }
+                ++rank;
               }
-              ++rank;
             }
+            const uint32_t before = min(eq_taken, need);
+            eq_taken += t2;
+            nwin += min(eq_taken, need) - before;
           }
-          eq_taken += tot;
         }
       }
     }
     __syncthreads();
     if (sort_cands) {
-      const uint32_t nc = min(s_ncand, (uint32_t)cap);
-      const int cp = pow2_at_least_dev(nc);
-      for (int i = nc + tid; i < cp; i += NT) cand[i] = 0ull;
-      __syncthreads();
-      bitonic_sort_u64<NT, true>(cand, cp);
-      const uint32_t w0 = s_nwin;
-      for (uint32_t i = tid; i < need && i < nc && w0 + i < (uint32_t)kpow2; i += NT)
-        win[w0 + i] = cand[i];
+      const uint32_t nc = min(ncand, (uint32_t)cap);
+      if (nc <= 64) {
+        wave_sort_u64<true>(cand, nc, 0ull);
+      } else {
+        const int cp = max(pow2_at_least_dev(nc), NT);
+        for (int i = nc + tid; i < cp; i += NT) cand[i] = 0ull;
+        __syncthreads();
+        block_sort_u64_n<NT, true>(cand, cp);
+      }
+      for (uint32_t i = tid; i < need && i < nc && nwin + i < (uint32_t)kpow2; i += NT)
+        win[nwin + i] = cand[i];
       __syncthreads();
     }
     for (int i = keff + tid; i < kpow2; i += NT) win[i] = 0ull;
     __syncthreads();
   }
 
-  // 4. Rank order and emit with the slot lookup.
-  bitonic_sort_u64<NT, true>(win, kpow2);
+  // 4. Rank order: bucket sort on the score bits spread over the winners'
+  // range (buckets of equal-score runs are then ordered by position), or a
+  // full sort when the buckets come out uneven or do not fit.
+  const uint64_t* ranked = win;
+  {
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int i = tid; i < keff; i += NT) {
+      const uint32_t hi = (uint32_t)(win[i] >> 32);
+      kmn = min(kmn, hi);
+      kmx = max(kmx, hi);
+    }
+    block_minmax<NT>(kmn, kmx, tmp);
+    bool done = false;
+    if (cap >= keff) {
+      const uint32_t range = kmx - kmn;
+      const int shift = range < (uint32_t)kBins ? 0 : (32 - __clz(range)) - 11;
+      auto bucket = [&](uint64_t x) {
+        return (int)((kmx - (uint32_t)(x >> 32)) >> shift);
+      };
+      done = bucket_sort_u64<NT, true>(win, cand, keff, kBins, bucket, hist, tmp, 64);
+      if (done) ranked = cand;
+    }
+    if (!done) block_sort_u64_n<NT, true>(win, kpow2);
+  }
   int32_t* op = sel_pos + ((size_t)b * n_tok + j) * k;
   int32_t* os = sel_slot + ((size_t)b * n_tok + j) * k;
   const int32_t* cs = cache_slots + (size_t)b * L;
   for (int i = tid; i < k; i += NT) {
     if (i < keff) {
-      const int pos = (int)(~(uint32_t)win[i]);
+      const int pos = (int)(~(uint32_t)ranked[i]);
       op[i] = pos;
       os[i] = cs[pos];
     } else {
@@ -223,19 +320,27 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, hipStream_t s) {
-  const int kpow2 = pow2_at_least(k);
+  // Sort buffers hold at least one key per thread.
+  const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
   size_t cap = (kLdsBudget - (size_t)kpow2 * 8) / 8;
   if (cap > 4096) cap = 4096;
   int capp = 1;
   while ((size_t)capp * 2 <= cap) capp <<= 1;
   const size_t lds = ((size_t)kpow2 + capp) * sizeof(uint64_t);
-  hipError_t e = hipFuncSetAttribute((const void*)topk_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+  // Rows of at most one chunk stay in registers for all passes.
+  const bool res = d.ctx_len <= CHUNK;
+  const void* fn = res ? (const void*)topk_kernel<true> : (const void*)topk_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)kLdsBudget);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(d.batch * n_tok), dim3(NT), lds, s,
-                     scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                     d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
+  if (res)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
+                       d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
+                       d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ extern "C" {
  *   lat_dim    576 = c_KV[512] + k_R[64]
  *   v_dim      512
  *   topk       k  (1 .. 16384)
- *   pool_slots C  hot-pool slots per request (mtp*topk <= C)
+ *   pool_slots C  hot-pool slots per request (mtp*topk <= C <= 2^20 - 2)
  *   softmax_scale  multiplies the latent dot products before the softmax */
 typedef struct ess_dims {
   int32_t batch, mtp, ctx_len, idx_heads, idx_dim, mla_heads;
