@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget for the oracle CPU baseline (0 = skip)")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy (known "
+                        "bytes) for scaling the HBM traffic counters")
     return p.parse_args()
 
 
@@ -85,6 +88,17 @@ def main():
         return 2
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel(), "copy_bytes_written": b.numel(),
+                          "launches": 4}), flush=True)
+        return 0
 
     from decode_lightning_indexer_amd import ess
     from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
@@ -141,11 +155,17 @@ def main():
                             row_dst, post, stream)
         if ev is not None:
             ev[3].record(stream)
-        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
+        # Gather: the step's copy list host -> pool first (misses first at
+        # full link rate), then attention reading every row from the pool.
+        ess.ess_miss_copy(d, lists, lb.miss_pos, lb.miss_slot, n_miss_all[t],
+                          host.dev, lb.pool, stream)
+        if ev is not None:
+            ev[4].record(stream)
+        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, post, None, lb.n_sel,
                                   lb.pool, host.dev, lb.out, lb.lse, lb.ws,
                                   lb.ws_bytes, stream)
         if ev is not None:
-            ev[4].record(stream)
+            ev[5].record(stream)
 
     # First fill (top-C of token 0 at step 0 into the empty pool), untimed.
     lb.reset(stream)
@@ -157,7 +177,7 @@ def main():
         step(t)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -165,14 +185,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    stage_ms = np.zeros(4)
+    stage_ms = np.zeros(5)
     for e in evs:
-        for s in range(4):
+        for s in range(5):
             stage_ms[s] += e[s].elapsed_time(e[s + 1])
     stage_us = stage_ms / K * 1e3
     n_miss_tot = int(n_miss_all[W:].sum())
 
-    # The same steps without the per-stage events, as one call per step.
+    # The same steps without the per-stage events, as one ess_decode_step
+    # call per step (the gather inside copies the designated-writer miss rows
+    # first, then attends).
     lb.reset(stream)
     lb.q_idx.copy_(q_idx[0])
     ess.ess_decode_step(d, [lb.io()], n_vis, ess.ESS_MODE_FILL, stream)
@@ -243,27 +265,33 @@ def main():
     sel_bytes = B * m * k * 1152
     attn_flop = 2 * B * m * H * k * (576 + 512)
     attn_bytes = sel_bytes + B * m * H * (576 * 2 + 512 * 4)
-    names = ["index_scores", "topk_lookup", "pool_update", "sparse_mla_decode"]
+    names = ["index_scores", "topk_lookup", "pool_update", "miss_copy",
+             "sparse_mla_decode"]
     miss_bytes = n_miss_tot * 1152 / K
-    t_attn_bound = max(sel_bytes / (HBM_PEAK_GBPS * 1e3), miss_bytes / (host_gbps * 1e3),
-                       attn_flop / (BF16_PEAK_TFLOPS * 1e6))            # us
     roofs = {
-        "index_scores": {"bound": "hbm", "achieved": idx_bytes / (stage_us[0] * 1e3),
+        "index_scores": {"kernel": "index_scores_kernel", "bound": "hbm",
+                         "achieved": idx_bytes / (stage_us[0] * 1e3),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "bytes_per_launch": idx_bytes},
-        "sparse_mla_decode": {"bound": "host-link" if miss_bytes / (host_gbps * 1e3) >= sel_bytes / (HBM_PEAK_GBPS * 1e3) else "hbm",
-                              "achieved": miss_bytes / (stage_us[3] * 1e3),
-                              "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                              "bytes_per_launch": miss_bytes,
-                              "measured_ceiling": host_gbps,
-                              "frac_of_bound": t_attn_bound / stage_us[3]},
+        "miss_copy": {"kernel": "miss_copy_kernel", "bound": "host-link",
+                      "achieved": miss_bytes / (stage_us[3] * 1e3),
+                      "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                      "bytes_per_launch": miss_bytes,
+                      "measured_ceiling": host_gbps},
+        "sparse_mla_decode": {"kernel": "sparse_mla_kernel+mla_combine_kernel",
+                              "bound": "hbm",
+                              "achieved": attn_bytes / (stage_us[4] * 1e3),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "bytes_per_launch": attn_bytes,
+                              "tflops": attn_flop / (stage_us[4] * 1e6),
+                              "mfma_frac": attn_flop / (stage_us[4] * 1e6) / BF16_PEAK_TFLOPS},
     }
     for r in roofs.values():
         r["frac"] = r["achieved"] / r["peak"]
     dom = int(np.argmax(stage_us))
-    roof = dict(roofs.get(names[dom], {"bound": "alu", "achieved": None, "peak": None,
+    roof = dict(roofs.get(names[dom], {"kernel": names[dom], "bound": "alu",
+                                        "achieved": None, "peak": None,
                                         "unit": "us", "frac": None}))
-    roof["kernel"] = names[dom]
     roof["traffic"] = None
 
     steps_per_s = K / wall
@@ -283,10 +311,11 @@ def main():
         "steps_per_s_one_call": K / wall_plain,
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
         "indexer_gbps": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
-        "attention_tflops": attn_flop / (stage_us[3] * 1e-6) / 1e12,
+        "attention_tflops": attn_flop / (stage_us[4] * 1e-6) / 1e12,
         "misses_per_step": n_miss_tot / K,
         "miss_rate": n_miss_tot / (K * B * m * k),
         "miss_fetch_gbps": n_miss_tot * 1152 / K / (stage_us[3] * 1e-6) / 1e9,
+        "gather_us": float(stage_us[3] + stage_us[4]),
         "host_link_gbps_measured": host_gbps,
         "overlap": {"t_copy_us": t_copy, "t_attn_us": t_attn, "t_fused_us": t_fused,
                     "ratio": overlap, "bound": overlap_bound,
