@@ -75,19 +75,31 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ host, float* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
-    int rows_per_chunk, int nchunk, float scale_log2) {
+    int rows_per_chunk, int nchunk, int head_groups, int n_bj,
+    float scale_log2) {
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
   __shared__ int code[kMaxChunkRows];   // >= 0: pool slot; < 0: ~host position
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int chunk = nchunk - 1 - (int)blockIdx.z;   // lowest ranks first
-  const int bj = blockIdx.y;
+  // Workgroup -> (head group, row chunk).  Consecutive workgroup ids go to
+  // the 8 XCDs in turn, each with its own L2; the head groups of one chunk
+  // get ids that are multiples of 8 apart, so they run on the same XCD close
+  // together and the second reads the chunk's latents from that L2.  Items
+  // (request-token, chunk) are numbered with the chunk slowest and lowest
+  // ranks first; ids past the last item (padding to whole rounds) exit.
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, round = wg >> 3;
+  const int hg = round % head_groups;
+  const int item = (round / head_groups) * 8 + xcd;
+  if (item >= n_bj * nchunk) return;
+  const int bj = item % n_bj;
+  const int chunk = nchunk - 1 - item / n_bj;
   const int b = bj / m;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
-  const int h0 = blockIdx.x * (NW * 16) + wave * 16;
+  const int h0 = hg * (NW * 16) + wave * 16;
 
   const int32_t* rpos = sel_pos + (size_t)bj * k;
   const int32_t* rsrc = sel_src + (size_t)bj * k;
@@ -319,13 +331,15 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     uint16_t* pool, const uint16_t* host, float* part_acc,
                     float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  // Chunk index slowest, so every (request, token)'s lowest-rank chunk is
-  // dispatched before any higher-rank chunk.
-  dim3 grid(p.head_groups, d.batch * d.mtp, p.nchunk);
+  // 1-D grid over (item, head group) in whole rounds of 8 XCDs.
+  const int items = d.batch * d.mtp * p.nchunk;
+  const int rounds = ((items + 7) / 8) * p.head_groups;
+  dim3 grid(rounds * 8);
   hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), 0, s, q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
-                     d.topk, p.rows_per_chunk, p.nchunk, scale_log2);
+                     d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
+                     d.batch * d.mtp, scale_log2);
   return hipGetLastError();
 }
 
@@ -338,7 +352,7 @@ MlaPlan plan_sparse_mla(const ess_dims& d) {
   p.head_groups = H / p.heads_per_wg;
   // Enough workgroups to cover the chip about twice; more chunks also mean
   // more partial traffic, so stop there.
-  int target = 512;
+  int target = 256;
   if (const char* env = std::getenv("ESS_MLA_TARGET_WGS")) {
     const int v = std::atoi(env);
     if (v > 0) target = v;
