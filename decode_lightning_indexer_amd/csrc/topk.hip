@@ -83,25 +83,32 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   const int keff = min(k, n);
   const bool vec = (L & 3) == 0;     // rows start 16-byte aligned
 
+  // Keys of one chunk for this thread.  A chunk wholly inside the visible
+  // row (the common case) takes eight unconditional 16-byte loads, all in
+  // flight together; a partial chunk takes bounds-checked scalar loads.
   uint32_t kr[KPT];
-  auto load = [&](int base) {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int p0 = base + (v * NT + tid) * 4;
-      if (vec && p0 + 3 < n) {
-        const float4 f = *reinterpret_cast<const float4*>(srow + p0);
-        kr[4 * v + 0] = ord_key(f.x);
-        kr[4 * v + 1] = ord_key(f.y);
-        kr[4 * v + 2] = ord_key(f.z);
-        kr[4 * v + 3] = ord_key(f.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          kr[4 * v + e] = (p0 + e < n) ? ord_key(srow[p0 + e]) : 0u;
-      }
-    }
-  };
-  auto pos_of = [&](int base, int v, int e) { return base + (v * NT + tid) * 4 + e; };
+#define ESS_TOPK_LOAD(BASE)                                                   \
+  do {                                                                        \
+    const int base_ = (BASE);                                                 \
+    if (vec && base_ + CHUNK <= n) {                                          \
+      float4 f_[VPT];                                                         \
+      _Pragma("unroll") for (int v = 0; v < VPT; ++v)                         \
+        f_[v] = *reinterpret_cast<const float4*>(srow + base_ + (v * NT + tid) * 4); \
+      _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                       \
+        kr[4 * v + 0] = ord_key(f_[v].x);                                     \
+        kr[4 * v + 1] = ord_key(f_[v].y);                                     \
+        kr[4 * v + 2] = ord_key(f_[v].z);                                     \
+        kr[4 * v + 3] = ord_key(f_[v].w);                                     \
+      }                                                                       \
+    } else {                                                                  \
+      _Pragma("unroll") for (int v = 0; v < VPT; ++v)                         \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                       \
+          const int p_ = base_ + (v * NT + tid) * 4 + e;                      \
+          kr[4 * v + e] = p_ < n ? ord_key(srow[p_]) : 0u;                    \
+        }                                                                     \
+    }                                                                         \
+  } while (0)
+#define pos_of(BASE, V, E) ((BASE) + ((V) * NT + tid) * 4 + (E))
   const int nchunks = (n + CHUNK - 1) / CHUNK;
 
   if (keff == n) {
@@ -110,12 +117,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       win[i] = i < n ? full_key(ord_key(srow[i]), i) : 0ull;
     __syncthreads();
   } else {
-    if (RES) load(0);
+    if (RES) ESS_TOPK_LOAD(0);
     // 1. Range of the keys.
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     for (int c = 0; c < nchunks; ++c) {
       const int base = c * CHUNK;
-      if (!RES) load(base);
+      if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       __syncthreads();
       for (int c = 0; c < nchunks; ++c) {
         const int base = c * CHUNK;
-        if (!RES) load(base);
+        if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
 #pragma unroll
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     uint32_t nwin = 0, ncand = 0;
     for (int c = 0; c < nchunks; ++c) {
       const int base = c * CHUNK;
-      if (!RES) load(base);
+      if (!RES) ESS_TOPK_LOAD(base);
       uint32_t mine = 0;
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
         // All keys in the bin are equal: take them in position order.  The
         // positions of slice v are contiguous per thread and ordered by
         // thread, so a workgroup scan gives each its rank.
-#pragma unroll 1
+#pragma unroll
         for (int v = 0; v < VPT; ++v) {
           int n_eq = 0;
 #pragma unroll
@@ -312,6 +319,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     }
   }
   if (tid == 0) n_sel[b * n_tok + j] = keff;
+#undef pos_of
+#undef ESS_TOPK_LOAD
 }
 
 }  // namespace
