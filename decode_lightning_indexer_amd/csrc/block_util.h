@@ -170,22 +170,25 @@ __device__ void block_sort_u64_n(uint64_t* a, int n) {
   }
 }
 
-// Bucket sort of n 64-bit keys from src into dst (both LDS, not aliased):
-// histogram over nb buckets (a multiple of NT), exclusive scan, scatter,
-// then one thread insertion-sorts each bucket.  bucket(key) must be
+// Bucket sort of n 64-bit keys in LDS: histogram over nb buckets (a
+// multiple of NT), exclusive scan, scatter into the scratch array g grouped
+// by bucket, then every key finds its place by counting the keys of its own
+// bucket that go before it (equal keys keep their grouped order), so the
+// cost grows with the largest bucket rather than its square, and no thread
+// walks a bucket alone.  The sorted keys end back in a.  bucket(key) must be
 // monotone in the output order (DESC: larger keys never in a later bucket).
-// Returns false - leaving dst undefined - when a bucket holds more than
+// Returns false - with a unchanged - when a bucket holds more than
 // max_bucket keys; the caller then sorts another way.  cnt: nb words of LDS;
 // tmp: NT/64 + 1 words.  Ends with a barrier.
 template <int NT, bool DESC, typename BucketFn>
-__device__ bool bucket_sort_u64(const uint64_t* src, uint64_t* dst, int n,
-                                int nb, BucketFn bucket, uint32_t* cnt,
-                                uint32_t* tmp, int max_bucket) {
+__device__ bool bucket_sort_u64(uint64_t* a, uint64_t* g, int n, int nb,
+                                BucketFn bucket, uint32_t* cnt, uint32_t* tmp,
+                                int max_bucket) {
   const int t = threadIdx.x;
   const int bpt = nb / NT;   // buckets per thread
   for (int i = t; i < nb; i += NT) cnt[i] = 0;
   __syncthreads();
-  for (int i = t; i < n; i += NT) atomicAdd(&cnt[bucket(src[i])], 1u);
+  for (int i = t; i < n; i += NT) atomicAdd(&cnt[bucket(a[i])], 1u);
   __syncthreads();
   uint32_t mine = 0, big = 0;
   for (int q = 0; q < bpt; ++q) {
@@ -204,26 +207,43 @@ __device__ bool bucket_sort_u64(const uint64_t* src, uint64_t* dst, int n,
   }
   __syncthreads();
   for (int i = t; i < n; i += NT) {
-    const uint64_t x = src[i];
-    dst[atomicAdd(&cnt[bucket(x)], 1u)] = x;
+    const uint64_t x = a[i];
+    g[atomicAdd(&cnt[bucket(x)], 1u)] = x;
   }
   __syncthreads();
   // cnt[b] is now the end of bucket b, so bucket b spans [cnt[b-1], cnt[b]).
-  for (int q = 0; q < bpt; ++q) {
-    const int b = t * bpt + q;
+  for (int i = t; i < n; i += NT) {
+    const uint64_t x = g[i];
+    const int b = bucket(x);
     const int lo = b == 0 ? 0 : (int)cnt[b - 1], hi = (int)cnt[b];
-    for (int i = lo + 1; i < hi; ++i) {
-      const uint64_t x = dst[i];
-      int j = i - 1;
-      while (j >= lo && (DESC ? dst[j] < x : dst[j] > x)) {
-        dst[j + 1] = dst[j];
-        --j;
-      }
-      dst[j + 1] = x;
+    int r = lo;
+    for (int q = lo; q < hi; ++q) {
+      const uint64_t y = g[q];
+      r += (DESC ? y > x : y < x) || (y == x && q < i);
     }
+    a[r] = x;
   }
   __syncthreads();
   return true;
+}
+
+// Bitonic sort across the 64 lanes of one wave, one key per lane (lane i
+// ends with the i-th key in order).  Must be reached by the whole wave.
+template <bool DESC>
+__device__ __forceinline__ uint64_t wave_bitonic_u64(uint64_t x, int i) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+      const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)hi, stride) << 32) |
+                         (uint32_t)__shfl_xor((int)lo, stride);
+      const bool lower = (i & stride) == 0;
+      const bool down = ((i & size) == 0) == DESC;
+      x = (lower == down) ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  }
+  return x;
 }
 
 // Bitonic sort of up to 64 keys by one wave (wave 0), one key per lane;
@@ -233,19 +253,7 @@ template <bool DESC>
 __device__ void wave_sort_u64(uint64_t* a, int n, uint64_t pad) {
   if (threadIdx.x < 64) {
     const int i = threadIdx.x;
-    uint64_t x = i < n ? a[i] : pad;
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-        const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)hi, stride) << 32) |
-                           (uint32_t)__shfl_xor((int)lo, stride);
-        const bool lower = (i & stride) == 0;
-        const bool down = ((i & size) == 0) == DESC;
-        x = (lower == down) ? (x > y ? x : y) : (x < y ? x : y);
-      }
-    }
+    const uint64_t x = wave_bitonic_u64<DESC>(i < n ? a[i] : pad, i);
     if (i < n) a[i] = x;
   }
   __syncthreads();

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
   }
   __syncthreads();
   // Sort by position: buckets of the position's top 11 bits (selections are
-  // spread over the context, so buckets hold a few entries each), each then
-  // insertion-sorted on the whole entry; a full sort if the buckets come out
+  // spread over the context, so buckets hold a few entries each), ordered
+  // within a bucket on the whole entry; a full sort if the buckets come out
   // uneven or there is no room for a second buffer.
   {
     bool done = false;
@@ -145,8 +145,7 @@ __global__ __launch_bounds__(NT) void pool_update_kernel(
         return bk < kSortBuckets ? bk : kSortBuckets - 1;   // dropped entries last
       };
       done = bucket_sort_u64<NT, false>(smem_ent, smem_ent + epow2, n_e, kSortBuckets,
-                                        bucket, bcnt, tmp, 64);
-      if (done) ent = smem_ent + epow2;
+                                        bucket, bcnt, tmp, 256);
     }
     if (!done) block_sort_u64_n<NT, false>(smem_ent, epow2);
   }

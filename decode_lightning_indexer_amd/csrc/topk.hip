@@ -16,13 +16,16 @@
 //   1. min and max of the order-preserving keys of the visible positions;
 //   2. radix passes of up to 11 bits starting at the highest bit where min
 //      and max differ, each narrowing the bin that holds the k-th key, until
-//      that bin holds at most `cap` keys (usually after one pass);
-//   3. one collect pass: keys above the bin are winners, keys in the bin are
-//      candidates; the candidates are sorted in LDS on the full 64-bit key
-//      and the best `need` of them join the winners.  If the bin is still
-//      too large after all 32 bits (a run of equal scores), the equal keys
-//      are taken in position order with a workgroup scan;
-//   4. bitonic sort of the k winners (rank order) and the emit pass.
+//      that bin holds at most one wave's worth of keys or the bits run out;
+//   3. keys above the bin are winners: a histogram of them over 2048 buckets
+//      of equal score width, a scan, and a scatter into LDS grouped by
+//      bucket.  Keys in the bin are candidates: one wave sorts them and the
+//      best `need` take the last ranks (a bin of equal keys too large for a
+//      wave takes them in position order with workgroup scans);
+//   4. each winner's rank is its bucket's start plus the number of larger
+//      keys in its bucket; it is written straight to that rank of the
+//      outputs with its slot.  A bucket too large for that (a long run of
+//      equal or near-equal scores) falls back to a full bitonic sort.
 #include "block_util.h"
 #include "ess_internal.h"
 
@@ -31,7 +34,8 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int kBins = 2048;
-constexpr size_t kLdsBudget = 160 * 1024 - 16 * 1024;  // leave static LDS room
+constexpr int kSmall = 64;       // candidates sorted by one wave
+constexpr int kMaxBucket = 256;  // larger winner buckets take the full sort
 
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -43,10 +47,6 @@ __device__ __forceinline__ uint64_t full_key(uint32_t ok, int pos) {
   return ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)pos);
 }
 
-__device__ __forceinline__ bool above_fixed(uint32_t key, uint32_t prefix,
-                                            int lo_fixed) {
-  return ((uint64_t)key >> lo_fixed) > ((uint64_t)prefix >> lo_fixed);
-}
 __device__ __forceinline__ bool in_fixed(uint32_t key, uint32_t prefix,
                                          int lo_fixed) {
   return ((uint64_t)key >> lo_fixed) == ((uint64_t)prefix >> lo_fixed);
@@ -65,13 +65,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int n_tok, int k, int kpow2, int cap) {
-  extern __shared__ uint64_t smem[];
-  uint64_t* win = smem;              // kpow2 winners
-  uint64_t* cand = smem + kpow2;     // cap candidates
+    int n_tok, int k, int kpow2) {
+  extern __shared__ uint64_t grp[];  // kpow2: winners grouped by bucket
   __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t cand[kSmall];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
-  __shared__ uint32_t s_bin_need, s_bin_cnt;
+  __shared__ uint32_t s_bin_need, s_bin_cnt, s_nc;
   __shared__ int s_bin;
 
   const int tid = threadIdx.x;
@@ -82,6 +81,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   n = n < 0 ? 0 : (n > L ? L : n);
   const int keff = min(k, n);
   const bool vec = (L & 3) == 0;     // rows start 16-byte aligned
+  int32_t* op = sel_pos + ((size_t)b * n_tok + j) * k;
+  int32_t* os = sel_slot + ((size_t)b * n_tok + j) * k;
+  const int32_t* cs = cache_slots + (size_t)b * L;
+  for (int i = keff + tid; i < k; i += NT) {
+    op[i] = -1;
+    os[i] = -1;
+  }
+  if (tid == 0) n_sel[b * n_tok + j] = keff;
+  if (keff == 0) return;
 
   // Keys of one chunk for this thread.  A chunk wholly inside the visible
   // row (the common case) takes eight unconditional 16-byte loads, all in
@@ -111,37 +119,36 @@ __global__ __launch_bounds__(NT) void topk_kernel(
 #define pos_of(BASE, V, E) ((BASE) + ((V) * NT + tid) * 4 + (E))
   const int nchunks = (n + CHUNK - 1) / CHUNK;
 
-  if (keff == n) {
-    // Every visible position is selected.
-    for (int i = tid; i < kpow2; i += NT)
-      win[i] = i < n ? full_key(ord_key(srow[i]), i) : 0ull;
-    __syncthreads();
-  } else {
-    if (RES) ESS_TOPK_LOAD(0);
-    // 1. Range of the keys.
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int c = 0; c < nchunks; ++c) {
-      const int base = c * CHUNK;
-      if (!RES) ESS_TOPK_LOAD(base);
+  if (RES) ESS_TOPK_LOAD(0);
+  // 1. Range of the keys.
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int c = 0; c < nchunks; ++c) {
+    const int base = c * CHUNK;
+    if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-      for (int v = 0; v < VPT; ++v)
+    for (int v = 0; v < VPT; ++v)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (pos_of(base, v, e) < n) {
-            mn = min(mn, kr[4 * v + e]);
-            mx = max(mx, kr[4 * v + e]);
-          }
-    }
-    block_minmax<NT>(mn, mx, tmp);
+      for (int e = 0; e < 4; ++e)
+        if (pos_of(base, v, e) < n) {
+          mn = min(mn, kr[4 * v + e]);
+          mx = max(mx, kr[4 * v + e]);
+        }
+  }
+  block_minmax<NT>(mn, mx, tmp);
+
+  // Winners are the keys >= win_lo; candidates the keys in [bin_lo, win_lo),
+  // of which the best `need` are taken.
+  uint64_t bin_lo = 0, win_lo = 0;
+  uint32_t need = 0, cnt = 0;
+  if (keff < n) {
     // Bits at and above lo_fixed are common to every key in the bin that
     // holds the k-th key; `prefix` carries them.
     int lo_fixed = (mn == mx) ? 0 : 32 - __clz(mn ^ mx);
     uint32_t prefix = mn;
-    uint32_t need = keff;      // keys still to take from the current bin
-    uint32_t cnt = n;          // keys in the current bin
-
+    need = keff;
+    cnt = n;
     // 2. Radix passes until the bin is small or the bits run out.
-    while (cnt > (uint32_t)cap && lo_fixed > 0) {
+    while (cnt > (uint32_t)kSmall && lo_fixed > 0) {
       const int hi = lo_fixed - 1;
       const int lo = hi >= 10 ? hi - 10 : 0;
       const int nb = 1 << (hi - lo + 1);
@@ -183,142 +190,143 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       need = s_bin_need;
       cnt = s_bin_cnt;
       lo_fixed = lo;
-      __syncthreads();
+      // The next writes of s_bin* and hist come after further barriers.
     }
-
-    // 3. Collect winners above the bin and the bin's candidates, compacted
-    // with workgroup scans (winner and candidate counts packed in one word:
-    // winners <= kpow2 <= 16384 and candidates <= cap fit 16 bits each).
-    const bool sort_cands = cnt <= (uint32_t)cap;
-    uint32_t eq_taken = 0;  // ordered path: equal keys taken so far
-    uint32_t nwin = 0, ncand = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int base = c * CHUNK;
-      if (!RES) ESS_TOPK_LOAD(base);
-      uint32_t mine = 0;
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = kr[4 * v + e];
-          if (pos_of(base, v, e) < n) {
-            if (above_fixed(key, prefix, lo_fixed)) mine += 1u << 16;
-            else if (sort_cands && in_fixed(key, prefix, lo_fixed)) mine += 1u;
-          }
-        }
-      uint32_t tot;
-      const uint32_t ex = block_exscan<NT>(mine, tmp, &tot);
-      uint32_t wat = nwin + (ex >> 16), cat = ncand + (ex & 0xFFFFu);
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int p = pos_of(base, v, e);
-          const uint32_t key = kr[4 * v + e];
-          if (p < n) {
-            // The counts guarantee wat < kpow2 and cat < cap; the checks
-            // only keep LDS writes in bounds if that ever failed.
-            if (above_fixed(key, prefix, lo_fixed)) {
-              if (wat < (uint32_t)kpow2) win[wat] = full_key(key, p);
-              ++wat;
-            } else if (sort_cands && in_fixed(key, prefix, lo_fixed)) {
-              if (cat < (uint32_t)cap) cand[cat] = full_key(key, p);
-              ++cat;
-            }
-          }
-        }
-      nwin += tot >> 16;
-      ncand += tot & 0xFFFFu;
-      if (!sort_cands) {
-        // All keys in the bin are equal: take them in position order.  The
-        // positions of slice v are contiguous per thread and ordered by
-        // thread, so a workgroup scan gives each its rank.
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-          int n_eq = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (pos_of(base, v, e) < n && in_fixed(kr[4 * v + e], prefix, lo_fixed)) ++n_eq;
-          if (__syncthreads_count(n_eq) > 0) {
-            uint32_t t2;
-            uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
-            uint32_t taken_before = min(eq_taken, need);
-            uint32_t at = nwin + (min(rank, need) - taken_before);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int p = pos_of(base, v, e);
-              if (p < n && in_fixed(kr[4 * v + e], prefix, lo_fixed)) {
-                if (rank < need) {
-                  if (at < (uint32_t)kpow2) win[at] = full_key(kr[4 * v + e], p);
-                  ++at;
-                }
-                ++rank;
-              }
-            }
-            const uint32_t before = min(eq_taken, need);
-            eq_taken += t2;
-            nwin += min(eq_taken, need) - before;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (sort_cands) {
-      const uint32_t nc = min(ncand, (uint32_t)cap);
-      if (nc <= 64) {
-        wave_sort_u64<true>(cand, nc, 0ull);
-      } else {
-        const int cp = max(pow2_at_least_dev(nc), NT);
-        for (int i = nc + tid; i < cp; i += NT) cand[i] = 0ull;
-        __syncthreads();
-        block_sort_u64_n<NT, true>(cand, cp);
-      }
-      for (uint32_t i = tid; i < need && i < nc && nwin + i < (uint32_t)kpow2; i += NT)
-        win[nwin + i] = cand[i];
-      __syncthreads();
-    }
-    for (int i = keff + tid; i < kpow2; i += NT) win[i] = 0ull;
-    __syncthreads();
+    bin_lo = ((uint64_t)prefix >> lo_fixed) << lo_fixed;
+    win_lo = bin_lo + (1ull << lo_fixed);
   }
+  const uint32_t nwin = (uint32_t)keff - need;
+  const bool small_bin = need > 0 && cnt <= (uint32_t)kSmall;
+  const bool ordered = need > 0 && !small_bin;   // a run of equal keys
 
-  // 4. Rank order: bucket sort on the score bits spread over the winners'
-  // range (buckets of equal-score runs are then ordered by position), or a
-  // full sort when the buckets come out uneven or do not fit.
-  const uint64_t* ranked = win;
+  // Winner buckets of equal width over [max(win_lo, mn), mx], larger keys
+  // first.
+  const uint32_t wlo = win_lo > (uint64_t)mn ? (uint32_t)min(win_lo, (uint64_t)mx) : mn;
+  const uint32_t range = mx - wlo;
+  const int shift = range < (uint32_t)kBins ? 0 : (32 - __clz(range)) - 11;
+#define bucket_of(KEY) ((int)((mx - (KEY)) >> shift))
+
+  // 3. Histogram of the winners; candidates appended (at most kSmall).
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int base = c * CHUNK;
+    if (!RES) ESS_TOPK_LOAD(base);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = pos_of(base, v, e);
+        const uint32_t key = kr[4 * v + e];
+        if (p < n) {
+          if ((uint64_t)key >= win_lo) {
+            atomicAdd(&hist[bucket_of(key)], 1u);
+          } else if (small_bin && (uint64_t)key >= bin_lo) {
+            const uint32_t at = atomicAdd(&s_nc, 1u);
+            if (at < (uint32_t)kSmall) cand[at] = full_key(key, p);
+          }
+        }
+      }
+  }
+  __syncthreads();
+  // Bucket starts: thread t owns buckets 2t and 2t+1.
+  bool too_big;
   {
-    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    for (int i = tid; i < keff; i += NT) {
-      const uint32_t hi = (uint32_t)(win[i] >> 32);
-      kmn = min(kmn, hi);
-      kmx = max(kmx, hi);
-    }
-    block_minmax<NT>(kmn, kmx, tmp);
-    bool done = false;
-    if (cap >= keff) {
-      const uint32_t range = kmx - kmn;
-      const int shift = range < (uint32_t)kBins ? 0 : (32 - __clz(range)) - 11;
-      auto bucket = [&](uint64_t x) {
-        return (int)((kmx - (uint32_t)(x >> 32)) >> shift);
-      };
-      done = bucket_sort_u64<NT, true>(win, cand, keff, kBins, bucket, hist, tmp, 64);
-      if (done) ranked = cand;
-    }
-    if (!done) block_sort_u64_n<NT, true>(win, kpow2);
+    const uint32_t c0 = hist[2 * tid], c1 = hist[2 * tid + 1];
+    uint32_t tot;
+    const uint32_t off = block_exscan<NT>(c0 + c1, tmp, &tot);
+    too_big = __syncthreads_or(max(c0, c1) > (uint32_t)kMaxBucket);
+    hist[2 * tid] = off;
+    hist[2 * tid + 1] = off + c0;
   }
-  int32_t* op = sel_pos + ((size_t)b * n_tok + j) * k;
-  int32_t* os = sel_slot + ((size_t)b * n_tok + j) * k;
-  const int32_t* cs = cache_slots + (size_t)b * L;
-  for (int i = tid; i < k; i += NT) {
-    if (i < keff) {
-      const int pos = (int)(~(uint32_t)ranked[i]);
+  __syncthreads();
+  // Scatter the winners into their buckets; a run of equal keys in the bin
+  // is taken in position order: the positions of slice v are contiguous per
+  // thread and ordered by thread, so a workgroup scan gives each its rank.
+  uint32_t eq_taken = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const int base = c * CHUNK;
+    if (!RES) ESS_TOPK_LOAD(base);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = pos_of(base, v, e);
+        const uint32_t key = kr[4 * v + e];
+        if (p < n && (uint64_t)key >= win_lo) {
+          // The histogram bounds every bucket's fill inside [0, nwin).
+          const uint32_t at = atomicAdd(&hist[bucket_of(key)], 1u);
+          if (at < (uint32_t)kpow2) grp[at] = full_key(key, p);
+        }
+      }
+    if (ordered) {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        int n_eq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pos_of(base, v, e) < n && (uint64_t)kr[4 * v + e] == bin_lo) ++n_eq;
+        if (eq_taken < need && __syncthreads_count(n_eq) > 0) {
+          uint32_t t2;
+          uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int p = pos_of(base, v, e);
+            if (p < n && (uint64_t)kr[4 * v + e] == bin_lo) {
+              if (rank < need) {
+                op[nwin + rank] = p;
+                os[nwin + rank] = cs[p];
+              }
+              ++rank;
+            }
+          }
+          eq_taken += t2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Candidates: the last wave sorts them and writes the best `need`.
+  if (small_bin && tid >= NT - 64) {
+    const int i = tid - (NT - 64);
+    const uint32_t nc = min(s_nc, (uint32_t)kSmall);
+    // Real keys carry ~pos >= 2^31 in the low word, so 0 sorts after them.
+    const uint64_t x = wave_bitonic_u64<true>(i < (int)nc ? cand[i] : 0ull, i);
+    if ((uint32_t)i < need) {
+      const int pos = (int)(~(uint32_t)x);
+      op[nwin + i] = pos;
+      os[nwin + i] = cs[pos];
+    }
+  }
+
+  // 4. Winners' ranks.  hist[b] is now the end of bucket b, so bucket b
+  // spans [hist[b-1], hist[b]).
+  if (!too_big) {
+    for (int i = tid; i < (int)nwin; i += NT) {
+      const uint64_t x = grp[i];
+      const int pos = (int)(~(uint32_t)x);
+      const int32_t sl = cs[pos];
+      const int bk = bucket_of((uint32_t)(x >> 32));
+      const int lo = bk == 0 ? 0 : (int)hist[bk - 1];
+      const int hi = (int)hist[bk];
+      int r = lo;
+      for (int q = lo; q < hi; ++q) r += grp[q] > x;
+      op[r] = pos;
+      os[r] = sl;
+    }
+  } else {
+    for (int i = nwin + tid; i < kpow2; i += NT) grp[i] = 0ull;
+    __syncthreads();
+    block_sort_u64_n<NT, true>(grp, kpow2);
+    for (int i = tid; i < (int)nwin; i += NT) {
+      const int pos = (int)(~(uint32_t)grp[i]);
       op[i] = pos;
       os[i] = cs[pos];
-    } else {
-      op[i] = -1;
-      os[i] = -1;
     }
   }
-  if (tid == 0) n_sel[b * n_tok + j] = keff;
+#undef bucket_of
 #undef pos_of
 #undef ESS_TOPK_LOAD
 }
@@ -329,27 +337,23 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, hipStream_t s) {
-  // Sort buffers hold at least one key per thread.
+  // The fallback sort needs a power of two of at least one key per thread.
   const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
-  size_t cap = (kLdsBudget - (size_t)kpow2 * 8) / 8;
-  if (cap > 4096) cap = 4096;
-  int capp = 1;
-  while ((size_t)capp * 2 <= cap) capp <<= 1;
-  const size_t lds = ((size_t)kpow2 + capp) * sizeof(uint64_t);
+  const size_t lds = (size_t)kpow2 * sizeof(uint64_t);
   // Rows of at most one chunk stay in registers for all passes.
   const bool res = d.ctx_len <= CHUNK;
   const void* fn = res ? (const void*)topk_kernel<true> : (const void*)topk_kernel<false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kLdsBudget);
+                                     (int)lds);
   if (e != hipSuccess) return e;
   if (res)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
                        scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
+                       d.ctx_len, d.mtp, n_tok, k, kpow2);
   else
     hipLaunchKernelGGL(topk_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
                        scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, n_tok, k, kpow2, capp);
+                       d.ctx_len, d.mtp, n_tok, k, kpow2);
   return hipGetLastError();
 }
 
