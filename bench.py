@@ -40,6 +40,12 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (known "
                         "bytes) for scaling the HBM traffic counters")
+    p.add_argument("--trace-summary", metavar="CSV",
+                   help="summarise a rocprofv3 kernel_trace.csv or "
+                        "counter_collection.csv of a run with the same "
+                        "--steps/--warmup: per kernel, the dispatches of the "
+                        "timed steps only (all dispatches if the file holds no "
+                        "timed window), then exit")
     return p.parse_args()
 
 
@@ -79,8 +85,88 @@ def cpu_baseline(wl, seconds):
                       f"fill excluded), {spent:.1f} s of step time"}
 
 
+# Kernels whose counters give roofline.traffic, with the source each is
+# built from; a recorded figure only counts while that source is unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_32k-b16.txt")
+KERNEL_SOURCES = {
+    "index_scores_kernel": "index_scores.hip",
+    "topk_kernel": "topk.hip",
+    "pool_update_kernel": "pool_update.hip",
+    "miss_copy_kernel": "miss_copy.hip",
+    "sparse_mla_kernel": "sparse_mla.hip",
+    "mla_combine_kernel": "sparse_mla.hip",
+}
+
+
+def source_digest(kernel):
+    import hashlib
+    src = os.path.join(ROOT, "decode_lightning_indexer_amd", "csrc",
+                       KERNEL_SOURCES[kernel])
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
+    there is none or the kernel's source has changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                w = line.split()
+                if len(w) == 4 and w[0] == "traffic" and w[1] == kernel:
+                    return float(w[2]) if w[3] == source_digest(kernel) else None
+    except OSError:
+        pass
+    return None
+
+
+def trace_summary(path, steps, warmup):
+    """Per-kernel mean duration (and mean counter value, for a counter run)
+    over the timed steps: the window from the first timed step's
+    index_scores_kernel to the next one after the timed steps (dispatch 0 is
+    the pool's first fill)."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    def short(n):
+        n = n.replace("ess::(anonymous namespace)::", "").replace("void ", "")
+        return n.split("(")[0]
+    starts = [int(r["Start_Timestamp"]) for r in rows
+              if short(r["Kernel_Name"]).startswith("index_scores_kernel")]
+    windowed = len(starts) > warmup + steps + 1
+    if windowed:
+        lo, hi = starts[warmup + 1], starts[warmup + steps + 1]
+        rows = [r for r in rows if lo <= int(r["Start_Timestamp"]) < hi]
+    agg = {}
+    for r in rows:
+        a = agg.setdefault(short(r["Kernel_Name"]), {"n": 0, "us": 0.0, "ctr": 0.0})
+        a["n"] += 1
+        a["us"] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "Counter_Value" in r:
+            a["ctr"] += float(r["Counter_Value"])
+    ctr = rows[0].get("Counter_Name") if rows else None
+    print(f"# {'timed steps' if windowed else 'all dispatches'}: {path}")
+    head = f"{'kernel':48s} {'dispatches':>10s} {'mean_us':>9s}"
+    if ctr:
+        head += f" {('mean_' + ctr + '_KiB'):>22s}"
+    print(head)
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["us"]):
+        if windowed and a["n"] < steps:
+            continue                  # not a per-step kernel
+        line = f"{name[:48]:48s} {a['n']:10d} {a['us'] / a['n']:9.2f}"
+        if ctr:
+            line += f" {a['ctr'] / a['n']:22.1f}"
+        print(line)
+    for name in KERNEL_SOURCES:
+        print(f"# source {name} {source_digest(name)}")
+    return 0
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        return trace_summary(args.trace_summary, args.steps, args.warmup)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not "
               "supported (requests shard across GPUs with no exchange; see "
@@ -292,7 +378,7 @@ def main():
     roof = dict(roofs.get(names[dom], {"kernel": names[dom], "bound": "alu",
                                         "achieved": None, "peak": None,
                                         "unit": "us", "frac": None}))
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(roof["kernel"]) if roof["kernel"] in KERNEL_SOURCES else None
 
     steps_per_s = K / wall
     res = {

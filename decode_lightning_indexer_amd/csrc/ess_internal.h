@@ -69,7 +69,7 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
 struct MlaPlan {
   int heads_per_wg;   // 16 * waves
   int head_groups;    // H / heads_per_wg
-  int rows_per_chunk; // multiple of 32
+  int rows_per_chunk; // multiple of 64 (a tile per sub-group)
   int nchunk;         // chunks of rows per (request, token)
 };
 MlaPlan plan_sparse_mla(const ess_dims& d);

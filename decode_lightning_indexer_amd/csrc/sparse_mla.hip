@@ -27,8 +27,17 @@
 // A miss row that another token's row writes (MTP ways sharing a miss)
 // is read straight from host memory inside the attention kernel.
 //
-// Per workgroup: one (request, token), 16 * NW heads (16 per wave), one
-// chunk of rows, walked in 32-row tiles staged once in LDS, row-major.
+// Per workgroup: one (request, token), 16 heads per wave, one chunk of rows
+// split between two sub-groups of waves that take alternate 32-row tiles
+// (each sub-group holds the same heads).  Tiles go from memory straight into
+// LDS (gfx950's 16-byte global-to-LDS load, one 1 KB block per wave
+// instruction), row-major with a 16-byte pad per row; each sub-group has
+// two tile buffers, so one tile is in flight while the other is computed,
+// with one workgroup barrier per tile and no registers held for staging.
+// Padding and unusable rows load a zero row.  At the end the second
+// sub-group's running state is merged into the first's through LDS, and the
+// chunk's partial is written normalised, in fp16, with its running max and
+// sum in fp32.
 //   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
 //                                           rows from LDS, B = Q in registers
 //   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T, B = P in registers
@@ -52,15 +61,24 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-constexpr int kTile = 32;            // tokens per LDS tile
-constexpr int kKStride = kLat + 8;   // bf16 per row-major row (1168 B)
-constexpr int kChunks16 = kLat / 8;  // 16-byte pieces per latent row (72)
-constexpr int kMaxChunkRows = 512;   // rows per chunk held in LDS tables
+constexpr int kTile = 32;                       // tokens per LDS tile
+constexpr int kRowSlots = kLat / 8 + 1;         // 16-byte slots per row (72 + pad)
+constexpr int kKStride = kRowSlots * 8;         // bf16 per row-major row (1168 B)
+constexpr int kChunks16 = kLat / 8;             // 16-byte pieces per latent row (72)
+constexpr int kTileLoads = (kTile * kRowSlots + 63) / 64;   // wave loads per tile (37)
+constexpr int kTileSlots = kTileLoads * 64;     // slots per tile buffer (2368)
+constexpr int kStages = 2;                      // tile buffers per sub-group
+constexpr int kMaxChunkRows = 512;              // rows per chunk held in LDS tables
+constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 + kMaxChunkRows * 4;
 constexpr int kCopyRows = 32;        // rows scanned per copy workgroup
 constexpr int kCopyThreads = 256;
 constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
+
+// A zero latent row: the source of padding rows and unusable rows.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kLat] = {};
 
 __device__ __forceinline__ v2u tr_read(const uint16_t* p) {
   const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -68,20 +86,39 @@ __device__ __forceinline__ v2u tr_read(const uint16_t* p) {
   return __builtin_bit_cast(v2u, v);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
+// One wave instruction: lane l copies 16 bytes from `src` to LDS at
+// lds_block + 16 l (lds_block is the same for the whole wave).  Issued as
+// inline assembly so that the compiler does not wait for it before
+// unrelated LDS reads; the caller waits (vmcnt) and synchronises before
+// reading the block.
+__device__ __forceinline__ void load_lds16(const void* src, const void* lds_block) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
+      const __attribute__((address_space(3))) void*)lds_block);
+  // An SALU write of M0 needs one wait state before an LDS-DMA load reads it.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(base), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+}
+
+template <int WPS>
+__global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
-    const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
-    const uint16_t* __restrict__ host, float* __restrict__ part_acc,
+    const int32_t* __restrict__ n_sel, const uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ host, _Float16* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKStride];
-  __shared__ int code[kMaxChunkRows];   // >= 0: pool slot; < 0: ~host position
+  constexpr int NT = 2 * WPS * 64;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  int* code = reinterpret_cast<int*>(smem + (size_t)2 * kStages * kTileSlots * 8);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sg = wave / WPS, wv = wave - sg * WPS;
   const int g = lane >> 4, c = lane & 15;
   // Workgroup -> (head group, row chunk).  Consecutive workgroup ids go to
   // the 8 XCDs in turn, each with its own L2; the head groups of one chunk
@@ -99,14 +136,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
   const int b = bj / m;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
-  const int h0 = hg * (NW * 16) + wave * 16;
+  const int h0 = hg * (WPS * 16) + wv * 16;
 
   const int32_t* rpos = sel_pos + (size_t)bj * k;
   const int32_t* rsrc = sel_src + (size_t)bj * k;
   const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
   const uint16_t* pool_b = pool + (size_t)b * C * kLat;
   const uint16_t* host_b = host + (size_t)b * L * kLat;
-  uint16_t* pool_w = pool + (size_t)b * C * kLat;
 
   // Row sources of the chunk, once: hits read their slot, designated-writer
   // misses their new slot (filled by the copy kernel that runs first), other
@@ -137,49 +173,49 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
   for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kPer = (kTile * kChunks16 + NT - 1) / NT;   // pieces per thread
+  // Tiles of the chunk: sub-group s takes tiles s, s + 2, ...; both run the
+  // same number of iterations (the barriers are workgroup-wide).
+  const int ntile = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
+  const int iters = (ntile + 1) / 2;
+  uint16_t* ring = smem + (size_t)sg * kStages * kTileSlots * 8;
+
+  // Issue the loads of this sub-group's tile of iteration `it` into buffer
+  // it % kStages: LDS slot q of the buffer holds row q / kRowSlots, piece
+  // q % kRowSlots (the pad piece and slots past the tile repeat a valid
+  // 16 bytes of the zero row or of the row).
+  auto issue = [&](int it) {
+    const int tt = 2 * it + sg;
+    if (tt >= ntile) return;
+    const int t0 = r0 + tt * kTile;
+    uint16_t* buf = ring + (size_t)(it % kStages) * kTileSlots * 8;
+    for (int j = wv; j < kTileLoads; j += WPS) {
+      const int q = j * 64 + lane;
+      const int row = q / kRowSlots, piece = q - row * kRowSlots;
+      const uint16_t* src = g_zero_row;
+      const int i = t0 + row;
+      if (row < kTile && i < r1) {
+        const int cd = code[i - r0];
+        if (cd != kNoRow)
+          src = cd >= 0 ? pool_b + (size_t)cd * kLat : host_b + (size_t)(~cd) * kLat;
+      }
+      load_lds16(src + (piece < kChunks16 ? piece : 0) * 8, buf + (size_t)j * 64 * 8);
+    }
+  };
+
   // Transposed-read address of this lane within a tile half: token
   // 4 g + (c / 4), columns 4 (c % 4) .. of each 16-column group.
   const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4;
 
-  // Tile loads go to registers one tile ahead: tile t+1's loads are in
-  // flight while tile t is computed.  Consecutive threads take consecutive
-  // 16-byte pieces of a row.
-  v4u data[kPer];
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int q = threadIdx.x + u * NT;
-      data[u] = v4u{0u, 0u, 0u, 0u};
-      if (q < kTile * kChunks16) {
-        const int r = q / kChunks16, ch = q - r * kChunks16;
-        const int i = t0 + r;
-        if (i < r1) {
-          const int cd = code[i - r0];
-          if (cd != kNoRow) {
-            const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
-                                           : host_b + (size_t)(~cd) * kLat;
-            data[u] = *reinterpret_cast<const v4u*>(rowp + ch * 8);
-          }
-        }
-      }
-    }
-  };
   __syncthreads();            // row table visible to every wave
-  if (r0 < r1) load_tile(r0);
-
-  for (int t0 = r0; t0 < r1; t0 += kTile) {
-    __syncthreads();   // previous tile fully consumed
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int q = threadIdx.x + u * NT;
-      if (q < kTile * kChunks16) {
-        const int r = q / kChunks16, ch = q - r * kChunks16;
-        *reinterpret_cast<v4u*>(&krow[r * kKStride + ch * 8]) = data[u];
-      }
-    }
-    __syncthreads();
-    if (t0 + kTile < r1) load_tile(t0 + kTile);
+  issue(0);
+  for (int it = 0; it < iters; ++it) {
+    wait_vmem_all();          // this wave's loads of tile `it` have landed
+    __syncthreads();          // ... and every wave's; tile it-1 consumed
+    issue(it + 1);
+    const int tt = 2 * it + sg;
+    if (tt >= ntile) continue;
+    const int t0 = r0 + tt * kTile;
+    const uint16_t* krow = ring + (size_t)(it % kStages) * kTileSlots * 8;
 
     // S^T for two 16-token halves of the tile.
     v4f s[2];
@@ -236,11 +272,43 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     }
   }
 
-  // Unnormalised partial: O^T rows 16 nt + 4 g + r of head h0 + c.
-  float* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal;
+  // Merge sub-group 1 into sub-group 0 (same heads, same lane layout)
+  // through LDS, in fixed order.
+  __syncthreads();            // every tile consumed; the ring is free
+  v4f* ostage = reinterpret_cast<v4f*>(smem);                  // [wv][nt][lane]
+  float2* mlstage = reinterpret_cast<float2*>(smem + (size_t)WPS * (kVal / 16) * 64 * 8);
+  if (sg == 1) {
 #pragma unroll
-  for (int nt = 0; nt < kVal / 16; ++nt)
-    *reinterpret_cast<v4f*>(pa + nt * 16 + g * 4) = oacc[nt];
+    for (int nt = 0; nt < kVal / 16; ++nt) ostage[(wv * (kVal / 16) + nt) * 64 + lane] = oacc[nt];
+    mlstage[wv * 64 + lane] = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  if (sg == 1) return;
+  const float2 o1 = mlstage[wv * 64 + lane];
+  float w0 = 1.f, w1 = 0.f;
+  if (o1.y > 0.f) {
+    if (l_run > 0.f) {
+      const float M = fmaxf(m_run, o1.x);
+      w0 = exp2f(m_run - M);
+      w1 = exp2f(o1.x - M);
+      m_run = M;
+    } else {
+      w0 = 0.f;
+      w1 = 1.f;
+      m_run = o1.x;
+    }
+    l_run = w0 * l_run + w1 * o1.y;
+  }
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c.
+  _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal;
+#pragma unroll
+  for (int nt = 0; nt < kVal / 16; ++nt) {
+    v4f o = oacc[nt] * w0;
+    if (w1 != 0.f) o += ostage[(wv * (kVal / 16) + nt) * 64 + lane] * w1;
+    o *= inv;
+    *reinterpret_cast<v4h*>(pa + nt * 16 + g * 4) = __builtin_convertvector(o, v4h);
+  }
   if (g == 0)
     part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(m_run, l_run);
 }
@@ -297,9 +365,10 @@ __global__ __launch_bounds__(kCopyThreads) void miss_rows_copy_kernel(
   }
 }
 
-// Merge the chunk partials of one (request, token, head) in chunk order.
+// Merge the chunk partials of one (request, token, head) in chunk order;
+// each partial is normalised, so its weight is 2^(m - M) times its sum.
 __global__ __launch_bounds__(128) void mla_combine_kernel(
-    const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
+    const _Float16* __restrict__ part_acc, const float2* __restrict__ part_ml,
     float* __restrict__ out, float* __restrict__ lse, int H, int nchunk) {
   const int h = blockIdx.x, bj = blockIdx.y, t = threadIdx.x;
   const float2* ml = part_ml + (size_t)bj * nchunk * H + h;
@@ -313,29 +382,33 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(
   for (int ci = 0; ci < nchunk; ++ci) {
     const float2 v = ml[(size_t)ci * H];
     if (!(v.y > 0.f)) continue;
-    const float w = exp2f(v.x - M);
-    den += w * v.y;
-    const v4f a = *reinterpret_cast<const v4f*>(
+    const float w = exp2f(v.x - M) * v.y;
+    den += w;
+    const v4h pk = *reinterpret_cast<const v4h*>(
         part_acc + (((size_t)bj * nchunk + ci) * H + h) * kVal + t * 4);
-    acc += w * a;
+    acc += w * __builtin_convertvector(pk, v4f);
   }
   const float inv = 1.f / den;
   *reinterpret_cast<v4f*>(out + ((size_t)bj * H + h) * kVal + t * 4) = acc * inv;
   if (lse && t == 0) lse[(size_t)bj * H + h] = (M + log2f(den)) * 0.69314718055994531f;
 }
 
-template <int NW>
+template <int WPS>
 hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
-                    uint16_t* pool, const uint16_t* host, float* part_acc,
+                    const uint16_t* pool, const uint16_t* host, _Float16* part_acc,
                     float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kMlaLds);
+  if (e != hipSuccess) return e;
   // 1-D grid over (item, head group) in whole rounds of 8 XCDs.
   const int items = d.batch * d.mtp * p.nchunk;
   const int rounds = ((items + 7) / 8) * p.head_groups;
   dim3 grid(rounds * 8);
-  hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), 0, s, q,
+  hipLaunchKernelGGL((sparse_mla_kernel<WPS>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
@@ -350,22 +423,23 @@ MlaPlan plan_sparse_mla(const ess_dims& d) {
   const int H = d.mla_heads;
   p.heads_per_wg = (H % 64 == 0) ? 64 : (H % 48 == 0) ? 48 : (H % 32 == 0) ? 32 : 16;
   p.head_groups = H / p.heads_per_wg;
-  // Enough workgroups to cover the chip about twice; more chunks also mean
-  // more partial traffic, so stop there.
+  // One workgroup per compute unit (each holds nearly all of a CU's LDS);
+  // more chunks would also mean more partial traffic.
   int target = 256;
   if (const char* env = std::getenv("ESS_MLA_TARGET_WGS")) {
     const int v = std::atoi(env);
     if (v > 0) target = v;
   }
   const int base = d.batch * d.mtp * p.head_groups;
-  const int max_chunks = (d.topk + kTile - 1) / kTile;
+  // A chunk is a whole number of tile pairs (one tile per sub-group).
+  const int max_chunks = (d.topk + 2 * kTile - 1) / (2 * kTile);
   int nchunk = (target + base - 1) / base;
   const int min_chunks = (d.topk + kMaxChunkRows - 1) / kMaxChunkRows;
   if (nchunk < min_chunks) nchunk = min_chunks;   // miss list fits in LDS
   if (nchunk < 1) nchunk = 1;
   if (nchunk > max_chunks) nchunk = max_chunks;
   const int per = (d.topk + nchunk - 1) / nchunk;
-  p.rows_per_chunk = (per + kTile - 1) / kTile * kTile;
+  p.rows_per_chunk = (per + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
   p.nchunk = (d.topk + p.rows_per_chunk - 1) / p.rows_per_chunk;
   return p;
 }
@@ -373,7 +447,7 @@ MlaPlan plan_sparse_mla(const ess_dims& d) {
 size_t sparse_mla_ws_bytes(const ess_dims& d) {
   const MlaPlan p = plan_sparse_mla(d);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
-  return align_up(parts * kVal * sizeof(float), 256) +
+  return align_up(parts * kVal * sizeof(_Float16), 256) +
          align_up(parts * sizeof(float2), 256);
 }
 
@@ -395,9 +469,9 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
     if (ce != hipSuccess) return ce;
   }
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
-  float* part_acc = static_cast<float*>(ws);
+  _Float16* part_acc = static_cast<_Float16*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(
-      static_cast<char*>(ws) + align_up(parts * kVal * sizeof(float), 256));
+      static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
   switch (p.heads_per_wg / 16) {
     case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
