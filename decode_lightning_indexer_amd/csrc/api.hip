@@ -325,15 +325,21 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }
+  const int lstride = d->mtp * d->topk;
   if (mode == ESS_MODE_INLINE) {
+    // Misses first in time: the update's miss list lands in the pool (the
+    // copy runs alone at the host link's rate), then the attention reads
+    // every selected row from its slot.
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
       e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, stream);
       if (e == hipSuccess)
-        e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot,
-                                   io.row_dst, io.n_sel, io.pool,
-                                   io.host_view, io.out, io.lse, io.ws,
-                                   stream);
+        e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
+                                  io.n_miss, io.host_view, io.pool, stream);
+      if (e == hipSuccess)
+        e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot_post,
+                                   nullptr, io.n_sel, io.pool, io.host_view,
+                                   io.out, io.lse, io.ws, stream);
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }
@@ -346,7 +352,6 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   if ((s = get_events((size_t)n_layers + 1, &ev)) != ESS_OK) return s;
   e = hipEventRecord(ev[n_layers], stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[n_layers], 0);
-  const int lstride = d->mtp * d->topk;
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
     const ess_layer_io& io = layers[l];
     e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, side);

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const int chunk = nchunk - 1 - item / n_bj;
   const int b = bj / m;
   const int r0 = chunk * rows_per_chunk;
-  const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
+  const int rend = min(k, r0 + rows_per_chunk);    // rows the table covers
   const int h0 = hg * (WPS * 16) + wv * 16;
 
   const int32_t* rpos = sel_pos + (size_t)bj * k;
@@ -147,7 +147,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   // Row sources of the chunk, once: hits read their slot, designated-writer
   // misses their new slot (filled by the copy kernel that runs first), other
   // misses host memory.  Out-of-range values (caller error) give zero rows.
-  for (int i = r0 + threadIdx.x; i < r1; i += NT) {
+  // The table covers the chunk up to k, so its loads do not wait for n_sel;
+  // entries at or past n_sel are never used.
+  for (int i = r0 + threadIdx.x; i < rend; i += NT) {
     const int src = rsrc[i], pos = rpos[i];
     const int dst = rdst ? rdst[i] : -1;
     int cd = kNoRow;
@@ -168,6 +170,8 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32);
   }
 
+  const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
+
   float m_run = -__builtin_inff(), l_run = 0.f;
   v4f oacc[kVal / 16];
 #pragma unroll
@@ -182,23 +186,32 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   // Issue the loads of this sub-group's tile of iteration `it` into buffer
   // it % kStages: LDS slot q of the buffer holds row q / kRowSlots, piece
   // q % kRowSlots (the pad piece and slots past the tile repeat a valid
-  // 16 bytes of the zero row or of the row).
+  // 16 bytes of the zero row or of the row).  Unrolled and branch-free, so
+  // the row-table reads of all of a wave's loads are in flight together.
   auto issue = [&](int it) {
     const int tt = 2 * it + sg;
     if (tt >= ntile) return;
     const int t0 = r0 + tt * kTile;
     uint16_t* buf = ring + (size_t)(it % kStages) * kTileSlots * 8;
-    for (int j = wv; j < kTileLoads; j += WPS) {
-      const int q = j * 64 + lane;
-      const int row = q / kRowSlots, piece = q - row * kRowSlots;
-      const uint16_t* src = g_zero_row;
-      const int i = t0 + row;
-      if (row < kTile && i < r1) {
-        const int cd = code[i - r0];
-        if (cd != kNoRow)
-          src = cd >= 0 ? pool_b + (size_t)cd * kLat : host_b + (size_t)(~cd) * kLat;
+    constexpr int kPerWave = (kTileLoads + WPS - 1) / WPS;
+    // Recomputed per tile (a few ALU ops per load) rather than hoisted out
+    // of the tile loop, where the compiler would keep them all live.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int u = 0; u < kPerWave; ++u) {
+      const int j = wv + u * WPS;
+      if (j < kTileLoads) {
+        const int q = j * 64 + ln;
+        const int row = q / kRowSlots, piece = q - row * kRowSlots;
+        const int rr = min(row, kTile - 1);
+        const int cd = code[t0 - r0 + rr];
+        const bool use = row < kTile && t0 + row < r1 && cd != kNoRow;
+        const int off = (piece < kChunks16 ? piece : 0) * 8;
+        const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
+                                       : host_b + (size_t)(~cd) * kLat;
+        load_lds16((use ? rowp : g_zero_row) + off, buf + (size_t)j * 64 * 8);
       }
-      load_lds16(src + (piece < kChunks16 ? piece : 0) * 8, buf + (size_t)j * 64 * 8);
     }
   };
 
@@ -272,45 +285,63 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     }
   }
 
-  // Merge sub-group 1 into sub-group 0 (same heads, same lane layout)
-  // through LDS, in fixed order.
+  // Merge the two sub-groups (same heads, same lane layout) through LDS, in
+  // fixed order: each hands the other the half of its accumulator in the
+  // other's value columns (sub-group s finishes columns [256 s, 256 s + 256))
+  // and both write their half of the partial.
   __syncthreads();            // every tile consumed; the ring is free
-  v4f* ostage = reinterpret_cast<v4f*>(smem);                  // [wv][nt][lane]
-  float2* mlstage = reinterpret_cast<float2*>(smem + (size_t)WPS * (kVal / 16) * 64 * 8);
-  if (sg == 1) {
+  constexpr int kHalf = kVal / 32;                   // 16-column groups per half
+  v4f* ostage = reinterpret_cast<v4f*>(smem);        // [sg][wv][nt][lane]
+  float2* mlstage = reinterpret_cast<float2*>(smem + (size_t)2 * WPS * kHalf * 64 * 8);
+  // Register indices stay compile-time constants (one branch per half).
+  v4f* mystage = ostage + (size_t)(sg * WPS + wv) * kHalf * 64 + lane;
+  if (sg == 0) {
 #pragma unroll
-    for (int nt = 0; nt < kVal / 16; ++nt) ostage[(wv * (kVal / 16) + nt) * 64 + lane] = oacc[nt];
-    mlstage[wv * 64 + lane] = make_float2(m_run, l_run);
+    for (int u = 0; u < kHalf; ++u) mystage[u * 64] = oacc[kHalf + u];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kHalf; ++u) mystage[u * 64] = oacc[u];
   }
+  mlstage[(sg * WPS + wv) * 64 + lane] = make_float2(m_run, l_run);
   __syncthreads();
-  if (sg == 1) return;
-  const float2 o1 = mlstage[wv * 64 + lane];
-  float w0 = 1.f, w1 = 0.f;
-  if (o1.y > 0.f) {
-    if (l_run > 0.f) {
-      const float M = fmaxf(m_run, o1.x);
-      w0 = exp2f(m_run - M);
-      w1 = exp2f(o1.x - M);
-      m_run = M;
+  const float2 mine = make_float2(m_run, l_run);
+  const float2 other = mlstage[((1 - sg) * WPS + wv) * 64 + lane];
+  // Sub-group 0's state first, then sub-group 1's, on both sides.
+  const float2 s0 = sg == 0 ? mine : other, s1 = sg == 0 ? other : mine;
+  float w0 = 1.f, w1 = 0.f, M = s0.x, l = s0.y;
+  if (s1.y > 0.f) {
+    if (s0.y > 0.f) {
+      M = fmaxf(s0.x, s1.x);
+      w0 = exp2f(s0.x - M);
+      w1 = exp2f(s1.x - M);
     } else {
       w0 = 0.f;
       w1 = 1.f;
-      m_run = o1.x;
+      M = s1.x;
     }
-    l_run = w0 * l_run + w1 * o1.y;
+    l = w0 * s0.y + w1 * s1.y;
   }
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float wm = sg == 0 ? w0 : w1, wo = sg == 0 ? w1 : w0;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c.
-  _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal;
-#pragma unroll
-  for (int nt = 0; nt < kVal / 16; ++nt) {
-    v4f o = oacc[nt] * w0;
-    if (w1 != 0.f) o += ostage[(wv * (kVal / 16) + nt) * 64 + lane] * w1;
-    o *= inv;
-    *reinterpret_cast<v4h*>(pa + nt * 16 + g * 4) = __builtin_convertvector(o, v4h);
+  _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal +
+                 sg * (kVal / 2) + g * 4;
+  const v4f* theirs = ostage + (size_t)((1 - sg) * WPS + wv) * kHalf * 64 + lane;
+#define ESS_MLA_FINISH(BASE)                                                   \
+  _Pragma("unroll") for (int u = 0; u < kHalf; ++u) {                          \
+    v4f o = oacc[(BASE) + u] * wm;                                             \
+    if (wo != 0.f) o += theirs[u * 64] * wo;                                   \
+    o *= inv;                                                                  \
+    *reinterpret_cast<v4h*>(pa + u * 16) = __builtin_convertvector(o, v4h);    \
   }
-  if (g == 0)
-    part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(m_run, l_run);
+  if (sg == 0) {
+    ESS_MLA_FINISH(0)
+  } else {
+    ESS_MLA_FINISH(kHalf)
+  }
+#undef ESS_MLA_FINISH
+  if (sg == 0 && g == 0)
+    part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(M, l);
 }
 
 // Designated-writer miss rows host -> their slot, spread over the chip: each
@@ -367,29 +398,54 @@ __global__ __launch_bounds__(kCopyThreads) void miss_rows_copy_kernel(
 
 // Merge the chunk partials of one (request, token, head) in chunk order;
 // each partial is normalised, so its weight is 2^(m - M) times its sum.
-__global__ __launch_bounds__(128) void mla_combine_kernel(
+// 64 threads per head, 8 values each (16-byte fp16 loads), 4 heads per
+// workgroup.  Chunks go in groups of 8 whose loads are all in flight
+// together, folded in with a running maximum (fixed order).
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+constexpr int kCombineHeads = 4;
+constexpr int kCombineGroup = 8;
+__global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
     const _Float16* __restrict__ part_acc, const float2* __restrict__ part_ml,
     float* __restrict__ out, float* __restrict__ lse, int H, int nchunk) {
-  const int h = blockIdx.x, bj = blockIdx.y, t = threadIdx.x;
+  const int bj = blockIdx.y;
+  const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
+  const int t = threadIdx.x & 63;
   const float2* ml = part_ml + (size_t)bj * nchunk * H + h;
-  float M = -__builtin_inff();
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const float2 v = ml[(size_t)ci * H];
-    if (v.y > 0.f) M = fmaxf(M, v.x);
-  }
-  float den = 0.f;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const float2 v = ml[(size_t)ci * H];
-    if (!(v.y > 0.f)) continue;
-    const float w = exp2f(v.x - M) * v.y;
-    den += w;
-    const v4h pk = *reinterpret_cast<const v4h*>(
-        part_acc + (((size_t)bj * nchunk + ci) * H + h) * kVal + t * 4);
-    acc += w * __builtin_convertvector(pk, v4f);
+  const _Float16* pp = part_acc + ((size_t)bj * nchunk * H + h) * kVal + t * 8;
+  float M = -__builtin_inff(), den = 0.f;
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  for (int c0 = 0; c0 < nchunk; c0 += kCombineGroup) {
+    float2 v[kCombineGroup];
+    v8h x[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const int ci = min(c0 + u, nchunk - 1);
+      v[u] = ml[(size_t)ci * H];
+      x[u] = *reinterpret_cast<const v8h*>(pp + (size_t)ci * H * kVal);
+      if (c0 + u >= nchunk) v[u].y = 0.f;          // past the last chunk
+    }
+    float mg = M;
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u)
+      if (v[u].y > 0.f) mg = fmaxf(mg, v[u].x);
+    if (mg == -__builtin_inff()) continue;          // nothing yet
+    const float sc = exp2f(M - mg);                 // 0 while M is -inf
+    den *= sc;
+    a0 *= sc;
+    a1 *= sc;
+    M = mg;
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const float w = v[u].y > 0.f ? exp2f(v[u].x - M) * v[u].y : 0.f;
+      den += w;
+      a0 += w * __builtin_convertvector(x[u].lo, v4f);
+      a1 += w * __builtin_convertvector(x[u].hi, v4f);
+    }
   }
   const float inv = 1.f / den;
-  *reinterpret_cast<v4f*>(out + ((size_t)bj * H + h) * kVal + t * 4) = acc * inv;
+  float* op = out + ((size_t)bj * H + h) * kVal + t * 8;
+  *reinterpret_cast<v4f*>(op) = a0 * inv;
+  *reinterpret_cast<v4f*>(op + 4) = a1 * inv;
   if (lse && t == 0) lse[(size_t)bj * H + h] = (M + log2f(den)) * 0.69314718055994531f;
 }
 
@@ -480,8 +536,9 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
     default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(d.mla_heads, d.batch * d.mtp),
-                     dim3(kVal / 4), 0, s, part_acc, part_ml, out, lse,
+  hipLaunchKernelGGL(mla_combine_kernel,
+                     dim3(d.mla_heads / kCombineHeads, d.batch * d.mtp),
+                     dim3(64 * kCombineHeads), 0, s, part_acc, part_ml, out, lse,
                      d.mla_heads, p.nchunk);
   return hipGetLastError();
 }

@@ -224,7 +224,8 @@ enum {
   ESS_MODE_FILL = 0,     /* first fill: top-C of token 0, empty-pool update,
                             host -> pool copy; no attention                  */
   ESS_MODE_INLINE = 1,   /* per layer on `stream`: scores, top-k, pool update,
-                            attention reading misses from host in-kernel     */
+                            the update's miss list copied host -> pool, then
+                            attention reading every row from the pool        */
   ESS_MODE_PREFETCH = 2  /* layer l+1's scores, top-k, update and miss copy
                             run on `side` while layer l's attention runs on
                             `stream`; attention then reads only the pool     */
