@@ -133,6 +133,13 @@ def trace_summary(path, steps, warmup):
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     def short(n):
+        import re
+        m = re.match(r"_ZN3ess12_GLOBAL__N_1(\d+)", n)   # names left mangled
+        if m:
+            ln = int(m.group(1))
+            base = n[m.end():m.end() + ln]
+            t = re.match(r"IL[ib](\d+)EE", n[m.end() + ln:])
+            return base + (f"<{t.group(1)}>" if t else "")
         n = n.replace("ess::(anonymous namespace)::", "").replace("void ", "")
         return n.split("(")[0]
     starts = [int(r["Start_Timestamp"]) for r in rows

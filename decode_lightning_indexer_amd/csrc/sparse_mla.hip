@@ -124,8 +124,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   // the 8 XCDs in turn, each with its own L2; the head groups of one chunk
   // get ids that are multiples of 8 apart, so they run on the same XCD close
   // together and the second reads the chunk's latents from that L2.  Items
-  // (request-token, chunk) are numbered with the chunk slowest and lowest
-  // ranks first; ids past the last item (padding to whole rounds) exit.
+  // (request-token, chunk) are numbered with the chunk slowest, the chunk
+  // nearest the top-k cut first (where rows miss most); ids past the last
+  // item (padding to whole rounds) exit.
   const int wg = blockIdx.x;
   const int xcd = wg & 7, round = wg >> 3;
   const int hg = round % head_groups;
