@@ -72,14 +72,15 @@ struct MlaPlan {
   int rows_per_chunk; // multiple of 64 (a tile per sub-group)
   int nchunk;         // chunks of rows per (request, token)
 };
-MlaPlan plan_sparse_mla(const ess_dims& d);
-size_t sparse_mla_ws_bytes(const ess_dims& d);
+// target_wgs: workgroups to aim for (0: the whole chip, one per CU).
+MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs = 0);
+size_t sparse_mla_ws_bytes(const ess_dims& d, int target_wgs = 0);
 hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              const int32_t* sel_pos, const int32_t* sel_src,
                              const int32_t* row_dst, const int32_t* n_sel,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
-                             hipStream_t s);
+                             hipStream_t s, int target_wgs = 0);
 
 // ---- miss copy ----------------------------------------------------------
 hipError_t launch_miss_copy(const ess_dims& d, int list_stride,

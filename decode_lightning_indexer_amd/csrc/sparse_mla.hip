@@ -51,8 +51,6 @@
 // Softmax runs in the log2 domain with a running max and sum per head.
 #include "ess_internal.h"
 
-#include <cstdlib>
-
 namespace ess {
 namespace {
 
@@ -475,18 +473,14 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
 
 }  // namespace
 
-MlaPlan plan_sparse_mla(const ess_dims& d) {
+MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs) {
   MlaPlan p;
   const int H = d.mla_heads;
   p.heads_per_wg = (H % 64 == 0) ? 64 : (H % 48 == 0) ? 48 : (H % 32 == 0) ? 32 : 16;
   p.head_groups = H / p.heads_per_wg;
   // One workgroup per compute unit (each holds nearly all of a CU's LDS);
   // more chunks would also mean more partial traffic.
-  int target = 256;
-  if (const char* env = std::getenv("ESS_MLA_TARGET_WGS")) {
-    const int v = std::atoi(env);
-    if (v > 0) target = v;
-  }
+  const int target = target_wgs > 0 ? target_wgs : 256;
   const int base = d.batch * d.mtp * p.head_groups;
   // A chunk is a whole number of tile pairs (one tile per sub-group).
   const int max_chunks = (d.topk + 2 * kTile - 1) / (2 * kTile);
@@ -501,8 +495,8 @@ MlaPlan plan_sparse_mla(const ess_dims& d) {
   return p;
 }
 
-size_t sparse_mla_ws_bytes(const ess_dims& d) {
-  const MlaPlan p = plan_sparse_mla(d);
+size_t sparse_mla_ws_bytes(const ess_dims& d, int target_wgs) {
+  const MlaPlan p = plan_sparse_mla(d, target_wgs);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   return align_up(parts * kVal * sizeof(_Float16), 256) +
          align_up(parts * sizeof(float2), 256);
@@ -513,8 +507,8 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              const int32_t* row_dst, const int32_t* n_sel,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
-                             hipStream_t s) {
-  const MlaPlan p = plan_sparse_mla(d);
+                             hipStream_t s, int target_wgs) {
+  const MlaPlan p = plan_sparse_mla(d, target_wgs);
   if (row_dst) {
     // Misses first: every designated-writer miss row lands in its slot
     // before the attention reads it there.
