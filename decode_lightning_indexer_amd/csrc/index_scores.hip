@@ -9,11 +9,11 @@
 //
 // Mapping onto v_mfma_f32_16x16x128_f8f6f4 (A: 16x128, B: 128x16, D: 16x16):
 //   A = 16 query heads x 128 dims (held in registers for the whole kernel),
-//   B = 128 dims x 16 positions (one 32-byte piece of a key row per lane,
-//       two coalesced 16-byte loads),
+//   B = 128 dims x 16 positions (32 bytes of a key row per lane, two
+//       16-byte loads),
 //   D[head][pos] -> each lane holds 4 heads of one position; it applies the
 //   ReLU and head weight to its 4 heads, and two lane exchanges finish the
-//   head sum.  Lane group g (lanes 16g..16g+15) feeds dims [32g, 32g+32) of
+//   head sum.  Lane group g (lanes 16g..16g+15) feeds the same 32 dims of
 //   both operands, so A and B agree on the reduction index.
 // Inputs with integer values in [-7, 7] and integer weights keep every
 // partial sum an integer below 2^24, so the fp32 result is exact.
@@ -30,27 +30,51 @@ constexpr int kThreads = 256;     // 4 waves
 constexpr int kGroups = 4;        // 16-position groups per wave iteration
 constexpr int kSpan = 1024;       // positions per workgroup
 
-// 32 bytes of a row for lane group g (zeros past a 64-wide row).  Key rows
-// are streamed once per step, so they are loaded non-temporally.
+// The 32 reduction-index bytes of a row held by lane group g: bytes
+// [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) (zeros past a 64-wide
+// row).  Queries and keys use the same assignment, so the reduction is
+// unchanged, and each of the two loads of a wave reads 64 contiguous bytes
+// of each of its 16 rows.  Key rows are streamed once per step, so they are
+// loaded non-temporally.
 template <int DI, bool STREAM>
 __device__ __forceinline__ v8i load_piece(const uint8_t* row, int g) {
-  if (DI == 128 || g < 2) {
-    const v4u* p = reinterpret_cast<const v4u*>(row + g * 32);
-    v4u a, b;
-    if (STREAM) {
-      a = __builtin_nontemporal_load(p);
-      b = __builtin_nontemporal_load(p + 1);
-    } else {
-      a = p[0];
-      b = p[1];
-    }
-    v8i v = {(int)a.x, (int)a.y, (int)a.z, (int)a.w,
-             (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-    return v;
+  const v4u* p = reinterpret_cast<const v4u*>(row + g * 16);
+  v4u a, b = {0u, 0u, 0u, 0u};
+  if (STREAM) {
+    a = __builtin_nontemporal_load(p);
+    if (DI == 128) b = __builtin_nontemporal_load(p + 4);
+  } else {
+    a = p[0];
+    if (DI == 128) b = p[4];
   }
-  v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
-  return z;
+  v8i v = {(int)a.x, (int)a.y, (int)a.z, (int)a.w,
+           (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  return v;
 }
+
+// Key rows are staged through LDS so that the loads from memory are fully
+// contiguous: each wave owns two buffers of 64 rows and copies its next 64
+// rows (DI * 64 contiguous bytes) with gfx950's 16-byte global-to-LDS load,
+// one 1 KB block per wave instruction, while it computes the current 64.
+// Rows sit at a stride of DI + 16 bytes in LDS (the pad slot repeats a valid
+// 16 bytes), which makes the operand reads conflict-free.  A wave reads only
+// its own buffers, so its own vmcnt wait is all the synchronisation needed.
+constexpr int kRows = kGroups * 16;   // rows per wave iteration
+
+__device__ __forceinline__ void load_lds16(const void* src, const void* lds_block) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
+      const __attribute__((address_space(3))) void*)lds_block);
+  // An SALU write of M0 needs one wait state before an LDS-DMA load reads it.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(base), "v"(src) : "memory", "m0");
+}
+
+template <int DI>
+struct Stage {
+  static constexpr int kSlots = DI / 16 + 1;           // 16-byte slots per row
+  static constexpr int kLoads = kSlots;                // wave loads per 64 rows
+  static constexpr int kBytes = kRows * kSlots * 16;   // one buffer
+};
 
 // NT: 16-row tiles of the [m * H_I][DI] query matrix; MT: query tokens m.
 template <int DI, int NT, int MT>
@@ -58,11 +82,14 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const int32_t* __restrict__ n_vis,
     float* __restrict__ scores, int L, int HI) {
+  using S = Stage<DI>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;   // lane group: reduction slice / output rows
   const int c = lane & 15;   // position within a 16-group / head row
   const int b = blockIdx.y;
+  uint8_t* buf0 = smem + (size_t)wave * 2 * S::kBytes;
 
   // Query tiles and head weights for this lane, resident in registers.
   constexpr int kTilesPerTok = NT / MT;   // a 16-row tile never straddles tokens
@@ -84,13 +111,43 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   const int span0 = blockIdx.x * kSpan;
   const int span1 = min(L, span0 + kSpan);
 
-  for (int p0 = span0 + wave * kGroups * 16; p0 < span1;
-       p0 += (kThreads / 64) * kGroups * 16) {
+  // Copy rows [p, p + kRows) into buffer `which`: LDS slot s of the buffer
+  // holds row s / kSlots, piece s % kSlots (rows past L repeat row L - 1).
+  auto stage = [&](int p, int which) {
+    uint8_t* buf = buf0 + which * S::kBytes;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // recomputed per call, not kept live
+#pragma unroll
+    for (int j = 0; j < S::kLoads; ++j) {
+      const int slot = j * 64 + ln;
+      const int r = slot / S::kSlots, pc = slot - r * S::kSlots;
+      const int row = min(p + r, L - 1);
+      const int off = pc < DI / 16 ? pc * 16 : 0;
+      load_lds16(kb + (size_t)row * DI + off, buf + j * 1024);
+    }
+  };
+
+  constexpr int kStep = (kThreads / 64) * kRows;
+  int p0 = span0 + wave * kRows;
+  int which = 0;
+  if (p0 < span1) stage(p0, 0);
+  for (; p0 < span1; p0 += kStep, which ^= 1) {
+    const bool more = p0 + kStep < span1;
+    if (more) stage(p0 + kStep, which ^ 1);
+    // This buffer's loads are older than the kLoads just issued.
+    if (more)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (S::kLoads & 15) | ((S::kLoads >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    const uint8_t* rows = buf0 + which * S::kBytes;
     v8i kv[kGroups];
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
-      const int pos = min(p0 + u * 16 + c, L - 1);
-      kv[u] = load_piece<DI, true>(kb + (size_t)pos * DI, g);
+      const v4u* pr = reinterpret_cast<const v4u*>(rows + (u * 16 + c) * S::kSlots * 16 + g * 16);
+      const v4u x = pr[0];
+      const v4u y = DI == 128 ? pr[4] : v4u{0u, 0u, 0u, 0u};
+      kv[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                  (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     }
     float mine[MT];
 #pragma unroll
@@ -135,8 +192,13 @@ hipError_t launch_t(const ess_dims& d, const uint8_t* q, const float* w,
                     const uint8_t* k, const int32_t* n_vis, float* scores,
                     hipStream_t s) {
   dim3 grid((d.ctx_len + kSpan - 1) / kSpan, d.batch);
+  const size_t lds = (size_t)(kThreads / 64) * 2 * Stage<DI>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)index_scores_kernel<DI, NT, MT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((index_scores_kernel<DI, NT, MT>), grid, dim3(kThreads),
-                     0, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads);
+                     lds, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads);
   return hipGetLastError();
 }
 
