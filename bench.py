@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget for the oracle CPU baseline (0 = skip)")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the 128K and multi-layer prefetch measurements")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (known "
                         "bytes) for scaling the HBM traffic counters")
@@ -171,6 +173,154 @@ def trace_summary(path, steps, warmup):
     for name in KERNEL_SOURCES:
         print(f"# source {name} {source_digest(name)}")
     return 0
+
+
+def staged_inputs(wl, layer, dev):
+    """Index queries and absorbed queries of every step of one layer, in
+    device memory (the timed region then reads nothing from the host but
+    the misses)."""
+    import numpy as np
+    import torch
+    from synth import gen
+    q_all, w, n_vis = gen.index_inputs(wl, layer)
+    qi = torch.from_numpy(q_all).to(dev)
+    qa = torch.empty((wl.steps, wl.batch, wl.mtp, wl.mla_heads, 576),
+                     dtype=torch.int16, device=dev)
+    for t in range(wl.steps):
+        qa[t].copy_(torch.from_numpy(gen.abs_query(wl, layer, t).view(np.int16)))
+    return qi, qa, w, n_vis
+
+
+def run_steps(args, name, n_layers, modes, K, W):
+    """Whole steps of a workload through ess_decode_step: per mode, from the
+    same first fill, W warm-up steps then K timed steps.  Returns per-mode
+    step times, misses of the last step, and the last step's miss copies
+    replayed alone (the host-link time a step needs)."""
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
+    from synth import gen, get_workload
+
+    dev = "cuda"
+    wl = get_workload(name).with_(steps=W + K)
+    d = dims_of(wl)
+    B, m, L, k = wl.batch, wl.mtp, wl.ctx_len, wl.topk
+    t0 = time.perf_counter()
+    hosts, lbs, qis, qas = [], [], [], []
+    n_vis = None
+    for l in range(n_layers):
+        h = HostStore((B, L, 576))
+        gen.fill_latents(wl, l, h.array)
+        lb = LayerBuffers(d, h)
+        kb = np.empty((B, L, wl.idx_dim), np.uint8)
+        gen.fill_index_keys(wl, l, kb)
+        lb.k_idx.copy_(torch.from_numpy(kb))
+        del kb
+        qi, qa, w, nv = staged_inputs(wl, l, dev)
+        lb.w_idx.copy_(torch.from_numpy(w))
+        n_vis = torch.from_numpy(nv).to(dev)
+        hosts.append(h); lbs.append(lb); qis.append(qi); qas.append(qa)
+    torch.cuda.synchronize()
+    log(args, f"{name}: {n_layers} layer(s) ready in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()              # default priority
+
+    def ios(t):
+        out = []
+        for l, lb in enumerate(lbs):
+            io = lb.io()
+            io.q_idx = qis[l][t].data_ptr()
+            io.q_abs = qas[l][t].data_ptr()
+            out.append(io)
+        return out
+
+    steps = [ios(t) for t in range(W + K)]
+    res = {}
+    for mode in modes:
+        for lb in lbs:
+            lb.reset(stream)
+        ess.ess_decode_step(d, steps[0], n_vis, ess.ESS_MODE_FILL, stream)
+        for t in range(W):
+            ess.ess_decode_step(d, steps[t], n_vis, mode, stream, side)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(K):
+            ess.ess_decode_step(d, steps[W + i], n_vis, mode, stream, side)
+        torch.cuda.synchronize()
+        res[mode] = (time.perf_counter() - t1) / K
+    n_miss = sum(int(lb.n_miss.sum()) for lb in lbs)
+    # The last step's miss lists copied again, alone: host-link time of a step.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for lb in lbs:
+        ess.ess_miss_copy(d, m * k, lb.miss_pos, lb.miss_slot, lb.n_miss,
+                          lb.host.dev, lb.pool, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t_copy = ev[0].elapsed_time(ev[1]) * 1e-3
+    for h in hosts:
+        h.free()
+    return res, n_miss, t_copy, wl
+
+
+def extra_measurements(args):
+    """The 128K / MTP=2 configuration at its three query-drift rates, and the
+    16-layer configuration's per-layer shape over 4 layers with and without
+    side-stream prefetch."""
+    from decode_lightning_indexer_amd import ess
+    out = {}
+    K, W = 16, 4
+    for name in ("128k-b8-mtp2-r099", "128k-b8-mtp2-r095", "128k-b8-mtp2-r080"):
+        res, n_miss, t_copy, wl = run_steps(args, name, 1, [ess.ESS_MODE_INLINE], K, W)
+        t = res[ess.ESS_MODE_INLINE]
+        out[name] = {"steps_per_s": 1 / t, "query_tok_s": wl.batch * wl.mtp / t,
+                     "us_per_step": t * 1e6, "rho": wl.rho,
+                     "misses_last_step": n_miss,
+                     "miss_rate_last_step": n_miss / (wl.batch * wl.mtp * wl.topk),
+                     "miss_copy_us_last_step": t_copy * 1e6}
+    name = "64k-b32-16layer"
+    n_layers = 4
+    res, n_miss, t_copy, wl = run_steps(
+        args, name, n_layers, [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH], K, W)
+    ti, tp = res[ess.ESS_MODE_INLINE], res[ess.ESS_MODE_PREFETCH]
+    # Prefetch hides the next layer's selection under this layer's copy and
+    # attention: the share of the step's non-copy work that disappears, and
+    # how much of each step the host link is busy.
+    out[name] = {"layers_timed": n_layers,
+                 "inline_us_per_step": ti * 1e6, "prefetch_us_per_step": tp * 1e6,
+                 "query_tok_s_prefetch": wl.batch * wl.mtp / tp,
+                 "misses_last_step": n_miss,
+                 "miss_copy_us_last_step": t_copy * 1e6,
+                 "link_busy_inline": t_copy / ti, "link_busy_prefetch": t_copy / tp,
+                 "hidden_noncopy_fraction": (ti - tp) / (ti - t_copy) if ti > t_copy else None}
+    return out
+
+
+def indexer_flushed(d, lb, q_idx, n_vis, stream, reps=10):
+    """Indexer kernel time alone: back to back, and each call after reading
+    512 MB of other data (evicts the 256 MB last-level cache, which the
+    67 MB index cache would otherwise sit in, without leaving dirty lines to
+    write back)."""
+    import torch
+    from decode_lightning_indexer_amd import ess
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 2)]
+    for i in range(reps):
+        scratch.sum()
+        ev[2 * i].record(stream)
+        ess.ess_index_scores(d, q_idx, lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    flushed = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
+    ev[-2].record(stream)
+    for _ in range(reps):
+        ess.ess_index_scores(d, q_idx, lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
+    ev[-1].record(stream)
+    torch.cuda.synchronize()
+    warm = ev[-2].elapsed_time(ev[-1]) / reps
+    del scratch
+    return flushed * 1e-3, warm * 1e-3
 
 
 def main():
@@ -354,6 +504,8 @@ def main():
     torch.cuda.synchronize()
     host_gbps = B * C * 1152 / (ev_h[0].elapsed_time(ev_h[1]) * 1e-3) / 1e9
 
+    t_idx_flushed, t_idx_warm = indexer_flushed(d, lb, q_idx[W + K - 1], n_vis, stream)
+
     # Algorithmic bytes / flops per launch.
     idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
     idx_flop = 2 * B * m * wl.idx_heads * wl.idx_dim * L
@@ -367,7 +519,9 @@ def main():
         "index_scores": {"kernel": "index_scores_kernel", "bound": "hbm",
                          "achieved": idx_bytes / (stage_us[0] * 1e3),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "bytes_per_launch": idx_bytes},
+                         "bytes_per_launch": idx_bytes,
+                         "alone_cache_flushed_gbps": idx_bytes / t_idx_flushed / 1e9,
+                         "alone_back_to_back_gbps": idx_bytes / t_idx_warm / 1e9},
         "miss_copy": {"kernel": "miss_copy_kernel", "bound": "host-link",
                       "achieved": miss_bytes / (stage_us[3] * 1e3),
                       "peak": PCIE5_X16_GBPS, "unit": "GB/s",
@@ -417,10 +571,14 @@ def main():
         "roofline": roof,
         "rooflines": roofs,
     }
+    host.free()
+    del lb, q_idx, q_abs
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["extra"] = extra_measurements(args)
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
-    host.free()
     print(json.dumps(res), flush=True)
     return 0
 

@@ -344,25 +344,27 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }
 
-  // Prefetch: the side stream selects every layer and copies its misses into
-  // the pool, running ahead; the main stream runs layer l's attention once
-  // layer l's copy is done, so layer l+1's selection and copy overlap layer
-  // l's attention.
+  // Prefetch: the side stream selects every layer (scores, top-k, pool
+  // update) back to back, running ahead; the main stream copies layer l's
+  // misses into the pool once layer l is selected, then runs its attention.
+  // Layer l+1's selection thus runs under layer l's copy and attention, and
+  // the host link carries the copies nearly back to back.  (Measured on
+  // MI355X: a miss copy beside an attention slows both, so the two stay on
+  // one stream.)
   hipEvent_t* ev;
   if ((s = get_events((size_t)n_layers + 1, &ev)) != ESS_OK) return s;
   e = hipEventRecord(ev[n_layers], stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[n_layers], 0);
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
-    const ess_layer_io& io = layers[l];
-    e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, side);
-    if (e == hipSuccess)
-      e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
-                                io.n_miss, io.host_view, io.pool, side);
+    e = enqueue_select(*d, layers[l], n_vis, d->topk, d->mtp, side);
     if (e == hipSuccess) e = hipEventRecord(ev[l], side);
   }
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
     const ess_layer_io& io = layers[l];
     e = hipStreamWaitEvent(stream, ev[l], 0);
+    if (e == hipSuccess)
+      e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
+                                io.n_miss, io.host_view, io.pool, stream);
     if (e == hipSuccess)
       e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot_post,
                                  nullptr, io.n_sel, io.pool, io.host_view,

@@ -226,9 +226,11 @@ enum {
   ESS_MODE_INLINE = 1,   /* per layer on `stream`: scores, top-k, pool update,
                             the update's miss list copied host -> pool, then
                             attention reading every row from the pool        */
-  ESS_MODE_PREFETCH = 2  /* layer l+1's scores, top-k, update and miss copy
-                            run on `side` while layer l's attention runs on
-                            `stream`; attention then reads only the pool     */
+  ESS_MODE_PREFETCH = 2  /* every layer's scores, top-k and update run ahead
+                            on `side`; `stream` copies layer l's misses as
+                            soon as layer l is selected, then attends, so
+                            layer l+1's selection overlaps layer l's copy
+                            and attention; attention reads only the pool     */
 };
 
 /* A whole decode step over n_layers layers (ESS concept page: layer-wise
