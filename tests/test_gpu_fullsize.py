@@ -38,6 +38,15 @@ def test_128k_b8_mtp2_full_size():
     assert np.all(recs["steps"][-1][0]["n_sel"] == wl.topk)
 
 
+def test_128k_b8_mtp2_heavy_misses_full_size():
+    # About half of every step's selection misses: the LRU ring turns over
+    # fast (victim scans over dead entries, compaction when it fills).
+    wl = get_workload("128k-b8-mtp2-r080").with_(steps=3)
+    recs = _check(wl, requests=[3])
+    n_miss = sum(int(s[0]["n_miss"].sum()) for s in recs["steps"][1:])
+    assert n_miss > 0.3 * 2 * wl.batch * wl.mtp * wl.topk
+
+
 def test_1m_b1_c16k_full_size():
     wl = get_workload("1m-b1-c16k").with_(steps=4)
     _check(wl, requests=[0])
