@@ -274,6 +274,12 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
   hipError_t e = ess::launch_index_scores(d, io.q_idx, io.w_idx, io.k_idx,
                                           n_vis, io.scores, st);
   if (e != hipSuccess) return e;
+  if (ess::select_update_fits(d, k, n_tok))
+    return ess::launch_select_update(d, k, io.scores, n_vis, io.cache_slots,
+                                     io.sel_pos, io.sel_slot, io.n_sel,
+                                     io.slot_pos, io.lru_state, io.miss_pos,
+                                     io.miss_slot, io.n_miss, io.n_evict,
+                                     io.row_dst, io.sel_slot_post, st);
   e = ess::launch_topk(d, k, n_tok, io.scores, n_vis, io.cache_slots,
                        io.sel_pos, io.sel_slot, io.n_sel, st);
   if (e != hipSuccess) return e;

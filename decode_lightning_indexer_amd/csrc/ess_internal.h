@@ -57,6 +57,17 @@ inline size_t lru_bytes_per_req(int C) {
 
 hipError_t launch_pool_reset(const ess_dims& d, int32_t* cache_slots,
                              int32_t* slot_pos, void* lru, hipStream_t s);
+// Top-k and residency update of one query token per request in one kernel
+// (select_update_fits tells when it applies).
+bool select_update_fits(const ess_dims& d, int k, int n_tok);
+hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
+                                const int32_t* n_vis, int32_t* cache_slots,
+                                int32_t* sel_pos, int32_t* sel_slot,
+                                int32_t* n_sel, int32_t* slot_pos, void* lru,
+                                int32_t* miss_pos, int32_t* miss_slot,
+                                int32_t* n_miss, int32_t* n_evict,
+                                int32_t* row_dst, int32_t* sel_slot_post,
+                                hipStream_t s);
 hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               const int32_t* sel_pos, const int32_t* n_sel,
                               int32_t* cache_slots, int32_t* slot_pos,

@@ -20,31 +20,19 @@
 // O(|union|) per update.  When the ring would overflow, its live entries
 // (at most C) are compacted to the front in order.
 //
-// One 1024-thread workgroup per request.
-#include "block_util.h"
-#include "ess_internal.h"
+#include "pool_update_body.h"
 
 namespace ess {
 namespace {
 
-constexpr int NT = 1024;
-constexpr int kSortBuckets = 2048;
-constexpr int kTwoBufferMax = 4096;   // entries sorted out of place up to this
-
-struct Ring {
-  int32_t slot;
-  int32_t stamp;
-};
-
-__device__ __forceinline__ LruHeader* hdr_of(void* lru, size_t stride, int b) {
-  return reinterpret_cast<LruHeader*>(static_cast<char*>(lru) + stride * b);
-}
+using pool::NT;
+using pool::kTwoBufferMax;
 
 __global__ __launch_bounds__(NT) void pool_reset_kernel(
     int32_t* __restrict__ cache_slots, int32_t* __restrict__ slot_pos,
     void* lru, size_t stride, int L, int C) {
   const int b = blockIdx.y;
-  LruHeader* h = hdr_of(lru, stride, b);
+  LruHeader* h = pool::hdr_of(lru, stride, b);
   int32_t* stamp = reinterpret_cast<int32_t*>(h + 1);
   const int i0 = blockIdx.x * NT + threadIdx.x;
   for (int i = i0; i < L; i += gridDim.x * NT) cache_slots[(size_t)b * L + i] = -1;
@@ -62,239 +50,10 @@ __global__ __launch_bounds__(NT) void pool_reset_kernel(
   }
 }
 
-// Entry layout (64 bits, sorted ascending): position (28 bits) | token (2) |
-// row (14) | slot + 1 (20; 0 until known).  Sorting on the whole value
-// orders positions ascending and, for a repeated position, the smallest
-// token first; the slot field is filled in place once a position's slot
-// after the update is known, so every row's outputs come from LDS.
-__device__ __forceinline__ uint64_t make_entry(int pos, int j, int i) {
-  return ((uint64_t)(uint32_t)pos << 36) | ((uint64_t)j << 34) | ((uint64_t)i << 20);
-}
-__device__ __forceinline__ int ent_pos(uint64_t e) { return (int)(e >> 36); }
-__device__ __forceinline__ int ent_tok(uint64_t e) { return (int)((e >> 34) & 3); }
-__device__ __forceinline__ int ent_row(uint64_t e) { return (int)((e >> 20) & 0x3FFF); }
-__device__ __forceinline__ int ent_slot(uint64_t e) { return (int)(e & 0xFFFFF) - 1; }
-__device__ __forceinline__ uint64_t with_slot(uint64_t e, int slot) {
-  return (e & ~0xFFFFFull) | (uint64_t)(slot + 1);
-}
-constexpr uint64_t kNoEntry = ~0ull;
-
-__global__ __launch_bounds__(NT) void pool_update_kernel(
-    const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ n_sel,
-    int32_t* __restrict__ cache_slots, int32_t* __restrict__ slot_pos,
-    void* lru, size_t stride, int32_t* __restrict__ miss_pos,
-    int32_t* __restrict__ miss_slot, int32_t* __restrict__ n_miss_out,
-    int32_t* __restrict__ n_evict_out, int32_t* __restrict__ row_dst,
-    int32_t* __restrict__ sel_slot_post, int L, int C, int k, int n_tok,
-    int epow2, int two_buffers, int pos_shift) {
+// One 1024-thread workgroup per request.
+__global__ __launch_bounds__(NT) void pool_update_kernel(pool::Args a) {
   extern __shared__ uint64_t smem_ent[];       // epow2 entries (x2: sort target)
-  __shared__ uint32_t tmp[NT / 64 + 1];
-  __shared__ uint32_t bcnt[kSortBuckets];
-  __shared__ int s_head_new;
-  uint64_t* ent = smem_ent;
-
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  LruHeader* h = hdr_of(lru, stride, b);
-  int32_t* stamp = reinterpret_cast<int32_t*>(h + 1);
-  Ring* ring = reinterpret_cast<Ring*>(stamp + C);
-  int32_t* cs = cache_slots + (size_t)b * L;
-  int32_t* sp = slot_pos + (size_t)b * C;
-  const size_t list0 = (size_t)b * n_tok * k;   // copy-list base
-  const size_t rows0 = (size_t)b * n_tok * k;   // per-row arrays base
-
-  const int head0 = h->head, tail0 = h->tail, free_head = h->free_head;
-  const int epoch = h->epoch, cap = h->cap;
-
-  int off[5];
-  off[0] = 0;
-  for (int j = 0; j < n_tok; ++j)
-    off[j + 1] = off[j] + min(max(n_sel[b * n_tok + j], 0), k);
-  const int n_e = off[n_tok];
-
-  // 0. Row outputs start empty.
-  for (int i = tid; i < n_tok * k; i += NT) {
-    row_dst[rows0 + i] = -1;
-    sel_slot_post[rows0 + i] = -1;
-  }
-  // 1. Entries of every way, then sort.  Out-of-range positions are dropped
-  // (they sort last and end the scan).
-  for (int e = tid; e < epow2; e += NT) {
-    uint64_t key = kNoEntry;
-    if (e < n_e) {
-      int j = 0;
-      while (e >= off[j + 1]) ++j;
-      const int i = e - off[j];
-      const int pos = sel_pos[rows0 + (size_t)j * k + i];
-      if (pos >= 0 && pos < L) key = make_entry(pos, j, i);
-      else h->err = 2;
-    }
-    ent[e] = key;
-  }
-  __syncthreads();
-  // Sort by position: buckets of the position's top 11 bits (selections are
-  // spread over the context, so buckets hold a few entries each), ordered
-  // within a bucket on the whole entry; a full sort if the buckets come out
-  // uneven or there is no room for a second buffer.
-  {
-    bool done = false;
-    if (two_buffers) {
-      const int shift = pos_shift;
-      auto bucket = [&](uint64_t x) {
-        const int bk = ent_pos(x) >> shift;
-        return bk < kSortBuckets ? bk : kSortBuckets - 1;   // dropped entries last
-      };
-      done = bucket_sort_u64<NT, false>(smem_ent, smem_ent + epow2, n_e, kSortBuckets,
-                                        bucket, bcnt, tmp, 256);
-    }
-    if (!done) block_sort_u64_n<NT, false>(smem_ent, epow2);
-  }
-
-  // 2. Unique positions (first entry of each run) and their lookup; a hit's
-  // slot goes into its entry and its stamp moves to this update (its old
-  // ring entry dies).
-  const int per = (epow2 + NT - 1) / NT;       // entries per thread, contiguous
-  const int e0 = tid * per;
-  auto head_of_run = [&](int e) {
-    return e == 0 || ent_pos(ent[e - 1]) != ent_pos(ent[e]);
-  };
-  uint32_t n_u_mine = 0, n_m_mine = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = e0 + q;
-    if (e >= n_e || ent[e] == kNoEntry) break;
-    if (head_of_run(e)) {
-      ++n_u_mine;
-      const int slot = cs[ent_pos(ent[e])];
-      if (slot >= 0 && slot < C) {
-        stamp[slot] = epoch;
-        ent[e] = with_slot(ent[e], slot);
-      } else {
-        ++n_m_mine;
-      }
-    }
-  }
-  uint32_t n_u, n_miss;
-  const uint32_t u_base = block_exscan<NT>(n_u_mine, tmp, &n_u);
-  const uint32_t m_base = block_exscan<NT>(n_m_mine, tmp, &n_miss);
-
-  // 3. Victims: never-used slots first, then the ring from its head.
-  const int n_free = C - free_head;
-  const int use_free = min((int)n_miss, n_free);
-  const int n_ev = (int)n_miss - use_free;
-  int head = head0;
-  int found = 0;
-  if (n_ev > 0) {
-    if (tid == 0) s_head_new = head0;
-    while (found < n_ev) {
-      const int idx = head + tid;
-      bool live = false;
-      int slot = -1;
-      if (idx < tail0) {
-        const Ring r = ring[idx];
-        slot = r.slot;
-        live = slot >= 0 && slot < C && stamp[slot] == r.stamp;
-      }
-      uint32_t tot;
-      const uint32_t rank = block_exscan<NT>(live ? 1u : 0u, tmp, &tot);
-      if (live && found + (int)rank < n_ev) {
-        const int v = found + (int)rank;
-        miss_slot[list0 + use_free + v] = slot;
-        const int old = sp[slot];
-        if (old >= 0 && old < L) cs[old] = -1;   // evict
-        if (v == n_ev - 1) s_head_new = idx + 1;
-      }
-      __syncthreads();
-      if (found + (int)tot >= n_ev) {
-        head = s_head_new;
-        found = n_ev;
-      } else {
-        found += (int)tot;
-        head += NT;
-        if (head >= tail0) {                   // ran dry: inconsistent state
-          if (tid == 0) h->err = 1;
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // 4. Pair misses (ascending position) with victims (in victim order).  A
-  // ring that ran dry (inconsistent state, flagged above) leaves the misses
-  // past the victims found unpaired.
-  {
-    const int paired = use_free + found;
-    uint32_t mi = m_base;
-    for (int q = 0; q < per; ++q) {
-      const int e = e0 + q;
-      if (e >= n_e || ent[e] == kNoEntry) break;
-      if (!head_of_run(e) || ent_slot(ent[e]) >= 0) continue;   // hit
-      const int pos = ent_pos(ent[e]);
-      const int v = (int)mi < use_free ? free_head + (int)mi
-                                       : miss_slot[list0 + mi];
-      if ((int)mi < paired && v >= 0 && v < C) {
-        cs[pos] = v;
-        sp[v] = pos;
-        stamp[v] = epoch;
-        miss_pos[list0 + mi] = pos;
-        miss_slot[list0 + mi] = v;
-        row_dst[rows0 + (size_t)ent_tok(ent[e]) * k + ent_row(ent[e])] = v;
-        ent[e] = with_slot(ent[e], v);
-      }
-      ++mi;
-    }
-  }
-  __syncthreads();
-
-  // 5. Make room on the ring: compact live entries to the front in order.
-  int tail = tail0;
-  if (tail + (int)n_u > cap) {
-    int dst = 0;
-    for (int src = head; src < tail; src += NT) {
-      const int idx = src + tid;
-      Ring r = {0, 0};
-      bool live = false;
-      if (idx < tail) {
-        r = ring[idx];
-        live = r.slot >= 0 && r.slot < C && stamp[r.slot] == r.stamp;
-      }
-      uint32_t tot;
-      const uint32_t rank = block_exscan<NT>(live ? 1u : 0u, tmp, &tot);
-      if (live) ring[dst + rank] = r;
-      dst += (int)tot;
-      __syncthreads();
-    }
-    head = 0;
-    tail = dst;
-  }
-
-  // 6. Push the union in ascending position order with current slots, and
-  // every row's slot after the update (from its run's first entry, at most
-  // n_tok - 1 entries back).
-  for (int q = 0, u = (int)u_base; q < per; ++q) {
-    const int e = e0 + q;
-    if (e >= n_e || ent[e] == kNoEntry) break;
-    const uint64_t x = ent[e];
-    int hd = e;
-    while (hd > 0 && ent_pos(ent[hd - 1]) == ent_pos(x)) --hd;
-    const int slot = ent_slot(ent[hd]);
-    sel_slot_post[rows0 + (size_t)ent_tok(x) * k + ent_row(x)] = slot;
-    if (hd == e) {
-      Ring r;
-      r.slot = slot;
-      r.stamp = epoch;
-      ring[tail + u] = r;
-      ++u;
-    }
-  }
-  if (tid == 0) {
-    h->head = head;
-    h->tail = tail + (int)n_u;
-    h->free_head = free_head + use_free;
-    h->epoch = epoch + 1;
-    n_miss_out[b] = (int)n_miss;
-    n_evict_out[b] = n_ev;
-  }
+  pool::update_request<false>(a, blockIdx.x, smem_ent, nullptr, nullptr, 0);
 }
 
 }  // namespace
@@ -330,11 +89,11 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)(kMaxTopk * sizeof(uint64_t)));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pool_update_kernel, dim3(d.batch), dim3(NT), lds, s,
-                     sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
+  const pool::Args a{sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
                      miss_pos, miss_slot, n_miss, n_evict, row_dst,
                      sel_slot_post, d.ctx_len, d.pool_slots, k, n_tok, epow2,
-                     two, pos_shift);
+                     two, pos_shift};
+  hipLaunchKernelGGL(pool_update_kernel, dim3(d.batch), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 

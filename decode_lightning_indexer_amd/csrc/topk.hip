@@ -28,6 +28,7 @@
 //      equal or near-equal scores) falls back to a full bitonic sort.
 #include "block_util.h"
 #include "ess_internal.h"
+#include "pool_update_body.h"
 
 namespace ess {
 namespace {
@@ -36,6 +37,7 @@ constexpr int NT = 1024;
 constexpr int kBins = 2048;
 constexpr int kSmall = 64;       // candidates sorted by one wave
 constexpr int kMaxBucket = 256;  // larger winner buckets take the full sort
+constexpr int kFusedMaxK = 4096;  // top-k + update in one workgroup up to this k
 
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -60,13 +62,17 @@ constexpr int VPT = 8;                 // 16-byte loads per thread per chunk
 constexpr int KPT = VPT * 4;           // keys per thread per chunk
 constexpr int CHUNK = NT * KPT;        // 32768 keys
 
-template <bool RES>
-__global__ __launch_bounds__(NT) void topk_kernel(
+// Top-k of one (request, token) row by a 1024-thread workgroup; returns the
+// number selected.  grp: kpow2 winners of LDS.  FUSE: the outputs are also
+// left in LDS (rpos, rslot) for the residency update that follows in the
+// same workgroup.
+template <bool RES, bool FUSE>
+__device__ int topk_row(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int n_tok, int k, int kpow2) {
-  extern __shared__ uint64_t grp[];  // kpow2: winners grouped by bucket
+    int n_tok, int k, int kpow2, int row, uint64_t* grp, int32_t* rpos,
+    int32_t* rslot) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t cand[kSmall];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
@@ -74,7 +80,6 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   __shared__ int s_bin;
 
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;
   const int b = row / n_tok, j = row % n_tok;
   const float* srow = scores + ((size_t)b * m + j) * L;
   int n = n_vis[b * m + j];
@@ -89,7 +94,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     os[i] = -1;
   }
   if (tid == 0) n_sel[b * n_tok + j] = keff;
-  if (keff == 0) return;
+  if (keff == 0) return 0;
+  // Output row r: the selection and its slot.
+#define EMIT(R, POS, SLOT)                                                    \
+  do {                                                                        \
+    op[R] = (POS);                                                            \
+    os[R] = (SLOT);                                                           \
+    if (FUSE) {                                                               \
+      rpos[R] = (POS);                                                        \
+      rslot[R] = (SLOT);                                                      \
+    }                                                                         \
+  } while (0)
 
   // Keys of one chunk for this thread.  A chunk wholly inside the visible
   // row (the common case) takes eight unconditional 16-byte loads, all in
@@ -274,10 +289,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
           for (int e = 0; e < 4; ++e) {
             const int p = pos_of(base, v, e);
             if (p < n && (uint64_t)kr[4 * v + e] == bin_lo) {
-              if (rank < need) {
-                op[nwin + rank] = p;
-                os[nwin + rank] = cs[p];
-              }
+              if (rank < need) EMIT(nwin + rank, p, cs[p]);
               ++rank;
             }
           }
@@ -296,8 +308,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     const uint64_t x = wave_bitonic_u64<true>(i < (int)nc ? cand[i] : 0ull, i);
     if ((uint32_t)i < need) {
       const int pos = (int)(~(uint32_t)x);
-      op[nwin + i] = pos;
-      os[nwin + i] = cs[pos];
+      EMIT(nwin + i, pos, cs[pos]);
     }
   }
 
@@ -313,8 +324,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
       const int hi = (int)hist[bk];
       int r = lo;
       for (int q = lo; q < hi; ++q) r += grp[q] > x;
-      op[r] = pos;
-      os[r] = sl;
+      EMIT(r, pos, sl);
     }
   } else {
     for (int i = nwin + tid; i < kpow2; i += NT) grp[i] = 0ull;
@@ -322,13 +332,45 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     block_sort_u64_n<NT, true>(grp, kpow2);
     for (int i = tid; i < (int)nwin; i += NT) {
       const int pos = (int)(~(uint32_t)grp[i]);
-      op[i] = pos;
-      os[i] = cs[pos];
+      EMIT(i, pos, cs[pos]);
     }
   }
+#undef EMIT
 #undef bucket_of
 #undef pos_of
 #undef ESS_TOPK_LOAD
+  return keff;
+}
+
+template <bool RES>
+__global__ __launch_bounds__(NT) void topk_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
+    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
+    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
+    int n_tok, int k, int kpow2) {
+  extern __shared__ uint64_t grp[];  // kpow2: winners grouped by bucket
+  topk_row<RES, false>(scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel, L, m,
+                       n_tok, k, kpow2, blockIdx.x, grp, nullptr, nullptr);
+}
+
+// One query token per request: the top-k and the residency update of a
+// request in one workgroup.  The update starts from the selections and
+// slots the top-k leaves in LDS, so neither is read back from memory, and
+// the step saves a kernel boundary.
+template <bool RES>
+__global__ __launch_bounds__(NT) void select_update_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
+    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
+    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
+    int k, int kpow2, pool::Args pa, int rank_off) {
+  extern __shared__ uint64_t dyn[];  // top-k winners, then the update's entries
+  int32_t* rpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dyn) + rank_off);
+  int32_t* rslot = rpos + k;
+  const int keff = topk_row<RES, true>(scores, n_vis, cache_slots, sel_pos, sel_slot,
+                                       n_sel, L, m, 1, k, kpow2, blockIdx.x, dyn,
+                                       rpos, rslot);
+  __syncthreads();   // ranked selections complete; the winners' buffer is free
+  pool::update_request<true>(pa, blockIdx.x, dyn, rpos, rslot, keff);
 }
 
 }  // namespace
@@ -354,6 +396,49 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
     hipLaunchKernelGGL(topk_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
                        scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
                        d.ctx_len, d.mtp, n_tok, k, kpow2);
+  return hipGetLastError();
+}
+
+bool select_update_fits(const ess_dims& d, int k, int n_tok) {
+  return n_tok == 1 && k <= kFusedMaxK;
+}
+
+hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
+                                const int32_t* n_vis, int32_t* cache_slots,
+                                int32_t* sel_pos, int32_t* sel_slot,
+                                int32_t* n_sel, int32_t* slot_pos, void* lru,
+                                int32_t* miss_pos, int32_t* miss_slot,
+                                int32_t* n_miss, int32_t* n_evict,
+                                int32_t* row_dst, int32_t* sel_slot_post,
+                                hipStream_t s) {
+  const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
+  const int epow2 = kpow2;
+  const int two = epow2 <= pool::kTwoBufferMax ? 1 : 0;
+  int bits = 0;
+  while ((1 << bits) < d.ctx_len) ++bits;
+  const int pos_shift = bits > 11 ? bits - 11 : 0;
+  const pool::Args pa{sel_pos, n_sel, cache_slots, slot_pos, lru,
+                      lru_bytes_per_req(d.pool_slots), miss_pos, miss_slot,
+                      n_miss, n_evict, row_dst, sel_slot_post, d.ctx_len,
+                      d.pool_slots, k, 1, epow2, two, pos_shift};
+  const size_t topk_bytes = (size_t)kpow2 * sizeof(uint64_t);
+  const size_t upd_bytes = (size_t)epow2 * sizeof(uint64_t) * (two ? 2 : 1);
+  const size_t rank_off = align_up(topk_bytes > upd_bytes ? topk_bytes : upd_bytes, 16);
+  const size_t lds = rank_off + 2 * (size_t)k * sizeof(int32_t);
+  const bool res = d.ctx_len <= CHUNK;
+  const void* fn = res ? (const void*)select_update_kernel<true>
+                       : (const void*)select_update_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  if (res)
+    hipLaunchKernelGGL(select_update_kernel<true>, dim3(d.batch), dim3(NT), lds, s,
+                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
+                       d.ctx_len, d.mtp, k, kpow2, pa, (int)rank_off);
+  else
+    hipLaunchKernelGGL(select_update_kernel<false>, dim3(d.batch), dim3(NT), lds, s,
+                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
+                       d.ctx_len, d.mtp, k, kpow2, pa, (int)rank_off);
   return hipGetLastError();
 }
 
