@@ -75,9 +75,8 @@ typedef enum ess_status {
   ESS_ERR_NOMEM = -5         /* host allocation failed / workspace too small */
 } ess_status;
 
-/* Bytes of workspace the calls below need for these dims (top-k scratch and
- * the attention's split-row partials).  One workspace serves one stream at a
- * time. */
+/* Bytes of workspace the calls below need for these dims (the attention's
+ * split-row partials).  One workspace serves one stream at a time. */
 size_t ess_workspace_bytes(const ess_dims* d);
 
 /* Bytes of the opaque per-layer LRU state (B requests): per request a header,
@@ -117,7 +116,8 @@ ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
  *                  (-1: not resident); -1 beyond n_sel
  * Inputs scores [B][m][L], n_vis [B][m], cache_slots [B][L]; outputs
  * sel_pos, sel_slot [B][n_tok][k] and n_sel [B][n_tok].  1 <= n_tok <= m,
- * 1 <= k <= 16384.  Scores must not be NaN.  ws: ess_workspace_bytes. */
+ * 1 <= k <= 16384.  Scores must not be NaN.  ws, ws_bytes: not used (the
+ * selection runs in on-chip memory); NULL and 0 are fine. */
 ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
                            const float* scores, const int32_t* n_vis,
                            const int32_t* cache_slots, int32_t* sel_pos,
@@ -185,7 +185,8 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
  * H2D load of the copy triples; ESS concept page: small-block transfers of
  * latent entries).  For each b and i < n_miss[b]:
  *   pool[b][miss_slot[b*list_stride + i]] = host_view[b][miss_pos[b*list_stride + i]]
- * Used for the first fill and for side-stream prefetch. */
+ * Used for the first fill and, by ess_decode_step, for every layer's misses
+ * after its update. */
 ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
                          const int32_t* miss_pos, const int32_t* miss_slot,
                          const int32_t* n_miss, const uint16_t* host_view,
