@@ -229,18 +229,30 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const int t0 = r0 + tt * kTile;
     const uint16_t* krow = ring + (size_t)(it % kStages) * kTileSlots * 8;
 
-    // S^T for two 16-token halves of the tile.
+    // S^T for the two 16-token halves of the tile: the two accumulator
+    // chains interleaved, and each step's operand reads issued before the
+    // previous step's MFMAs, so LDS latency overlaps the matrix work.
     v4f s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = &krow[(mt * 16 + c) * kKStride + g * 8];
+    {
+      const uint16_t* arow0 = &krow[c * kKStride + g * 8];
+      const uint16_t* arow1 = arow0 + 16 * kKStride;
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(arow0);
+      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(arow1);
 #pragma unroll
       for (int kk = 0; kk < kLat / 32; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + kk * 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc, 0, 0, 0);
+        bf16x8 n0 = a0, n1 = a1;
+        if (kk + 1 < kLat / 32) {
+          n0 = *reinterpret_cast<const bf16x8*>(arow0 + (kk + 1) * 32);
+          n1 = *reinterpret_cast<const bf16x8*>(arow1 + (kk + 1) * 32);
+        }
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], acc1, 0, 0, 0);
+        a0 = n0;
+        a1 = n1;
       }
-      s[mt] = acc;
+      s[0] = acc0;
+      s[1] = acc1;
     }
 
     // Online softmax for head h0 + c over this tile's tokens
@@ -272,15 +284,24 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
 
     // O^T += V^T P^T over the tile; V^T read transposed from the tile rows:
     // tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, column nt*16 + c.
+    // The next column block's reads are issued before this block's MFMA.
+    {
+      const uint16_t* vbase = &krow[tr_off];
+      v2u lo = tr_read(vbase), hi = tr_read(vbase + 16 * kKStride);
 #pragma unroll
-    for (int nt = 0; nt < kVal / 16; ++nt) {
-      const uint16_t* base = &krow[tr_off + nt * 16];
-      const v2u lo = tr_read(base);
-      const v2u hi = tr_read(base + 16 * kKStride);
-      const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
-      const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
-      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt] * alpha,
-                                                         0, 0, 0);
+      for (int nt = 0; nt < kVal / 16; ++nt) {
+        v2u nlo = lo, nhi = hi;
+        if (nt + 1 < kVal / 16) {
+          nlo = tr_read(vbase + (nt + 1) * 16);
+          nhi = tr_read(vbase + (nt + 1) * 16 + 16 * kKStride);
+        }
+        const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt] * alpha,
+                                                           0, 0, 0);
+        lo = nlo;
+        hi = nhi;
+      }
     }
   }
 
