@@ -4,9 +4,11 @@
 Workload: 32K context, 16 requests, one query token per step, 64x128 fp8
 indexer, top-2048, 128-head absorbed MLA over 576-wide bf16 latents, a hot
 pool of 8192 slots per request, latents in pinned host memory.  One step =
-indexer scores -> top-k with the slot lookup -> pool update -> the step's
-misses copied host -> pool -> attention over the selected rows (+ combine),
-for all 16 requests.  All per-step inputs (the drifting indexer queries and
+indexer scores -> top-k with the slot lookup -> pool update -> gather +
+attention over the selected rows (+ combine), for all 16 requests; with one
+query token per request the gather reads each miss from host memory inside
+the attention kernel and writes it to its pool slot from the tile (with
+several tokens the step's misses are copied host -> pool first).  All per-step inputs (the drifting indexer queries and
 the absorbed queries) are staged in device memory before the timed region;
 the pool's first fill runs before the warm-up steps.
 
@@ -386,6 +388,15 @@ def main():
 
     n_miss_all = torch.zeros((wl.steps, B), dtype=torch.int32, device=dev)
 
+    # One query token per request: misses are read from host memory inside
+    # the attention kernel (written to their slots from the tile).  Several
+    # tokens: the miss list is copied first, then the attention reads the pool.
+    fused = m == 1
+    names = (["index_scores", "topk_lookup", "pool_update", "gather_attention"] if fused
+             else ["index_scores", "topk_lookup", "pool_update", "miss_copy",
+                   "sparse_mla_decode"])
+    n_st = len(names)
+
     def step(t, ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -401,8 +412,13 @@ def main():
                             row_dst, post, stream)
         if ev is not None:
             ev[3].record(stream)
-        # Gather: the step's copy list host -> pool first (misses first at
-        # full link rate), then attention reading every row from the pool.
+        if fused:
+            ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
+                                      lb.pool, host.dev, lb.out, lb.lse, lb.ws,
+                                      lb.ws_bytes, stream)
+            if ev is not None:
+                ev[4].record(stream)
+            return
         ess.ess_miss_copy(d, lists, lb.miss_pos, lb.miss_slot, n_miss_all[t],
                           host.dev, lb.pool, stream)
         if ev is not None:
@@ -423,7 +439,7 @@ def main():
         step(t)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -431,9 +447,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    stage_ms = np.zeros(5)
+    stage_ms = np.zeros(n_st)
     for e in evs:
-        for s in range(5):
+        for s in range(n_st):
             stage_ms[s] += e[s].elapsed_time(e[s + 1])
     stage_us = stage_ms / K * 1e3
     n_miss_tot = int(n_miss_all[W:].sum())
@@ -459,7 +475,9 @@ def main():
     wall_plain = time.perf_counter() - t1
 
     # Overlap on the same steps' miss lists (the pages' OverlapRatio):
-    # T_fused = attention reading misses from host inside the kernel,
+    # T_fused = the gather call with per-row writer slots (one token per
+    # request: misses read from host inside the attention kernel and
+    # written to their slots from the tile; several: copied first),
     # T_copy  = the miss list copied host -> pool alone,
     # T_attn  = attention with every row read from the pool.
     ev_ov = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ov)]
@@ -512,9 +530,13 @@ def main():
     sel_bytes = B * m * k * 1152
     attn_flop = 2 * B * m * H * k * (576 + 512)
     attn_bytes = sel_bytes + B * m * H * (576 * 2 + 512 * 4)
-    names = ["index_scores", "topk_lookup", "pool_update", "miss_copy",
-             "sparse_mla_decode"]
     miss_bytes = n_miss_tot * 1152 / K
+    t_gather = float(stage_us[names.index("gather_attention")] if fused
+                     else stage_us[3] + stage_us[4])
+    # The attention's own HBM and MFMA rates: timed alone with every row in
+    # the pool when the gather is fused (the fused call is paced by the link).
+    t_attn_st = float(t_attn if fused else stage_us[-1])
+    attn_kernels = "sparse_mla_kernel+mla_combine_kernel"
     roofs = {
         "index_scores": {"kernel": "index_scores_kernel", "bound": "hbm",
                          "achieved": idx_bytes / (stage_us[0] * 1e3),
@@ -522,26 +544,43 @@ def main():
                          "bytes_per_launch": idx_bytes,
                          "alone_cache_flushed_gbps": idx_bytes / t_idx_flushed / 1e9,
                          "alone_back_to_back_gbps": idx_bytes / t_idx_warm / 1e9},
-        "miss_copy": {"kernel": "miss_copy_kernel", "bound": "host-link",
-                      "achieved": miss_bytes / (stage_us[3] * 1e3),
-                      "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                      "bytes_per_launch": miss_bytes,
-                      "measured_ceiling": host_gbps},
-        "sparse_mla_decode": {"kernel": "sparse_mla_kernel+mla_combine_kernel",
-                              "bound": "hbm",
-                              "achieved": attn_bytes / (stage_us[4] * 1e3),
-                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "bytes_per_launch": attn_bytes,
-                              "tflops": attn_flop / (stage_us[4] * 1e6),
-                              "mfma_frac": attn_flop / (stage_us[4] * 1e6) / BF16_PEAK_TFLOPS},
     }
+    attn_view = {"attention_us": t_attn_st,
+                 "hbm_gbps": attn_bytes / (t_attn_st * 1e3),
+                 "hbm_bytes_per_launch": attn_bytes,
+                 "hbm_frac": attn_bytes / (t_attn_st * 1e3) / HBM_PEAK_GBPS,
+                 "tflops": attn_flop / (t_attn_st * 1e6),
+                 "mfma_frac": attn_flop / (t_attn_st * 1e6) / BF16_PEAK_TFLOPS}
+    if fused:
+        # The host link sets the pace of the fused call: its misses cross
+        # it while the attention's HBM reads and MFMA work run.
+        roofs["gather_attention"] = {
+            "kernel": attn_kernels, "bound": "host-link",
+            "achieved": miss_bytes / (t_gather * 1e3), "peak": PCIE5_X16_GBPS,
+            "unit": "GB/s", "bytes_per_launch": miss_bytes,
+            "measured_ceiling": host_gbps, **attn_view}
+    else:
+        roofs["miss_copy"] = {"kernel": "miss_copy_kernel", "bound": "host-link",
+                              "achieved": miss_bytes / (stage_us[3] * 1e3),
+                              "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                              "bytes_per_launch": miss_bytes,
+                              "measured_ceiling": host_gbps}
+        roofs["sparse_mla_decode"] = {"kernel": attn_kernels, "bound": "hbm",
+                                      "achieved": attn_view["hbm_gbps"],
+                                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                      "bytes_per_launch": attn_bytes,
+                                      "tflops": attn_view["tflops"],
+                                      "mfma_frac": attn_view["mfma_frac"]}
     for r in roofs.values():
         r["frac"] = r["achieved"] / r["peak"]
     dom = int(np.argmax(stage_us))
     roof = dict(roofs.get(names[dom], {"kernel": names[dom], "bound": "alu",
                                         "achieved": None, "peak": None,
                                         "unit": "us", "frac": None}))
-    roof["traffic"] = recorded_traffic(roof["kernel"]) if roof["kernel"] in KERNEL_SOURCES else None
+    parts = [recorded_traffic(kn) for kn in roof["kernel"].split("+")
+             if kn in KERNEL_SOURCES]
+    roof["traffic"] = (sum(parts) if parts and all(x is not None for x in parts)
+                       and len(parts) == len(roof["kernel"].split("+")) else None)
 
     res = {
         "metric": "sparse decode steps/s & query-tok/s at 32K/128K; indexer HBM GB/s; miss-fetch GB/s",
@@ -554,16 +593,17 @@ def main():
         "config": {"workload": base.name,
                    "batch": B, "mtp": m, "ctx_len": L, "idx_heads": wl.idx_heads,
                    "idx_dim": wl.idx_dim, "topk": k, "mla_heads": H,
-                   "pool_slots": C, "rho": wl.rho, "miss_mode": "inline"},
+                   "pool_slots": C, "rho": wl.rho,
+                   "miss_mode": "in-kernel" if fused else "copy-first"},
         "steps_per_s": K / wall_plain,
         "steps_per_s_staged": K / wall,
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
         "indexer_gbps": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
-        "attention_tflops": attn_flop / (stage_us[4] * 1e-6) / 1e12,
+        "attention_tflops": attn_view["tflops"],
         "misses_per_step": n_miss_tot / K,
         "miss_rate": n_miss_tot / (K * B * m * k),
-        "miss_fetch_gbps": n_miss_tot * 1152 / K / (stage_us[3] * 1e-6) / 1e9,
-        "gather_us": float(stage_us[3] + stage_us[4]),
+        "miss_fetch_gbps": miss_bytes / (t_gather * 1e3),
+        "gather_us": t_gather,
         "host_link_gbps_measured": host_gbps,
         "overlap": {"t_copy_us": t_copy, "t_attn_us": t_attn, "t_fused_us": t_fused,
                     "ratio": overlap, "bound": overlap_bound,

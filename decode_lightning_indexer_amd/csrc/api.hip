@@ -289,6 +289,27 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                  io.n_evict, io.row_dst, io.sel_slot_post, st);
 }
 
+// Gather + attention of one selected layer.  One query token per request:
+// the attention reads each miss from host memory into its tile and writes it
+// to its slot from there, so the host reads run under the attention's work.
+// Several tokens: the update's miss list (each union miss once) is copied
+// first at the host link's rate, then the attention reads every row from
+// its slot.
+static hipError_t enqueue_attention(const ess_dims& d, const ess_layer_io& io,
+                                    hipStream_t st) {
+  if (d.mtp == 1)
+    return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
+                                  io.row_dst, io.n_sel, io.pool, io.host_view,
+                                  io.out, io.lse, io.ws, st);
+  hipError_t e = ess::launch_miss_copy(d, d.mtp * d.topk, io.miss_pos,
+                                       io.miss_slot, io.n_miss, io.host_view,
+                                       io.pool, st);
+  if (e != hipSuccess) return e;
+  return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot_post,
+                                nullptr, io.n_sel, io.pool, io.host_view,
+                                io.out, io.lse, io.ws, st);
+}
+
 ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
                            const ess_layer_io* layers, const int32_t* n_vis,
                            int32_t mode, hipStream_t stream,
@@ -331,32 +352,22 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }
-  const int lstride = d->mtp * d->topk;
   if (mode == ESS_MODE_INLINE) {
-    // Misses first in time: the update's miss list lands in the pool (the
-    // copy runs alone at the host link's rate), then the attention reads
-    // every selected row from its slot.
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
       e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, stream);
-      if (e == hipSuccess)
-        e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
-                                  io.n_miss, io.host_view, io.pool, stream);
-      if (e == hipSuccess)
-        e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot_post,
-                                   nullptr, io.n_sel, io.pool, io.host_view,
-                                   io.out, io.lse, io.ws, stream);
+      if (e == hipSuccess) e = enqueue_attention(*d, io, stream);
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }
 
   // Prefetch: the side stream selects every layer (scores, top-k, pool
-  // update) back to back, running ahead; the main stream copies layer l's
-  // misses into the pool once layer l is selected, then runs its attention.
-  // Layer l+1's selection thus runs under layer l's copy and attention, and
-  // the host link carries the copies nearly back to back.  (Measured on
-  // MI355X: a miss copy beside an attention slows both, so the two stay on
-  // one stream.)
+  // update) back to back, running ahead; the main stream runs layer l's
+  // gather + attention once layer l is selected.  Layer l+1's selection thus
+  // runs under layer l's miss transfer and attention, and the host link
+  // carries the layers' misses nearly back to back.  (Measured on MI355X: a
+  // miss copy kernel beside an attention slows both, so the transfer and
+  // the attention stay on one stream.)
   hipEvent_t* ev;
   if ((s = get_events((size_t)n_layers + 1, &ev)) != ESS_OK) return s;
   e = hipEventRecord(ev[n_layers], stream);
@@ -368,13 +379,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
     const ess_layer_io& io = layers[l];
     e = hipStreamWaitEvent(stream, ev[l], 0);
-    if (e == hipSuccess)
-      e = ess::launch_miss_copy(*d, lstride, io.miss_pos, io.miss_slot,
-                                io.n_miss, io.host_view, io.pool, stream);
-    if (e == hipSuccess)
-      e = ess::launch_sparse_mla(*d, io.q_abs, io.sel_pos, io.sel_slot_post,
-                                 nullptr, io.n_sel, io.pool, io.host_view,
-                                 io.out, io.lse, io.ws, stream);
+    if (e == hipSuccess) e = enqueue_attention(*d, io, stream);
   }
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }

@@ -13,19 +13,21 @@
 // rows in rank order, in fixed chunks of rows combined in fixed order; no
 // atomics.  Which rows came from host memory changes no arithmetic.
 //
-// Miss handling on MI355X: a miss costs a host-link read (~54 GB/s
+// Miss handling on MI355X: a miss costs a host-link read (~55 GB/s
 // measured) against an HBM read for a hit (8 TB/s), so the host link sets
-// the pace.  The pages fuse the copy into the attention so the copy hides
-// under it and put the misses at the head of the selection (same section).
-// Here the misses go first in time instead: one copy kernel spreads every
-// designated-writer miss row of the call evenly over the whole chip (rows
-// near the top-k cut miss most, so per-chunk copying leaves a few
-// workgroups with most of the rows), then the attention kernel reads those
-// rows from their new slots.  Measured on MI355X, the copy runs at the
-// link's rate only when nothing else is in flight: overlapping it with the
-// HBM-bound attention made both slower than running them back to back.
-// A miss row that another token's row writes (MTP ways sharing a miss)
-// is read straight from host memory inside the attention kernel.
+// the pace.  With one query token per request the kernel does what the
+// pages describe: a designated-writer miss is loaded from host memory into
+// the tile like any other row, and the first head group stores it from the
+// tile to its pool slot.  The host reads then run while the attention works
+// on the rows already in LDS.  The two head groups of a chunk run on one XCD
+// close together, so the second group's read of a host row comes from that
+// XCD's L2 and each miss crosses the link once (measured: 4.4K misses per
+// step at 32K x 16 take 116 us in this kernel, where two crossings alone
+// would need over 180 us).  With several tokens a miss selected by more
+// than one token would still cross the link once per token, so the
+// designated-writer rows are copied to their slots first by a copy kernel
+// spread over the chip, and the attention reads them there; a miss row that
+// another token writes is read from host memory inside the kernel.
 //
 // Per workgroup: one (request, token), 16 heads per wave, one chunk of rows
 // split between two sub-groups of waves that take alternate 32-row tiles
@@ -70,7 +72,11 @@ constexpr int kTileLoads = (kTile * kRowSlots + 63) / 64;   // wave loads per ti
 constexpr int kTileSlots = kTileLoads * 64;     // slots per tile buffer (2368)
 constexpr int kStages = 2;                      // tile buffers per sub-group
 constexpr int kMaxChunkRows = 512;              // rows per chunk held in LDS tables
-constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 + kMaxChunkRows * 4;
+constexpr int kMaxChunkTiles = kMaxChunkRows / kTile;
+// Tile rings, then the row table, the writer slots and the per-tile writer
+// masks.
+constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 +
+                           (size_t)kMaxChunkRows * 4 * 2 + kMaxChunkTiles * 4;
 constexpr int kCopyRows = 32;        // rows scanned per copy workgroup
 constexpr int kCopyThreads = 256;
 constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
@@ -105,14 +111,16 @@ template <int WPS>
 __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
-    const int32_t* __restrict__ n_sel, const uint16_t* __restrict__ pool,
+    const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ host, _Float16* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
-    float scale_log2) {
+    float scale_log2, int fuse_writes) {
   constexpr int NT = 2 * WPS * 64;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   int* code = reinterpret_cast<int*>(smem + (size_t)2 * kStages * kTileSlots * 8);
+  int* wdst = code + kMaxChunkRows;
+  unsigned* wmask = reinterpret_cast<unsigned*>(wdst + kMaxChunkRows);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -140,24 +148,44 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const int32_t* rpos = sel_pos + (size_t)bj * k;
   const int32_t* rsrc = sel_src + (size_t)bj * k;
   const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
-  const uint16_t* pool_b = pool + (size_t)b * C * kLat;
+  uint16_t* pool_b = pool + (size_t)b * C * kLat;
   const uint16_t* host_b = host + (size_t)b * L * kLat;
 
-  // Row sources of the chunk, once: hits read their slot, designated-writer
-  // misses their new slot (filled by the copy kernel that runs first), other
-  // misses host memory.  Out-of-range values (caller error) give zero rows.
-  // The table covers the chunk up to k, so its loads do not wait for n_sel;
-  // entries at or past n_sel are never used.
-  for (int i = r0 + threadIdx.x; i < rend; i += NT) {
-    const int src = rsrc[i], pos = rpos[i];
-    const int dst = rdst ? rdst[i] : -1;
-    int cd = kNoRow;
-    if (src >= 0) {
-      if (src < C) cd = src;
-    } else if (pos >= 0 && pos < L) {
-      cd = (dst >= 0 && dst < C) ? dst : ~pos;
+  // Row sources of the chunk, once: hits read their slot, other misses host
+  // memory.  A designated-writer miss reads its new slot when a copy kernel
+  // ran first; with fused writes it reads host memory and the first head
+  // group stores the row from the tile to that slot (wdst, and one bit per
+  // row in its tile's mask).  Out-of-range values (caller error) give zero
+  // rows.  The table covers the chunk up to k, so its loads do not wait for
+  // n_sel; entries at or past n_sel are never used.  Each wave fills 64
+  // consecutive rows (two whole tiles, as r0 is a multiple of 64).
+  const bool writer_wg = fuse_writes && hg == 0;
+  for (int i0 = r0 + wave * 64; i0 < rend; i0 += NT) {
+    const int i = i0 + lane;
+    bool wr = false;
+    if (i < rend) {
+      const int src = rsrc[i], pos = rpos[i];
+      const int dst = rdst ? rdst[i] : -1;
+      int cd = kNoRow;
+      if (src >= 0) {
+        if (src < C) cd = src;
+      } else if (pos >= 0 && pos < L) {
+        const bool owns = dst >= 0 && dst < C;
+        cd = owns && !fuse_writes ? dst : ~pos;
+        if (owns && writer_wg) {
+          wdst[i - r0] = dst;
+          wr = true;
+        }
+      }
+      code[i - r0] = cd;
     }
-    code[i - r0] = cd;
+    if (fuse_writes) {
+      const unsigned long long bal = __ballot(wr);
+      if (lane == 0) {
+        wmask[(i0 - r0) >> 5] = (unsigned)bal;
+        wmask[((i0 - r0) >> 5) + 1] = (unsigned)(bal >> 32);
+      }
+    }
   }
 
   // Q fragments: lane holds Q[h0 + c][32 kk + 8 g .. + 8].
@@ -301,6 +329,26 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
                                                            0, 0, 0);
         lo = nlo;
         hi = nhi;
+      }
+    }
+
+    // Fused writes: this tile's writer rows (read from host memory) go from
+    // the tile to their pool slots, one row per wave in turn.  Only rows
+    // below n_sel were loaded.
+    if (writer_wg) {
+      unsigned msk = __builtin_amdgcn_readfirstlane(wmask[tt]);
+      if (r1 - t0 < kTile) msk &= (1u << (r1 - t0)) - 1u;
+      int n = 0;
+      while (msk) {
+        const int r = __builtin_ctz(msk);
+        msk &= msk - 1u;
+        if (n++ % WPS == wv) {
+          const int dst = __builtin_amdgcn_readfirstlane(wdst[t0 - r0 + r]);
+          const v4u* srow = reinterpret_cast<const v4u*>(krow + r * kKStride);
+          v4u* drow = reinterpret_cast<v4u*>(pool_b + (size_t)dst * kLat);
+          drow[lane] = srow[lane];
+          if (lane < kChunks16 - 64) drow[64 + lane] = srow[64 + lane];
+        }
       }
     }
   }
@@ -473,8 +521,8 @@ template <int WPS>
 hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
-                    const uint16_t* pool, const uint16_t* host, _Float16* part_acc,
-                    float2* part_ml, hipStream_t s) {
+                    uint16_t* pool, const uint16_t* host, _Float16* part_acc,
+                    float2* part_ml, bool fuse, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
   hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -488,7 +536,7 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
-                     d.batch * d.mtp, scale_log2);
+                     d.batch * d.mtp, scale_log2, fuse ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -530,9 +578,13 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              float* out, float* lse, void* ws,
                              hipStream_t s, int target_wgs) {
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
-  if (row_dst) {
-    // Misses first: every designated-writer miss row lands in its slot
-    // before the attention reads it there.
+  // One query token per request: the attention reads each miss from host
+  // memory and writes it to its slot from the tile (one host read per miss).
+  // Several tokens: a miss selected by more than one token would cross the
+  // host link once per token, so the designated-writer rows are copied to
+  // their slots first and the attention reads them there.
+  const bool fuse = row_dst != nullptr && d.mtp == 1;
+  if (row_dst && !fuse) {
     dim3 cg((d.topk + kCopyRows - 1) / kCopyRows, d.batch * d.mtp);
     hipLaunchKernelGGL(miss_rows_copy_kernel, cg, dim3(kCopyThreads), 0, s,
                        sel_pos, sel_src, row_dst, n_sel, pool, host,
@@ -546,10 +598,10 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
       static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
   switch (p.heads_per_wg / 16) {
-    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
+    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
+    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
+    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel,

@@ -163,13 +163,18 @@ ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
  *   z_i   = softmax_scale * <q_abs[b][j][h], row_i>
  *   out[b][j][h][:] = sum_i softmax(z)_i * row_i[0:512]
  *   lse[b][j][h]    = log sum_i exp(z_i)                 (lse may be NULL)
- * If row_dst is not NULL, every miss row (sel_src[i] < 0) with
- * row_dst[i] >= 0 is copied from host memory to pool[b][row_dst[i]] before
- * the attention reads it from there (that slot must be one no other
- * selected row reads, as the slots from ess_pool_update are); other miss
- * rows are read from host memory inside the attention kernel.  The
- * reduction order is the rank order in fixed chunks combined in fixed order,
- * so the result does not depend on which rows came from host memory.
+ * If row_dst is not NULL, every miss row (sel_src[i] < 0, i < n_sel) with
+ * row_dst[i] >= 0 is in pool[b][row_dst[i]] when the call's work completes
+ * (that slot must be one no other selected row reads, as the slots from
+ * ess_pool_update are).  With m == 1 the attention kernel reads such a row
+ * from host memory into its tile and writes it to the slot from there (one
+ * host read per miss, under the attention's own work); with m > 1 these
+ * rows are copied to their slots first (a miss shared by several tokens
+ * crosses the host link once) and the attention reads them there.  Other
+ * miss rows are read from host memory inside the attention kernel.  The
+ * reduction order is the rank order in fixed chunks combined in fixed
+ * order, so the result does not depend on which rows came from host
+ * memory.
  *   q_abs [B][m][H][576] bf16; sel_pos, sel_src, row_dst [B][m][k];
  *   n_sel [B][m]; pool [B][C][576] bf16; host_view [B][L][576] bf16;
  *   out [B][m][H][512] float; lse [B][m][H] float. */
@@ -185,8 +190,8 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
  * H2D load of the copy triples; ESS concept page: small-block transfers of
  * latent entries).  For each b and i < n_miss[b]:
  *   pool[b][miss_slot[b*list_stride + i]] = host_view[b][miss_pos[b*list_stride + i]]
- * Used for the first fill and, by ess_decode_step, for every layer's misses
- * after its update. */
+ * Used for the first fill and, by ess_decode_step with m > 1, for every
+ * layer's misses after its update. */
 ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
                          const int32_t* miss_pos, const int32_t* miss_slot,
                          const int32_t* n_miss, const uint16_t* host_view,
@@ -225,13 +230,16 @@ enum {
   ESS_MODE_FILL = 0,     /* first fill: top-C of token 0, empty-pool update,
                             host -> pool copy; no attention                  */
   ESS_MODE_INLINE = 1,   /* per layer on `stream`: scores, top-k, pool update,
-                            the update's miss list copied host -> pool, then
-                            attention reading every row from the pool        */
+                            then gather + attention: with m == 1 the
+                            attention reads each miss from host memory and
+                            writes it to its slot from the tile; with m > 1
+                            the update's miss list is copied host -> pool
+                            first and the attention reads only the pool     */
   ESS_MODE_PREFETCH = 2  /* every layer's scores, top-k and update run ahead
-                            on `side`; `stream` copies layer l's misses as
-                            soon as layer l is selected, then attends, so
-                            layer l+1's selection overlaps layer l's copy
-                            and attention; attention reads only the pool     */
+                            on `side`; `stream` runs layer l's gather +
+                            attention (as in ESS_MODE_INLINE) as soon as
+                            layer l is selected, so layer l+1's selection
+                            overlaps layer l's miss transfer and attention  */
 };
 
 /* A whole decode step over n_layers layers (ESS concept page: layer-wise

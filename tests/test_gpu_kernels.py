@@ -225,6 +225,13 @@ def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
                         dst[b, j, i] = s       # designated writer
                 s, hit = slot_of[p]
                 src[b, j, i] = s if hit else -1
+        # Rows at or past n_sel are never used: writer slots planted there
+        # must stay untouched.
+        for j in range(m):
+            for i in range(n_sel[b, j], min(n_sel[b, j] + 2, k)):
+                if free:
+                    sel[b, j, i] = i % L
+                    dst[b, j, i] = free.pop()
     d = dims(batch=B, mtp=m, ctx_len=L, mla_heads=H, topk=k, pool_slots=C)
     ws_bytes = ess.ess_workspace_bytes(d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -241,12 +248,15 @@ def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
             ref, rlse = attend(qa[b, j], host.array[b, sel[b, j, :n]], 1 / 24)
             assert_attn_close(got[b, j], ref, (b, j))
             lse_close(glse[b, j], rlse, (b, j))
-    # Misses landed in their slots, bit for bit.
+    # Misses landed in their slots, bit for bit; every other slot unchanged.
     gp = h(pool_t)
     for b in range(B):
+        written = np.zeros(C, bool)
         for j in range(m):
-            for i in np.nonzero(dst[b, j] >= 0)[0]:
+            for i in np.nonzero(dst[b, j, :n_sel[b, j]] >= 0)[0]:
                 assert np.array_equal(gp[b, dst[b, j, i]], host.array[b, sel[b, j, i]])
+                written[dst[b, j, i]] = True
+        assert np.array_equal(gp[b, ~written], pool[b, ~written]), b
     # Placement invariance: every row now read from the pool.
     src2 = src.copy()
     for b in range(B):
