@@ -5,10 +5,9 @@ Workload: 32K context, 16 requests, one query token per step, 64x128 fp8
 indexer, top-2048, 128-head absorbed MLA over 576-wide bf16 latents, a hot
 pool of 8192 slots per request, latents in pinned host memory.  One step =
 indexer scores -> top-k with the slot lookup -> pool update -> gather +
-attention over the selected rows (+ combine), for all 16 requests; with one
-query token per request the gather reads each miss from host memory inside
-the attention kernel and writes it to its pool slot from the tile (with
-several tokens the step's misses are copied host -> pool first).  All per-step inputs (the drifting indexer queries and
+attention over the selected rows (+ combine), for all 16 requests; the
+gather reads each miss from host memory inside the attention kernel and
+writes it to its pool slot from the tile.  All per-step inputs (the drifting indexer queries and
 the absorbed queries) are staged in device memory before the timed region;
 the pool's first fill runs before the warm-up steps.
 
@@ -388,13 +387,9 @@ def main():
 
     n_miss_all = torch.zeros((wl.steps, B), dtype=torch.int32, device=dev)
 
-    # One query token per request: misses are read from host memory inside
-    # the attention kernel (written to their slots from the tile).  Several
-    # tokens: the miss list is copied first, then the attention reads the pool.
-    fused = m == 1
-    names = (["index_scores", "topk_lookup", "pool_update", "gather_attention"] if fused
-             else ["index_scores", "topk_lookup", "pool_update", "miss_copy",
-                   "sparse_mla_decode"])
+    # Misses are read from host memory inside the attention kernel and
+    # written to their slots from the tile.
+    names = ["index_scores", "topk_lookup", "pool_update", "gather_attention"]
     n_st = len(names)
 
     def step(t, ev=None):
@@ -412,22 +407,11 @@ def main():
                             row_dst, post, stream)
         if ev is not None:
             ev[3].record(stream)
-        if fused:
-            ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
-                                      lb.pool, host.dev, lb.out, lb.lse, lb.ws,
-                                      lb.ws_bytes, stream)
-            if ev is not None:
-                ev[4].record(stream)
-            return
-        ess.ess_miss_copy(d, lists, lb.miss_pos, lb.miss_slot, n_miss_all[t],
-                          host.dev, lb.pool, stream)
-        if ev is not None:
-            ev[4].record(stream)
-        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, post, None, lb.n_sel,
+        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
                                   lb.pool, host.dev, lb.out, lb.lse, lb.ws,
                                   lb.ws_bytes, stream)
         if ev is not None:
-            ev[5].record(stream)
+            ev[4].record(stream)
 
     # First fill (top-C of token 0 at step 0 into the empty pool), untimed.
     lb.reset(stream)
@@ -475,9 +459,8 @@ def main():
     wall_plain = time.perf_counter() - t1
 
     # Overlap on the same steps' miss lists (the pages' OverlapRatio):
-    # T_fused = the gather call with per-row writer slots (one token per
-    # request: misses read from host inside the attention kernel and
-    # written to their slots from the tile; several: copied first),
+    # T_fused = the gather call with per-row writer slots (misses read from
+    # host inside the attention kernel, written to their slots from the tile),
     # T_copy  = the miss list copied host -> pool alone,
     # T_attn  = attention with every row read from the pool.
     ev_ov = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ov)]
@@ -531,11 +514,10 @@ def main():
     attn_flop = 2 * B * m * H * k * (576 + 512)
     attn_bytes = sel_bytes + B * m * H * (576 * 2 + 512 * 4)
     miss_bytes = n_miss_tot * 1152 / K
-    t_gather = float(stage_us[names.index("gather_attention")] if fused
-                     else stage_us[3] + stage_us[4])
+    t_gather = float(stage_us[names.index("gather_attention")])
     # The attention's own HBM and MFMA rates: timed alone with every row in
-    # the pool when the gather is fused (the fused call is paced by the link).
-    t_attn_st = float(t_attn if fused else stage_us[-1])
+    # the pool (the fused call is paced by the host link).
+    t_attn_st = float(t_attn)
     attn_kernels = "sparse_mla_kernel+mla_combine_kernel"
     roofs = {
         "index_scores": {"kernel": "index_scores_kernel", "bound": "hbm",
@@ -551,26 +533,13 @@ def main():
                  "hbm_frac": attn_bytes / (t_attn_st * 1e3) / HBM_PEAK_GBPS,
                  "tflops": attn_flop / (t_attn_st * 1e6),
                  "mfma_frac": attn_flop / (t_attn_st * 1e6) / BF16_PEAK_TFLOPS}
-    if fused:
-        # The host link sets the pace of the fused call: its misses cross
-        # it while the attention's HBM reads and MFMA work run.
-        roofs["gather_attention"] = {
-            "kernel": attn_kernels, "bound": "host-link",
-            "achieved": miss_bytes / (t_gather * 1e3), "peak": PCIE5_X16_GBPS,
-            "unit": "GB/s", "bytes_per_launch": miss_bytes,
-            "measured_ceiling": host_gbps, **attn_view}
-    else:
-        roofs["miss_copy"] = {"kernel": "miss_copy_kernel", "bound": "host-link",
-                              "achieved": miss_bytes / (stage_us[3] * 1e3),
-                              "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                              "bytes_per_launch": miss_bytes,
-                              "measured_ceiling": host_gbps}
-        roofs["sparse_mla_decode"] = {"kernel": attn_kernels, "bound": "hbm",
-                                      "achieved": attn_view["hbm_gbps"],
-                                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                      "bytes_per_launch": attn_bytes,
-                                      "tflops": attn_view["tflops"],
-                                      "mfma_frac": attn_view["mfma_frac"]}
+    # The host link sets the pace of the fused call: its misses cross it
+    # while the attention's HBM reads and MFMA work run.
+    roofs["gather_attention"] = {
+        "kernel": attn_kernels, "bound": "host-link",
+        "achieved": miss_bytes / (t_gather * 1e3), "peak": PCIE5_X16_GBPS,
+        "unit": "GB/s", "bytes_per_launch": miss_bytes,
+        "measured_ceiling": host_gbps, **attn_view}
     for r in roofs.values():
         r["frac"] = r["achieved"] / r["peak"]
     dom = int(np.argmax(stage_us))
@@ -594,7 +563,7 @@ def main():
                    "batch": B, "mtp": m, "ctx_len": L, "idx_heads": wl.idx_heads,
                    "idx_dim": wl.idx_dim, "topk": k, "mla_heads": H,
                    "pool_slots": C, "rho": wl.rho,
-                   "miss_mode": "in-kernel" if fused else "copy-first"},
+                   "miss_mode": "in-kernel"},
         "steps_per_s": K / wall_plain,
         "steps_per_s_staged": K / wall,
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},

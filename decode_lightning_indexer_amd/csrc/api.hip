@@ -289,24 +289,13 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                  io.n_evict, io.row_dst, io.sel_slot_post, st);
 }
 
-// Gather + attention of one selected layer.  One query token per request:
-// the attention reads each miss from host memory into its tile and writes it
-// to its slot from there, so the host reads run under the attention's work.
-// Several tokens: the update's miss list (each union miss once) is copied
-// first at the host link's rate, then the attention reads every row from
-// its slot.
+// Gather + attention of one selected layer: the attention reads each miss
+// from host memory into its tile and writes it to its slot from there, so
+// the host reads run under the attention's own work.
 static hipError_t enqueue_attention(const ess_dims& d, const ess_layer_io& io,
                                     hipStream_t st) {
-  if (d.mtp == 1)
-    return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
-                                  io.row_dst, io.n_sel, io.pool, io.host_view,
-                                  io.out, io.lse, io.ws, st);
-  hipError_t e = ess::launch_miss_copy(d, d.mtp * d.topk, io.miss_pos,
-                                       io.miss_slot, io.n_miss, io.host_view,
-                                       io.pool, st);
-  if (e != hipSuccess) return e;
-  return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot_post,
-                                nullptr, io.n_sel, io.pool, io.host_view,
+  return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
+                                io.row_dst, io.n_sel, io.pool, io.host_view,
                                 io.out, io.lse, io.ws, st);
 }
 

@@ -15,19 +15,18 @@
 //
 // Miss handling on MI355X: a miss costs a host-link read (~55 GB/s
 // measured) against an HBM read for a hit (8 TB/s), so the host link sets
-// the pace.  With one query token per request the kernel does what the
-// pages describe: a designated-writer miss is loaded from host memory into
-// the tile like any other row, and the first head group stores it from the
-// tile to its pool slot.  The host reads then run while the attention works
-// on the rows already in LDS.  The two head groups of a chunk run on one XCD
-// close together, so the second group's read of a host row comes from that
-// XCD's L2 and each miss crosses the link once (measured: 4.4K misses per
-// step at 32K x 16 take 116 us in this kernel, where two crossings alone
-// would need over 180 us).  With several tokens a miss selected by more
-// than one token would still cross the link once per token, so the
-// designated-writer rows are copied to their slots first by a copy kernel
-// spread over the chip, and the attention reads them there; a miss row that
-// another token writes is read from host memory inside the kernel.
+// the pace.  The kernel does what the pages describe: a designated-writer
+// miss is loaded from host memory into the tile like any other row, and the
+// first head group of its token stores it from the tile to its pool slot.
+// The host reads then run while the attention works on the rows already in
+// LDS.  The workgroups of one (request, chunk) - every token and head group
+// - run on one XCD close together, so a host row that another of them has
+// just read comes from that XCD's L2: the second head group's reads, and a
+// miss that the request's tokens share at nearby ranks, cross the link once
+// (measured at 32K x 16: 4.4K misses per step take 116 us in this kernel,
+// where two crossings alone would need over 180 us).  A miss row that
+// another token writes is read from host memory too, never from the slot
+// being written.
 //
 // Per workgroup: one (request, token), 16 heads per wave, one chunk of rows
 // split between two sub-groups of waves that take alternate 32-row tiles
@@ -77,8 +76,6 @@ constexpr int kMaxChunkTiles = kMaxChunkRows / kTile;
 // masks.
 constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 +
                            (size_t)kMaxChunkRows * 4 * 2 + kMaxChunkTiles * 4;
-constexpr int kCopyRows = 32;        // rows scanned per copy workgroup
-constexpr int kCopyThreads = 256;
 constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
 
 // A zero latent row: the source of padding rows and unusable rows.
@@ -115,7 +112,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ host, _Float16* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
-    float scale_log2, int fuse_writes) {
+    float scale_log2) {
   constexpr int NT = 2 * WPS * 64;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   int* code = reinterpret_cast<int*>(smem + (size_t)2 * kStages * kTileSlots * 8);
@@ -126,21 +123,24 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sg = wave / WPS, wv = wave - sg * WPS;
   const int g = lane >> 4, c = lane & 15;
-  // Workgroup -> (head group, row chunk).  Consecutive workgroup ids go to
-  // the 8 XCDs in turn, each with its own L2; the head groups of one chunk
-  // get ids that are multiples of 8 apart, so they run on the same XCD close
-  // together and the second reads the chunk's latents from that L2.  Items
-  // (request-token, chunk) are numbered with the chunk slowest, the chunk
-  // nearest the top-k cut first (where rows miss most); ids past the last
-  // item (padding to whole rounds) exit.
+  // Workgroup -> (token, head group, row chunk).  Consecutive workgroup ids
+  // go to the 8 XCDs in turn, each with its own L2; the m * head_groups
+  // workgroups of one (request, chunk) group get ids that are multiples of 8
+  // apart, so they run on the same XCD close together and share the chunk's
+  // rows through that L2.  Groups are numbered with the chunk slowest, the
+  // chunk nearest the top-k cut first (where rows miss most); ids past the
+  // last group (padding to whole rounds) exit.
   const int wg = blockIdx.x;
   const int xcd = wg & 7, round = wg >> 3;
-  const int hg = round % head_groups;
-  const int item = (round / head_groups) * 8 + xcd;
-  if (item >= n_bj * nchunk) return;
-  const int bj = item % n_bj;
-  const int chunk = nchunk - 1 - item / n_bj;
-  const int b = bj / m;
+  const int per = m * head_groups;
+  const int sub = round % per;
+  const int hg = sub % head_groups;
+  const int grp = (round / per) * 8 + xcd;
+  const int n_b = n_bj / m;
+  if (grp >= n_b * nchunk) return;
+  const int b = grp % n_b;
+  const int chunk = nchunk - 1 - grp / n_b;
+  const int bj = b * m + sub / head_groups;
   const int r0 = chunk * rows_per_chunk;
   const int rend = min(k, r0 + rows_per_chunk);    // rows the table covers
   const int h0 = hg * (WPS * 16) + wv * 16;
@@ -151,15 +151,14 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   uint16_t* pool_b = pool + (size_t)b * C * kLat;
   const uint16_t* host_b = host + (size_t)b * L * kLat;
 
-  // Row sources of the chunk, once: hits read their slot, other misses host
-  // memory.  A designated-writer miss reads its new slot when a copy kernel
-  // ran first; with fused writes it reads host memory and the first head
-  // group stores the row from the tile to that slot (wdst, and one bit per
+  // Row sources of the chunk, once: hits read their slot, misses host
+  // memory.  Given writer slots, the first head group stores each
+  // designated-writer miss from the tile to its slot (wdst, and one bit per
   // row in its tile's mask).  Out-of-range values (caller error) give zero
   // rows.  The table covers the chunk up to k, so its loads do not wait for
   // n_sel; entries at or past n_sel are never used.  Each wave fills 64
   // consecutive rows (two whole tiles, as r0 is a multiple of 64).
-  const bool writer_wg = fuse_writes && hg == 0;
+  const bool writer_wg = rdst != nullptr && hg == 0;
   for (int i0 = r0 + wave * 64; i0 < rend; i0 += NT) {
     const int i = i0 + lane;
     bool wr = false;
@@ -170,16 +169,15 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       if (src >= 0) {
         if (src < C) cd = src;
       } else if (pos >= 0 && pos < L) {
-        const bool owns = dst >= 0 && dst < C;
-        cd = owns && !fuse_writes ? dst : ~pos;
-        if (owns && writer_wg) {
+        cd = ~pos;
+        if (writer_wg && dst >= 0 && dst < C) {
           wdst[i - r0] = dst;
           wr = true;
         }
       }
       code[i - r0] = cd;
     }
-    if (fuse_writes) {
+    if (rdst) {
       const unsigned long long bal = __ballot(wr);
       if (lane == 0) {
         wmask[(i0 - r0) >> 5] = (unsigned)bal;
@@ -332,7 +330,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       }
     }
 
-    // Fused writes: this tile's writer rows (read from host memory) go from
+    // Writer rows: this tile's designated-writer misses (read from host) go from
     // the tile to their pool slots, one row per wave in turn.  Only rows
     // below n_sel were loaded.
     if (writer_wg) {
@@ -412,58 +410,6 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(M, l);
 }
 
-// Designated-writer miss rows host -> their slot, spread over the chip: each
-// workgroup scans kCopyRows rows of one (request, token), lists its misses in
-// LDS, then copies them with all threads, every host read of a thread in
-// flight together.
-__global__ __launch_bounds__(kCopyThreads) void miss_rows_copy_kernel(
-    const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ sel_src,
-    const int32_t* __restrict__ row_dst, const int32_t* __restrict__ n_sel,
-    uint16_t* __restrict__ pool, const uint16_t* __restrict__ host, int L,
-    int C, int m, int k) {
-  __shared__ int mpos[kCopyRows], mdst[kCopyRows];
-  __shared__ int s_n;
-  const int bj = blockIdx.y, b = bj / m;
-  const int r0 = blockIdx.x * kCopyRows;
-  const int r1 = min(min(n_sel[bj], k), r0 + kCopyRows);
-  if (threadIdx.x == 0) s_n = 0;
-  __syncthreads();
-  if (threadIdx.x < kCopyRows) {
-    const int i = r0 + threadIdx.x;
-    if (i < r1) {
-      const size_t o = (size_t)bj * k + i;
-      const int src = sel_src[o], dst = row_dst[o], pos = sel_pos[o];
-      if (src < 0 && dst >= 0 && dst < C && pos >= 0 && pos < L) {
-        const int at = atomicAdd(&s_n, 1);
-        mpos[at] = pos;
-        mdst[at] = dst;
-      }
-    }
-  }
-  __syncthreads();
-  const int npieces = s_n * kChunks16;
-  const uint16_t* hb = host + (size_t)b * L * kLat;
-  uint16_t* pb = pool + (size_t)b * C * kLat;
-  constexpr int kBatch = (kCopyRows * kChunks16 + kCopyThreads - 1) / kCopyThreads;
-  v4u buf[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int q = threadIdx.x + u * kCopyThreads;
-    if (q < npieces) {
-      const int j = q / kChunks16, ch = q - j * kChunks16;
-      buf[u] = *reinterpret_cast<const v4u*>(hb + (size_t)mpos[j] * kLat + ch * 8);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int q = threadIdx.x + u * kCopyThreads;
-    if (q < npieces) {
-      const int j = q / kChunks16, ch = q - j * kChunks16;
-      *reinterpret_cast<v4u*>(pb + (size_t)mdst[j] * kLat + ch * 8) = buf[u];
-    }
-  }
-}
-
 // Merge the chunk partials of one (request, token, head) in chunk order;
 // each partial is normalised, so its weight is 2^(m - M) times its sum.
 // 64 threads per head, 8 values each (16-byte fp16 loads), 4 heads per
@@ -522,21 +468,21 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
                     uint16_t* pool, const uint16_t* host, _Float16* part_acc,
-                    float2* part_ml, bool fuse, hipStream_t s) {
+                    float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
   hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)kMlaLds);
   if (e != hipSuccess) return e;
-  // 1-D grid over (item, head group) in whole rounds of 8 XCDs.
-  const int items = d.batch * d.mtp * p.nchunk;
-  const int rounds = ((items + 7) / 8) * p.head_groups;
+  // 1-D grid over (group, token, head group) in whole rounds of 8 XCDs.
+  const int groups = d.batch * p.nchunk;
+  const int rounds = ((groups + 7) / 8) * d.mtp * p.head_groups;
   dim3 grid(rounds * 8);
   hipLaunchKernelGGL((sparse_mla_kernel<WPS>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
-                     d.batch * d.mtp, scale_log2, fuse ? 1 : 0);
+                     d.batch * d.mtp, scale_log2);
   return hipGetLastError();
 }
 
@@ -578,30 +524,16 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              float* out, float* lse, void* ws,
                              hipStream_t s, int target_wgs) {
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
-  // One query token per request: the attention reads each miss from host
-  // memory and writes it to its slot from the tile (one host read per miss).
-  // Several tokens: a miss selected by more than one token would cross the
-  // host link once per token, so the designated-writer rows are copied to
-  // their slots first and the attention reads them there.
-  const bool fuse = row_dst != nullptr && d.mtp == 1;
-  if (row_dst && !fuse) {
-    dim3 cg((d.topk + kCopyRows - 1) / kCopyRows, d.batch * d.mtp);
-    hipLaunchKernelGGL(miss_rows_copy_kernel, cg, dim3(kCopyThreads), 0, s,
-                       sel_pos, sel_src, row_dst, n_sel, pool, host,
-                       d.ctx_len, d.pool_slots, d.mtp, d.topk);
-    hipError_t ce = hipGetLastError();
-    if (ce != hipSuccess) return ce;
-  }
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   _Float16* part_acc = static_cast<_Float16*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
   switch (p.heads_per_wg / 16) {
-    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
-    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
-    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
-    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, fuse, s); break;
+    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel,

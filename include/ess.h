@@ -166,12 +166,10 @@ ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
  * If row_dst is not NULL, every miss row (sel_src[i] < 0, i < n_sel) with
  * row_dst[i] >= 0 is in pool[b][row_dst[i]] when the call's work completes
  * (that slot must be one no other selected row reads, as the slots from
- * ess_pool_update are).  With m == 1 the attention kernel reads such a row
- * from host memory into its tile and writes it to the slot from there (one
- * host read per miss, under the attention's own work); with m > 1 these
- * rows are copied to their slots first (a miss shared by several tokens
- * crosses the host link once) and the attention reads them there.  Other
- * miss rows are read from host memory inside the attention kernel.  The
+ * ess_pool_update are): the attention kernel reads such a row from host
+ * memory into its tile and writes it to the slot from there (one host read
+ * per miss, under the attention's own work).  Every miss row, whoever
+ * writes it, is read from host memory inside the attention kernel.  The
  * reduction order is the rank order in fixed chunks combined in fixed
  * order, so the result does not depend on which rows came from host
  * memory.
@@ -190,8 +188,7 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
  * H2D load of the copy triples; ESS concept page: small-block transfers of
  * latent entries).  For each b and i < n_miss[b]:
  *   pool[b][miss_slot[b*list_stride + i]] = host_view[b][miss_pos[b*list_stride + i]]
- * Used for the first fill and, by ess_decode_step with m > 1, for every
- * layer's misses after its update. */
+ * Used for the first fill. */
 ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
                          const int32_t* miss_pos, const int32_t* miss_slot,
                          const int32_t* n_miss, const uint16_t* host_view,
@@ -230,11 +227,9 @@ enum {
   ESS_MODE_FILL = 0,     /* first fill: top-C of token 0, empty-pool update,
                             host -> pool copy; no attention                  */
   ESS_MODE_INLINE = 1,   /* per layer on `stream`: scores, top-k, pool update,
-                            then gather + attention: with m == 1 the
-                            attention reads each miss from host memory and
-                            writes it to its slot from the tile; with m > 1
-                            the update's miss list is copied host -> pool
-                            first and the attention reads only the pool     */
+                            then gather + attention: the attention reads
+                            each miss from host memory and writes it to its
+                            slot from the tile                              */
   ESS_MODE_PREFETCH = 2  /* every layer's scores, top-k and update run ahead
                             on `side`; `stream` runs layer l's gather +
                             attention (as in ESS_MODE_INLINE) as soon as
