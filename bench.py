@@ -399,7 +399,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos,
-                            sel_slot, lb.n_sel, None, 0, stream)
+                            sel_slot, lb.n_sel, lb.ws, lb.ws_bytes, stream)
         if ev is not None:
             ev[2].record(stream)
         ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos,
@@ -470,7 +470,7 @@ def main():
         t = W + K + i
         ess.ess_index_scores(d, q_idx[t], lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
         ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos,
-                            sel_slot, lb.n_sel, None, 0, stream)
+                            sel_slot, lb.n_sel, lb.ws, lb.ws_bytes, stream)
         ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos,
                             lb.lru, lb.miss_pos, lb.miss_slot, lb.n_miss, lb.n_evict,
                             row_dst, post, stream)

@@ -108,13 +108,24 @@ ess_status get_events(size_t n, hipEvent_t** out) {
   return ESS_OK;
 }
 
+// Workspace layout: the attention's partials, then the top-k levels' lists
+// (sized for the step's top-k and for the first fill's top-C).
+size_t attn_region(const ess_dims& d) {
+  return ess::align_up(ess::sparse_mla_ws_bytes(d), 256);
+}
+size_t topk_region(const ess_dims& d) {
+  const size_t a = ess::topk_ws_bytes(d, d.topk, d.mtp);
+  const size_t b = ess::topk_ws_bytes(d, d.pool_slots, 1);
+  return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t ess_workspace_bytes(const ess_dims* d) {
   if (check_dims(d, "ess_workspace_bytes") != ESS_OK) return 0;
-  return ess::sparse_mla_ws_bytes(*d);
+  return attn_region(*d) + topk_region(*d);
 }
 
 size_t ess_lru_state_bytes(const ess_dims* d) {
@@ -159,8 +170,6 @@ ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
                            const int32_t* cache_slots, int32_t* sel_pos,
                            int32_t* sel_slot, int32_t* n_sel, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   const char* fn = "ess_topk_lookup";
   ess_status s = check_dims(d, fn);
   if (s != ESS_OK) return s;
@@ -171,8 +180,16 @@ ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
   ESS_NONNULL(sel_pos);
   ESS_NONNULL(sel_slot);
   ESS_NONNULL(n_sel);
+  const size_t need = ess::topk_ws_bytes(*d, k, n_tok);
+  if (need > 0 && ws && (reinterpret_cast<uintptr_t>(ws) & 15))
+    return fail(ESS_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(ESS_ERR_NOMEM,
+                "%s: rows of %d keys select in levels over a workspace of %zu "
+                "bytes (have %zu)", fn, d->ctx_len, need, ws ? ws_bytes : 0);
   hipError_t e = ess::launch_topk(*d, k, n_tok, scores, n_vis, cache_slots,
-                                  sel_pos, sel_slot, n_sel, stream);
+                                  sel_pos, sel_slot, n_sel,
+                                  need > 0 ? ws : nullptr, stream);
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }
 
@@ -224,6 +241,8 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
   ESS_NONNULL(host_view);
   ESS_NONNULL(out);
   ESS_NONNULL(ws);
+  if (reinterpret_cast<uintptr_t>(ws) & 15)
+    return fail(ESS_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   const size_t need = ess::sparse_mla_ws_bytes(*d);
   if (ws_bytes < need)
     return fail(ESS_ERR_NOMEM, "%s: workspace of %zu bytes, need %zu", fn,
@@ -264,13 +283,17 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
   if (mode != ESS_MODE_FILL && (!io.q_abs || !io.out || !io.ws))
     return fail(ESS_ERR_INVALID, "%s: layer %d has a NULL attention buffer",
                 fn, l);
+  if (io.ws && (reinterpret_cast<uintptr_t>(io.ws) & 15))
+    return fail(ESS_ERR_INVALID, "%s: layer %d workspace must be 16-byte aligned",
+                fn, l);
   return ESS_OK;
 }
 
-// Scores, top-k and pool update of one layer on one stream.
+// Scores, top-k and pool update of one layer on one stream; tws: the
+// layer's top-k region of its workspace (nullptr: one workgroup per row).
 static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                  const int32_t* n_vis, int k, int n_tok,
-                                 hipStream_t st) {
+                                 void* tws, hipStream_t st) {
   hipError_t e = ess::launch_index_scores(d, io.q_idx, io.w_idx, io.k_idx,
                                           n_vis, io.scores, st);
   if (e != hipSuccess) return e;
@@ -279,9 +302,9 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                      io.sel_pos, io.sel_slot, io.n_sel,
                                      io.slot_pos, io.lru_state, io.miss_pos,
                                      io.miss_slot, io.n_miss, io.n_evict,
-                                     io.row_dst, io.sel_slot_post, st);
+                                     io.row_dst, io.sel_slot_post, tws, st);
   e = ess::launch_topk(d, k, n_tok, io.scores, n_vis, io.cache_slots,
-                       io.sel_pos, io.sel_slot, io.n_sel, st);
+                       io.sel_pos, io.sel_slot, io.n_sel, tws, st);
   if (e != hipSuccess) return e;
   return ess::launch_pool_update(d, k, n_tok, io.sel_pos, io.n_sel,
                                  io.cache_slots, io.slot_pos, io.lru_state,
@@ -321,7 +344,13 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   }
   if (mode == ESS_MODE_PREFETCH && (side == stream))
     return fail(ESS_ERR_INVALID, "%s: prefetch needs a second stream", fn);
-  const size_t ws_need = ess::sparse_mla_ws_bytes(*d);
+  const size_t ws_need = attn_region(*d) + topk_region(*d);
+  // The top-k region of a layer's workspace (the first fill uses it only
+  // when the layer brings a full workspace; it is not required there).
+  auto tws = [&](const ess_layer_io& io) -> void* {
+    if (!io.ws || io.ws_bytes < ws_need || topk_region(*d) == 0) return nullptr;
+    return static_cast<char*>(io.ws) + attn_region(*d);
+  };
   for (int l = 0; l < n_layers; ++l) {
     if ((s = check_layer(layers[l], mode, l)) != ESS_OK) return s;
     if (mode != ESS_MODE_FILL && layers[l].ws_bytes < ws_need)
@@ -334,7 +363,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     const int C = d->pool_slots;
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
-      e = enqueue_select(*d, io, n_vis, C, 1, stream);
+      e = enqueue_select(*d, io, n_vis, C, 1, tws(io), stream);
       if (e == hipSuccess)
         e = ess::launch_miss_copy(*d, C, io.miss_pos, io.miss_slot, io.n_miss,
                                   io.host_view, io.pool, stream);
@@ -344,7 +373,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   if (mode == ESS_MODE_INLINE) {
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
-      e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, stream);
+      e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, tws(io), stream);
       if (e == hipSuccess) e = enqueue_attention(*d, io, stream);
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
@@ -362,7 +391,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   e = hipEventRecord(ev[n_layers], stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[n_layers], 0);
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
-    e = enqueue_select(*d, layers[l], n_vis, d->topk, d->mtp, side);
+    e = enqueue_select(*d, layers[l], n_vis, d->topk, d->mtp, tws(layers[l]), side);
     if (e == hipSuccess) e = hipEventRecord(ev[l], side);
   }
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {

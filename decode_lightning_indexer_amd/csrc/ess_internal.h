@@ -32,10 +32,15 @@ hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
                                hipStream_t s);
 
 // ---- top-k --------------------------------------------------------------
+// Workspace of the multi-level selection of rows longer than 32768 keys
+// (0 when it does not apply: short rows, or k > 4096).  With ws == nullptr
+// the top-k runs one workgroup per row over the whole row.
+size_t topk_ws_bytes(const ess_dims& d, int k, int n_tok);
 hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
-                       int32_t* sel_slot, int32_t* n_sel, hipStream_t s);
+                       int32_t* sel_slot, int32_t* n_sel, void* ws,
+                       hipStream_t s);
 
 // ---- pool ---------------------------------------------------------------
 // Per-request LRU state: header, slot stamps [C], ring of (slot, stamp).
@@ -67,7 +72,7 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
                                 int32_t* miss_pos, int32_t* miss_slot,
                                 int32_t* n_miss, int32_t* n_evict,
                                 int32_t* row_dst, int32_t* sel_slot_post,
-                                hipStream_t s);
+                                void* ws, hipStream_t s);
 hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               const int32_t* sel_pos, const int32_t* n_sel,
                               int32_t* cache_slots, int32_t* slot_pos,

@@ -26,6 +26,18 @@
 //      keys in its bucket; it is written straight to that rank of the
 //      outputs with its slot.  A bucket too large for that (a long run of
 //      equal or near-equal scores) falls back to a full bitonic sort.
+//
+// Rows longer than one register-resident chunk (32768 keys) and k <= 4096:
+// one workgroup per row would stream the row once per pass from one CU
+// (~480 us at 1M keys), so the row is reduced in levels first.  A level
+// splits its input into chunks, one workgroup each, and writes each chunk's
+// exact top-k as (key, position) pairs in ascending position order, densely
+// (chunk s at s * k).  The row's top-k lies inside the union of its chunks'
+// top-k, so a level loses no winner; levels repeat until at most one chunk
+// of candidates is left, and the final workgroup selects from that list as
+// above, with positions read from the list.  The candidates stay in
+// position order, so "equal keys: lower position first" is still the order
+// of the list.
 #include "block_util.h"
 #include "ess_internal.h"
 #include "pool_update_body.h"
@@ -38,6 +50,7 @@ constexpr int kBins = 2048;
 constexpr int kSmall = 64;       // candidates sorted by one wave
 constexpr int kMaxBucket = 256;  // larger winner buckets take the full sort
 constexpr int kFusedMaxK = 4096;  // top-k + update in one workgroup up to this k
+constexpr int kLevelMaxK = 4096;  // multi-level selection up to this k (>= 8x per level)
 
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -62,38 +75,63 @@ constexpr int VPT = 8;                 // 16-byte loads per thread per chunk
 constexpr int KPT = VPT * 4;           // keys per thread per chunk
 constexpr int CHUNK = NT * KPT;        // 32768 keys
 
-// Top-k of one (request, token) row by a 1024-thread workgroup; returns the
-// number selected.  grp: kpow2 winners of LDS.  FUSE: the outputs are also
-// left in LDS (rpos, rslot) for the residency update that follows in the
-// same workgroup.
-template <bool RES, bool FUSE>
-__device__ int topk_row(
-    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
-    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
-    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int n_tok, int k, int kpow2, int row, uint64_t* grp, int32_t* rpos,
-    int32_t* rslot) {
+// One selection input: a run of a scores row (entry i is position pos0 + i)
+// or, with EXPL, a candidate list of order-preserving keys with explicit
+// positions in ascending order.  n entries; vec: 16-byte aligned start.
+struct RowIn {
+  const float* score;
+  const uint32_t* key;
+  const int32_t* pos;
+  int n;
+  bool vec;
+  int pos0;
+};
+
+// Rank-order outputs (with the slot of each winner) or, with POSORD, the
+// selected (key, position) pairs in input order.
+struct RowOut {
+  int32_t* op;
+  int32_t* os;
+  const int32_t* cs;
+  int32_t* n_sel;      // may be null
+  uint32_t* okey;      // POSORD
+  int32_t* opos;       // POSORD
+  int32_t* rpos;       // FUSE
+  int32_t* rslot;      // FUSE
+};
+
+// Top-k of one input by a 1024-thread workgroup; returns the number
+// selected.  grp: kpow2 winners of LDS (rank order only).  FUSE: the
+// outputs are also left in LDS (rpos, rslot) for the residency update that
+// follows in the same workgroup.
+template <bool RES, bool FUSE, bool EXPL, bool POSORD>
+__device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
+                        uint64_t* grp) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t cand[kSmall];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
   __shared__ uint32_t s_bin_need, s_bin_cnt, s_nc;
   __shared__ int s_bin;
+  __shared__ uint64_t s_thr;
 
   const int tid = threadIdx.x;
-  const int b = row / n_tok, j = row % n_tok;
-  const float* srow = scores + ((size_t)b * m + j) * L;
-  int n = n_vis[b * m + j];
-  n = n < 0 ? 0 : (n > L ? L : n);
+  const float* srow = in.score;
+  const uint32_t* krow = in.key;
+  const int32_t* prow = in.pos;
+  const int pos0 = in.pos0;
+  const int n = in.n;
   const int keff = min(k, n);
-  const bool vec = (L & 3) == 0;     // rows start 16-byte aligned
-  int32_t* op = sel_pos + ((size_t)b * n_tok + j) * k;
-  int32_t* os = sel_slot + ((size_t)b * n_tok + j) * k;
-  const int32_t* cs = cache_slots + (size_t)b * L;
-  for (int i = keff + tid; i < k; i += NT) {
-    op[i] = -1;
-    os[i] = -1;
+  const bool vec = in.vec;
+  int32_t* op = out.op;
+  int32_t* os = out.os;
+  const int32_t* cs = out.cs;
+  if (!POSORD) {
+    for (int i = keff + tid; i < k; i += NT) {
+      op[i] = -1;
+      os[i] = -1;
+    }
+    if (tid == 0 && out.n_sel) *out.n_sel = keff;
   }
-  if (tid == 0) n_sel[b * n_tok + j] = keff;
   if (keff == 0) return 0;
   // Output row r: the selection and its slot.
 #define EMIT(R, POS, SLOT)                                                    \
@@ -101,8 +139,8 @@ __device__ int topk_row(
     op[R] = (POS);                                                            \
     os[R] = (SLOT);                                                           \
     if (FUSE) {                                                               \
-      rpos[R] = (POS);                                                        \
-      rslot[R] = (SLOT);                                                      \
+      out.rpos[R] = (POS);                                                    \
+      out.rslot[R] = (SLOT);                                                  \
     }                                                                         \
   } while (0)
 
@@ -114,24 +152,44 @@ __device__ int topk_row(
   do {                                                                        \
     const int base_ = (BASE);                                                 \
     if (vec && base_ + CHUNK <= n) {                                          \
-      float4 f_[VPT];                                                         \
-      _Pragma("unroll") for (int v = 0; v < VPT; ++v)                         \
-        f_[v] = *reinterpret_cast<const float4*>(srow + base_ + (v * NT + tid) * 4); \
-      _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                       \
-        kr[4 * v + 0] = ord_key(f_[v].x);                                     \
-        kr[4 * v + 1] = ord_key(f_[v].y);                                     \
-        kr[4 * v + 2] = ord_key(f_[v].z);                                     \
-        kr[4 * v + 3] = ord_key(f_[v].w);                                     \
+      if constexpr (EXPL) {                                                   \
+        uint4 a_[VPT];                                                        \
+        _Pragma("unroll") for (int v = 0; v < VPT; ++v)                       \
+          a_[v] = *reinterpret_cast<const uint4*>(krow + base_ + (v * NT + tid) * 4); \
+        _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                     \
+          kr[4 * v + 0] = a_[v].x;                                            \
+          kr[4 * v + 1] = a_[v].y;                                            \
+          kr[4 * v + 2] = a_[v].z;                                            \
+          kr[4 * v + 3] = a_[v].w;                                            \
+        }                                                                     \
+      } else {                                                                \
+        float4 f_[VPT];                                                       \
+        _Pragma("unroll") for (int v = 0; v < VPT; ++v)                       \
+          f_[v] = *reinterpret_cast<const float4*>(srow + base_ + (v * NT + tid) * 4); \
+        _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                     \
+          kr[4 * v + 0] = ord_key(f_[v].x);                                   \
+          kr[4 * v + 1] = ord_key(f_[v].y);                                   \
+          kr[4 * v + 2] = ord_key(f_[v].z);                                   \
+          kr[4 * v + 3] = ord_key(f_[v].w);                                   \
+        }                                                                     \
       }                                                                       \
     } else {                                                                  \
       _Pragma("unroll") for (int v = 0; v < VPT; ++v)                         \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                       \
           const int p_ = base_ + (v * NT + tid) * 4 + e;                      \
-          kr[4 * v + e] = p_ < n ? ord_key(srow[p_]) : 0u;                    \
+          if constexpr (EXPL) {                                               \
+            kr[4 * v + e] = p_ < n ? krow[p_] : 0u;                           \
+          } else {                                                            \
+            kr[4 * v + e] = p_ < n ? ord_key(srow[p_]) : 0u;                  \
+          }                                                                   \
         }                                                                     \
     }                                                                         \
   } while (0)
+  // Index of a held key in the input, and its position (a candidate list's
+  // positions are read only for the keys that need one: winners and the
+  // bin's candidates, about k of the row's keys).
 #define pos_of(BASE, V, E) ((BASE) + ((V) * NT + tid) * 4 + (E))
+#define real_pos(BASE, V, E) (EXPL ? prow[pos_of(BASE, V, E)] : pos0 + pos_of(BASE, V, E))
   const int nchunks = (n + CHUNK - 1) / CHUNK;
 
   if (RES) ESS_TOPK_LOAD(0);
@@ -214,6 +272,92 @@ __device__ int topk_row(
   const bool small_bin = need > 0 && cnt <= (uint32_t)kSmall;
   const bool ordered = need > 0 && !small_bin;   // a run of equal keys
 
+  if constexpr (POSORD) {
+    // The selected pairs in input order: keys above the bin; of a small bin
+    // the `need` largest full keys (one wave sorts the bin, the need-th
+    // becomes a threshold); of a run of equal keys the first `need`.
+    if (small_bin) {
+      if (tid == 0) s_nc = 0;
+      __syncthreads();
+      for (int c = 0; c < nchunks; ++c) {
+        const int base = c * CHUNK;
+        if (!RES) ESS_TOPK_LOAD(base);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = kr[4 * v + e];
+            if (pos_of(base, v, e) < n && (uint64_t)key >= bin_lo &&
+                (uint64_t)key < win_lo) {
+              const uint32_t at = atomicAdd(&s_nc, 1u);
+              if (at < (uint32_t)kSmall) cand[at] = full_key(key, real_pos(base, v, e));
+            }
+          }
+      }
+      __syncthreads();
+      if (tid >= NT - 64) {
+        const int i = tid - (NT - 64);
+        const uint32_t nc = min(s_nc, (uint32_t)kSmall);
+        const uint64_t x = wave_bitonic_u64<true>(i < (int)nc ? cand[i] : 0ull, i);
+        if ((uint32_t)i == need - 1) s_thr = x;
+      }
+      __syncthreads();
+    }
+    const uint64_t thr = small_bin ? s_thr : 0ull;
+    uint32_t at = 0, eq_taken = 0;   // uniform
+    for (int c = 0; c < nchunks; ++c) {
+      const int base = c * CHUNK;
+      if (!RES) ESS_TOPK_LOAD(base);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        uint32_t eq_rank = need;     // rank of this thread's first equal key
+        if (ordered) {
+          int n_eq = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (pos_of(base, v, e) < n && (uint64_t)kr[4 * v + e] == bin_lo) ++n_eq;
+          if (eq_taken < need && __syncthreads_count(n_eq) > 0) {
+            uint32_t t2;
+            eq_rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
+            eq_taken += t2;
+          }
+        }
+        bool sel[4];
+        int cnt_sel = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = kr[4 * v + e];
+          bool t = false;
+          if (pos_of(base, v, e) < n) {
+            if ((uint64_t)key >= win_lo) {
+              t = true;
+            } else if (small_bin) {
+              t = (uint64_t)key >= bin_lo && full_key(key, real_pos(base, v, e)) >= thr;
+            } else if (ordered && (uint64_t)key == bin_lo) {
+              t = eq_rank < need;
+              ++eq_rank;
+            }
+          }
+          sel[e] = t;
+          cnt_sel += t;
+        }
+        uint32_t tot;
+        uint32_t o = at + block_exscan<NT>(cnt_sel, tmp, &tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (sel[e]) {
+            if (o < (uint32_t)keff) {   // exactly keff are selected
+              out.okey[o] = kr[4 * v + e];
+              out.opos[o] = real_pos(base, v, e);
+            }
+            ++o;
+          }
+        at += tot;
+      }
+    }
+    return keff;
+  } else {
+
   // Winner buckets of equal width over [max(win_lo, mn), mx], larger keys
   // first.
   const uint32_t wlo = win_lo > (uint64_t)mn ? (uint32_t)min(win_lo, (uint64_t)mx) : mn;
@@ -239,7 +383,7 @@ __device__ int topk_row(
             atomicAdd(&hist[bucket_of(key)], 1u);
           } else if (small_bin && (uint64_t)key >= bin_lo) {
             const uint32_t at = atomicAdd(&s_nc, 1u);
-            if (at < (uint32_t)kSmall) cand[at] = full_key(key, p);
+            if (at < (uint32_t)kSmall) cand[at] = full_key(key, real_pos(base, v, e));
           }
         }
       }
@@ -272,7 +416,7 @@ __device__ int topk_row(
         if (p < n && (uint64_t)key >= win_lo) {
           // The histogram bounds every bucket's fill inside [0, nwin).
           const uint32_t at = atomicAdd(&hist[bucket_of(key)], 1u);
-          if (at < (uint32_t)kpow2) grp[at] = full_key(key, p);
+          if (at < (uint32_t)kpow2) grp[at] = full_key(key, real_pos(base, v, e));
         }
       }
     if (ordered) {
@@ -287,8 +431,8 @@ __device__ int topk_row(
           uint32_t rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int p = pos_of(base, v, e);
-            if (p < n && (uint64_t)kr[4 * v + e] == bin_lo) {
+            if (pos_of(base, v, e) < n && (uint64_t)kr[4 * v + e] == bin_lo) {
+              const int p = real_pos(base, v, e);
               if (rank < need) EMIT(nwin + rank, p, cs[p]);
               ++rank;
             }
@@ -338,8 +482,22 @@ __device__ int topk_row(
 #undef EMIT
 #undef bucket_of
 #undef pos_of
+#undef real_pos
 #undef ESS_TOPK_LOAD
   return keff;
+  }
+}
+
+// Candidates a level leaves of n entries: k per full chunk and min(k, rest)
+// of the last (k <= CHUNK).
+__host__ __device__ __forceinline__ int level_count(int n, int k) {
+  return (n / CHUNK) * k + min(k, n % CHUNK);
+}
+
+__device__ __forceinline__ int visible(const int32_t* n_vis, int b, int m, int j,
+                                       int L) {
+  const int n = n_vis[b * m + j];
+  return n < 0 ? 0 : (n > L ? L : n);
 }
 
 template <bool RES>
@@ -349,39 +507,173 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
     int n_tok, int k, int kpow2) {
   extern __shared__ uint64_t grp[];  // kpow2: winners grouped by bucket
-  topk_row<RES, false>(scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel, L, m,
-                       n_tok, k, kpow2, blockIdx.x, grp, nullptr, nullptr);
+  const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
+  const size_t o = ((size_t)b * n_tok + j) * k;
+  const RowIn in{scores + ((size_t)b * m + j) * L, nullptr, nullptr,
+                 visible(n_vis, b, m, j, L), (L & 3) == 0, 0};
+  const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
+                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr};
+  topk_row<RES, false, false, false>(in, k, kpow2, out, grp);
+}
+
+// One level of a long row's reduction: workgroup (s, row) writes the exact
+// top-k of chunk s of the row's current list as (key, position) pairs in
+// position order at s * k of the next list.  Level 1 reads the scores.
+template <bool EXPL>
+__global__ __launch_bounds__(NT) void topk_level_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
+    const uint32_t* __restrict__ ikey, const int32_t* __restrict__ ipos,
+    uint32_t* __restrict__ okey, int32_t* __restrict__ opos, size_t cap, int L,
+    int m, int n_tok, int k, int level) {
+  const int row = blockIdx.y, b = row / n_tok, j = row % n_tok;
+  int n = visible(n_vis, b, m, j, L);
+  for (int l = 1; l < level; ++l) n = level_count(n, k);
+  const int base = blockIdx.x * CHUNK;
+  if (base >= n) return;      // this row's list is shorter
+  const int ns = min(CHUNK, n - base);
+  const size_t rb = (size_t)row * cap;
+  RowIn in;
+  if constexpr (EXPL)
+    in = RowIn{nullptr, ikey + rb + base, ipos + rb + base, ns,
+               ((rb + base) & 3) == 0, 0};
+  else
+    in = RowIn{scores + ((size_t)b * m + j) * L + base, nullptr, nullptr, ns,
+               (L & 3) == 0, base};
+  const size_t ob = rb + (size_t)blockIdx.x * k;
+  const RowOut out{nullptr, nullptr, nullptr, nullptr, okey + ob, opos + ob,
+                   nullptr, nullptr};
+  topk_row<true, false, EXPL, true>(in, k, 0, out, nullptr);
+}
+
+// The final selection of a long row from its candidate list after `levels`
+// levels: rank order with slots.
+__global__ __launch_bounds__(NT) void topk_final_kernel(
+    const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cpos,
+    size_t cap, const int32_t* __restrict__ n_vis,
+    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
+    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
+    int n_tok, int k, int kpow2, int levels) {
+  extern __shared__ uint64_t grp[];
+  const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
+  int n = visible(n_vis, b, m, j, L);
+  for (int l = 0; l < levels; ++l) n = level_count(n, k);
+  const size_t rb = (size_t)row * cap, o = ((size_t)b * n_tok + j) * k;
+  const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
+  const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
+                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr};
+  topk_row<true, false, true, false>(in, k, kpow2, out, grp);
 }
 
 // One query token per request: the top-k and the residency update of a
 // request in one workgroup.  The update starts from the selections and
 // slots the top-k leaves in LDS, so neither is read back from memory, and
-// the step saves a kernel boundary.
-template <bool RES>
+// the step saves a kernel boundary.  With levels > 0 the top-k reads the
+// request's candidate list instead of its scores.
+template <bool RES, bool EXPL>
 __global__ __launch_bounds__(NT) void select_update_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
-    const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
-    int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int k, int kpow2, pool::Args pa, int rank_off) {
+    const float* __restrict__ scores, const uint32_t* __restrict__ ckey,
+    const int32_t* __restrict__ cpos, size_t cap,
+    const int32_t* __restrict__ n_vis, const int32_t* __restrict__ cache_slots,
+    int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_slot,
+    int32_t* __restrict__ n_sel, int L, int m, int k, int kpow2, int levels,
+    pool::Args pa, int rank_off) {
   extern __shared__ uint64_t dyn[];  // top-k winners, then the update's entries
   int32_t* rpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dyn) + rank_off);
   int32_t* rslot = rpos + k;
-  const int keff = topk_row<RES, true>(scores, n_vis, cache_slots, sel_pos, sel_slot,
-                                       n_sel, L, m, 1, k, kpow2, blockIdx.x, dyn,
-                                       rpos, rslot);
+  const int b = blockIdx.x;
+  int n = visible(n_vis, b, m, 0, L);
+  const size_t o = (size_t)b * k;
+  const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L, n_sel + b,
+                   nullptr, nullptr, rpos, rslot};
+  int keff;
+  if constexpr (EXPL) {
+    for (int l = 0; l < levels; ++l) n = level_count(n, k);
+    const size_t rb = (size_t)b * cap;
+    const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
+    keff = topk_row<true, true, true, false>(in, k, kpow2, out, dyn);
+  } else {
+    const RowIn in{scores + (size_t)b * m * L, nullptr, nullptr, n, (L & 3) == 0, 0};
+    keff = topk_row<RES, true, false, false>(in, k, kpow2, out, dyn);
+  }
   __syncthreads();   // ranked selections complete; the winners' buffer is free
-  pool::update_request<true>(pa, blockIdx.x, dyn, rpos, rslot, keff);
+  pool::update_request<true>(pa, b, dyn, rpos, rslot, keff);
+}
+
+// Levels a row of L entries needs before one workgroup holds it (0: none, or
+// k too large for levels to shrink the row).
+int n_levels(int L, int k) {
+  if (k > kLevelMaxK) return 0;
+  int nl = 0;
+  for (int n = L; n > CHUNK; n = level_count(n, k)) ++nl;
+  return nl;
+}
+
+size_t level_cap(int L, int k) { return (size_t)((L + CHUNK - 1) / CHUNK) * k; }
+
+size_t level_half(size_t rows, size_t cap) { return align_up(rows * cap * 4, 256); }
+
+// Enqueue the levels of every row; *key, *pos: the list the final
+// selection reads.
+hipError_t enqueue_levels(const ess_dims& d, int k, int n_tok, int nl,
+                          const float* scores, const int32_t* n_vis, void* ws,
+                          const uint32_t** fkey, const int32_t** fpos,
+                          hipStream_t s) {
+  const size_t cap = level_cap(d.ctx_len, k);
+  const int rows = d.batch * n_tok;
+  const size_t half = level_half(rows, cap);
+  char* w = static_cast<char*>(ws);
+  uint32_t* key[2] = {reinterpret_cast<uint32_t*>(w), reinterpret_cast<uint32_t*>(w + 2 * half)};
+  int32_t* pos[2] = {reinterpret_cast<int32_t*>(w + half), reinterpret_cast<int32_t*>(w + 3 * half)};
+  int n = d.ctx_len;
+  for (int l = 1; l <= nl; ++l) {
+    const int chunks = (n + CHUNK - 1) / CHUNK;
+    const int ob = (l - 1) & 1, ib = ob ^ 1;
+    if (l == 1)
+      hipLaunchKernelGGL(topk_level_kernel<false>, dim3(chunks, rows), dim3(NT), 0, s,
+                         scores, n_vis, nullptr, nullptr, key[ob], pos[ob], cap,
+                         d.ctx_len, d.mtp, n_tok, k, l);
+    else
+      hipLaunchKernelGGL(topk_level_kernel<true>, dim3(chunks, rows), dim3(NT), 0, s,
+                         scores, n_vis, key[ib], pos[ib], key[ob], pos[ob], cap,
+                         d.ctx_len, d.mtp, n_tok, k, l);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    n = level_count(n, k);
+  }
+  *fkey = key[(nl - 1) & 1];
+  *fpos = pos[(nl - 1) & 1];
+  return hipSuccess;
 }
 
 }  // namespace
 
+size_t topk_ws_bytes(const ess_dims& d, int k, int n_tok) {
+  if (n_levels(d.ctx_len, k) == 0) return 0;
+  return 4 * level_half((size_t)d.batch * n_tok, level_cap(d.ctx_len, k));
+}
+
 hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
-                       int32_t* sel_slot, int32_t* n_sel, hipStream_t s) {
+                       int32_t* sel_slot, int32_t* n_sel, void* ws,
+                       hipStream_t s) {
   // The fallback sort needs a power of two of at least one key per thread.
   const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
   const size_t lds = (size_t)kpow2 * sizeof(uint64_t);
+  const int nl = ws ? n_levels(d.ctx_len, k) : 0;
+  if (nl > 0) {
+    const uint32_t* fk;
+    const int32_t* fp;
+    hipError_t e = enqueue_levels(d, k, n_tok, nl, scores, n_vis, ws, &fk, &fp, s);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)topk_final_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_final_kernel, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                       fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
+                       sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
+    return hipGetLastError();
+  }
   // Rows of at most one chunk stay in registers for all passes.
   const bool res = d.ctx_len <= CHUNK;
   const void* fn = res ? (const void*)topk_kernel<true> : (const void*)topk_kernel<false>;
@@ -410,7 +702,7 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
                                 int32_t* miss_pos, int32_t* miss_slot,
                                 int32_t* n_miss, int32_t* n_evict,
                                 int32_t* row_dst, int32_t* sel_slot_post,
-                                hipStream_t s) {
+                                void* ws, hipStream_t s) {
   const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
   const int epow2 = kpow2;
   const int two = epow2 <= pool::kTwoBufferMax ? 1 : 0;
@@ -425,20 +717,32 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
   const size_t upd_bytes = (size_t)epow2 * sizeof(uint64_t) * (two ? 2 : 1);
   const size_t rank_off = align_up(topk_bytes > upd_bytes ? topk_bytes : upd_bytes, 16);
   const size_t lds = rank_off + 2 * (size_t)k * sizeof(int32_t);
+  const int nl = ws ? n_levels(d.ctx_len, k) : 0;
+  const uint32_t* fk = nullptr;
+  const int32_t* fp = nullptr;
   const bool res = d.ctx_len <= CHUNK;
-  const void* fn = res ? (const void*)select_update_kernel<true>
-                       : (const void*)select_update_kernel<false>;
+  const void* fn = nl > 0 ? (const void*)select_update_kernel<true, true>
+                   : res  ? (const void*)select_update_kernel<true, false>
+                          : (const void*)select_update_kernel<false, false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  if (res)
-    hipLaunchKernelGGL(select_update_kernel<true>, dim3(d.batch), dim3(NT), lds, s,
-                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, k, kpow2, pa, (int)rank_off);
+  if (nl > 0) {
+    e = enqueue_levels(d, k, 1, nl, scores, n_vis, ws, &fk, &fp, s);
+    if (e != hipSuccess) return e;
+  }
+  const size_t cap = level_cap(d.ctx_len, k);
+#define ESS_SU_LAUNCH(R, X)                                                    \
+  hipLaunchKernelGGL((select_update_kernel<R, X>), dim3(d.batch), dim3(NT), lds, s, \
+                     scores, fk, fp, cap, n_vis, cache_slots, sel_pos, sel_slot,   \
+                     n_sel, d.ctx_len, d.mtp, k, kpow2, nl, pa, (int)rank_off)
+  if (nl > 0)
+    ESS_SU_LAUNCH(true, true);
+  else if (res)
+    ESS_SU_LAUNCH(true, false);
   else
-    hipLaunchKernelGGL(select_update_kernel<false>, dim3(d.batch), dim3(NT), lds, s,
-                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, k, kpow2, pa, (int)rank_off);
+    ESS_SU_LAUNCH(false, false);
+#undef ESS_SU_LAUNCH
   return hipGetLastError();
 }
 

@@ -75,8 +75,10 @@ typedef enum ess_status {
   ESS_ERR_NOMEM = -5         /* host allocation failed / workspace too small */
 } ess_status;
 
-/* Bytes of workspace the calls below need for these dims (the attention's
- * split-row partials).  One workspace serves one stream at a time. */
+/* Bytes of workspace the calls below need for these dims: the attention's
+ * split-row partials, then (ctx_len > 32768 with topk or pool_slots <= 4096)
+ * the candidate lists of the top-k's levels.  One workspace serves one
+ * stream at a time; it must be 16-byte aligned. */
 size_t ess_workspace_bytes(const ess_dims* d);
 
 /* Bytes of the opaque per-layer LRU state (B requests): per request a header,
@@ -116,8 +118,13 @@ ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
  *                  (-1: not resident); -1 beyond n_sel
  * Inputs scores [B][m][L], n_vis [B][m], cache_slots [B][L]; outputs
  * sel_pos, sel_slot [B][n_tok][k] and n_sel [B][n_tok].  1 <= n_tok <= m,
- * 1 <= k <= 16384.  Scores must not be NaN.  ws, ws_bytes: not used (the
- * selection runs in on-chip memory); NULL and 0 are fine. */
+ * 1 <= k <= 16384.  Scores must not be NaN.  Rows of at most 32768 keys,
+ * and any k > 4096, select in on-chip memory (ws and ws_bytes are not used;
+ * NULL and 0 are fine).  Longer rows with k <= 4096 select in levels: each
+ * 32768-key chunk's top-k is written to ws as candidates until one
+ * workgroup holds the row's list; ws must then hold ess_workspace_bytes(d)
+ * bytes (enough for k = d->topk with n_tok <= d->mtp, and for
+ * k = d->pool_slots with n_tok = 1), else ESS_ERR_NOMEM. */
 ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
                            const float* scores, const int32_t* n_vis,
                            const int32_t* cache_slots, int32_t* sel_pos,

@@ -104,3 +104,24 @@ def test_decode_step_argument_checks(L):
 def test_status_strings(L):
     for code, text in ((0, "ok"), (-3, "pool capacity exceeded"), (-4, "HIP runtime error")):
         assert L.ess_status_string(code).decode() == text
+
+
+def test_long_rows_need_a_topk_workspace(L):
+    # Rows over 32768 keys with k <= 4096 select in levels whose candidate
+    # lists (two buffers of keys and positions, k per 32768-key chunk and
+    # row) sit after the attention's partials; the first fill's top-C
+    # (n_tok = 1) is covered too.
+    short = _d(topk=2048, pool_slots=4096)
+    long_ = _d(ctx_len=100000, topk=2048, pool_slots=4096)
+    chunks = -(-100000 // 32768)
+    step = 4 * (2 * 1) * chunks * 2048 * 4       # B=2 rows, k=2048
+    fill = 4 * (2 * 1) * chunks * 4096 * 4       # k=C=4096
+    assert ess.ess_workspace_bytes(long_) - ess.ess_workspace_bytes(short) == max(step, fill)
+    # k > 4096 never uses levels.
+    assert ess.ess_workspace_bytes(_d(ctx_len=100000, topk=8192, pool_slots=16384)) == \
+        ess.ess_workspace_bytes(_d(topk=8192, pool_slots=16384))
+    st = _status(lambda: ess.ess_topk_lookup(long_, 2048, 1, P, P, P, P, P, P, stream=0))
+    assert st == "out of memory"
+    assert "levels" in L.ess_last_error().decode()
+    st = _status(lambda: ess.ess_topk_lookup(long_, 2048, 1, P, P, P, P, P, P, P + 4, 1 << 30, stream=0))
+    assert st == "invalid argument"

@@ -81,6 +81,15 @@ def _scores(kind, rng, shape):
     ("indexer_like", 1, 2, 1, 30000, 16384, False),  # fill-size k, token 0 only
     ("int_ties", 3, 1, 1, 1, 1, False),
     ("float", 1, 3, 3, 2049, 7, True),
+    # Rows longer than 32768 keys select in levels (k <= 4096).
+    ("int_ties", 2, 1, 1, 70000, 1000, True),
+    ("equal", 1, 1, 1, 100000, 2048, False),      # one run of equal keys
+    ("zeros", 1, 1, 1, 50000, 513, False),        # +-0, k not a multiple of 4
+    ("wide", 1, 1, 1, 1 << 20, 2048, False),      # two levels
+    ("indexer_like", 2, 2, 2, 131072, 2048, True),
+    ("indexer_like", 1, 1, 1, 1 << 20, 4096, False),
+    ("float", 1, 1, 1, 300000, 7, True),
+    ("float", 1, 1, 1, 40000, 5000, False),       # k > 4096: one workgroup
 ])
 def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
     rng = np.random.default_rng(zlib.crc32(f"{kind}-{L}-{k}".encode()))
@@ -94,7 +103,9 @@ def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
     sp = torch.empty((B, n_tok, k), dtype=torch.int32, device="cuda")
     ss = torch.empty_like(sp)
     ns = torch.empty((B, n_tok), dtype=torch.int32, device="cuda")
-    ess.ess_topk_lookup(d, k, n_tok, t(s), t(n_vis), t(cs), sp, ss, ns)
+    wsb = ess.ess_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ess.ess_topk_lookup(d, k, n_tok, t(s), t(n_vis), t(cs), sp, ss, ns, ws, wsb)
     sync()
     for b in range(B):
         rp, rs, rn = topk_lookup(s[b, :n_tok].astype(np.float64), n_vis[b, :n_tok], k, cs[b])
