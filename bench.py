@@ -266,13 +266,15 @@ def run_steps(args, name, n_layers, modes, K, W):
 
 
 def extra_measurements(args):
-    """The 128K / MTP=2 configuration at its three query-drift rates, and the
-    16-layer configuration's per-layer shape over 4 layers with and without
+    """The 128K / MTP=2 configuration at its three query-drift rates, the
+    1M-token single request at both pool sizes, and the 16-layer
+    configuration's per-layer shape over 4 layers with and without
     side-stream prefetch."""
     from decode_lightning_indexer_amd import ess
     out = {}
     K, W = 16, 4
-    for name in ("128k-b8-mtp2-r099", "128k-b8-mtp2-r095", "128k-b8-mtp2-r080"):
+    for name in ("128k-b8-mtp2-r099", "128k-b8-mtp2-r095", "128k-b8-mtp2-r080",
+                 "1m-b1-c8k", "1m-b1-c16k"):
         res, n_miss, t_copy, wl = run_steps(args, name, 1, [ess.ESS_MODE_INLINE], K, W)
         t = res[ess.ESS_MODE_INLINE]
         out[name] = {"steps_per_s": 1 / t, "query_tok_s": wl.batch * wl.mtp / t,

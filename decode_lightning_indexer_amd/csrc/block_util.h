@@ -46,6 +46,39 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* tmp,
   return res;
 }
 
+// The same over uint64 values; used with several 16-bit counts packed in
+// one word (each field's total must stay below 2^16).  tmp: NT/64 + 1 words.
+template <int NT>
+__device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, uint64_t* tmp,
+                                                     uint64_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    const uint64_t t = lane < NW ? tmp[lane] : 0ull;
+    uint64_t ti = t;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const uint64_t y = __shfl_up(ti, o);
+      if (lane >= o) ti += y;
+    }
+    if (lane < NW) tmp[lane] = ti - t;
+    if (lane == NW - 1) tmp[NW] = ti;
+  }
+  __syncthreads();
+  const uint64_t res = tmp[wv] + x - v;
+  *total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
 // Minimum and maximum of a uint32 over the workgroup.  tmp: 2*(NT/64) words.
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx,

@@ -74,6 +74,10 @@ __device__ __forceinline__ bool in_fixed(uint32_t key, uint32_t prefix,
 constexpr int VPT = 8;                 // 16-byte loads per thread per chunk
 constexpr int KPT = VPT * 4;           // keys per thread per chunk
 constexpr int CHUNK = NT * KPT;        // 32768 keys
+// Candidate lists carry a position with each key; both stay in registers
+// with half the keys per thread.
+constexpr int VPT_E = 4;
+constexpr int CHUNK_E = NT * VPT_E * 4;   // 16384 candidates
 
 // One selection input: a run of a scores row (entry i is position pos0 + i)
 // or, with EXPL, a candidate list of order-preserving keys with explicit
@@ -107,12 +111,18 @@ struct RowOut {
 template <bool RES, bool FUSE, bool EXPL, bool POSORD>
 __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
                         uint64_t* grp) {
+  static_assert(!POSORD || RES, "position-order output needs the row in registers");
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t cand[kSmall];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
   __shared__ uint32_t s_bin_need, s_bin_cnt, s_nc;
   __shared__ int s_bin;
   __shared__ uint64_t s_thr;
+  __shared__ uint64_t tmp64[NT / 64 + 1];
+  // Keys per thread: candidate lists hold half as many, with positions.
+  constexpr int TV = EXPL ? VPT_E : VPT;
+  constexpr int TK = TV * 4;
+  constexpr int TC = NT * TK;
 
   const int tid = threadIdx.x;
   const float* srow = in.score;
@@ -147,26 +157,34 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
   // Keys of one chunk for this thread.  A chunk wholly inside the visible
   // row (the common case) takes eight unconditional 16-byte loads, all in
   // flight together; a partial chunk takes bounds-checked scalar loads.
-  uint32_t kr[KPT];
+  uint32_t kr[TK];
+  int32_t pr[TK];   // positions of a candidate list's keys (EXPL only)
 #define ESS_TOPK_LOAD(BASE)                                                   \
   do {                                                                        \
     const int base_ = (BASE);                                                 \
-    if (vec && base_ + CHUNK <= n) {                                          \
+    if (vec && base_ + TC <= n) {                                          \
       if constexpr (EXPL) {                                                   \
-        uint4 a_[VPT];                                                        \
-        _Pragma("unroll") for (int v = 0; v < VPT; ++v)                       \
+        uint4 a_[TV];                                                         \
+        int4 q_[TV];                                                          \
+        _Pragma("unroll") for (int v = 0; v < TV; ++v) {                      \
           a_[v] = *reinterpret_cast<const uint4*>(krow + base_ + (v * NT + tid) * 4); \
-        _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                     \
+          q_[v] = *reinterpret_cast<const int4*>(prow + base_ + (v * NT + tid) * 4);  \
+        }                                                                     \
+        _Pragma("unroll") for (int v = 0; v < TV; ++v) {                      \
           kr[4 * v + 0] = a_[v].x;                                            \
           kr[4 * v + 1] = a_[v].y;                                            \
           kr[4 * v + 2] = a_[v].z;                                            \
           kr[4 * v + 3] = a_[v].w;                                            \
+          pr[4 * v + 0] = q_[v].x;                                            \
+          pr[4 * v + 1] = q_[v].y;                                            \
+          pr[4 * v + 2] = q_[v].z;                                            \
+          pr[4 * v + 3] = q_[v].w;                                            \
         }                                                                     \
       } else {                                                                \
-        float4 f_[VPT];                                                       \
-        _Pragma("unroll") for (int v = 0; v < VPT; ++v)                       \
+        float4 f_[TV];                                                       \
+        _Pragma("unroll") for (int v = 0; v < TV; ++v)                       \
           f_[v] = *reinterpret_cast<const float4*>(srow + base_ + (v * NT + tid) * 4); \
-        _Pragma("unroll") for (int v = 0; v < VPT; ++v) {                     \
+        _Pragma("unroll") for (int v = 0; v < TV; ++v) {                     \
           kr[4 * v + 0] = ord_key(f_[v].x);                                   \
           kr[4 * v + 1] = ord_key(f_[v].y);                                   \
           kr[4 * v + 2] = ord_key(f_[v].z);                                   \
@@ -174,32 +192,31 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
         }                                                                     \
       }                                                                       \
     } else {                                                                  \
-      _Pragma("unroll") for (int v = 0; v < VPT; ++v)                         \
+      _Pragma("unroll") for (int v = 0; v < TV; ++v)                         \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                       \
           const int p_ = base_ + (v * NT + tid) * 4 + e;                      \
           if constexpr (EXPL) {                                               \
             kr[4 * v + e] = p_ < n ? krow[p_] : 0u;                           \
+            pr[4 * v + e] = p_ < n ? prow[p_] : 0;                            \
           } else {                                                            \
             kr[4 * v + e] = p_ < n ? ord_key(srow[p_]) : 0u;                  \
           }                                                                   \
         }                                                                     \
     }                                                                         \
   } while (0)
-  // Index of a held key in the input, and its position (a candidate list's
-  // positions are read only for the keys that need one: winners and the
-  // bin's candidates, about k of the row's keys).
+  // Index of a held key in the input, and its position.
 #define pos_of(BASE, V, E) ((BASE) + ((V) * NT + tid) * 4 + (E))
-#define real_pos(BASE, V, E) (EXPL ? prow[pos_of(BASE, V, E)] : pos0 + pos_of(BASE, V, E))
-  const int nchunks = (n + CHUNK - 1) / CHUNK;
+#define real_pos(BASE, V, E) (EXPL ? pr[4 * (V) + (E)] : pos0 + pos_of(BASE, V, E))
+  const int nchunks = (n + TC - 1) / TC;
 
   if (RES) ESS_TOPK_LOAD(0);
   // 1. Range of the keys.
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int c = 0; c < nchunks; ++c) {
-    const int base = c * CHUNK;
+    const int base = c * TC;
     if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
+    for (int v = 0; v < TV; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (pos_of(base, v, e) < n) {
@@ -228,10 +245,10 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
       for (int c = 0; c < nchunks; ++c) {
-        const int base = c * CHUNK;
+        const int base = c * TC;
         if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-        for (int v = 0; v < VPT; ++v)
+        for (int v = 0; v < TV; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t key = kr[4 * v + e];
@@ -280,10 +297,10 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       if (tid == 0) s_nc = 0;
       __syncthreads();
       for (int c = 0; c < nchunks; ++c) {
-        const int base = c * CHUNK;
+        const int base = c * TC;
         if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-        for (int v = 0; v < VPT; ++v)
+        for (int v = 0; v < TV; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t key = kr[4 * v + e];
@@ -304,26 +321,48 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       __syncthreads();
     }
     const uint64_t thr = small_bin ? s_thr : 0ull;
-    uint32_t at = 0, eq_taken = 0;   // uniform
+    // Index order is group-major (v, then thread, then e): the counts of a
+    // thread's groups go through packed scans, 16 bits per group, four
+    // groups per 64-bit word.
+    constexpr int NW = (TV + 3) / 4;
+#define ESS_FIELD(W, V) ((uint32_t)(((W)[(V) >> 2] >> (16 * ((V) & 3))) & 0xFFFFu))
+    uint32_t at = 0;   // uniform
     for (int c = 0; c < nchunks; ++c) {
-      const int base = c * CHUNK;
+      const int base = c * TC;
       if (!RES) ESS_TOPK_LOAD(base);
+      // Ranks of equal keys in a run (first `need` in index order win).
+      uint32_t eqr[TV];
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        uint32_t eq_rank = need;     // rank of this thread's first equal key
-        if (ordered) {
-          int n_eq = 0;
+      for (int v = 0; v < TV; ++v) eqr[v] = need;
+      if (ordered) {
+        uint64_t pk[NW], pre[NW], tot[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) pk[w] = 0;
+#pragma unroll
+        for (int v = 0; v < TV; ++v) {
+          uint64_t n_eq = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (pos_of(base, v, e) < n && (uint64_t)kr[4 * v + e] == bin_lo) ++n_eq;
-          if (eq_taken < need && __syncthreads_count(n_eq) > 0) {
-            uint32_t t2;
-            eq_rank = eq_taken + block_exscan<NT>(n_eq, tmp, &t2);
-            eq_taken += t2;
-          }
+          pk[v >> 2] |= n_eq << (16 * (v & 3));
         }
-        bool sel[4];
-        int cnt_sel = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) pre[w] = block_exscan_u64<NT>(pk[w], tmp64, &tot[w]);
+        uint32_t acc = 0;
+#pragma unroll
+        for (int v = 0; v < TV; ++v) {
+          eqr[v] = acc + ESS_FIELD(pre, v);
+          acc += ESS_FIELD(tot, v);
+        }
+        // (equal keys of earlier chunks precede; a single chunk here)
+      }
+      uint32_t selm = 0;
+      uint64_t sk[NW], pre[NW], tot[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sk[w] = 0;
+#pragma unroll
+      for (int v = 0; v < TV; ++v) {
+        uint64_t cv = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = kr[4 * v + e];
@@ -334,27 +373,33 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
             } else if (small_bin) {
               t = (uint64_t)key >= bin_lo && full_key(key, real_pos(base, v, e)) >= thr;
             } else if (ordered && (uint64_t)key == bin_lo) {
-              t = eq_rank < need;
-              ++eq_rank;
+              t = eqr[v] < need;
+              ++eqr[v];
             }
           }
-          sel[e] = t;
-          cnt_sel += t;
+          selm |= (uint32_t)t << (4 * v + e);
+          cv += t;
         }
-        uint32_t tot;
-        uint32_t o = at + block_exscan<NT>(cnt_sel, tmp, &tot);
+        sk[v >> 2] |= cv << (16 * (v & 3));
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w) pre[w] = block_exscan_u64<NT>(sk[w], tmp64, &tot[w]);
+#pragma unroll
+      for (int v = 0; v < TV; ++v) {
+        uint32_t o = at + ESS_FIELD(pre, v);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (sel[e]) {
+          if ((selm >> (4 * v + e)) & 1u) {
             if (o < (uint32_t)keff) {   // exactly keff are selected
               out.okey[o] = kr[4 * v + e];
               out.opos[o] = real_pos(base, v, e);
             }
             ++o;
           }
-        at += tot;
+        at += ESS_FIELD(tot, v);
       }
     }
+#undef ESS_FIELD
     return keff;
   } else {
 
@@ -370,10 +415,10 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
   if (tid == 0) s_nc = 0;
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
-    const int base = c * CHUNK;
+    const int base = c * TC;
     if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
+    for (int v = 0; v < TV; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int p = pos_of(base, v, e);
@@ -405,10 +450,10 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
   // thread and ordered by thread, so a workgroup scan gives each its rank.
   uint32_t eq_taken = 0;
   for (int c = 0; c < nchunks; ++c) {
-    const int base = c * CHUNK;
+    const int base = c * TC;
     if (!RES) ESS_TOPK_LOAD(base);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
+    for (int v = 0; v < TV; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int p = pos_of(base, v, e);
@@ -421,7 +466,7 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       }
     if (ordered) {
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) {
+      for (int v = 0; v < TV; ++v) {
         int n_eq = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -489,9 +534,14 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
 }
 
 // Candidates a level leaves of n entries: k per full chunk and min(k, rest)
-// of the last (k <= CHUNK).
-__host__ __device__ __forceinline__ int level_count(int n, int k) {
-  return (n / CHUNK) * k + min(k, n % CHUNK);
+// of the last (k <= chunk).  Level 1 reads the scores in chunks of CHUNK,
+// later levels candidate lists in chunks of CHUNK_E.
+__host__ __device__ __forceinline__ int level_chunk(int level) {
+  return level == 1 ? CHUNK : CHUNK_E;
+}
+__host__ __device__ __forceinline__ int level_count(int n, int k, int level) {
+  const int c = level_chunk(level);
+  return (n / c) * k + min(k, n % c);
 }
 
 __device__ __forceinline__ int visible(const int32_t* n_vis, int b, int m, int j,
@@ -527,10 +577,11 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(
     int m, int n_tok, int k, int level) {
   const int row = blockIdx.y, b = row / n_tok, j = row % n_tok;
   int n = visible(n_vis, b, m, j, L);
-  for (int l = 1; l < level; ++l) n = level_count(n, k);
-  const int base = blockIdx.x * CHUNK;
+  for (int l = 1; l < level; ++l) n = level_count(n, k, l);
+  constexpr int kChunk = EXPL ? CHUNK_E : CHUNK;
+  const int base = blockIdx.x * kChunk;
   if (base >= n) return;      // this row's list is shorter
-  const int ns = min(CHUNK, n - base);
+  const int ns = min(kChunk, n - base);
   const size_t rb = (size_t)row * cap;
   RowIn in;
   if constexpr (EXPL)
@@ -556,7 +607,7 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   extern __shared__ uint64_t grp[];
   const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
   int n = visible(n_vis, b, m, j, L);
-  for (int l = 0; l < levels; ++l) n = level_count(n, k);
+  for (int l = 1; l <= levels; ++l) n = level_count(n, k, l);
   const size_t rb = (size_t)row * cap, o = ((size_t)b * n_tok + j) * k;
   const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
@@ -587,7 +638,7 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
                    nullptr, nullptr, rpos, rslot};
   int keff;
   if constexpr (EXPL) {
-    for (int l = 0; l < levels; ++l) n = level_count(n, k);
+    for (int l = 1; l <= levels; ++l) n = level_count(n, k, l);
     const size_t rb = (size_t)b * cap;
     const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
     keff = topk_row<true, true, true, false>(in, k, kpow2, out, dyn);
@@ -599,12 +650,13 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
   pool::update_request<true>(pa, b, dyn, rpos, rslot, keff);
 }
 
-// Levels a row of L entries needs before one workgroup holds it (0: none, or
-// k too large for levels to shrink the row).
+// Levels a row of L entries needs before one workgroup holds its candidate
+// list (0: the row fits one register-resident chunk, or k is too large for
+// levels to shrink the row).
 int n_levels(int L, int k) {
-  if (k > kLevelMaxK) return 0;
-  int nl = 0;
-  for (int n = L; n > CHUNK; n = level_count(n, k)) ++nl;
+  if (k > kLevelMaxK || L <= CHUNK) return 0;
+  int nl = 1;
+  for (int n = level_count(L, k, 1); n > CHUNK_E; n = level_count(n, k, nl)) ++nl;
   return nl;
 }
 
@@ -626,7 +678,7 @@ hipError_t enqueue_levels(const ess_dims& d, int k, int n_tok, int nl,
   int32_t* pos[2] = {reinterpret_cast<int32_t*>(w + half), reinterpret_cast<int32_t*>(w + 3 * half)};
   int n = d.ctx_len;
   for (int l = 1; l <= nl; ++l) {
-    const int chunks = (n + CHUNK - 1) / CHUNK;
+    const int chunks = (n + level_chunk(l) - 1) / level_chunk(l);
     const int ob = (l - 1) & 1, ib = ob ^ 1;
     if (l == 1)
       hipLaunchKernelGGL(topk_level_kernel<false>, dim3(chunks, rows), dim3(NT), 0, s,
@@ -638,7 +690,7 @@ hipError_t enqueue_levels(const ess_dims& d, int k, int n_tok, int nl,
                          d.ctx_len, d.mtp, n_tok, k, l);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    n = level_count(n, k);
+    n = level_count(n, k, l);
   }
   *fkey = key[(nl - 1) & 1];
   *fpos = pos[(nl - 1) & 1];
