@@ -121,7 +121,7 @@ ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
  * 1 <= k <= 16384.  Scores must not be NaN.  Rows of at most 32768 keys,
  * and any k > 4096, select in on-chip memory (ws and ws_bytes are not used;
  * NULL and 0 are fine).  Longer rows with k <= 4096 select in levels: each
- * 32768-key chunk's top-k is written to ws as candidates until one
+ * 16384-key chunk's top-k is written to ws as candidates until one
  * workgroup holds the row's list; ws must then hold ess_workspace_bytes(d)
  * bytes (enough for k = d->topk with n_tok <= d->mtp, and for
  * k = d->pool_slots with n_tok = 1), else ESS_ERR_NOMEM. */

@@ -108,12 +108,12 @@ def test_status_strings(L):
 
 def test_long_rows_need_a_topk_workspace(L):
     # Rows over 32768 keys with k <= 4096 select in levels whose candidate
-    # lists (two buffers of keys and positions, k per 32768-key chunk and
+    # lists (two buffers of keys and positions, k per 16384-key chunk and
     # row) sit after the attention's partials; the first fill's top-C
     # (n_tok = 1) is covered too.
     short = _d(topk=2048, pool_slots=4096)
     long_ = _d(ctx_len=100000, topk=2048, pool_slots=4096)
-    chunks = -(-100000 // 32768)
+    chunks = -(-100000 // 16384)
     step = 4 * (2 * 1) * chunks * 2048 * 4       # B=2 rows, k=2048
     fill = 4 * (2 * 1) * chunks * 4096 * 4       # k=C=4096
     assert ess.ess_workspace_bytes(long_) - ess.ess_workspace_bytes(short) == max(step, fill)
