@@ -23,10 +23,11 @@ __device__ __forceinline__ LruHeader* hdr_of(void* lru, size_t stride, int b) {
 }
 
 // Entry layout (64 bits, sorted ascending): position (28 bits) | token (2) |
-// row (14) | slot + 1 (20; 0 until known).  Sorting on the whole value
-// orders positions ascending and, for a repeated position, the smallest
-// token first; the slot field is filled in place once a position's slot
-// after the update is known, so every row's outputs come from LDS.
+// row (14) | slot + 1 (20; a hit's slot from the start, 0 for a miss until
+// it is paired).  Sorting on the whole value orders positions ascending
+// and, for a repeated position, the smallest token first (the entries of a
+// position carry the same slot); a miss's run head gets its slot in place
+// once paired, so every row's outputs come from LDS.
 __device__ __forceinline__ uint64_t make_entry(int pos, int j, int i) {
   return ((uint64_t)(uint32_t)pos << 36) | ((uint64_t)j << 34) | ((uint64_t)i << 20);
 }
@@ -101,20 +102,48 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
     row_dst[rows0 + i] = -1;
     sel_slot_post[rows0 + i] = -1;
   }
-  // 1. Entries of every way, then sort.  Out-of-range positions are dropped
-  // (they sort last and end the scan).
-  for (int e = tid; e < epow2; e += NT) {
-    uint64_t key = kNoEntry;
-    if (e < n_e) {
-      int j = 0;
-      while (e >= off[j + 1]) ++j;
-      const int i = e - off[j];
-      const int pos = PRESEL ? pre_pos[i] : sel_pos[rows0 + (size_t)j * k + i];
-      if (pos >= 0 && pos < L) key = make_entry(pos, j, i);
-      else h->err = 2;
+  // 1. Entries of every way, each with its position's slot before this
+  // update (the selection's own lookup, or cache_slots: every thread's reads
+  // are independent and in flight together), then sort.  Out-of-range
+  // positions are dropped (they sort last and end the scan).
+  bool bad = false;
+  constexpr int kU = 4;   // entries per thread whose reads are in flight together
+  for (int eb = tid; eb < epow2; eb += kU * NT) {
+    int pos[kU], row[kU], tok[kU], slot[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = eb + u * NT;
+      pos[u] = -1;
+      row[u] = 0;
+      tok[u] = 0;
+      if (e < n_e) {
+        int j = 0;
+        while (e >= off[j + 1]) ++j;
+        tok[u] = j;
+        row[u] = e - off[j];
+        pos[u] = PRESEL ? pre_pos[row[u]] : sel_pos[rows0 + (size_t)j * k + row[u]];
+      }
     }
-    ent[e] = key;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      slot[u] = pos[u] >= 0 && pos[u] < L ? (PRESEL ? pre_slot[row[u]] : cs[pos[u]]) : -1;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = eb + u * NT;
+      if (e >= epow2) break;
+      uint64_t key = kNoEntry;
+      if (e < n_e) {
+        if (pos[u] >= 0 && pos[u] < L) {
+          key = make_entry(pos[u], tok[u], row[u]);
+          if (slot[u] >= 0 && slot[u] < C) key = with_slot(key, slot[u]);
+        } else {
+          bad = true;
+        }
+      }
+      ent[e] = key;
+    }
   }
+  if (bad) h->err = 2;
   __syncthreads();
   // Sort by position: buckets of the position's top 11 bits (selections are
   // spread over the context, so buckets hold a few entries each), ordered
@@ -134,9 +163,8 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
     if (!done) block_sort_u64_n<NT, false>(smem_ent, epow2);
   }
 
-  // 2. Unique positions (first entry of each run) and their lookup; a hit's
-  // slot goes into its entry and its stamp moves to this update (its old
-  // ring entry dies).
+  // 2. Unique positions (first entry of each run): a hit's stamp moves to
+  // this update (its old ring entry dies).
   const int per = (epow2 + NT - 1) / NT;       // entries per thread, contiguous
   const int e0 = tid * per;
   auto head_of_run = [&](int e) {
@@ -148,14 +176,9 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
     if (e >= n_e || ent[e] == kNoEntry) break;
     if (head_of_run(e)) {
       ++n_u_mine;
-      // The selection's own lookup, when it came with one.
-      const int slot = PRESEL ? pre_slot[ent_row(ent[e])] : cs[ent_pos(ent[e])];
-      if (slot >= 0 && slot < C) {
-        stamp[slot] = epoch;
-        ent[e] = with_slot(ent[e], slot);
-      } else {
-        ++n_m_mine;
-      }
+      const int slot = ent_slot(ent[e]);
+      if (slot >= 0) stamp[slot] = epoch;
+      else ++n_m_mine;
     }
   }
   uint32_t n_u, n_miss;
