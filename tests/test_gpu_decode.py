@@ -58,3 +58,14 @@ def test_prefetch_mode_equals_inline():
                 assert np.array_equal(la[key], lb[key]), key
     for layer in range(3):
         compare_with_oracle(wl, b, layer=layer, requests=[1])
+
+
+def test_long_rows_fill_and_steps_select_in_levels():
+    # 50K positions with C = 3000 and k = 512: the first fill's top-C and every
+    # step's top-k run the multi-level selection (rows over 32768 keys, k and
+    # C <= 4096), for two requests with two MTP ways each.
+    wl = get_workload("tiny-4k").with_(
+        name="long-levels", batch=2, mtp=2, ctx_len=50000, idx_heads=16,
+        idx_dim=64, mla_heads=16, topk=512, pool_slots=3000, steps=3, rho=0.9)
+    recs = gpu_sequence(wl)
+    compare_with_oracle(wl, recs)

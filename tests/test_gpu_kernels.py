@@ -90,6 +90,7 @@ def _scores(kind, rng, shape):
     ("indexer_like", 1, 1, 1, 1 << 20, 4096, False),
     ("float", 1, 1, 1, 300000, 7, True),
     ("float", 1, 1, 1, 40000, 5000, False),       # k > 4096: one workgroup
+    ("float", 2, 3, 1, 40000, 100, True),         # n_tok < m on long rows
 ])
 def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
     rng = np.random.default_rng(zlib.crc32(f"{kind}-{L}-{k}".encode()))
