@@ -61,12 +61,23 @@ __device__ __forceinline__ v8i load_piece(const uint8_t* row, int g) {
 // its own buffers, so its own vmcnt wait is all the synchronisation needed.
 constexpr int kRows = kGroups * 16;   // rows per wave iteration
 
-__device__ __forceinline__ void load_lds16(const void* src, const void* lds_block) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
+// One wave instruction: lane l copies the 16 bytes at base + off to LDS at
+// lds_block + 16 l.  base is the same for the whole wave (scalar registers),
+// off a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t off,
+                                           const void* lds_block) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
       const __attribute__((address_space(3))) void*)lds_block);
+  // readfirstlane returns int: each half goes through uint32_t so that the
+  // low half is zero-extended (a sign-extended low half with bit 31 set would
+  // fill the upper half with ones).
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(b64 >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)b64);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   // An SALU write of M0 needs one wait state before an LDS-DMA load reads it.
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(base), "v"(src) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(off), "s"(sb) : "memory", "m0");
 }
 
 template <int DI>
@@ -113,17 +124,21 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 
   // Copy rows [p, p + kRows) into buffer `which`: LDS slot s of the buffer
   // holds row s / kSlots, piece s % kSlots (rows past L repeat row L - 1).
+  // Slot j * 64 + lane of every buffer is the same (row, piece) pair
+  // relative to p, so the pairs come from lane / kSlots and lane % kSlots
+  // once, and a load needs only its row clamp and byte offset.
+  const int q0 = lane / S::kSlots, r0 = lane - q0 * S::kSlots;
   auto stage = [&](int p, int which) {
     uint8_t* buf = buf0 + which * S::kBytes;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));   // recomputed per call, not kept live
 #pragma unroll
     for (int j = 0; j < S::kLoads; ++j) {
-      const int slot = j * 64 + ln;
-      const int r = slot / S::kSlots, pc = slot - r * S::kSlots;
+      const int t = r0 + (j * 64) % S::kSlots;           // < 2 kSlots
+      const int wrap = t >= S::kSlots ? 1 : 0;
+      const int r = (j * 64) / S::kSlots + q0 + wrap;    // row of the slot
+      const int pc = t - wrap * S::kSlots;               // piece of the slot
       const int row = min(p + r, L - 1);
-      const int off = pc < DI / 16 ? pc * 16 : 0;
-      load_lds16(kb + (size_t)row * DI + off, buf + j * 1024);
+      const uint32_t off = (uint32_t)row * DI + (pc < DI / 16 ? pc * 16 : 0);
+      load_lds16(kb, off, buf + j * 1024);
     }
   };
 
