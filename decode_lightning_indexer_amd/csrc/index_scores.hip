@@ -167,35 +167,44 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     float mine[MT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) mine[j] = 0.f;
+    // Group u's MFMAs are issued before group u - 1's epilogue reads its
+    // results, so the matrix unit works while the epilogue runs (two sets of
+    // accumulators, alternating).
+    v4f accs[2][NT];
+#define ESS_IDX_MFMA(U)                                                         \
+  _Pragma("unroll") for (int t = 0; t < NT; ++t)                                \
+    accs[(U) & 1][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(       \
+        qa[t], kv[U], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    // ReLU as a signed-integer max of the bits: a finite float is positive
+    // exactly when its bits are, and -0 maps to +0 (one instruction; fmaxf
+    // also quiets NaNs, which cannot occur here).
+#define ESS_IDX_EPI(U)                                                          \
+  {                                                                             \
+    float part[MT];                                                             \
+    _Pragma("unroll") for (int j = 0; j < MT; ++j) part[j] = 0.f;               \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t) {                            \
+      float s = 0.f;                                                            \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r)                             \
+        s += wv[t][r] * __int_as_float(max(__float_as_int(accs[(U) & 1][t][r]), 0)); \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j)                            \
+        if (t / kTilesPerTok == j) part[j] += s;                                \
+    }                                                                           \
+    _Pragma("unroll") for (int j = 0; j < MT; ++j) {                            \
+      float v = part[j];                                                        \
+      v += __shfl_xor(v, 16);                                                   \
+      v += __shfl_xor(v, 32);                                                   \
+      if (g == (U)) mine[j] = v;   /* lane group U stores group U */            \
+    }                                                                           \
+  }
+    ESS_IDX_MFMA(0)
 #pragma unroll
-    for (int u = 0; u < kGroups; ++u) {
-      float part[MT];
-#pragma unroll
-      for (int j = 0; j < MT; ++j) part[j] = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            qa[t], kv[u], acc, 0, 0, 0, 0, 0, 0);
-        float s = 0.f;
-#pragma unroll
-        // ReLU as a signed-integer max of the bits: a finite float is
-        // positive exactly when its bits are, and -0 maps to +0 (one
-        // instruction; fmaxf also quiets NaNs, which cannot occur here).
-        for (int r = 0; r < 4; ++r)
-          s += wv[t][r] * __int_as_float(max(__float_as_int(acc[r]), 0));
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-          if (t / kTilesPerTok == j) part[j] += s;
-      }
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        float v = part[j];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (g == u) mine[j] = v;   // lane group u stores group u
-      }
+    for (int u = 1; u < kGroups; ++u) {
+      ESS_IDX_MFMA(u)
+      ESS_IDX_EPI(u - 1)
     }
+    ESS_IDX_EPI(kGroups - 1)
+#undef ESS_IDX_EPI
+#undef ESS_IDX_MFMA
     const int pos = p0 + g * 16 + c;
     if (pos < span1) {
 #pragma unroll
