@@ -182,13 +182,11 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   {                                                                             \
     float part[MT];                                                             \
     _Pragma("unroll") for (int j = 0; j < MT; ++j) part[j] = 0.f;               \
-    _Pragma("unroll") for (int t = 0; t < NT; ++t) {                            \
-      float s = 0.f;                                                            \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t)                              \
       _Pragma("unroll") for (int r = 0; r < 4; ++r)                             \
-        s += wv[t][r] * __int_as_float(max(__float_as_int(accs[(U) & 1][t][r]), 0)); \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j)                            \
-        if (t / kTilesPerTok == j) part[j] += s;                                \
-    }                                                                           \
+        part[t / kTilesPerTok] = fmaf(                                          \
+            wv[t][r], __int_as_float(max(__float_as_int(accs[(U) & 1][t][r]), 0)), \
+            part[t / kTilesPerTok]);                                            \
     _Pragma("unroll") for (int j = 0; j < MT; ++j) {                            \
       float v = part[j];                                                        \
       v += __shfl_xor(v, 16);                                                   \
