@@ -293,20 +293,30 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    // The running maximum moves only when some head of the wave sees a tile
+    // maximum more than 2^8 above it (log2 domain); otherwise every
+    // p = 2^(z - m_run) stays at most 256 and the accumulators keep their
+    // reference, so the 128 rescale multiplies are skipped (the sum and the
+    // accumulators always share one reference, so the result is the same).
+    if (__ballot(mx > m_run + 8.f) != 0ull) {   // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = exp2f(z[e] - m_new);
+      const float p = exp2f(z[e] - m_run);
       psum += p;
       pb[e] = (__bf16)p;
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
 
     // O^T += V^T P^T over the tile; V^T read transposed from the tile rows:
     // tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, column nt*16 + c.
@@ -323,8 +333,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
         }
         const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
-        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt] * alpha,
-                                                           0, 0, 0);
+        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt], 0, 0, 0);
         lo = nlo;
         hi = nhi;
       }
