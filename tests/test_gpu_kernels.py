@@ -308,3 +308,35 @@ def test_miss_copy():
         untouched = np.setdiff1d(np.arange(C), ms[b, :nm[b]])
         assert not gp[b, untouched].any()
     host.free()
+
+
+def test_topk_random_shapes_around_the_level_boundary():
+    # Seeded shapes on both sides of the 32768-key register-resident row and
+    # the 16384-key level chunk: ragged visibility (k >= n_vis inside a
+    # level), k not a multiple of 4, one or several tokens, every score kind.
+    rng = np.random.default_rng(20261202)
+    kinds = ["int_ties", "indexer_like", "float", "wide", "zeros"]
+    for case in range(14):
+        kind = kinds[case % len(kinds)]
+        L = int(rng.choice([16383, 16385, 32767, 32768, 32769, 49153,
+                            int(rng.integers(33000, 140000))]))
+        B, m = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        n_tok = int(rng.integers(1, m + 1))
+        k = int(rng.choice([1, 3, 257, 1024, 2047, 4096]))
+        s = _scores(kind, rng, (B, m, L))
+        n_vis = rng.integers(1, L + 1, (B, m)).astype(np.int32)
+        cs = np.where(rng.random((B, L)) < 0.3, rng.integers(0, 16384, (B, L)), -1).astype(np.int32)
+        d = dims(batch=B, mtp=m, ctx_len=L, topk=k, pool_slots=16384)
+        sp = torch.empty((B, n_tok, k), dtype=torch.int32, device="cuda")
+        ss = torch.empty_like(sp)
+        ns = torch.empty((B, n_tok), dtype=torch.int32, device="cuda")
+        wsb = ess.ess_workspace_bytes(d)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        ess.ess_topk_lookup(d, k, n_tok, t(s), t(n_vis), t(cs), sp, ss, ns, ws, wsb)
+        sync()
+        for b in range(B):
+            rp, rs, rn = topk_lookup(s[b, :n_tok].astype(np.float64), n_vis[b, :n_tok], k, cs[b])
+            where = (case, kind, L, B, m, n_tok, k, b)
+            assert np.array_equal(h(ns)[b], rn), where
+            assert np.array_equal(h(sp)[b], rp), where
+            assert np.array_equal(h(ss)[b], rs), where
