@@ -300,30 +300,36 @@ def extra_measurements(args):
     return out
 
 
-def indexer_flushed(d, lb, q_idx, n_vis, stream, reps=10):
-    """Indexer kernel time alone: back to back, and each call after reading
-    512 MB of other data (evicts the 256 MB last-level cache, which the
-    67 MB index cache would otherwise sit in, without leaving dirty lines to
-    write back)."""
+def indexer_alone(d, lb, q_idx, n_vis, stream, reps=16):
+    """Indexer kernel time alone, launches back to back with events only
+    around the whole run: over copies of the index cache taken in turn,
+    enough of them (>= 512 MB) that each launch finds its keys evicted from
+    the 256 MB last-level cache (the 16-layer shape's situation: every
+    layer's cache is read once per step), and over the one cache again and
+    again (which then stays in the last-level cache)."""
     import torch
     from decode_lightning_indexer_amd import ess
-    scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 2)]
+    key_bytes = lb.k_idx.numel()
+    n_copies = max(2, -(-(512 << 20) // key_bytes))
+    copies = [lb.k_idx.clone() for _ in range(n_copies)]
+    reps = max(reps, 2 * n_copies)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(n_copies):          # warm-up: one pass over the copies
+        ess.ess_index_scores(d, q_idx, lb.w_idx, copies[i], n_vis, lb.scores, stream)
+    ev[0].record(stream)
     for i in range(reps):
-        scratch.sum()
-        ev[2 * i].record(stream)
-        ess.ess_index_scores(d, q_idx, lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
-        ev[2 * i + 1].record(stream)
-    torch.cuda.synchronize()
-    flushed = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
-    ev[-2].record(stream)
+        ess.ess_index_scores(d, q_idx, lb.w_idx, copies[i % n_copies], n_vis, lb.scores, stream)
+    ev[1].record(stream)
+    ev[2].record(stream)
     for _ in range(reps):
         ess.ess_index_scores(d, q_idx, lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
-    ev[-1].record(stream)
+    ev[3].record(stream)
     torch.cuda.synchronize()
-    warm = ev[-2].elapsed_time(ev[-1]) / reps
-    del scratch
-    return flushed * 1e-3, warm * 1e-3
+    cold = ev[0].elapsed_time(ev[1]) / reps
+    warm = ev[2].elapsed_time(ev[3]) / reps
+    del copies
+    torch.cuda.empty_cache()
+    return cold * 1e-3, warm * 1e-3, n_copies
 
 
 def main():
@@ -507,7 +513,7 @@ def main():
     torch.cuda.synchronize()
     host_gbps = B * C * 1152 / (ev_h[0].elapsed_time(ev_h[1]) * 1e-3) / 1e9
 
-    t_idx_flushed, t_idx_warm = indexer_flushed(d, lb, q_idx[W + K - 1], n_vis, stream)
+    t_idx_cold, t_idx_warm, n_idx_copies = indexer_alone(d, lb, q_idx[W + K - 1], n_vis, stream)
 
     # Algorithmic bytes / flops per launch.
     idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
@@ -522,12 +528,18 @@ def main():
     t_attn_st = float(t_attn)
     attn_kernels = "sparse_mla_kernel+mla_combine_kernel"
     roofs = {
+        # achieved: launches back to back, each reading its keys from HBM
+        # (a different copy of the index cache each time); beside it the
+        # same launches over one cache (last-level-cache resident) and the
+        # event-timed stage inside the step (with its dispatch gap).
         "index_scores": {"kernel": "index_scores_kernel", "bound": "hbm",
-                         "achieved": idx_bytes / (stage_us[0] * 1e3),
+                         "achieved": idx_bytes / t_idx_cold / 1e9,
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "bytes_per_launch": idx_bytes,
-                         "alone_cache_flushed_gbps": idx_bytes / t_idx_flushed / 1e9,
-                         "alone_back_to_back_gbps": idx_bytes / t_idx_warm / 1e9},
+                         "us_from_hbm": t_idx_cold * 1e6,
+                         "index_cache_copies": n_idx_copies,
+                         "same_cache_back_to_back_gbps": idx_bytes / t_idx_warm / 1e9,
+                         "in_step_event_timed_gbps": idx_bytes / (stage_us[0] * 1e3)},
     }
     attn_view = {"attention_us": t_attn_st,
                  "hbm_gbps": attn_bytes / (t_attn_st * 1e3),
@@ -569,7 +581,8 @@ def main():
         "steps_per_s": K / wall_plain,
         "steps_per_s_staged": K / wall,
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
-        "indexer_gbps": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
+        "indexer_gbps": idx_bytes / t_idx_cold / 1e9,
+        "indexer_gbps_in_step": idx_bytes / (stage_us[0] * 1e-6) / 1e9,
         "attention_tflops": attn_view["tflops"],
         "misses_per_step": n_miss_tot / K,
         "miss_rate": n_miss_tot / (K * B * m * k),

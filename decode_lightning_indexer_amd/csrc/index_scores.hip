@@ -56,9 +56,13 @@ __device__ __forceinline__ v8i load_piece(const uint8_t* row, int g) {
 // contiguous: each wave owns two buffers of 64 rows and copies its next 64
 // rows (DI * 64 contiguous bytes) with gfx950's 16-byte global-to-LDS load,
 // one 1 KB block per wave instruction, while it computes the current 64.
-// Rows sit at a stride of DI + 16 bytes in LDS (the pad slot repeats a valid
-// 16 bytes), which makes the operand reads conflict-free.  A wave reads only
-// its own buffers, so its own vmcnt wait is all the synchronisation needed.
+// Rows are stored unpadded, with the 16-byte pieces of each row permuted
+// (piece p of buffer row r at slot p ^ f(r), f(r) = (r / (256 / DI)) mod
+// (DI / 16)): the 16 rows that the 16 lanes of a lane group read for one
+// operand then fall in 16 different 16-byte bank groups, so the operand
+// reads are conflict-free, and every load still reads one contiguous 1 KB
+// block (the permutation stays within rows).  A wave reads only its own
+// buffers, so its own vmcnt wait is all the synchronisation needed.
 constexpr int kRows = kGroups * 16;   // rows per wave iteration
 
 // One wave instruction: lane l copies the 16 bytes at base + off to LDS at
@@ -82,9 +86,14 @@ __device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t off,
 
 template <int DI>
 struct Stage {
-  static constexpr int kSlots = DI / 16 + 1;           // 16-byte slots per row
-  static constexpr int kLoads = kSlots;                // wave loads per 64 rows
-  static constexpr int kBytes = kRows * kSlots * 16;   // one buffer
+  static constexpr int kSlots = DI / 16;               // 16-byte pieces per row
+  static constexpr int kPerBank = 256 / DI;            // rows per 256 bytes
+  static constexpr int kLoads = kRows * kSlots / 64;   // wave loads per 64 rows
+  static constexpr int kBytes = kRows * DI;            // one buffer
+  // Slot of piece p of buffer row r.
+  static __device__ __forceinline__ int slot(int r, int p) {
+    return p ^ ((r / kPerBank) % kSlots);
+  }
 };
 
 // NT: 16-row tiles of the [m * H_I][DI] query matrix; MT: query tokens m.
@@ -122,22 +131,19 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   const int span0 = blockIdx.x * kSpan;
   const int span1 = min(L, span0 + kSpan);
 
-  // Copy rows [p, p + kRows) into buffer `which`: LDS slot s of the buffer
-  // holds row s / kSlots, piece s % kSlots (rows past L repeat row L - 1).
-  // Slot j * 64 + lane of every buffer is the same (row, piece) pair
-  // relative to p, so the pairs come from lane / kSlots and lane % kSlots
-  // once, and a load needs only its row clamp and byte offset.
-  const int q0 = lane / S::kSlots, r0 = lane - q0 * S::kSlots;
+  // Copy rows [p, p + kRows) into buffer `which`: load j writes slots
+  // 64 j .. 64 j + 63, i.e. rows 64 j / kSlots + lane / kSlots, slot
+  // lane % kSlots, which holds piece slot ^ f(row) of the row (rows past L
+  // repeat row L - 1).
+  const int lr = lane / S::kSlots, ls = lane % S::kSlots;
   auto stage = [&](int p, int which) {
     uint8_t* buf = buf0 + which * S::kBytes;
 #pragma unroll
     for (int j = 0; j < S::kLoads; ++j) {
-      const int t = r0 + (j * 64) % S::kSlots;           // < 2 kSlots
-      const int wrap = t >= S::kSlots ? 1 : 0;
-      const int r = (j * 64) / S::kSlots + q0 + wrap;    // row of the slot
-      const int pc = t - wrap * S::kSlots;               // piece of the slot
+      const int r = j * (64 / S::kSlots) + lr;           // row in the buffer
+      const int pc = S::slot(r, ls);                     // piece in that slot
       const int row = min(p + r, L - 1);
-      const uint32_t off = (uint32_t)row * DI + (pc < DI / 16 ? pc * 16 : 0);
+      const uint32_t off = (uint32_t)row * DI + pc * 16;
       load_lds16(kb, off, buf + j * 1024);
     }
   };
@@ -155,12 +161,15 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
     const uint8_t* rows = buf0 + which * S::kBytes;
+    // Lane (g, c) reads pieces g and g + 4 of rows 16 u + c; f(16 u + c)
+    // does not depend on u.
     v8i kv[kGroups];
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
-      const v4u* pr = reinterpret_cast<const v4u*>(rows + (u * 16 + c) * S::kSlots * 16 + g * 16);
-      const v4u x = pr[0];
-      const v4u y = DI == 128 ? pr[4] : v4u{0u, 0u, 0u, 0u};
+      const uint8_t* pr = rows + (u * 16 + c) * DI;
+      const v4u x = *reinterpret_cast<const v4u*>(pr + S::slot(c, g) * 16);
+      const v4u y = DI == 128 ? *reinterpret_cast<const v4u*>(pr + S::slot(c, g + 4) * 16)
+                              : v4u{0u, 0u, 0u, 0u};
       kv[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
                   (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     }
