@@ -128,15 +128,25 @@ def recorded_traffic(kernel):
 
 
 def trace_summary(path, steps, warmup):
-    """Per-kernel mean duration (and mean counter value, for a counter run)
-    over the timed steps: the window from the first timed step's
-    index_scores_kernel to the next one after the timed steps (dispatch 0 is
-    the pool's first fill)."""
+    """Per-kernel mean duration (and mean value of each counter, for a
+    counter run) over the timed steps: the window from the first timed
+    step's index_scores_kernel to the next one after the timed steps
+    (dispatch 0 is the pool's first fill).  A counter file has one row per
+    (dispatch, counter)."""
     import csv
+    import re
     rows = list(csv.DictReader(open(path)))
-    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # One record per dispatch: name, start, end and its counters.
+    disp = {}
+    for r in rows:
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Start_Timestamp"])
+        d = disp.setdefault(key, {"name": r["Kernel_Name"], "t0": int(r["Start_Timestamp"]),
+                                  "t1": int(r["End_Timestamp"]), "ctr": {}})
+        if "Counter_Name" in r:
+            d["ctr"][r["Counter_Name"]] = d["ctr"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ds = sorted(disp.values(), key=lambda d: d["t0"])
+
     def short(n):
-        import re
         m = re.match(r"_ZN3ess12_GLOBAL__N_1(\d+)", n)   # names left mangled
         if m:
             ln = int(m.group(1))
@@ -145,31 +155,30 @@ def trace_summary(path, steps, warmup):
             return base + (f"<{t.group(1)}>" if t else "")
         n = n.replace("ess::(anonymous namespace)::", "").replace("void ", "")
         return n.split("(")[0]
-    starts = [int(r["Start_Timestamp"]) for r in rows
-              if short(r["Kernel_Name"]).startswith("index_scores_kernel")]
+    starts = [d["t0"] for d in ds if short(d["name"]).startswith("index_scores_kernel")]
     windowed = len(starts) > warmup + steps + 1
     if windowed:
         lo, hi = starts[warmup + 1], starts[warmup + steps + 1]
-        rows = [r for r in rows if lo <= int(r["Start_Timestamp"]) < hi]
+        ds = [d for d in ds if lo <= d["t0"] < hi]
+    ctrs = sorted({c for d in ds for c in d["ctr"]})
     agg = {}
-    for r in rows:
-        a = agg.setdefault(short(r["Kernel_Name"]), {"n": 0, "us": 0.0, "ctr": 0.0})
+    for d in ds:
+        a = agg.setdefault(short(d["name"]), {"n": 0, "us": 0.0, "ctr": {}})
         a["n"] += 1
-        a["us"] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if "Counter_Value" in r:
-            a["ctr"] += float(r["Counter_Value"])
-    ctr = rows[0].get("Counter_Name") if rows else None
+        a["us"] += (d["t1"] - d["t0"]) / 1e3
+        for c, v in d["ctr"].items():
+            a["ctr"][c] = a["ctr"].get(c, 0.0) + v
     print(f"# {'timed steps' if windowed else 'all dispatches'}: {path}")
     head = f"{'kernel':48s} {'dispatches':>10s} {'mean_us':>9s}"
-    if ctr:
-        head += f" {('mean_' + ctr + '_KiB'):>22s}"
+    for c in ctrs:
+        head += f" {c:>26s}"
     print(head)
     for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["us"]):
         if windowed and a["n"] < steps:
             continue                  # not a per-step kernel
         line = f"{name[:48]:48s} {a['n']:10d} {a['us'] / a['n']:9.2f}"
-        if ctr:
-            line += f" {a['ctr'] / a['n']:22.1f}"
+        for c in ctrs:
+            line += f" {a['ctr'].get(c, 0.0) / a['n']:26.1f}"
         print(line)
     for name in KERNEL_SOURCES:
         print(f"# source {name} {source_digest(name)}")
