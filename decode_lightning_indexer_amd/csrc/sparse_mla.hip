@@ -32,7 +32,7 @@
 // split between two sub-groups of waves that take alternate 32-row tiles
 // (each sub-group holds the same heads).  Tiles go from memory straight into
 // LDS (gfx950's 16-byte global-to-LDS load, one 1 KB block per wave
-// instruction), row-major with a 16-byte pad per row; each sub-group has
+// instruction), row-major with a 32-byte pad per row; each sub-group has
 // two tile buffers, so one tile is in flight while the other is computed,
 // with one workgroup barrier per tile and no registers held for staging.
 // Padding and unusable rows load a zero row.  At the end the second
@@ -69,7 +69,7 @@ constexpr int kTile = 32;                       // tokens per LDS tile
 // banks (at 73 slots rows 0 and 7 overlap; counters showed ~43 % of the
 // kernel's LDS cycles stalled on bank conflicts, now none).
 constexpr int kRowSlots = kLat / 8 + 2;         // 16-byte slots per row (72 + 2 pad)
-constexpr int kKStride = kRowSlots * 8;         // bf16 per row-major row (1168 B)
+constexpr int kKStride = kRowSlots * 8;         // bf16 per row-major row (1184 B)
 constexpr int kChunks16 = kLat / 8;             // 16-byte pieces per latent row (72)
 constexpr int kTileLoads = (kTile * kRowSlots + 63) / 64;   // wave loads per tile (37)
 constexpr int kTileSlots = kTileLoads * 64;     // slots per tile buffer (2368)
