@@ -14,10 +14,12 @@ Plain, slow and written to be checked by eye against the pages:
                 and the five-step miss handling;
   * attention - dense float64 softmax over the selected latents;
   * decode    - a whole decode sequence (fill, then T steps) per request;
-  * footprint - the pages' per-token byte arithmetic.
+  * footprint - the pages' per-token byte arithmetic;
+  * policies  - offline replay of the pool under the LRU, Random and Score
+                eviction policies (miss counts per step).
 
 Every function is pinned by tests under tests/ against values the pages
 print, closed forms, special cases and brute force.  Parts without such a pin
 are marked "parity unpinned" in their docstring.
 """
-from . import formats, indexer, topk, pool, attention, decode, footprint  # noqa: F401
+from . import formats, indexer, topk, pool, attention, decode, footprint, policies  # noqa: F401
