@@ -43,13 +43,20 @@ def hipcc() -> str:
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                  if f.endswith(".hip"))
+                  if f.endswith(".hip") or f.endswith(".cpp"))
+
+
+# Host-only C++ (no device code): compiled as plain C++ by the same driver.
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+              "-x", "c++"]
 
 
 def _compile(src, cc, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     extra = EXTRA.get(os.path.basename(src), [])
-    cmd = [cc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    flags = HOST_FLAGS if src.endswith(".cpp") else FLAGS
+    cmd = [cc, *flags, *extra, "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

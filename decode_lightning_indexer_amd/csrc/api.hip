@@ -8,6 +8,7 @@
 #include <string>
 #include <vector>
 
+#include "ess_host.h"
 #include "ess_internal.h"
 
 namespace {
@@ -23,6 +24,20 @@ ess_status fail(ess_status s, const char* fmt, ...) {
   g_err = buf;
   return s;
 }
+
+}  // namespace
+
+ess_status ess::host_fail(ess_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+namespace {
 
 ess_status hip_fail(hipError_t e, const char* what) {
   return fail(ESS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

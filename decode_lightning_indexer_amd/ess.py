@@ -21,11 +21,16 @@ ESS_MODE_FILL = 0
 ESS_MODE_INLINE = 1
 ESS_MODE_PREFETCH = 2
 
+ESS_EVICT_LRU = 0
+ESS_EVICT_RANDOM = 1
+ESS_EVICT_SCORE = 2
+
 EXPORTED = (
     "ess_workspace_bytes", "ess_lru_state_bytes", "ess_pool_reset",
     "ess_index_scores", "ess_topk_lookup", "ess_pool_update",
     "ess_sparse_mla_decode", "ess_miss_copy", "ess_decode_step",
-    "ess_host_alloc", "ess_host_free", "ess_status_string", "ess_last_error",
+    "ess_host_alloc", "ess_host_free", "ess_replay_evictions",
+    "ess_status_string", "ess_last_error",
 )
 
 
@@ -86,6 +91,8 @@ def lib():
                                      _I, _P, _P]),
             "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
             "ess_host_free": (_I, [_P]),
+            "ess_replay_evictions": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                          ctypes.c_uint64, _I, _P, _P]),
             "ess_status_string": (ctypes.c_char_p, [_I]),
             "ess_last_error": (ctypes.c_char_p, []),
         }
@@ -199,3 +206,24 @@ def ess_host_alloc(nbytes: int):
 
 def ess_host_free(host_ptr: int):
     _check("ess_host_free", lib().ess_host_free(host_ptr))
+
+
+def ess_replay_evictions(policy, pool_slots, scores, sel_pos, n_sel, seed=0,
+                         request=0):
+    """Host replay of one request's steps under an eviction policy.
+    scores float32 [T][m][L], sel_pos int32 [T][m][k], n_sel int32 [T][m]
+    (NumPy arrays in host memory).  Returns (n_miss, n_evict), int32 [T]."""
+    import numpy as np
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    sel_pos = np.ascontiguousarray(sel_pos, dtype=np.int32)
+    n_sel = np.ascontiguousarray(n_sel, dtype=np.int32)
+    T, m, L = scores.shape
+    if sel_pos.shape[:2] != (T, m) or n_sel.shape != (T, m):
+        raise ValueError("scores, sel_pos and n_sel disagree on steps or ways")
+    n_miss = np.zeros(T, np.int32)
+    n_evict = np.zeros(T, np.int32)
+    _check("ess_replay_evictions", lib().ess_replay_evictions(
+        policy, L, pool_slots, T, m, sel_pos.shape[2], scores.ctypes.data,
+        sel_pos.ctypes.data, n_sel.ctypes.data, seed, request,
+        n_miss.ctypes.data, n_evict.ctypes.data))
+    return n_miss, n_evict

@@ -260,6 +260,47 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
 ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view);
 ess_status ess_host_free(void* host_ptr);
 
+/* Eviction policies for ess_replay_evictions. */
+enum {
+  ESS_EVICT_LRU = 0,     /* least recently used: the pool's own policy      */
+  ESS_EVICT_RANDOM = 1,  /* uniformly random (SplitMix64 keys)               */
+  ESS_EVICT_SCORE = 2    /* lowest index score of the step                   */
+};
+
+/* Offline replay of one request's decode steps through a hot pool of
+ * pool_slots slots under an eviction policy (FlashOffloading analysis,
+ * decode ablation, first group, and Fig. 8: the recorded per-step top-k
+ * index sets replayed with only the eviction policy changed: Random, LRU,
+ * Score).  A host routine: every pointer is host memory, nothing touches
+ * the GPU.
+ *   scores  [steps][mtp][ctx_len] float: the index scores of every step and
+ *           way, -inf past a way's visible length;
+ *   sel_pos [steps][mtp][topk] int32, rank order; n_sel [steps][mtp];
+ *   n_miss, n_evict [steps] int32 outputs (n_evict may be NULL).
+ * The pool starts from the decode's first fill (the top-min(C, visible)
+ * positions of way 0 at step 0, score descending, position ascending).
+ * Per step: misses = the union of the ways' selections minus the
+ * residents; free slots serve misses first; each remaining miss evicts one
+ * resident outside the union, the smallest by the policy's order:
+ *   LRU    (last step whose union held it, position) - fill counts as the
+ *          step before step 0, so this is ess_pool_update's own order;
+ *   RANDOM (key, position), key = output number
+ *          (request << 48 | step << 32 | position) + 1 of SplitMix64
+ *          (Steele, Lea and Flood, OOPSLA 2014) seeded with `seed`;
+ *   SCORE  (the largest of the position's scores over the step's ways,
+ *          position).
+ * The pages' fourth policy (a score threshold plus a chunk scan) is named
+ * there without its rule and is not offered.  ESS_ERR_CAPACITY if a step's
+ * union exceeds pool_slots, ESS_ERR_INVALID for bad sizes, NULL arrays or a
+ * selected position outside [0, ctx_len); steps and request < 65536. */
+ess_status ess_replay_evictions(int32_t policy, int32_t ctx_len,
+                                int32_t pool_slots, int32_t steps,
+                                int32_t mtp, int32_t topk,
+                                const float* scores, const int32_t* sel_pos,
+                                const int32_t* n_sel, uint64_t seed,
+                                int32_t request, int32_t* n_miss,
+                                int32_t* n_evict);
+
 const char* ess_status_string(ess_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char* ess_last_error(void);
