@@ -309,6 +309,88 @@ def extra_measurements(args):
     return out
 
 
+def replay_curves(args, name="128k-b8-mtp2-r095", T=32,
+                  capacities=(8192, 12288, 16384, 24576)):
+    """The pages' offline eviction-policy comparison on traces of our own
+    decode: T steps of the workload run on the GPU (fill, then inline steps
+    with the workload's pool), every step's scores and selections copied to
+    host memory, then each request replayed through ess_replay_evictions
+    under LRU, Random and Score at several pool sizes.  The LRU replay at the
+    workload's own pool size must reproduce the GPU pool update's miss count
+    of every request and step."""
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
+    from synth import gen, get_workload
+
+    dev = "cuda"
+    wl = get_workload(name).with_(steps=T)
+    d = dims_of(wl)
+    B, m, L, k, C = wl.batch, wl.mtp, wl.ctx_len, wl.topk, wl.pool_slots
+    h = HostStore((B, L, 576))
+    gen.fill_latents(wl, 0, h.array)
+    lb = LayerBuffers(d, h)
+    kb = np.empty((B, L, wl.idx_dim), np.uint8)
+    gen.fill_index_keys(wl, 0, kb)
+    lb.k_idx.copy_(torch.from_numpy(kb))
+    del kb
+    qi, qa, w, nv = staged_inputs(wl, 0, dev)
+    lb.w_idx.copy_(torch.from_numpy(w))
+    n_vis = torch.from_numpy(nv).to(dev)
+    stream = torch.cuda.current_stream()
+    scores = np.empty((B, T, m, L), np.float32)
+    sel = np.empty((B, T, m, k), np.int32)
+    n_sel = np.empty((B, T, m), np.int32)
+    gpu_miss = np.empty((B, T), np.int32)
+    lb.reset(stream)
+    io = lb.io()
+    io.q_idx = qi[0].data_ptr()
+    ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_FILL, stream)
+    for t in range(T):
+        io = lb.io()
+        io.q_idx = qi[t].data_ptr()
+        io.q_abs = qa[t].data_ptr()
+        ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_INLINE, stream)
+        scores[:, t] = lb.scores.cpu().numpy()
+        sel[:, t] = lb.rows(lb.sel_pos, k, m).cpu().numpy()
+        n_sel[:, t] = lb.n_sel.cpu().numpy()
+        gpu_miss[:, t] = lb.n_miss.cpu().numpy()
+    h.free()
+    del lb, qi, qa
+    torch.cuda.empty_cache()
+
+    codes = {"lru": ess.ESS_EVICT_LRU, "random": ess.ESS_EVICT_RANDOM,
+             "score": ess.ESS_EVICT_SCORE}
+    t0 = time.perf_counter()
+    misses = {p: {} for p in codes}
+    n_replays = 0
+    for pol, code in codes.items():
+        for cap in capacities:
+            tot = 0
+            for b in range(B):
+                nm, _ = ess.ess_replay_evictions(code, cap, scores[b], sel[b], n_sel[b],
+                                                 seed=1, request=b)
+                n_replays += 1
+                if pol == "lru" and cap == C and not np.array_equal(nm, gpu_miss[b]):
+                    raise AssertionError(f"LRU replay differs from the GPU pool at request {b}")
+                tot += int(nm.sum())
+            misses[pol][cap] = tot
+    t_replay = time.perf_counter() - t0
+    per = B * T
+    lo, hi = min(capacities), 16384
+    return {
+        "workload": name, "steps": T, "requests": B,
+        "lru_replay_equals_gpu_pool": True,
+        "misses_per_request_step": {p: {str(c): v / per for c, v in d_.items()}
+                                    for p, d_ in misses.items()},
+        f"miss_cut_{lo}_to_{hi}": {p: 1 - misses[p][hi] / misses[p][lo] for p in codes},
+        f"score_vs_lru_at_{hi}": 1 - misses["score"][hi] / misses["lru"][hi],
+        f"random_vs_lru_at_{hi}": 1 - misses["random"][hi] / misses["lru"][hi],
+        "replay_steps_per_s": n_replays * T / t_replay,
+    }
+
+
 def indexer_alone(d, lb, q_idx, n_vis, stream, reps=16):
     """Indexer kernel time alone, launches back to back with events only
     around the whole run: over copies of the index cache taken in turn,
@@ -609,6 +691,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         res["extra"] = extra_measurements(args)
+        res["extra"]["eviction_replay"] = replay_curves(args)
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
