@@ -69,3 +69,48 @@ def test_long_rows_fill_and_steps_select_in_levels():
         idx_dim=64, mla_heads=16, topk=512, pool_slots=3000, steps=3, rho=0.9)
     recs = gpu_sequence(wl)
     compare_with_oracle(wl, recs)
+
+
+def test_lru_replay_reproduces_the_gpu_pool():
+    # The host replay of the recorded steps (ess_replay_evictions, LRU, the
+    # workload's pool size) gives the GPU pool update's miss count at every
+    # request and step; Score and Random replays of the same trace stay
+    # within the union of each step.
+    from decode_lightning_indexer_amd.runner import DecodeRunner
+    from decode_lightning_indexer_amd.session import HostStore, dims_of
+    from synth.device import LayerInputs
+    wl = get_workload("tiny-4k").with_(
+        name="replay", batch=3, mtp=2, ctx_len=6000, idx_heads=32, idx_dim=128,
+        mla_heads=16, topk=256, pool_slots=700, steps=8, rho=0.85)
+    B, m, k, T = wl.batch, wl.mtp, wl.topk, wl.steps
+    host = HostStore((B, wl.ctx_len, 576))
+    ins = LayerInputs(wl, 0)
+    run = DecodeRunner(dims_of(wl), [host])
+    lb = run.layers[0]
+    ins.upload_static(lb, host.array)
+    run.set_n_vis(ins.n_vis)
+    run.reset()
+    ins.upload_step(lb, 0)
+    run.fill()
+    scores = np.empty((B, T, m, wl.ctx_len), np.float32)
+    sel = np.empty((B, T, m, k), np.int32)
+    n_sel = np.empty((B, T, m), np.int32)
+    gpu = np.empty((B, T), np.int32)
+    for t in range(T):
+        ins.upload_step(lb, t)
+        run.step(ess.ESS_MODE_INLINE)
+        torch.cuda.synchronize()
+        scores[:, t] = lb.scores.cpu().numpy()
+        sel[:, t] = lb.rows(lb.sel_pos, k, m).cpu().numpy()
+        n_sel[:, t] = lb.n_sel.cpu().numpy()
+        gpu[:, t] = lb.n_miss.cpu().numpy()
+    host.free()
+    assert gpu[:, 1:].sum() > 0
+    for b in range(B):
+        nm, _ = ess.ess_replay_evictions(ess.ESS_EVICT_LRU, wl.pool_slots,
+                                         scores[b], sel[b], n_sel[b], request=b)
+        assert np.array_equal(nm, gpu[b]), b
+        for pol in (ess.ESS_EVICT_RANDOM, ess.ESS_EVICT_SCORE):
+            nm2, ev2 = ess.ess_replay_evictions(pol, wl.pool_slots, scores[b],
+                                                sel[b], n_sel[b], request=b)
+            assert np.all(ev2 <= nm2) and np.all(nm2 <= m * k)
