@@ -16,10 +16,12 @@ Plain, slow and written to be checked by eye against the pages:
   * decode    - a whole decode sequence (fill, then T steps) per request;
   * footprint - the pages' per-token byte arithmetic;
   * policies  - offline replay of the pool under the LRU, Random and Score
-                eviction policies (miss counts per step).
+                eviction policies (miss counts per step);
+  * prefill   - the four-buffer layer pipeline of the prefill: buffer
+                bindings, the data it leaves behind, the exposed-time bound.
 
 Every function is pinned by tests under tests/ against values the pages
 print, closed forms, special cases and brute force.  Parts without such a pin
 are marked "parity unpinned" in their docstring.
 """
-from . import formats, indexer, topk, pool, attention, decode, footprint, policies  # noqa: F401
+from . import formats, indexer, topk, pool, attention, decode, footprint, policies, prefill  # noqa: F401
