@@ -391,6 +391,104 @@ def replay_curves(args, name="128k-b8-mtp2-r095", T=32,
     }
 
 
+def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.0)):
+    """The four-buffer prefill pipeline (ess_prefill_layers) over NL layers
+    of n_hist history rows + n_new new rows of 576 bf16: per layer, the
+    history load (H2D) and the new rows' write-back (D2H) timed alone on
+    their streams, the stand-in compute timed alone (layer 0 resident), and
+    whole pipelined runs with the compute window set to about ratio x the
+    load time.  Exposed time = pipelined - compute only, against the pages'
+    per-layer bound max(0, tau_H2D - d_on tau_compute) (d_on = 2 layers for
+    the default prefetch) and the serial-link bound."""
+    import ctypes
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore
+
+    rows = n_hist + n_new
+    dev = "cuda"
+    store = HostStore((NL, rows, 576))
+    rng = np.random.default_rng(7)
+    block = rng.integers(-8, 9, (1024, 576)).astype(np.int16)
+    table = np.array([0xC100, 0xC0E0, 0xC0C0, 0xC0A0, 0xC080, 0xC040, 0xC000, 0xBF80,
+                      0x0000, 0x3F80, 0x4000, 0x4040, 0x4080, 0x40A0, 0x40C0, 0x40E0,
+                      0x4100], np.uint16)                # bf16 of -8 .. 8
+    pat = table[block + 8]
+    for r0 in range(0, rows, 1024):
+        r1 = min(rows, r0 + 1024)
+        store.array[:, r0:r1] = pat[:r1 - r0]
+    new = torch.from_numpy(table[rng.integers(-8, 9, (NL, n_new, 576)) + 8].view(np.int16)).to(dev)
+    bufs = torch.zeros((4, rows, 576), dtype=torch.int16, device=dev)
+    bufs[0, :n_hist] = torch.from_numpy(store.array[0, :n_hist].view(np.int16)).to(dev)
+    out = torch.zeros((NL, 576), dtype=torch.float32, device=dev)
+    ws = torch.empty(ess.ess_prefill_ws_bytes(rows), dtype=torch.uint8, device=dev)
+    sc, sh, sd = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    row_b = 576 * 2
+
+    def timed(stream, fn, reps=3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fn()
+        stream.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        stream.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1e-3
+
+    def h2d():
+        hip.hipMemcpyAsync(bufs[1].data_ptr(), store.host + row_b * rows, n_hist * row_b,
+                           1, sh.cuda_stream)
+
+    def d2h():
+        hip.hipMemcpyAsync(store.host + row_b * (rows + n_hist), bufs[1][n_hist:].data_ptr(),
+                           n_new * row_b, 2, sd.cuda_stream)
+
+    def call(n_layers, reps):
+        with torch.cuda.stream(sc):
+            ess.ess_prefill_layers(n_layers, rows, n_hist, n_new, store.host, new, bufs,
+                                   out, ws, compute_reps=reps, compute=sc, h2d=sh, d2h=sd)
+
+    t_h2d = timed(sh, h2d)
+    t_d2h = timed(sd, d2h)
+    # One layer (layer 0, resident): compute + its write-back; two rep counts
+    # give the time per rep of the stand-in compute.
+    call(NL, 1)                              # first use: events, kernels loaded
+    torch.cuda.synchronize()
+    ta = timed(sc, lambda: call(1, 4), reps=5)
+    tb = timed(sc, lambda: call(1, 24), reps=5)
+    per_rep = max(1e-6, (tb - ta) / 20)
+    runs = []
+    for ratio in ratios:
+        reps = max(1, int(round(ratio * t_h2d / per_rep)))
+        t_layer = timed(sc, lambda: call(1, reps))           # compute + write-back
+        t_c = max(1e-9, t_layer - t_d2h)
+        t_pipe = timed(sc, lambda: call(NL, reps), reps=2)
+        t_only = NL * t_c + t_d2h
+        exposed = max(0.0, t_pipe - t_only)
+        loads = (NL - 1) * t_h2d
+        runs.append({
+            "compute_reps": reps, "tau_compute_ms": t_c * 1e3,
+            "compute_over_load": t_c / t_h2d,
+            "t_pipelined_ms": t_pipe * 1e3, "t_compute_only_ms": t_only * 1e3,
+            "exposed_ms": exposed * 1e3,
+            "bound_pages_ms": (NL - 1) * max(0.0, t_h2d - 2 * t_c) * 1e3,
+            "bound_serial_link_ms": max(0.0, loads + t_c - NL * t_c) * 1e3,
+            "load_hidden_fraction": 1 - exposed / loads,
+        })
+    store.free()
+    return {"layers": NL, "history_rows": n_hist, "new_rows": n_new,
+            "layer_bytes": n_hist * row_b,
+            "tau_h2d_ms": t_h2d * 1e3, "h2d_gbps": n_hist * row_b / t_h2d / 1e9,
+            "tau_d2h_ms": t_d2h * 1e3, "d2h_gbps": n_new * row_b / t_d2h / 1e9,
+            "runs": runs}
+
+
 def indexer_alone(d, lb, q_idx, n_vis, stream, reps=16):
     """Indexer kernel time alone, launches back to back with events only
     around the whole run: over copies of the index cache taken in turn,
@@ -692,6 +790,7 @@ def main():
     if not args.no_extra:
         res["extra"] = extra_measurements(args)
         res["extra"]["eviction_replay"] = replay_curves(args)
+        res["extra"]["prefill_pipeline"] = prefill_pipeline(args)
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)

@@ -417,6 +417,128 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }
 
+size_t ess_prefill_ws_bytes(int32_t rows) {
+  return rows < 1 ? 0 : ess::prefill_ws_bytes(rows);
+}
+
+ess_status ess_prefill_layers(int32_t n_layers, int32_t rows, int32_t n_hist,
+                              int32_t n_new, uint16_t* host_kv,
+                              const uint16_t* new_kv, uint16_t* bufs,
+                              float* layer_out, void* ws, size_t ws_bytes,
+                              const int32_t* onload_layer_map,
+                              int32_t* binding, int32_t compute_reps,
+                              int32_t load_layer0, hipStream_t compute,
+                              hipStream_t h2d, hipStream_t d2h) {
+  const char* fn = "ess_prefill_layers";
+  if (n_layers < 1 || rows < 1 || n_hist < 0 || n_new < 0 ||
+      n_hist + n_new < 1 || n_hist + n_new > rows || compute_reps < 1)
+    return fail(ESS_ERR_INVALID,
+                "%s: bad sizes (n_layers %d, rows %d, n_hist %d, n_new %d, reps %d)",
+                fn, n_layers, rows, n_hist, n_new, compute_reps);
+  ESS_NONNULL(host_kv);
+  ESS_NONNULL(bufs);
+  ESS_NONNULL(layer_out);
+  ESS_NONNULL(ws);
+  if (n_new > 0) ESS_NONNULL(new_kv);
+  if (compute == h2d || compute == d2h || h2d == d2h)
+    return fail(ESS_ERR_INVALID, "%s: compute, h2d and d2h must be three streams", fn);
+  const size_t need = ess::prefill_ws_bytes(rows);
+  if (ws_bytes < need)
+    return fail(ESS_ERR_NOMEM, "%s: workspace of %zu bytes, need %zu", fn,
+                ws_bytes, need);
+
+  // Bindings (checked before anything is enqueued): layers 1..3 take B1..B3;
+  // layer i >= 1 releases its buffer after its compute and write-back, and
+  // its scheduling point binds the oldest released buffer to the map's
+  // layer.
+  constexpr int kBufs = 4;
+  std::vector<int> bind(n_layers, -1), freed_by(n_layers, -1), trigger(n_layers, -1);
+  std::vector<std::pair<int, int>> freeq;        // (buffer, released by layer)
+  bind[0] = 0;
+  for (int b = 1; b < kBufs; ++b) freeq.emplace_back(b, -1);
+  for (int l = 1; l < kBufs && l < n_layers; ++l) {
+    bind[l] = freeq.front().first;
+    freed_by[l] = freeq.front().second;
+    freeq.erase(freeq.begin());
+  }
+  for (int i = 0; i < n_layers; ++i) {
+    if (bind[i] < 0)
+      return fail(ESS_ERR_INVALID, "%s: layer %d is not loaded when its turn comes", fn, i);
+    if (i == 0) continue;
+    freeq.emplace_back(bind[i], i);
+    int j;
+    if (!onload_layer_map) {
+      j = i + kBufs - 1;
+      if (j >= n_layers) continue;
+    } else {
+      j = onload_layer_map[i];
+      if (j < 0) continue;
+    }
+    if (j <= i || j >= n_layers || bind[j] >= 0)
+      return fail(ESS_ERR_INVALID,
+                  "%s: onload_layer_map[%d] = %d is not a future, unloaded layer", fn, i, j);
+    bind[j] = freeq.front().first;
+    freed_by[j] = freeq.front().second;
+    trigger[j] = i;
+    freeq.erase(freeq.begin());
+  }
+  if (binding)
+    for (int l = 0; l < n_layers; ++l) binding[l] = bind[l];
+
+  // Events: per layer loaded (h2d), computed (compute), released (d2h).
+  hipEvent_t* ev;
+  ess_status st;
+  if ((st = get_events(3 * (size_t)n_layers + 1, &ev)) != ESS_OK) return st;
+  hipEvent_t* loaded = ev;
+  hipEvent_t* computed = ev + n_layers;
+  hipEvent_t* released = ev + 2 * (size_t)n_layers;
+  hipEvent_t start = ev[3 * (size_t)n_layers];
+  const size_t row_b = (size_t)ess::kLat * sizeof(uint16_t);
+  const size_t layer_rows = (size_t)rows * ess::kLat;
+  auto host_layer = [&](int l) { return host_kv + (size_t)l * layer_rows; };
+  auto buf_of = [&](int l) { return bufs + (size_t)bind[l] * layer_rows; };
+  float* part = static_cast<float*>(ws);
+
+  hipError_t e = hipEventRecord(start, compute);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h2d, start, 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(d2h, start, 0);
+  auto load = [&](int l) -> hipError_t {
+    hipError_t r = hipSuccess;
+    if (n_hist > 0)
+      r = hipMemcpyAsync(buf_of(l), host_layer(l), (size_t)n_hist * row_b,
+                         hipMemcpyHostToDevice, h2d);
+    if (r == hipSuccess) r = hipEventRecord(loaded[l], h2d);
+    return r;
+  };
+  if (e == hipSuccess && load_layer0) e = load(0);
+  for (int l = 1; l < n_layers && e == hipSuccess; ++l)
+    if (trigger[l] < 0) e = load(l);
+  for (int i = 0; i < n_layers && e == hipSuccess; ++i) {
+    if (i > 0 || load_layer0) e = hipStreamWaitEvent(compute, loaded[i], 0);
+    if (e == hipSuccess)
+      e = ess::launch_prefill_compute(n_new ? new_kv + (size_t)i * n_new * ess::kLat : nullptr,
+                                      n_new, buf_of(i), n_hist, compute_reps, part,
+                                      layer_out + (size_t)i * ess::kLat, compute);
+    if (e == hipSuccess) e = hipEventRecord(computed[i], compute);
+    if (e == hipSuccess) e = hipStreamWaitEvent(d2h, computed[i], 0);
+    if (e == hipSuccess && n_new > 0)
+      e = hipMemcpyAsync(host_layer(i) + (size_t)n_hist * ess::kLat,
+                         buf_of(i) + (size_t)n_hist * ess::kLat,
+                         (size_t)n_new * row_b, hipMemcpyDeviceToHost, d2h);
+    if (e == hipSuccess) e = hipEventRecord(released[i], d2h);
+    // Loads issued at this layer's scheduling point.
+    for (int j = i + 1; j < n_layers && e == hipSuccess; ++j) {
+      if (trigger[j] != i) continue;
+      e = hipStreamWaitEvent(h2d, released[freed_by[j]], 0);
+      if (e == hipSuccess && freed_by[j] != i) e = hipStreamWaitEvent(h2d, computed[i], 0);
+      if (e == hipSuccess) e = load(j);
+    }
+  }
+  // Every write-back done before later work on the compute stream.
+  if (e == hipSuccess) e = hipStreamWaitEvent(compute, released[n_layers - 1], 0);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
 ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view) {
   const char* fn = "ess_host_alloc";
   ESS_NONNULL(host_ptr);

@@ -30,6 +30,7 @@ EXPORTED = (
     "ess_index_scores", "ess_topk_lookup", "ess_pool_update",
     "ess_sparse_mla_decode", "ess_miss_copy", "ess_decode_step",
     "ess_host_alloc", "ess_host_free", "ess_replay_evictions",
+    "ess_prefill_ws_bytes", "ess_prefill_layers",
     "ess_status_string", "ess_last_error",
 )
 
@@ -93,6 +94,9 @@ def lib():
             "ess_host_free": (_I, [_P]),
             "ess_replay_evictions": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P,
                                           ctypes.c_uint64, _I, _P, _P]),
+            "ess_prefill_ws_bytes": (_S, [_I]),
+            "ess_prefill_layers": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _S,
+                                        _P, _P, _I, _I, _P, _P, _P]),
             "ess_status_string": (ctypes.c_char_p, [_I]),
             "ess_last_error": (ctypes.c_char_p, []),
         }
@@ -227,3 +231,29 @@ def ess_replay_evictions(policy, pool_slots, scores, sel_pos, n_sel, seed=0,
         sel_pos.ctypes.data, n_sel.ctypes.data, seed, request,
         n_miss.ctypes.data, n_evict.ctypes.data))
     return n_miss, n_evict
+
+
+def ess_prefill_ws_bytes(rows: int) -> int:
+    return lib().ess_prefill_ws_bytes(rows)
+
+
+def ess_prefill_layers(n_layers, rows, n_hist, n_new, host_kv, new_kv, bufs,
+                       layer_out, ws, onload_layer_map=None, compute_reps=1,
+                       load_layer0=False, compute=None, h2d=None, d2h=None):
+    """Four-buffer prefill over n_layers layers.  host_kv: host address of
+    pinned [n_layers][rows][576] bf16 (from ess_host_alloc); new_kv, bufs,
+    layer_out, ws: device tensors; onload_layer_map: int sequence or None.
+    Returns the buffer index of every layer (numpy int32)."""
+    import numpy as np
+    binding = np.full(n_layers, -1, np.int32)
+    m = None
+    if onload_layer_map is not None:
+        m = np.ascontiguousarray(onload_layer_map, dtype=np.int32)
+        if m.shape != (n_layers,):
+            raise ValueError("onload_layer_map needs one entry per layer")
+    _check("ess_prefill_layers", lib().ess_prefill_layers(
+        n_layers, rows, n_hist, n_new, _ptr(host_kv), _ptr(new_kv), _ptr(bufs),
+        _ptr(layer_out), _ptr(ws), ws.numel() * ws.element_size(),
+        None if m is None else m.ctypes.data, binding.ctypes.data, compute_reps,
+        1 if load_layer0 else 0, _stream(compute), _stream(h2d), _stream(d2h)))
+    return binding

@@ -260,6 +260,47 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
 ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view);
 ess_status ess_host_free(void* host_ptr);
 
+/* Bytes of device workspace ess_prefill_layers needs for buffers of `rows`
+ * rows (per-block partial sums of the stand-in compute); 0 if rows < 1. */
+size_t ess_prefill_ws_bytes(int32_t rows);
+
+/* Prefill over n_layers layers with four full-layer device buffers
+ * (FlashOffloading analysis, prefill section, Figs. 2 and 3): host memory
+ * keeps every layer's full history; B0 (bufs[0]) stays bound to layer 0 for
+ * the whole prefill and must already hold its history unless load_layer0
+ * is set; B1-B3 rotate over the later layers.  Layers 1, 2, 3 are bound to
+ * B1, B2, B3 before any compute; layer i >= 1 releases its buffer once its
+ * compute and its write-back are done, and at layer i's scheduling point
+ * the oldest released buffer is bound to layer onload_layer_map[i] (NULL:
+ * i + 3 while it exists; -1: none), whose load starts once that buffer is
+ * released and layer i is computed.  Per layer:
+ *   load   (stream h2d): host_kv[l][0:n_hist] -> buffer (layers >= 1);
+ *   compute (stream compute, after the load): new_kv[l] appended at rows
+ *          [n_hist, n_hist + n_new) of the buffer, then the stand-in
+ *          consumer - per-column sums of all n_hist + n_new rows into
+ *          layer_out[l][576], repeated compute_reps times (a knob for the
+ *          compute window; the result is the same);
+ *   write-back (stream d2h, after the compute): buffer rows
+ *          [n_hist, n_hist + n_new) -> host_kv[l][n_hist:].
+ *   host_kv   [n_layers][rows][576] bf16 in pinned host memory (the host
+ *             address from ess_host_alloc); new_kv [n_layers][n_new][576]
+ *             bf16, bufs [4][rows][576] bf16, layer_out [n_layers][576]
+ *             float, ws ess_prefill_ws_bytes(rows) bytes: device;
+ *   onload_layer_map [n_layers], binding [n_layers] (out: the buffer of
+ *             each layer, may be NULL): host arrays.
+ * The three streams must differ; on return all work, write-backs included,
+ * is ordered before later work on `compute`.  ESS_ERR_INVALID for bad
+ * sizes, NULL pointers, equal streams or a map that loads a layer twice,
+ * loads a past or bound layer, or leaves a layer unloaded at its turn. */
+ess_status ess_prefill_layers(int32_t n_layers, int32_t rows, int32_t n_hist,
+                              int32_t n_new, uint16_t* host_kv,
+                              const uint16_t* new_kv, uint16_t* bufs,
+                              float* layer_out, void* ws, size_t ws_bytes,
+                              const int32_t* onload_layer_map,
+                              int32_t* binding, int32_t compute_reps,
+                              int32_t load_layer0, hipStream_t compute,
+                              hipStream_t h2d, hipStream_t d2h);
+
 /* Eviction policies for ess_replay_evictions. */
 enum {
   ESS_EVICT_LRU = 0,     /* least recently used: the pool's own policy      */

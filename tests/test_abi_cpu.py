@@ -125,3 +125,23 @@ def test_long_rows_need_a_topk_workspace(L):
     assert "levels" in L.ess_last_error().decode()
     st = _status(lambda: ess.ess_topk_lookup(long_, 2048, 1, P, P, P, P, P, P, P + 4, 1 << 30, stream=0))
     assert st == "invalid argument"
+
+
+def test_prefill_argument_checks(L):
+    import torch
+    ws = torch.empty(ess.ess_prefill_ws_bytes(100), dtype=torch.uint8)   # host: never used
+    small = torch.empty(16, dtype=torch.uint8)
+
+    def call(NL=6, rows=100, n_hist=80, n_new=20, ws=ws, m=None, streams=(1, 2, 3)):
+        return _status(lambda: ess.ess_prefill_layers(
+            NL, rows, n_hist, n_new, P, P, P, P, ws, onload_layer_map=m,
+            compute=streams[0], h2d=streams[1], d2h=streams[2]))
+    assert call(n_hist=90) == "invalid argument"            # 90 + 20 > 100 rows
+    assert call(NL=0) == "invalid argument"
+    assert call(streams=(1, 1, 3)) == "invalid argument"
+    assert call(ws=small) == "out of memory"
+    assert call(m=[-1, 4, 4, -1, -1, -1]) == "invalid argument"   # layer 4 twice
+    assert call(m=[-1, -1, -1, -1, -1, -1]) == "invalid argument"  # 4, 5 never loaded
+    assert "not loaded" in L.ess_last_error().decode()
+    assert ess.ess_prefill_ws_bytes(0) == 0
+    assert ess.ess_prefill_ws_bytes(512) == 576 * 4 and ess.ess_prefill_ws_bytes(513) == 2 * 576 * 4
