@@ -1,6 +1,7 @@
 """Build libess.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Each .hip source under csrc/ compiles to an object in _build/ (in parallel),
+Each .hip (and host-only .cpp) source under csrc/ compiles to an object in
+_build/ (in parallel),
 then the objects link into decode_lightning_indexer_amd/libess.so.  No GPU is
 needed: hipcc cross-compiles for gfx950.
 """
