@@ -201,7 +201,7 @@ def staged_inputs(wl, layer, dev):
     return qi, qa, w, n_vis
 
 
-def run_steps(args, name, n_layers, modes, K, W):
+def run_steps(args, name, n_layers, modes, K, W, resident=False):
     """Whole steps of a workload through ess_decode_step: per mode, from the
     same first fill, W warm-up steps then K timed steps.  Returns per-mode
     step times, misses of the last step, and the last step's miss copies
@@ -269,6 +269,19 @@ def run_steps(args, name, n_layers, modes, K, W):
     ev[1].record(stream)
     torch.cuda.synchronize()
     t_copy = ev[0].elapsed_time(ev[1]) * 1e-3
+    if resident:
+        # The last step again: every row it selects is now in the pool, so
+        # this is the same step with no misses (selection, update and
+        # attention all run; nothing crosses the host link).
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ess.ess_decode_step(d, steps[W + K - 1], n_vis, ess.ESS_MODE_INLINE, stream, side)
+        ev[0].record(stream)
+        for _ in range(4):
+            ess.ess_decode_step(d, steps[W + K - 1], n_vis, ess.ESS_MODE_INLINE, stream, side)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res["resident"] = ev[0].elapsed_time(ev[1]) * 1e-3 / 4
+        res["resident_misses"] = sum(int(lb.n_miss.sum()) for lb in lbs)
     for h in hosts:
         h.free()
     return res, n_miss, t_copy, wl
@@ -294,8 +307,10 @@ def extra_measurements(args):
     name = "64k-b32-16layer"
     n_layers = 4
     res, n_miss, t_copy, wl = run_steps(
-        args, name, n_layers, [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH], K, W)
+        args, name, n_layers, [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH], K, W,
+        resident=True)
     ti, tp = res[ess.ESS_MODE_INLINE], res[ess.ESS_MODE_PREFETCH]
+    t_res = res["resident"]
     # Prefetch hides the next layer's selection under this layer's copy and
     # attention: the share of the step's non-copy work that disappears, and
     # how much of each step the host link is busy.
@@ -305,6 +320,14 @@ def extra_measurements(args):
                  "misses_last_step": n_miss,
                  "miss_copy_us_last_step": t_copy * 1e6,
                  "link_busy_inline": t_copy / ti, "link_busy_prefetch": t_copy / tp,
+                 # The multi-layer overlap of the miss transfer: (sum of the
+                 # step's copies + the step with every row resident - the
+                 # pipelined step) / the copies, with its bound.
+                 "resident_us_per_step": t_res * 1e6,
+                 "resident_step_misses": res["resident_misses"],
+                 "overlap_prefetch": (t_copy + t_res - tp) / t_copy,
+                 "overlap_inline": (t_copy + t_res - ti) / t_copy,
+                 "overlap_bound": min(1.0, t_res / t_copy),
                  "hidden_noncopy_fraction": (ti - tp) / (ti - t_copy) if ti > t_copy else None}
     return out
 
