@@ -4,7 +4,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -107,12 +106,14 @@ ess_status check_mla(const ess_dims* d, const char* fn) {
   return ESS_OK;
 }
 
-// Events for ordering the prefetch stream against the main stream.
-std::mutex g_ev_mu;
-std::vector<hipEvent_t> g_events;
+// Events that order one call's streams against each other.  Each host
+// thread has its own pool: a call records and waits on its events while it
+// enqueues (a wait takes the event's state at that moment), so a later call
+// on the same thread may reuse them, and calls on different threads never
+// share one.
+thread_local std::vector<hipEvent_t> g_events;
 
 ess_status get_events(size_t n, hipEvent_t** out) {
-  std::lock_guard<std::mutex> lk(g_ev_mu);
   while (g_events.size() < n) {
     hipEvent_t e;
     hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);

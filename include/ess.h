@@ -33,7 +33,9 @@
  *     < ctx_len, n_vis in [1, ctx_len]); a launch failure reported by the HIP
  *     runtime returns ESS_ERR_HIP.
  *   - Every call is asynchronous on the given stream; counts such as n_sel
- *     and n_miss stay in device memory.
+ *     and n_miss stay in device memory.  Calls from different host threads
+ *     may run at once (on different buffers): the events a call uses to
+ *     order its streams belong to the calling thread.
  *   - Layouts are row-major with the listed shapes; "bf16" arrays are passed
  *     as uint16_t bit patterns; fp8 arrays are OCP e4m3fn bytes.
  */

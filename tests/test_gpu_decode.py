@@ -114,3 +114,34 @@ def test_lru_replay_reproduces_the_gpu_pool():
             nm2, ev2 = ess.ess_replay_evictions(pol, wl.pool_slots, scores[b],
                                                 sel[b], n_sel[b], request=b)
             assert np.all(ev2 <= nm2) and np.all(nm2 <= m * k)
+
+
+def test_concurrent_sequences_on_two_threads():
+    # Two host threads run whole prefetch-mode sequences at once (each with
+    # its own buffers and side stream; the library's stream-ordering events
+    # are per thread): both equal the same sequences run one after another.
+    import threading
+    wls = [get_workload("tiny-4k").with_(name=f"thread{i}", batch=2, layers=2,
+                                          steps=3, seed=11 + i, miss_mode="prefetch")
+           for i in range(2)]
+    ref = [gpu_sequence(wl, mode=ess.ESS_MODE_PREFETCH) for wl in wls]
+    got = [None, None]
+    errs = []
+
+    def work(i):
+        try:
+            got[i] = gpu_sequence(wls[i], mode=ess.ESS_MODE_PREFETCH)
+        except Exception as e:          # surfaced below
+            errs.append(e)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    for i in range(2):
+        for sa, sb in zip(ref[i]["steps"], got[i]["steps"]):
+            for la, lb in zip(sa, sb):
+                for key in la:
+                    assert np.array_equal(la[key], lb[key]), (i, key)
