@@ -322,10 +322,12 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
   e = ess::launch_topk(d, k, n_tok, io.scores, n_vis, io.cache_slots,
                        io.sel_pos, io.sel_slot, io.n_sel, tws, st);
   if (e != hipSuccess) return e;
+  // The update takes each row's pre-update slot from the top-k's lookup.
   return ess::launch_pool_update(d, k, n_tok, io.sel_pos, io.n_sel,
                                  io.cache_slots, io.slot_pos, io.lru_state,
                                  io.miss_pos, io.miss_slot, io.n_miss,
-                                 io.n_evict, io.row_dst, io.sel_slot_post, st);
+                                 io.n_evict, io.row_dst, io.sel_slot_post, st,
+                                 io.sel_slot);
 }
 
 // Gather + attention of one selected layer: the attention reads each miss

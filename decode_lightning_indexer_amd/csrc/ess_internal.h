@@ -79,7 +79,8 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               void* lru, int32_t* miss_pos,
                               int32_t* miss_slot, int32_t* n_miss,
                               int32_t* n_evict, int32_t* row_dst,
-                              int32_t* sel_slot_post, hipStream_t s);
+                              int32_t* sel_slot_post, hipStream_t s,
+                              const int32_t* sel_slot_pre = nullptr);
 
 // ---- attention ----------------------------------------------------------
 struct MlaPlan {

@@ -76,7 +76,8 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               void* lru, int32_t* miss_pos,
                               int32_t* miss_slot, int32_t* n_miss,
                               int32_t* n_evict, int32_t* row_dst,
-                              int32_t* sel_slot_post, hipStream_t s) {
+                              int32_t* sel_slot_post, hipStream_t s,
+                              const int32_t* sel_slot_pre) {
   const size_t stride = lru_bytes_per_req(d.pool_slots);
   // The sort buffer holds at least one entry per thread.
   const int epow2 = pow2_at_least(n_tok * k) < NT ? NT : pow2_at_least(n_tok * k);
@@ -92,7 +93,7 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
   const pool::Args a{sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
                      miss_pos, miss_slot, n_miss, n_evict, row_dst,
                      sel_slot_post, d.ctx_len, d.pool_slots, k, n_tok, epow2,
-                     two, pos_shift};
+                     two, pos_shift, sel_slot_pre};
   hipLaunchKernelGGL(pool_update_kernel, dim3(d.batch), dim3(NT), lds, s, a);
   return hipGetLastError();
 }

@@ -54,6 +54,10 @@ struct Args {
   int32_t* row_dst;
   int32_t* sel_slot_post;
   int L, C, k, n_tok, epow2, two_buffers, pos_shift;
+  // Optional: every row's slot before this update as the top-k read it
+  // (cache_slots at sel_pos); read next to sel_pos instead of looking
+  // cache_slots up at each position after sel_pos arrives.
+  const int32_t* sel_slot_pre;
 };
 
 // The update of request b by a 1024-thread workgroup.  smem_ent: epow2
@@ -109,24 +113,29 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
   bool bad = false;
   constexpr int kU = 4;   // entries per thread whose reads are in flight together
   for (int eb = tid; eb < epow2; eb += kU * NT) {
-    int pos[kU], row[kU], tok[kU], slot[kU];
+    int pos[kU], row[kU], tok[kU], slot[kU], given[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int e = eb + u * NT;
       pos[u] = -1;
       row[u] = 0;
       tok[u] = 0;
+      given[u] = -1;
       if (e < n_e) {
         int j = 0;
         while (e >= off[j + 1]) ++j;
         tok[u] = j;
         row[u] = e - off[j];
         pos[u] = PRESEL ? pre_pos[row[u]] : sel_pos[rows0 + (size_t)j * k + row[u]];
+        if (!PRESEL && a.sel_slot_pre)
+          given[u] = a.sel_slot_pre[rows0 + (size_t)j * k + row[u]];
       }
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      slot[u] = pos[u] >= 0 && pos[u] < L ? (PRESEL ? pre_slot[row[u]] : cs[pos[u]]) : -1;
+      slot[u] = pos[u] >= 0 && pos[u] < L
+                    ? (PRESEL ? pre_slot[row[u]] : a.sel_slot_pre ? given[u] : cs[pos[u]])
+                    : -1;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int e = eb + u * NT;
