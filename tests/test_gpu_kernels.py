@@ -207,6 +207,9 @@ def _bf16(rng, shape, std):
     (1, 1, 32, 500, 45, 100, False, 0.0),     # all misses
     (1, 1, 48, 500, 33, 100, False, 1.0),     # all hits
     (1, 2, 16, 100, 200, 400, True, 0.6),     # k > L: n_sel ragged below k
+    # 8 requests x 2 tokens x 2 head groups: 8 chunks of 256 of the 2048
+    # rows, the chunk plan of the 128K workload.
+    (8, 2, 128, 6000, 2048, 4200, True, 0.7),
 ])
 def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
     rng = np.random.default_rng(H * 7 + k)
