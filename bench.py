@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the 128K and multi-layer prefetch measurements")
+    p.add_argument("--extra-only", choices=["prefill_pipeline", "eviction_replay"],
+                   help="only run one extra measurement and print its JSON (for "
+                        "profiling it alone)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (known "
                         "bytes) for scaling the HBM traffic counters")
@@ -548,6 +551,12 @@ def main():
     args = parse()
     if args.trace_summary:
         return trace_summary(args.trace_summary, args.steps, args.warmup)
+    if args.extra_only:
+        import torch
+        torch.cuda.set_device(0)
+        fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves}
+        print(json.dumps({args.extra_only: fn[args.extra_only](args)}), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not "
               "supported (requests shard across GPUs with no exchange; see "
