@@ -8,6 +8,14 @@ resident in device memory and leave its element type open; the reading taken
 is fp8 with integer values, which it represents exactly).
 
 bf16: the upper 16 bits of an IEEE binary32.
+
+The 656-byte fp8 latent entry (ESS concept page, the FlashTrans row: 656
+bytes per token per layer; the split 512 fp8 + 16 bytes of scales + 64 bf16
+is the reading taken, matching the page's per-token block size and its
+83.2 % / 16.8 % split): bytes 0..511 the c_KV values as fp8 e4m3fn, bytes
+512..527 four float32 scales, one per block of 128 c_KV values, bytes
+528..655 the 64 k_R values as bf16.  A latent value is code value x its
+block's scale; k_R is read as bf16.
 """
 import numpy as np
 
@@ -38,3 +46,15 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
     """uint16 array of bf16 bit patterns -> float64 array."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(np.float64)
+
+
+def decode_entries(entries: np.ndarray) -> np.ndarray:
+    """uint8 656-byte entries [n][656] -> float64 latents [n][576]."""
+    e = np.asarray(entries, dtype=np.uint8)
+    n = e.shape[0]
+    vals = decode_e4m3fn(e[:, :512]).reshape(n, 4, 128)
+    scale = np.ascontiguousarray(e[:, 512:528]).view(np.float32).astype(np.float64)
+    out = np.empty((n, 576), np.float64)
+    out[:, :512] = (vals * scale[:, :, None]).reshape(n, 512)
+    out[:, 512:] = decode_bf16(np.ascontiguousarray(e[:, 528:656]).view(np.uint16))
+    return out

@@ -64,6 +64,48 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (r >> np.uint32(16)).astype(np.uint16)
 
 
+# The 656-byte latent entry of an fp8 latent cache: c_KV as 512 fp8 e4m3fn
+# values, then one float32 scale per block of 128 of them (16 bytes), then
+# k_R as 64 bf16 (128 bytes).  Scales are powers of two, so every stored
+# value times its scale is exactly a bf16 value.
+ENTRY_BYTES = 656
+_E4M3_POS = np.array([(1.0 + (c & 7) / 8.0) * 2.0 ** (((c >> 3) & 15) - 7)
+                      if (c >> 3) & 15 else (c & 7) * 2.0 ** -9
+                      for c in range(127)])          # codes 0x00..0x7E, increasing
+
+
+def encode_e4m3_rne(x: np.ndarray) -> np.ndarray:
+    """float -> fp8 e4m3fn codes, round to nearest (ties to the even code),
+    |x| saturated at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 126)
+    lo = hi - 1
+    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a <= _E4M3_POS[0], 0, code)
+    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def encode_entries(bf16_rows: np.ndarray) -> np.ndarray:
+    """uint16 bf16 latents [n][576] -> uint8 656-byte entries [n][656]: each
+    block of 128 c_KV values scaled by 2^ceil(log2(max|x| / 448)) (1 for an
+    all-zero block) and rounded to fp8 e4m3fn; k_R kept as bf16."""
+    rows = np.asarray(bf16_rows, dtype=np.uint16)
+    n = rows.shape[0]
+    x = (rows[:, :512].astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    blocks = x.reshape(n, 4, 128)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0.0)
+    scale = np.ldexp(1.0, e.astype(np.int64))
+    q = encode_e4m3_rne(blocks / scale[:, :, None]).reshape(n, 512)
+    out = np.empty((n, ENTRY_BYTES), np.uint8)
+    out[:, :512] = q
+    out[:, 512:528] = scale.astype(np.float32).view(np.uint8).reshape(n, 16)
+    out[:, 528:] = np.ascontiguousarray(rows[:, 512:]).view(np.uint8).reshape(n, 128)
+    return out
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))

@@ -69,3 +69,49 @@ def test_generator_query_drift_statistics():
     a, b = q[:-1].ravel(), q[1:].ravel()
     corr = np.corrcoef(a, b)[0, 1]
     assert abs(corr - wl.rho) < 0.05
+
+
+def test_656_byte_entry_decodes_by_hand():
+    # One entry built by hand: c_KV block 0 holds 1.0 (0x38) and -448 (0xFE)
+    # at scale 2^-3; block 1 the smallest subnormal 2^-9 (0x01) at scale 1;
+    # block 2 the value 3.5 (0x46: 1.75 * 2) at scale 16; block 3 zeros at
+    # scale 2^-9; k_R: bf16 1.5 (0x3FC0) and -0.25 (0xBE80).
+    from oracle.formats import decode_entries
+    e = np.zeros((1, 656), np.uint8)
+    e[0, 0], e[0, 1] = 0x38, 0xFE
+    e[0, 128] = 0x01
+    e[0, 256] = 0x46
+    e[0, 512:528] = np.array([2.0 ** -3, 1.0, 16.0, 2.0 ** -9], np.float32).view(np.uint8)
+    kr = np.zeros(64, np.uint16)
+    kr[0], kr[63] = 0x3FC0, 0xBE80
+    e[0, 528:] = kr.view(np.uint8)
+    v = decode_entries(e)[0]
+    assert v[0] == 0.125 and v[1] == -56.0
+    assert v[128] == 2.0 ** -9 and v[256] == 56.0
+    assert v[512] == 1.5 and v[575] == -0.25
+    assert np.count_nonzero(v) == 6
+
+
+def test_656_byte_entries_round_trip_the_generator():
+    # The generator's entries: per block a power-of-two scale, every c_KV
+    # value within half an fp8 step of the bf16 latent (relative 2^-4 for
+    # normal codes, 2^-10 * scale absolute for subnormal ones), k_R exact,
+    # and every decoded value exactly a bf16 value.
+    from oracle.formats import decode_entries
+    from synth.gen import encode_entries
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((200, 576)) * 0.5).astype(np.float32)
+    x[7, :128] = 0.0                                   # an all-zero block
+    rows = gen.f32_to_bf16_bits(x)
+    ent = encode_entries(rows)
+    got = decode_entries(ent)
+    ref = decode_bf16(rows)
+    scale = np.ascontiguousarray(ent[:, 512:528]).view(np.float32).astype(np.float64)
+    m, ex = np.frexp(scale)
+    assert np.all(m == 0.5)                            # powers of two
+    s = np.repeat(scale, 128, axis=1)
+    err = np.abs(got[:, :512] - ref[:, :512])
+    assert np.all(err <= np.maximum(np.abs(ref[:, :512]) * 2.0 ** -4, s * 2.0 ** -10))
+    assert np.array_equal(got[:, 512:], ref[:, 512:])
+    assert np.array_equal(decode_bf16(gen.f32_to_bf16_bits(got.astype(np.float32))), got)
+    assert np.all(got[7, :128] == 0.0)
