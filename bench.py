@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the 128K and multi-layer prefetch measurements")
-    p.add_argument("--extra-only", choices=["prefill_pipeline", "eviction_replay"],
+    p.add_argument("--extra-only", choices=["prefill_pipeline", "eviction_replay",
+                                            "fp8_entries"],
                    help="only run one extra measurement and print its JSON (for "
                         "profiling it alone)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -204,11 +205,12 @@ def staged_inputs(wl, layer, dev):
     return qi, qa, w, n_vis
 
 
-def run_steps(args, name, n_layers, modes, K, W, resident=False):
+def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
     """Whole steps of a workload through ess_decode_step: per mode, from the
     same first fill, W warm-up steps then K timed steps.  Returns per-mode
     step times, misses of the last step, and the last step's miss copies
-    replayed alone (the host-link time a step needs)."""
+    replayed alone (the host-link time a step needs).  store="entries": the
+    host store holds the latents as 656-byte fp8 entries."""
     import numpy as np
     import torch
     from decode_lightning_indexer_amd import ess
@@ -223,9 +225,15 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False):
     hosts, lbs, qis, qas = [], [], [], []
     n_vis = None
     for l in range(n_layers):
-        h = HostStore((B, L, 576))
-        gen.fill_latents(wl, l, h.array)
-        lb = LayerBuffers(d, h)
+        if store == "entries":
+            h = HostStore((B, L, 656), np.uint8)
+            for b in range(B):
+                h.array[b] = gen.encode_entries(gen.latents(wl, l, b))
+            lb = LayerBuffers(d, None, entries=h)
+        else:
+            h = HostStore((B, L, 576))
+            gen.fill_latents(wl, l, h.array)
+            lb = LayerBuffers(d, h)
         kb = np.empty((B, L, wl.idx_dim), np.uint8)
         gen.fill_index_keys(wl, l, kb)
         lb.k_idx.copy_(torch.from_numpy(kb))
@@ -267,8 +275,12 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for lb in lbs:
-        ess.ess_miss_copy(d, m * k, lb.miss_pos, lb.miss_slot, lb.n_miss,
-                          lb.host.dev, lb.pool, stream)
+        if store == "entries":
+            ess.ess_miss_copy_entries(d, m * k, lb.miss_pos, lb.miss_slot,
+                                      lb.n_miss, lb.entries.dev, lb.pool, stream)
+        else:
+            ess.ess_miss_copy(d, m * k, lb.miss_pos, lb.miss_slot, lb.n_miss,
+                              lb.host.dev, lb.pool, stream)
     ev[1].record(stream)
     torch.cuda.synchronize()
     t_copy = ev[0].elapsed_time(ev[1]) * 1e-3
@@ -332,6 +344,34 @@ def extra_measurements(args):
                  "overlap_inline": (t_copy + t_res - ti) / t_copy,
                  "overlap_bound": min(1.0, t_res / t_copy),
                  "hidden_noncopy_fraction": (ti - tp) / (ti - t_copy) if ti > t_copy else None}
+    return out
+
+
+def fp8_entries(args, names=("32k-b16", "128k-b8-mtp2-r099")):
+    """The same steps with the host store holding 656-byte fp8 entries: the
+    misses cross the host link as entries and are dequantized into their
+    slots before the attention, which then reads every row from the pool.
+    Step time and the last step's entry copy replayed alone, beside the
+    bf16 store's figures (bytes per miss 656 against 1152)."""
+    from decode_lightning_indexer_amd import ess
+    out = {}
+    K, W = 16, 4
+    for name in names:
+        per = {}
+        for store in ("bf16", "entries"):
+            res, n_miss, t_copy, wl = run_steps(args, name, 1, [ess.ESS_MODE_INLINE],
+                                                K, W, store=store)
+            t = res[ess.ESS_MODE_INLINE]
+            nbytes = n_miss * (656 if store == "entries" else 1152)
+            per[store] = {"us_per_step": t * 1e6,
+                          "query_tok_s": wl.batch * wl.mtp / t,
+                          "misses_last_step": n_miss,
+                          "host_bytes_last_step": nbytes,
+                          "miss_copy_us_last_step": t_copy * 1e6,
+                          "miss_copy_gbps": nbytes / t_copy * 1e-9 if t_copy > 0 else None}
+        per["speedup"] = per["bf16"]["us_per_step"] / per["entries"]["us_per_step"]
+        out[name] = per
+        log(args, f"fp8 entries {name}: {per}")
     return out
 
 
@@ -554,7 +594,8 @@ def main():
     if args.extra_only:
         import torch
         torch.cuda.set_device(0)
-        fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves}
+        fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves,
+              "fp8_entries": fp8_entries}
         print(json.dumps({args.extra_only: fn[args.extra_only](args)}), flush=True)
         return 0
     if args.gpus != 1:
@@ -823,6 +864,7 @@ def main():
         res["extra"] = extra_measurements(args)
         res["extra"]["eviction_replay"] = replay_curves(args)
         res["extra"]["prefill_pipeline"] = prefill_pipeline(args)
+        res["extra"]["fp8_entries"] = fp8_entries(args)
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)

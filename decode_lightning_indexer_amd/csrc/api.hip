@@ -238,14 +238,14 @@ ess_status ess_pool_update(const ess_dims* d, int32_t k, int32_t n_tok,
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }
 
-ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
-                                 const int32_t* sel_pos,
-                                 const int32_t* sel_src,
-                                 const int32_t* row_dst, const int32_t* n_sel,
-                                 uint16_t* pool, const uint16_t* host_view,
-                                 float* out, float* lse, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "ess_sparse_mla_decode";
+static ess_status sparse_mla_call(const char* fn, const ess_dims* d,
+                                  const uint16_t* q_abs, const int32_t* sel_pos,
+                                  const int32_t* sel_src, const int32_t* row_dst,
+                                  const int32_t* n_sel, uint16_t* pool,
+                                  const uint16_t* host_view,
+                                  const uint8_t* entry_view, float* out,
+                                  float* lse, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   ess_status s = check_dims(d, fn);
   if (s != ESS_OK) return s;
   if ((s = check_mla(d, fn)) != ESS_OK) return s;
@@ -254,7 +254,10 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
   ESS_NONNULL(sel_src);
   ESS_NONNULL(n_sel);
   ESS_NONNULL(pool);
-  ESS_NONNULL(host_view);
+  if (!host_view && !entry_view)
+    return fail(ESS_ERR_INVALID, "%s: NULL host store", fn);
+  if (entry_view && (reinterpret_cast<uintptr_t>(entry_view) & 15))
+    return fail(ESS_ERR_INVALID, "%s: entry_view must be 16-byte aligned", fn);
   ESS_NONNULL(out);
   ESS_NONNULL(ws);
   if (reinterpret_cast<uintptr_t>(ws) & 15)
@@ -265,8 +268,33 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
                 ws_bytes, need);
   hipError_t e = ess::launch_sparse_mla(*d, q_abs, sel_pos, sel_src, row_dst,
                                         n_sel, pool, host_view, out, lse, ws,
-                                        stream);
+                                        stream, 0, entry_view);
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
+                                 const int32_t* sel_pos,
+                                 const int32_t* sel_src,
+                                 const int32_t* row_dst, const int32_t* n_sel,
+                                 uint16_t* pool, const uint16_t* host_view,
+                                 float* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "ess_sparse_mla_decode";
+  ESS_NONNULL(host_view);
+  return sparse_mla_call(fn, d, q_abs, sel_pos, sel_src, row_dst, n_sel, pool,
+                         host_view, nullptr, out, lse, ws, ws_bytes, stream);
+}
+
+ess_status ess_sparse_mla_decode_entries(
+    const ess_dims* d, const uint16_t* q_abs, const int32_t* sel_pos,
+    const int32_t* sel_src, const int32_t* row_dst, const int32_t* n_sel,
+    uint16_t* pool, const uint8_t* entry_view, float* out, float* lse,
+    void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "ess_sparse_mla_decode_entries";
+  ESS_NONNULL(entry_view);
+  return sparse_mla_call(fn, d, q_abs, sel_pos,
+                         sel_src, row_dst, n_sel, pool, nullptr, entry_view,
+                         out, lse, ws, ws_bytes, stream);
 }
 
 ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
@@ -288,9 +316,32 @@ ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }
 
+ess_status ess_miss_copy_entries(const ess_dims* d, int32_t list_stride,
+                                 const int32_t* miss_pos,
+                                 const int32_t* miss_slot,
+                                 const int32_t* n_miss,
+                                 const uint8_t* entry_view, uint16_t* pool,
+                                 hipStream_t stream) {
+  const char* fn = "ess_miss_copy_entries";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if (list_stride < 1)
+    return fail(ESS_ERR_INVALID, "%s: list_stride must be >= 1", fn);
+  ESS_NONNULL(miss_pos);
+  ESS_NONNULL(miss_slot);
+  ESS_NONNULL(n_miss);
+  ESS_NONNULL(entry_view);
+  ESS_NONNULL(pool);
+  if (reinterpret_cast<uintptr_t>(entry_view) & 15)
+    return fail(ESS_ERR_INVALID, "%s: entry_view must be 16-byte aligned", fn);
+  hipError_t e = ess::launch_entry_copy(*d, list_stride, miss_pos, miss_slot,
+                                        n_miss, entry_view, pool, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
 static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
   const char* fn = "ess_decode_step";
-  if (!io.q_idx || !io.w_idx || !io.k_idx || !io.host_view || !io.pool ||
+  if (!io.q_idx || !io.w_idx || !io.k_idx || (!io.host_view && !io.host_entries) || !io.pool ||
       !io.cache_slots || !io.slot_pos || !io.lru_state || !io.scores ||
       !io.sel_pos || !io.sel_slot || !io.n_sel || !io.row_dst ||
       !io.sel_slot_post || !io.miss_pos || !io.miss_slot || !io.n_miss ||
@@ -298,6 +349,9 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
     return fail(ESS_ERR_INVALID, "%s: layer %d has a NULL buffer", fn, l);
   if (mode != ESS_MODE_FILL && (!io.q_abs || !io.out || !io.ws))
     return fail(ESS_ERR_INVALID, "%s: layer %d has a NULL attention buffer",
+                fn, l);
+  if (io.host_entries && (reinterpret_cast<uintptr_t>(io.host_entries) & 15))
+    return fail(ESS_ERR_INVALID, "%s: layer %d host_entries must be 16-byte aligned",
                 fn, l);
   if (io.ws && (reinterpret_cast<uintptr_t>(io.ws) & 15))
     return fail(ESS_ERR_INVALID, "%s: layer %d workspace must be 16-byte aligned",
@@ -333,11 +387,16 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
 // Gather + attention of one selected layer: the attention reads each miss
 // from host memory into its tile and writes it to its slot from there, so
 // the host reads run under the attention's own work.
+// Gather + attention of one selected layer: the attention reads each miss
+// from host memory (a bf16 row, or a 656-byte fp8 entry it dequantizes in
+// the tile) and writes it to its slot from there, so the host reads run
+// under the attention's own work.
 static hipError_t enqueue_attention(const ess_dims& d, const ess_layer_io& io,
                                     hipStream_t st) {
   return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
-                                io.row_dst, io.n_sel, io.pool, io.host_view,
-                                io.out, io.lse, io.ws, st);
+                                io.row_dst, io.n_sel, io.pool,
+                                io.host_entries ? nullptr : io.host_view,
+                                io.out, io.lse, io.ws, st, 0, io.host_entries);
 }
 
 ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
@@ -383,8 +442,13 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
       const ess_layer_io& io = layers[l];
       e = enqueue_select(*d, io, n_vis, C, 1, tws(io), stream);
       if (e == hipSuccess)
-        e = ess::launch_miss_copy(*d, C, io.miss_pos, io.miss_slot, io.n_miss,
-                                  io.host_view, io.pool, stream);
+        e = io.host_entries
+                ? ess::launch_entry_copy(*d, C, io.miss_pos, io.miss_slot,
+                                         io.n_miss, io.host_entries, io.pool,
+                                         stream)
+                : ess::launch_miss_copy(*d, C, io.miss_pos, io.miss_slot,
+                                        io.n_miss, io.host_view, io.pool,
+                                        stream);
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
   }

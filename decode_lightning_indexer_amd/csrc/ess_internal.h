@@ -97,13 +97,21 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              const int32_t* row_dst, const int32_t* n_sel,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
-                             hipStream_t s, int target_wgs = 0);
+                             hipStream_t s, int target_wgs = 0,
+                             const uint8_t* entries = nullptr);
+// (entries non-null: misses are read from 656-byte fp8 entries [B][L][656]
+// instead of host, and dequantized in the tile.)
 
 // ---- miss copy ----------------------------------------------------------
 hipError_t launch_miss_copy(const ess_dims& d, int list_stride,
                             const int32_t* miss_pos, const int32_t* miss_slot,
                             const int32_t* n_miss, const uint16_t* host,
                             uint16_t* pool, hipStream_t s);
+// The same copy from 656-byte fp8 entries [B][L][656], dequantized to bf16.
+hipError_t launch_entry_copy(const ess_dims& d, int list_stride,
+                             const int32_t* miss_pos, const int32_t* miss_slot,
+                             const int32_t* n_miss, const uint8_t* host,
+                             uint16_t* pool, hipStream_t s);
 
 // ---- prefill pipeline ---------------------------------------------------
 // Per-block partial sums of the stand-in layer compute for `rows` rows.

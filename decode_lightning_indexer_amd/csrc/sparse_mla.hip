@@ -50,7 +50,15 @@
 // head and 8 tokens; those 8 tokens are exactly the lane's reduction slice
 // of the PV operand, so P never leaves registers.
 // Softmax runs in the log2 domain with a running max and sum per head.
+//
+// With a host store of 656-byte fp8 entries (c_KV in e4m3 with one
+// power-of-two scale per 128 values, k_R in bf16) a miss crosses the host
+// link as its 656 bytes instead of a 1152-byte row: the load puts the raw
+// entry into the last 41 slots of its tile row, and after the tile has
+// landed one wave per miss row expands it in place to the 576 bf16 values
+// the MFMAs and the pool write-back read (a second barrier per tile).
 #include "ess_internal.h"
+#include "fp8_entry.h"
 
 namespace ess {
 namespace {
@@ -81,6 +89,10 @@ constexpr int kMaxChunkTiles = kMaxChunkRows / kTile;
 constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 +
                            (size_t)kMaxChunkRows * 4 * 2 + kMaxChunkTiles * 4;
 constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
+// A miss read from a 656-byte fp8 entry lands raw in the last 41 slots of
+// its tile row and is expanded in place to 576 bf16 before the tile is read.
+constexpr int kRawSlot0 = kRowSlots - kEntryPieces;   // 33
+static_assert(kRawSlot0 > 0, "raw entry must fit in a tile row");
 
 // A zero latent row: the source of padding rows and unusable rows.
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[kLat] = {};
@@ -108,12 +120,29 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
 }
 
-template <int WPS>
+// Expand the raw entry in slots kRawSlot0.. of a tile row into the row's
+// 576 bf16 (one wave; lane l writes c_KV slot l, lanes 0-7 the k_R slots).
+// The output overlaps raw bytes other lanes read, so every lane's reads are
+// complete before any lane writes.
+__device__ __forceinline__ void expand_entry_row(uint16_t* row, int lane) {
+  const unsigned char* raw = reinterpret_cast<const unsigned char*>(row + kRawSlot0 * 8);
+  const uint2 q8 = *reinterpret_cast<const uint2*>(raw + lane * 8);
+  const float sc = *reinterpret_cast<const float*>(raw + kEntryScaleOff + (lane >> 4) * 4);
+  entry_v4u kr = {0u, 0u, 0u, 0u};
+  if (lane < 8) kr = *reinterpret_cast<const entry_v4u*>(raw + kEntryRopeOff + lane * 16);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const entry_v4u w = dequant8(q8.x, q8.y, sc);
+  *reinterpret_cast<entry_v4u*>(row + lane * 8) = w;
+  if (lane < 8) *reinterpret_cast<entry_v4u*>(row + (kVal / 8 + lane) * 8) = kr;
+}
+
+template <int WPS, bool kEnt>
 __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
-    const uint16_t* __restrict__ host, _Float16* __restrict__ part_acc,
+    const uint16_t* __restrict__ host, const unsigned char* __restrict__ entries,
+    _Float16* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
@@ -153,7 +182,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const int32_t* rsrc = sel_src + (size_t)bj * k;
   const int32_t* rdst = row_dst ? row_dst + (size_t)bj * k : nullptr;
   uint16_t* pool_b = pool + (size_t)b * C * kLat;
-  const uint16_t* host_b = host + (size_t)b * L * kLat;
+  // Misses come from bf16 rows (host) or, with kEnt, from fp8 entries.
+  const uint16_t* host_b = kEnt ? nullptr : host + (size_t)b * L * kLat;
+  const unsigned char* ent_b = kEnt ? entries + (size_t)b * L * kEntryBytes : nullptr;
 
   // Row sources of the chunk, once: hits read their slot, misses host
   // memory.  Given writer slots, the first head group stores each
@@ -237,9 +268,22 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
         const int cd = code[t0 - r0 + rr];
         const bool use = row < kTile && t0 + row < r1 && cd != kNoRow;
         const int off = (piece < kChunks16 ? piece : 0) * 8;
-        const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
-                                       : host_b + (size_t)(~cd) * kLat;
-        load_lds16((use ? rowp : g_zero_row) + off, buf + (size_t)j * 64 * 8);
+        if constexpr (kEnt) {
+          // A miss: its entry's 41 pieces into slots kRawSlot0.. of the row
+          // (the slots before them are overwritten by the expansion).
+          const int pe = cd < 0 ? ~cd : 0;
+          const void* src =
+              !use ? (const void*)(g_zero_row + off)
+              : cd >= 0 ? (const void*)(pool_b + (size_t)cd * kLat + off)
+              : piece >= kRawSlot0
+                  ? (const void*)(ent_b + (size_t)pe * kEntryBytes + (piece - kRawSlot0) * 16)
+                  : (const void*)g_zero_row;
+          load_lds16(src, buf + (size_t)j * 64 * 8);
+        } else {
+          const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
+                                         : host_b + (size_t)(~cd) * kLat;
+          load_lds16((use ? rowp : g_zero_row) + off, buf + (size_t)j * 64 * 8);
+        }
       }
     }
   };
@@ -255,6 +299,24 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     __syncthreads();          // ... and every wave's; tile it-1 consumed
     issue(it + 1);
     const int tt = 2 * it + sg;
+    if constexpr (kEnt) {
+      // Expand this tile's miss rows (the waves of the sub-group take them
+      // in turn), then make them visible to every wave.
+      if (tt < ntile) {
+        const int te = r0 + tt * kTile;
+        const int cd = code[te - r0 + min(lane, kTile - 1)];
+        const bool miss = lane < kTile && te + lane < r1 && cd < 0 && cd != kNoRow;
+        unsigned msk = (unsigned)__ballot(miss);
+        uint16_t* ebuf = ring + (size_t)(it % kStages) * kTileSlots * 8;
+        int n = 0;
+        while (msk) {
+          const int r = __builtin_ctz(msk);
+          msk &= msk - 1u;
+          if (n++ % WPS == wv) expand_entry_row(ebuf + (size_t)r * kKStride, lane);
+        }
+      }
+      __syncthreads();
+    }
     if (tt >= ntile) continue;
     const int t0 = r0 + tt * kTile;
     const uint16_t* krow = ring + (size_t)(it % kStages) * kTileSlots * 8;
@@ -476,14 +538,15 @@ __global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
   if (lse && t == 0) lse[(size_t)bj * H + h] = (M + log2f(den)) * 0.69314718055994531f;
 }
 
-template <int WPS>
+template <int WPS, bool kEnt>
 hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
-                    uint16_t* pool, const uint16_t* host, _Float16* part_acc,
+                    uint16_t* pool, const uint16_t* host,
+                    const unsigned char* entries, _Float16* part_acc,
                     float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS>,
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS, kEnt>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)kMlaLds);
   if (e != hipSuccess) return e;
@@ -491,8 +554,8 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
   const int groups = d.batch * p.nchunk;
   const int rounds = ((groups + 7) / 8) * d.mtp * p.head_groups;
   dim3 grid(rounds * 8);
-  hipLaunchKernelGGL((sparse_mla_kernel<WPS>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
-                     sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc,
+  hipLaunchKernelGGL((sparse_mla_kernel<WPS, kEnt>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
+                     sel_pos, sel_src, row_dst, n_sel, pool, host, entries, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
                      d.batch * d.mtp, scale_log2);
@@ -535,19 +598,26 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              const int32_t* row_dst, const int32_t* n_sel,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
-                             hipStream_t s, int target_wgs) {
+                             hipStream_t s, int target_wgs,
+                             const uint8_t* entries) {
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   _Float16* part_acc = static_cast<_Float16*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
+#define ESS_MLA_CASE(W)                                                        \
+  e = entries ? launch_t<W, true>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel,  \
+                                  pool, host, entries, part_acc, part_ml, s)      \
+              : launch_t<W, false>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, \
+                                   pool, host, nullptr, part_acc, part_ml, s)
   switch (p.heads_per_wg / 16) {
-    case 1: e = launch_t<1>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    case 2: e = launch_t<2>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    case 3: e = launch_t<3>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
-    default: e = launch_t<4>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host, part_acc, part_ml, s); break;
+    case 1: ESS_MLA_CASE(1); break;
+    case 2: ESS_MLA_CASE(2); break;
+    case 3: ESS_MLA_CASE(3); break;
+    default: ESS_MLA_CASE(4); break;
   }
+#undef ESS_MLA_CASE
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel,
                      dim3(d.mla_heads / kCombineHeads, d.batch * d.mtp),

@@ -28,7 +28,9 @@ ESS_EVICT_SCORE = 2
 EXPORTED = (
     "ess_workspace_bytes", "ess_lru_state_bytes", "ess_pool_reset",
     "ess_index_scores", "ess_topk_lookup", "ess_pool_update",
-    "ess_sparse_mla_decode", "ess_miss_copy", "ess_decode_step",
+    "ess_sparse_mla_decode", "ess_sparse_mla_decode_entries", "ess_miss_copy",
+    "ess_miss_copy_entries",
+    "ess_decode_step",
     "ess_host_alloc", "ess_host_free", "ess_replay_evictions",
     "ess_prefill_ws_bytes", "ess_prefill_layers",
     "ess_status_string", "ess_last_error",
@@ -61,7 +63,7 @@ class ess_layer_io(ctypes.Structure):
         "cache_slots", "slot_pos", "lru_state", "scores", "sel_pos",
         "sel_slot", "n_sel", "row_dst", "sel_slot_post", "miss_pos",
         "miss_slot", "n_miss", "n_evict", "out", "lse", "ws")] + [
-        ("ws_bytes", _S)]
+        ("ws_bytes", _S), ("host_entries", _P)]
 
 
 _lib = None
@@ -87,7 +89,10 @@ def lib():
                                      _P, _P, _P, _P]),
             "ess_sparse_mla_decode": (_I, [D, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _S, _P]),
+            "ess_sparse_mla_decode_entries": (_I, [D, _P, _P, _P, _P, _P, _P, _P,
+                                                   _P, _P, _P, _S, _P]),
             "ess_miss_copy": (_I, [D, _I, _P, _P, _P, _P, _P, _P]),
+            "ess_miss_copy_entries": (_I, [D, _I, _P, _P, _P, _P, _P, _P]),
             "ess_decode_step": (_I, [D, _I, ctypes.POINTER(ess_layer_io), _P,
                                      _I, _P, _P]),
             "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
@@ -185,11 +190,27 @@ def ess_sparse_mla_decode(d, q_abs, sel_pos, sel_src, row_dst, n_sel, pool,
         _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def ess_sparse_mla_decode_entries(d, q_abs, sel_pos, sel_src, row_dst, n_sel,
+                                  pool, entry_view, out, lse, ws, ws_bytes,
+                                  stream=None):
+    _check("ess_sparse_mla_decode_entries", lib().ess_sparse_mla_decode_entries(
+        ctypes.byref(d), _ptr(q_abs), _ptr(sel_pos), _ptr(sel_src),
+        _ptr(row_dst), _ptr(n_sel), _ptr(pool), _ptr(entry_view), _ptr(out),
+        _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def ess_miss_copy(d, list_stride, miss_pos, miss_slot, n_miss, host_view,
                   pool, stream=None):
     _check("ess_miss_copy", lib().ess_miss_copy(
         ctypes.byref(d), list_stride, _ptr(miss_pos), _ptr(miss_slot),
         _ptr(n_miss), _ptr(host_view), _ptr(pool), _stream(stream)))
+
+
+def ess_miss_copy_entries(d, list_stride, miss_pos, miss_slot, n_miss,
+                          entry_view, pool, stream=None):
+    _check("ess_miss_copy_entries", lib().ess_miss_copy_entries(
+        ctypes.byref(d), list_stride, _ptr(miss_pos), _ptr(miss_slot),
+        _ptr(n_miss), _ptr(entry_view), _ptr(pool), _stream(stream)))
 
 
 def ess_decode_step(d, layers, n_vis, mode, stream=None, side=None):

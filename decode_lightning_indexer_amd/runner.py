@@ -11,9 +11,13 @@ from .session import LayerBuffers
 
 
 class DecodeRunner:
-    def __init__(self, d: ess.ess_dims, hosts, device="cuda"):
+    def __init__(self, d: ess.ess_dims, hosts, device="cuda", entries=None):
+        """hosts: one bf16 HostStore per layer; entries: optionally one
+        656-byte-entry HostStore per layer (the host store then holds fp8
+        entries and hosts may hold None)."""
         self.d = d
-        self.layers = [LayerBuffers(d, h, device) for h in hosts]
+        entries = entries if entries is not None else [None] * len(hosts)
+        self.layers = [LayerBuffers(d, h, device, e) for h, e in zip(hosts, entries)]
         self.n_vis = torch.empty((d.batch, d.mtp), dtype=torch.int32,
                                  device=device)
         self.side = torch.cuda.Stream(device=device)

@@ -49,13 +49,15 @@ def dims_of(wl, **over) -> ess.ess_dims:
 class LayerBuffers:
     """Device buffers of one layer; `io()` packs them for ess_decode_step."""
 
-    def __init__(self, d: ess.ess_dims, host: HostStore, device="cuda"):
+    def __init__(self, d: ess.ess_dims, host: HostStore, device="cuda",
+                 entries: HostStore = None):
         B, m, L = d.batch, d.mtp, d.ctx_len
         C, k, H = d.pool_slots, d.topk, d.mla_heads
         lists = max(m * k, C)
         i32 = dict(dtype=torch.int32, device=device)
         self.d = d
-        self.host = host
+        self.host = host            # bf16 rows [B][L][576] (or None)
+        self.entries = entries      # 656-byte fp8 entries [B][L][656] (or None)
         self.k_idx = torch.empty((B, L, d.idx_dim), dtype=torch.uint8, device=device)
         self.q_idx = torch.empty((B, m, d.idx_heads, d.idx_dim), dtype=torch.uint8,
                                  device=device)
@@ -89,12 +91,13 @@ class LayerBuffers:
         p = lambda t: t.data_ptr()
         return ess.ess_layer_io(
             p(self.q_idx), p(self.w_idx), p(self.k_idx), p(self.q_abs),
-            self.host.dev, p(self.pool), p(self.cache_slots), p(self.slot_pos),
+            self.host.dev if self.host else None, p(self.pool),
+            p(self.cache_slots), p(self.slot_pos),
             p(self.lru), p(self.scores), p(self.sel_pos), p(self.sel_slot),
             p(self.n_sel), p(self.row_dst), p(self.sel_slot_post),
             p(self.miss_pos), p(self.miss_slot), p(self.n_miss),
             p(self.n_evict), p(self.out), p(self.lse), p(self.ws),
-            self.ws_bytes)
+            self.ws_bytes, self.entries.dev if self.entries else None)
 
     def rows(self, t, k, n_tok):
         """View of a flat per-row array as [B][n_tok][k]."""

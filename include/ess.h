@@ -11,7 +11,8 @@
  *   4+5. gather of the selected latents - hits from the pool
  *      in device memory, misses straight from mapped host
  *      memory - and absorbed-MLA attention over them         (ess_sparse_mla_decode)
- * plus a standalone host->pool copy of a miss list (ess_miss_copy) and a
+ * plus a standalone host->pool copy of a miss list (ess_miss_copy, and
+ * ess_miss_copy_entries from 656-byte fp8 entries) and a
  * whole-step entry point over several layers with side-stream prefetch
  * (ess_decode_step).
  *
@@ -193,6 +194,23 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
                                  float* out, float* lse, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* The same with a host store of 656-byte fp8 latent entries (layout under
+ * ess_miss_copy_entries): every miss row (sel_src[i] < 0) is read from
+ * entry_view[b][sel_pos[i]] (656 bytes over the host link) and dequantized in
+ * the attention's on-chip tile, so row_i is the dequantized entry; a
+ * designated-writer miss is written to its slot as those bf16 values.
+ * entry_view [B][L][656], 16-byte aligned.  Other arguments, the reduction
+ * order and the errors as in ess_sparse_mla_decode. */
+ess_status ess_sparse_mla_decode_entries(const ess_dims* d,
+                                         const uint16_t* q_abs,
+                                         const int32_t* sel_pos,
+                                         const int32_t* sel_src,
+                                         const int32_t* row_dst,
+                                         const int32_t* n_sel, uint16_t* pool,
+                                         const uint8_t* entry_view, float* out,
+                                         float* lse, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
+
 /* Copy a miss list from host memory into the pool (the pages' step 5, the
  * H2D load of the copy triples; ESS concept page: small-block transfers of
  * latent entries).  For each b and i < n_miss[b]:
@@ -202,6 +220,27 @@ ess_status ess_miss_copy(const ess_dims* d, int32_t list_stride,
                          const int32_t* miss_pos, const int32_t* miss_slot,
                          const int32_t* n_miss, const uint16_t* host_view,
                          uint16_t* pool, hipStream_t stream);
+
+/* The same copy from 656-byte fp8 latent entries (ESS concept page,
+ * FlashTrans row: transfers of 656-byte blocks; the layout is this library's
+ * reading of that size).  entry_view [B][L][656] bytes, 16-byte aligned,
+ * mapped pinned host memory (or device memory); entry s of request b is
+ *   bytes [0, 512)    c_KV as OCP e4m3fn
+ *   bytes [512, 528)  four float32 scales, scale j for c_KV[128j, 128j+128)
+ *   bytes [528, 656)  k_R as 64 bf16
+ * For each b and i < n_miss[b], with p = miss_pos[b*list_stride + i]:
+ *   pool[b][miss_slot[b*list_stride + i]][c] = bf16(e4m3(entry[p].c_KV[c]) *
+ *       scale[c / 128])      for c < 512   (round to nearest even)
+ *   pool[b][...][512 + r] = entry[p].k_R[r]      for r < 64
+ * With power-of-two scales and products in bf16's normal range the pool row
+ * is the dequantized entry exactly.  Each entry is read from host memory
+ * once (656 bytes instead of a 1152-byte bf16 row). */
+ess_status ess_miss_copy_entries(const ess_dims* d, int32_t list_stride,
+                                 const int32_t* miss_pos,
+                                 const int32_t* miss_slot,
+                                 const int32_t* n_miss,
+                                 const uint8_t* entry_view, uint16_t* pool,
+                                 hipStream_t stream);
 
 /* One layer's buffers for ess_decode_step.  Shapes as in the calls above;
  * miss_pos/miss_slot hold max(m*k, C) entries per request (the fill needs C);
@@ -230,6 +269,14 @@ typedef struct ess_layer_io {
   float* lse;                 /* [B][m][H] or NULL */
   void* ws;                   /* ess_workspace_bytes, one per layer */
   size_t ws_bytes;
+  const uint8_t* host_entries;  /* [B][L][656] fp8 entries (mapped pinned
+                                   host) or NULL.  Non-NULL: the host store
+                                   holds entries instead of bf16 rows
+                                   (host_view may then be NULL): the
+                                   attention reads misses as entries and
+                                   dequantizes them in its tile
+                                   (ess_sparse_mla_decode_entries), the
+                                   fill copies with ess_miss_copy_entries. */
 } ess_layer_io;
 
 enum {

@@ -78,8 +78,10 @@ def run_request(keys, q_steps, w, n_vis, qa_fn, host, *, steps, topk,
         yield rec
 
 
-def run_workload_request(wl, layer: int, b: int, steps=None, **kw):
-    """run_request on the seeded synthetic inputs of workload wl."""
+def run_workload_request(wl, layer: int, b: int, steps=None, host=None, **kw):
+    """run_request on the seeded synthetic inputs of workload wl (host: the
+    request's latents [L][576] in place of the generated ones, e.g. the
+    dequantized fp8 entries of a host store that holds entries)."""
     from synth import gen
     steps = wl.steps if steps is None else steps
     keys = gen.index_keys(wl, layer, b)
@@ -87,7 +89,7 @@ def run_workload_request(wl, layer: int, b: int, steps=None, **kw):
                   for j in range(wl.mtp)], axis=1)          # [T][m][H_I][d]
     w = np.stack([gen.head_weights(wl, layer, b, j) for j in range(wl.mtp)])
     n_vis = np.array([wl.n_vis(j) for j in range(wl.mtp)], np.int64)
-    host = gen.latents(wl, layer, b)
+    host = gen.latents(wl, layer, b) if host is None else np.asarray(host)
 
     def qa_fn(t):
         return gen.abs_query(wl, layer, t)[b]

@@ -6,6 +6,8 @@ from decode_lightning_indexer_amd import ess
 from decode_lightning_indexer_amd.runner import DecodeRunner
 from decode_lightning_indexer_amd.session import HostStore, dims_of
 from oracle import decode as odecode
+from oracle.formats import decode_entries
+from synth import gen
 from synth.device import LayerInputs
 
 DEV = "cuda"
@@ -65,17 +67,50 @@ def dims(**kw):
     return ess.make_dims(**base)
 
 
-def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None):
-    """Fill + steps on the GPU; per step and layer, every output as numpy."""
+def dequantized_latents(wl, layer):
+    """(entries [B][L][656], their dequantized latents [B][L][576] as bf16
+    bits) of a layer's generated latents."""
+    lat = np.empty((wl.batch, wl.ctx_len, 576), np.uint16)
+    gen.fill_latents(wl, layer, lat)
+    ent = gen.encode_entries(lat.reshape(-1, 576))
+    eff = gen.f32_to_bf16_bits(decode_entries(ent).astype(np.float32))
+    return ent.reshape(wl.batch, wl.ctx_len, 656), eff.reshape(lat.shape)
+
+
+def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None,
+                 store="bf16"):
+    """Fill + steps on the GPU; per step and layer, every output as numpy.
+    store: "bf16" (generated latents as bf16 rows), "entries" (656-byte fp8
+    entries of them) or "dequantized" (bf16 rows of the dequantized
+    entries)."""
     steps = wl.steps if steps is None else steps
     layers = wl.layers if layers is None else layers
     d = dims_of(wl)
     B, m, k, C = wl.batch, wl.mtp, wl.topk, wl.pool_slots
-    hosts = [HostStore((B, wl.ctx_len, 576)) for _ in range(layers)]
     ins = [LayerInputs(wl, l) for l in range(layers)]
-    run = DecodeRunner(d, hosts)
+    hosts, entries, rows = [], [], []
     for l in range(layers):
-        ins[l].upload_static(run.layers[l], hosts[l].array)
+        if store == "bf16":
+            hosts.append(HostStore((B, wl.ctx_len, 576)))
+            entries.append(None)
+            continue
+        ent, eff = dequantized_latents(wl, l)
+        rows.append(eff)
+        if store == "entries":
+            hosts.append(None)
+            entries.append(HostStore((B, wl.ctx_len, 656), np.uint8))
+            entries[-1].array[:] = ent
+        else:
+            hosts.append(HostStore((B, wl.ctx_len, 576)))
+            hosts[-1].array[:] = eff
+            entries.append(None)
+    run = DecodeRunner(d, hosts, entries=entries)
+    for l in range(layers):
+        if store == "bf16":
+            ins[l].upload_static(run.layers[l], hosts[l].array)
+            rows.append(hosts[l].array)
+        else:
+            ins[l].upload_static(run.layers[l], None, latents=False)
     run.set_n_vis(ins[0].n_vis)
     run.reset()
     for l in range(layers):
@@ -106,18 +141,23 @@ def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None):
         cs, pool = h(lb.cache_slots), h(lb.pool)
         for b in range(B):
             res = np.nonzero(cs[b] >= 0)[0]
-            assert np.array_equal(pool[b, cs[b, res]], hosts[l].array[b, res]), (l, b)
-    for hst in hosts:
-        hst.free()
+            assert np.array_equal(pool[b, cs[b, res]], rows[l][b, res]), (l, b)
+    for hst in hosts + entries:
+        if hst is not None:
+            hst.free()
     return recs
 
 
-def compare_with_oracle(wl, recs, layer=0, requests=None, steps=None):
+def compare_with_oracle(wl, recs, layer=0, requests=None, steps=None,
+                        host=None):
+    """host: the layer's latents [B][L][576] when they are not the generated
+    ones (a store of fp8 entries: their dequantized rows)."""
     requests = range(wl.batch) if requests is None else requests
     steps = len(recs["steps"]) if steps is None else steps
     worst = 0.0
     for b in requests:
-        it = odecode.run_workload_request(wl, layer, b, steps=steps)
+        it = odecode.run_workload_request(
+            wl, layer, b, steps=steps, host=None if host is None else host[b])
         fill = next(it)
         g = recs["fill"][layer]
         n = int(g["n_miss"][b])

@@ -145,3 +145,19 @@ def test_prefill_argument_checks(L):
     assert "not loaded" in L.ess_last_error().decode()
     assert ess.ess_prefill_ws_bytes(0) == 0
     assert ess.ess_prefill_ws_bytes(512) == 576 * 4 and ess.ess_prefill_ws_bytes(513) == 2 * 576 * 4
+
+
+def test_entry_copy_argument_checks(L):
+    d = _d()
+    st = lambda *a: _status(lambda: ess.ess_miss_copy_entries(*a, stream=0))
+    assert st(d, 0, P, P, P, P, P) == "invalid argument"          # list_stride
+    assert st(d, 8, P, P, P, 0, P) == "invalid argument"          # no entries
+    assert st(d, 8, P, P, P, P + 8, P) == "invalid argument"      # misaligned
+    assert st(_d(lat_dim=512), 8, P, P, P, P, P) == "unsupported shape"
+    # A layer with neither a bf16 store nor entries, and one whose entries
+    # are misaligned, are rejected by the whole step.
+    none = ess.ess_layer_io(*([P] * 4 + [0] + [P] * 17), 1 << 30, None)
+    mis = ess.ess_layer_io(*([P] * 4 + [0] + [P] * 17), 1 << 30, P + 8)
+    for io in (none, mis):
+        assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
+                                                   stream=0, side=1)) == "invalid argument"
