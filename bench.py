@@ -155,8 +155,12 @@ def trace_summary(path, steps, warmup):
         if m:
             ln = int(m.group(1))
             base = n[m.end():m.end() + ln]
-            t = re.match(r"IL[ib](\d+)EE", n[m.end() + ln:])
-            return base + (f"<{t.group(1)}>" if t else "")
+            t = re.match(r"I((?:L[ib]\d+E)+)E", n[m.end() + ln:])
+            if not t:
+                return base
+            args = [("false", "true")[int(v)] if k == "b" else v
+                    for k, v in re.findall(r"L([ib])(\d+)E", t.group(1))]
+            return base + "<" + ", ".join(args) + ">"
         n = n.replace("ess::(anonymous namespace)::", "").replace("void ", "")
         return n.split("(")[0]
     starts = [d["t0"] for d in ds if short(d["name"]).startswith("index_scores_kernel")]
@@ -217,6 +221,8 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
     from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
     from synth import gen, get_workload
 
+    from concurrent.futures import ThreadPoolExecutor
+
     dev = "cuda"
     wl = get_workload(name).with_(steps=W + K)
     d = dims_of(wl)
@@ -227,8 +233,11 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
     for l in range(n_layers):
         if store == "entries":
             h = HostStore((B, L, 656), np.uint8)
-            for b in range(B):
+
+            def enc(b, h=h, l=l):
                 h.array[b] = gen.encode_entries(gen.latents(wl, l, b))
+            with ThreadPoolExecutor(max_workers=8) as ex:
+                list(ex.map(enc, range(B)))
             lb = LayerBuffers(d, None, entries=h)
         else:
             h = HostStore((B, L, 576))
@@ -595,7 +604,7 @@ def main():
         import torch
         torch.cuda.set_device(0)
         fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves,
-              "fp8_entries": fp8_entries}
+              "fp8_entries": lambda a: fp8_entries(a, (a.workload,))}
         print(json.dumps({args.extra_only: fn[args.extra_only](args)}), flush=True)
         return 0
     if args.gpus != 1:
