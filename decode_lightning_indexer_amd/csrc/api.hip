@@ -1,6 +1,7 @@
 // C ABI of the sparse-decode library: host-side checks, launch dispatch and
 // the whole-step orchestration.  Every check happens before anything is
 // enqueued, so a nonzero status means the stream is untouched.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -353,6 +354,9 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
   if (io.host_entries && (reinterpret_cast<uintptr_t>(io.host_entries) & 15))
     return fail(ESS_ERR_INVALID, "%s: layer %d host_entries must be 16-byte aligned",
                 fn, l);
+  if (io.tail_rows && (io.tail_block < 1 || io.tail_start < 0))
+    return fail(ESS_ERR_INVALID, "%s: layer %d tail_block must be >= 1 and tail_start >= 0",
+                fn, l);
   if (io.ws && (reinterpret_cast<uintptr_t>(io.ws) & 15))
     return fail(ESS_ERR_INVALID, "%s: layer %d workspace must be 16-byte aligned",
                 fn, l);
@@ -393,10 +397,13 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
 // under the attention's own work.
 static hipError_t enqueue_attention(const ess_dims& d, const ess_layer_io& io,
                                     hipStream_t st) {
+  const ess::TailView tail{io.tail_rows, io.tail_start,
+                          io.tail_rows ? io.tail_block : 1};
   return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
                                 io.row_dst, io.n_sel, io.pool,
                                 io.host_entries ? nullptr : io.host_view,
-                                io.out, io.lse, io.ws, st, 0, io.host_entries);
+                                io.out, io.lse, io.ws, st, 0, io.host_entries,
+                                tail);
 }
 
 ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
@@ -482,6 +489,101 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     if (e == hipSuccess) e = enqueue_attention(*d, io, stream);
   }
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_tail_init(ess_tail* t, uint16_t* rows, int32_t block,
+                         int32_t n_ctx) {
+  const char* fn = "ess_tail_init";
+  ESS_NONNULL(t);
+  ESS_NONNULL(rows);
+  if (block < 1 || n_ctx < 0)
+    return fail(ESS_ERR_INVALID, "%s: block must be >= 1 and n_ctx >= 0", fn);
+  t->rows = rows;
+  t->block = block;
+  t->first = n_ctx;
+  t->n_ctx = n_ctx;
+  t->start = n_ctx;
+  t->events[0] = t->events[1] = nullptr;
+  for (int i = 0; i < 2; ++i) {
+    hipEvent_t e;
+    const hipError_t he = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (he != hipSuccess) {
+      ess_tail_release(t);
+      return hip_fail(he, fn);
+    }
+    t->events[i] = e;
+  }
+  return ESS_OK;
+}
+
+ess_status ess_tail_release(ess_tail* t) {
+  if (!t) return ESS_OK;
+  for (int i = 0; i < 2; ++i) {
+    if (t->events[i]) hipEventDestroy(static_cast<hipEvent_t>(t->events[i]));
+    t->events[i] = nullptr;
+  }
+  return ESS_OK;
+}
+
+ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
+                             const uint8_t* new_keys, const uint16_t* new_lat,
+                             uint8_t* k_idx, int32_t* n_vis, uint16_t* host_kv,
+                             hipStream_t stream, hipStream_t d2h) {
+  const char* fn = "ess_append_tokens";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_indexer(d, fn)) != ESS_OK) return s;
+  ESS_NONNULL(t);
+  ESS_NONNULL(new_keys);
+  ESS_NONNULL(new_lat);
+  ESS_NONNULL(k_idx);
+  ESS_NONNULL(n_vis);
+  ESS_NONNULL(host_kv);
+  if (!t->rows || !t->events[0] || !t->events[1])
+    return fail(ESS_ERR_INVALID, "%s: tail is not initialised (ess_tail_init)", fn);
+  if (stream == d2h)
+    return fail(ESS_ERR_INVALID, "%s: the write-back needs a stream of its own", fn);
+  const int m = d->mtp, B = d->batch, L = d->ctx_len, blk = t->block;
+  if (blk < m)
+    return fail(ESS_ERR_UNSUPPORTED, "%s: tail block of %d tokens < mtp %d", fn, blk, m);
+  const int n0 = t->n_ctx, n1 = n0 + m;
+  if (n1 > L)
+    return fail(ESS_ERR_INVALID, "%s: context of %d + %d tokens exceeds ctx_len %d",
+                fn, n0, m, L);
+  hipEvent_t* ev;
+  if ((s = get_events(1, &ev)) != ESS_OK) return s;
+  hipError_t e = hipSuccess;
+  // A block's buffer last held the block two before it: that block's
+  // write-back must finish before its rows are overwritten.
+  for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c)
+    if (c * blk >= n0 && c >= 2 && (c - 1) * blk - 1 >= t->first)
+      e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(t->events[c & 1]), 0);
+  if (e == hipSuccess)
+    e = ess::launch_append_tokens(*d, m, n0, blk, new_keys, new_lat, k_idx,
+                                  t->rows, n_vis, stream);
+  // Blocks filled by this append go back to the host store on d2h.
+  bool recorded = false;
+  for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c) {
+    const int last = (c + 1) * blk - 1;
+    if (last < n0 || last >= n1) continue;
+    if (!recorded) {
+      e = hipEventRecord(ev[0], stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(d2h, ev[0], 0);
+      recorded = true;
+    }
+    const int p0 = std::max(t->first, c * blk);
+    const size_t bytes = (size_t)(last + 1 - p0) * ess::kLat * sizeof(uint16_t);
+    for (int b = 0; b < B && e == hipSuccess; ++b)
+      e = hipMemcpyAsync(host_kv + ((size_t)b * L + p0) * ess::kLat,
+                         t->rows + ((size_t)b * 2 * blk + (c & 1) * blk + p0 % blk) * ess::kLat,
+                         bytes, hipMemcpyDeviceToHost, d2h);
+    if (e == hipSuccess)
+      e = hipEventRecord(static_cast<hipEvent_t>(t->events[c & 1]), d2h);
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  t->n_ctx = n1;
+  t->start = std::max(t->first, ((n1 - 1) / blk - 1) * blk);
+  return ESS_OK;
 }
 
 size_t ess_prefill_ws_bytes(int32_t rows) {

@@ -92,13 +92,23 @@ struct MlaPlan {
 // target_wgs: workgroups to aim for (0: the whole chip, one per CU).
 MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs = 0);
 size_t sparse_mla_ws_bytes(const ess_dims& d, int target_wgs = 0);
+// Device tail blocks of growing context: rows [B][2 * block][576] bf16;
+// position p >= start is held in row ((p / block) & 1) * block + p % block.
+// rows == nullptr: no tail.
+struct TailView {
+  const uint16_t* rows;
+  int start;
+  int block;
+};
+
 hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              const int32_t* sel_pos, const int32_t* sel_src,
                              const int32_t* row_dst, const int32_t* n_sel,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
                              hipStream_t s, int target_wgs = 0,
-                             const uint8_t* entries = nullptr);
+                             const uint8_t* entries = nullptr,
+                             TailView tail = TailView{nullptr, 0, 1});
 // (entries non-null: misses are read from 656-byte fp8 entries [B][L][656]
 // instead of host, and dequantized in the tile.)
 
@@ -112,6 +122,15 @@ hipError_t launch_entry_copy(const ess_dims& d, int list_stride,
                              const int32_t* miss_pos, const int32_t* miss_slot,
                              const int32_t* n_miss, const uint8_t* host,
                              uint16_t* pool, hipStream_t s);
+
+// ---- growing context ----------------------------------------------------
+// Append n_new tokens at positions n_ctx.. of every request: keys into k_idx
+// [B][L][d_I], latents into the tail rows [B][2*block][576], n_vis [B][m] =
+// n_ctx + 1 + j.
+hipError_t launch_append_tokens(const ess_dims& d, int n_new, int n_ctx,
+                                int block, const uint8_t* new_keys,
+                                const uint16_t* new_lat, uint8_t* k_idx,
+                                uint16_t* tail, int32_t* n_vis, hipStream_t s);
 
 // ---- prefill pipeline ---------------------------------------------------
 // Per-block partial sums of the stand-in layer compute for `rows` rows.

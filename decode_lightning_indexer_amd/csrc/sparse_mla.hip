@@ -51,6 +51,11 @@
 // of the PV operand, so P never leaves registers.
 // Softmax runs in the log2 domain with a running max and sum per head.
 //
+// With growing context the newest positions sit in two tail blocks in device
+// memory until written back to the host store; a selected position from
+// tail.start on is loaded from its tail row like a pool row (and, as a miss
+// with a writer slot, still written to that slot from the tile).
+//
 // With a host store of 656-byte fp8 entries (c_KV in e4m3 with one
 // power-of-two scale per 128 values, k_R in bf16) a miss crosses the host
 // link as its 656 bytes instead of a 1152-byte row: the load puts the raw
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ host, const unsigned char* __restrict__ entries,
-    _Float16* __restrict__ part_acc,
+    TailView tail, _Float16* __restrict__ part_acc,
     float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
@@ -185,6 +190,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   // Misses come from bf16 rows (host) or, with kEnt, from fp8 entries.
   const uint16_t* host_b = kEnt ? nullptr : host + (size_t)b * L * kLat;
   const unsigned char* ent_b = kEnt ? entries + (size_t)b * L * kEntryBytes : nullptr;
+  // Positions from tail.start on are read from the request's two tail blocks
+  // in device memory (row code C + tail row) instead of host memory.
+  const uint16_t* tail_b = tail.rows ? tail.rows + (size_t)b * 2 * tail.block * kLat : nullptr;
 
   // Row sources of the chunk, once: hits read their slot, misses host
   // memory.  Given writer slots, the first head group stores each
@@ -204,7 +212,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       if (src >= 0) {
         if (src < C) cd = src;
       } else if (pos >= 0 && pos < L) {
-        cd = ~pos;
+        cd = tail_b && pos >= tail.start
+                 ? C + ((pos / tail.block) & 1) * tail.block + pos % tail.block
+                 : ~pos;
         if (writer_wg && dst >= 0 && dst < C) {
           wdst[i - r0] = dst;
           wr = true;
@@ -274,14 +284,16 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
           const int pe = cd < 0 ? ~cd : 0;
           const void* src =
               !use ? (const void*)(g_zero_row + off)
+              : cd >= C ? (const void*)(tail_b + (size_t)(cd - C) * kLat + off)
               : cd >= 0 ? (const void*)(pool_b + (size_t)cd * kLat + off)
               : piece >= kRawSlot0
                   ? (const void*)(ent_b + (size_t)pe * kEntryBytes + (piece - kRawSlot0) * 16)
                   : (const void*)g_zero_row;
           load_lds16(src, buf + (size_t)j * 64 * 8);
         } else {
-          const uint16_t* rowp = cd >= 0 ? pool_b + (size_t)cd * kLat
-                                         : host_b + (size_t)(~cd) * kLat;
+          const uint16_t* rowp = cd >= C ? tail_b + (size_t)(cd - C) * kLat
+                                 : cd >= 0 ? pool_b + (size_t)cd * kLat
+                                           : host_b + (size_t)(~cd) * kLat;
           load_lds16((use ? rowp : g_zero_row) + off, buf + (size_t)j * 64 * 8);
         }
       }
@@ -543,8 +555,8 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
                     uint16_t* pool, const uint16_t* host,
-                    const unsigned char* entries, _Float16* part_acc,
-                    float2* part_ml, hipStream_t s) {
+                    const unsigned char* entries, TailView tail,
+                    _Float16* part_acc, float2* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
   hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS, kEnt>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -555,7 +567,7 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
   const int rounds = ((groups + 7) / 8) * d.mtp * p.head_groups;
   dim3 grid(rounds * 8);
   hipLaunchKernelGGL((sparse_mla_kernel<WPS, kEnt>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
-                     sel_pos, sel_src, row_dst, n_sel, pool, host, entries, part_acc,
+                     sel_pos, sel_src, row_dst, n_sel, pool, host, entries, tail, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
                      d.batch * d.mtp, scale_log2);
@@ -599,7 +611,7 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              uint16_t* pool, const uint16_t* host,
                              float* out, float* lse, void* ws,
                              hipStream_t s, int target_wgs,
-                             const uint8_t* entries) {
+                             const uint8_t* entries, TailView tail) {
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   _Float16* part_acc = static_cast<_Float16*>(ws);
@@ -608,9 +620,9 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
   hipError_t e;
 #define ESS_MLA_CASE(W)                                                        \
   e = entries ? launch_t<W, true>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel,  \
-                                  pool, host, entries, part_acc, part_ml, s)      \
+                                  pool, host, entries, tail, part_acc, part_ml, s) \
               : launch_t<W, false>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, \
-                                   pool, host, nullptr, part_acc, part_ml, s)
+                                   pool, host, nullptr, tail, part_acc, part_ml, s)
   switch (p.heads_per_wg / 16) {
     case 1: ESS_MLA_CASE(1); break;
     case 2: ESS_MLA_CASE(2); break;

@@ -32,6 +32,7 @@ EXPORTED = (
     "ess_miss_copy_entries",
     "ess_decode_step",
     "ess_host_alloc", "ess_host_free", "ess_replay_evictions",
+    "ess_tail_init", "ess_tail_release", "ess_append_tokens",
     "ess_prefill_ws_bytes", "ess_prefill_layers",
     "ess_status_string", "ess_last_error",
 )
@@ -63,7 +64,13 @@ class ess_layer_io(ctypes.Structure):
         "cache_slots", "slot_pos", "lru_state", "scores", "sel_pos",
         "sel_slot", "n_sel", "row_dst", "sel_slot_post", "miss_pos",
         "miss_slot", "n_miss", "n_evict", "out", "lse", "ws")] + [
-        ("ws_bytes", _S), ("host_entries", _P)]
+        ("ws_bytes", _S), ("host_entries", _P), ("tail_rows", _P),
+        ("tail_start", _I), ("tail_block", _I)]
+
+
+class ess_tail(ctypes.Structure):
+    _fields_ = [("rows", _P), ("block", _I), ("first", _I), ("n_ctx", _I),
+                ("start", _I), ("events", _P * 2)]
 
 
 _lib = None
@@ -96,6 +103,10 @@ def lib():
             "ess_decode_step": (_I, [D, _I, ctypes.POINTER(ess_layer_io), _P,
                                      _I, _P, _P]),
             "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+            "ess_tail_init": (_I, [ctypes.POINTER(ess_tail), _P, _I, _I]),
+            "ess_tail_release": (_I, [ctypes.POINTER(ess_tail)]),
+            "ess_append_tokens": (_I, [D, ctypes.POINTER(ess_tail), _P, _P, _P, _P,
+                                       _P, _P, _P]),
             "ess_host_free": (_I, [_P]),
             "ess_replay_evictions": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P,
                                           ctypes.c_uint64, _I, _P, _P]),
@@ -219,6 +230,26 @@ def ess_decode_step(d, layers, n_vis, mode, stream=None, side=None):
     _check("ess_decode_step", lib().ess_decode_step(
         ctypes.byref(d), len(layers), arr, _ptr(n_vis), mode,
         _stream(stream), _stream(side) if side is not None else None))
+
+
+def ess_tail_init(rows, block, n_ctx):
+    """A new ess_tail over the device tail rows [B][2*block][576]."""
+    t = ess_tail()
+    _check("ess_tail_init", lib().ess_tail_init(ctypes.byref(t), _ptr(rows), block, n_ctx))
+    return t
+
+
+def ess_tail_release(t):
+    _check("ess_tail_release", lib().ess_tail_release(ctypes.byref(t)))
+
+
+def ess_append_tokens(d, t, new_keys, new_lat, k_idx, n_vis, host_kv, stream=None,
+                      d2h=None):
+    """host_kv: the host store's CPU address (HostStore.host)."""
+    _check("ess_append_tokens", lib().ess_append_tokens(
+        ctypes.byref(d), ctypes.byref(t), _ptr(new_keys), _ptr(new_lat),
+        _ptr(k_idx), _ptr(n_vis), _ptr(host_kv), _stream(stream),
+        _stream(d2h) if d2h is not None else None))
 
 
 def ess_host_alloc(nbytes: int):

@@ -277,6 +277,12 @@ typedef struct ess_layer_io {
                                    dequantizes them in its tile
                                    (ess_sparse_mla_decode_entries), the
                                    fill copies with ess_miss_copy_entries. */
+  const uint16_t* tail_rows;  /* growing context: the tail blocks
+                                 (ess_tail.rows) or NULL */
+  int32_t tail_start;         /* ess_tail.start after the step's append:
+                                 positions from here on are read from
+                                 tail_rows instead of host memory */
+  int32_t tail_block;         /* ess_tail.block */
 } ess_layer_io;
 
 enum {
@@ -302,6 +308,52 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
                            const ess_layer_io* layers, const int32_t* n_vis,
                            int32_t mode, hipStream_t stream,
                            hipStream_t side);
+
+/* Growing context (FlashOffloading analysis, architecture section and
+ * Fig. 2: beside the C-slot hot cache the decode side keeps two tail blocks
+ * of new KV; host memory holds the authoritative copy, written back by
+ * block).  Each step appends its m tokens: their index keys go to the
+ * resident index cache and their latents to the open tail block in device
+ * memory.  When a block fills it is copied to the host store on a stream of
+ * its own; its rows stay readable from the tail until the block after next
+ * reuses its buffer, which first waits for that copy.  The pool's residency
+ * rules do not change: a selected position from `start` on that misses the
+ * pool is read from its tail row (device memory) instead of host memory,
+ * and written to its slot as any miss.
+ *
+ * State of one layer's tail: rows [B][2*block][576] bf16 device memory
+ * (caller-owned); position p >= start lives in row ((p / block) % 2) * block
+ * + p % block of its request.  first = the context length the tail started
+ * at (positions below it are already in the host store); n_ctx = current
+ * length; events: owned by the library between ess_tail_init and
+ * ess_tail_release. */
+typedef struct ess_tail {
+  uint16_t* rows;
+  int32_t block, first, n_ctx, start;
+  void* events[2];
+} ess_tail;
+
+/* Start a tail at context length n_ctx (block >= 1 tokens per tail block).
+ * Creates the two write-back events; ESS_ERR_HIP if that fails. */
+ess_status ess_tail_init(ess_tail* t, uint16_t* rows, int32_t block,
+                         int32_t n_ctx);
+/* Destroy the tail's events (its copies must have completed). */
+ess_status ess_tail_release(ess_tail* t);
+
+/* Append the step's m = d->mtp tokens of every request at positions
+ * t->n_ctx .. t->n_ctx + m - 1:
+ *   k_idx[b][n_ctx + j] = new_keys[b][j]      ([B][m][d_I] fp8 -> [B][L][d_I])
+ *   tail row of n_ctx + j = new_lat[b][j]     ([B][m][576] bf16)
+ *   n_vis[b][j] = n_ctx + 1 + j               (token j sees up to itself)
+ * on `stream`; every tail block this fills is copied to
+ * host_kv[b][p] (the host store's CPU address, [B][L][576]) for its
+ * positions p >= first, on `d2h` (a different stream).  Then t->n_ctx += m
+ * and t->start = max(first, start of the block before the newest one).
+ * Requires m <= block and n_ctx + m <= ctx_len. */
+ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
+                             const uint8_t* new_keys, const uint16_t* new_lat,
+                             uint8_t* k_idx, int32_t* n_vis, uint16_t* host_kv,
+                             hipStream_t stream, hipStream_t d2h);
 
 /* Pinned host memory mapped into the device address space (write-combined
  * off; coarse-grained).  *host_ptr is the CPU address, *dev_view the address

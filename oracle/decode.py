@@ -24,7 +24,7 @@ from .topk import topk_lookup, topk_positions
 
 def run_request(keys, q_steps, w, n_vis, qa_fn, host, *, steps, topk,
                 pool_slots, scale, v_dim=512, keep_scores=False,
-                check_pool=True):
+                check_pool=True, n_vis_fn=None):
     """Generator over the fill and the steps of one request.
 
     keys:    uint8 [L][d_I]            fp8 index keys
@@ -33,6 +33,11 @@ def run_request(keys, q_steps, w, n_vis, qa_fn, host, *, steps, topk,
     n_vis:   int [m]
     qa_fn:   t -> uint16 [m][H][D]     absorbed queries of step t (bf16 bits)
     host:    uint16 [L][D]             host latents (bf16 bits)
+    n_vis_fn: t -> int [m], the visible lengths of step t when the context
+             grows (n_vis then serves the first fill only).  Growth changes
+             which positions can be selected, nothing else: the method's
+             results do not depend on where a latent is held (host store,
+             pool or a tail block), so the oracle reads every row from host.
 
     Yields first a dict for the fill, then one dict per step t.
     """
@@ -49,8 +54,9 @@ def run_request(keys, q_steps, w, n_vis, qa_fn, host, *, steps, topk,
     yield dict(kind="fill", fill_pos=fill_pos, **fill)
 
     for t in range(steps):
-        s = index_scores(q_steps[t], w, keys, n_vis)
-        sel_pos, sel_slot, n_sel = topk_lookup(s, n_vis, topk, pool.cache_slots)
+        nv = n_vis if n_vis_fn is None else np.asarray(n_vis_fn(t), np.int64)
+        s = index_scores(q_steps[t], w, keys, nv)
+        sel_pos, sel_slot, n_sel = topk_lookup(s, nv, topk, pool.cache_slots)
         resident_before = pool.resident()
         upd = pool.update(sel_pos, n_sel)
         rows[upd["miss_slot"]] = host[upd["miss_pos"]]
@@ -78,10 +84,14 @@ def run_request(keys, q_steps, w, n_vis, qa_fn, host, *, steps, topk,
         yield rec
 
 
-def run_workload_request(wl, layer: int, b: int, steps=None, host=None, **kw):
+def run_workload_request(wl, layer: int, b: int, steps=None, host=None,
+                         grow_from=None, **kw):
     """run_request on the seeded synthetic inputs of workload wl (host: the
     request's latents [L][576] in place of the generated ones, e.g. the
-    dequantized fp8 entries of a host store that holds entries)."""
+    dequantized fp8 entries of a host store that holds entries).  grow_from
+    = L0: the context starts at L0 positions (the fill sees the last m of
+    them as the query tokens) and every step appends its m tokens, so step t
+    token j sees n_vis = L0 + t*m + 1 + j."""
     from synth import gen
     steps = wl.steps if steps is None else steps
     keys = gen.index_keys(wl, layer, b)
@@ -89,6 +99,10 @@ def run_workload_request(wl, layer: int, b: int, steps=None, host=None, **kw):
                   for j in range(wl.mtp)], axis=1)          # [T][m][H_I][d]
     w = np.stack([gen.head_weights(wl, layer, b, j) for j in range(wl.mtp)])
     n_vis = np.array([wl.n_vis(j) for j in range(wl.mtp)], np.int64)
+    if grow_from is not None:
+        m = wl.mtp
+        n_vis = np.array([grow_from - m + 1 + j for j in range(m)], np.int64)
+        kw["n_vis_fn"] = lambda t: [grow_from + t * m + 1 + j for j in range(m)]
     host = gen.latents(wl, layer, b) if host is None else np.asarray(host)
 
     def qa_fn(t):

@@ -161,3 +161,23 @@ def test_entry_copy_argument_checks(L):
     for io in (none, mis):
         assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
                                                    stream=0, side=1)) == "invalid argument"
+
+
+def test_tail_argument_checks(L):
+    d = _d()
+    t = ess.ess_tail()
+    assert _status(lambda: ess.ess_tail_init(0, 8, 100)) == "invalid argument"      # no rows
+    assert _status(lambda: ess.ess_tail_init(P, 0, 100)) == "invalid argument"      # block 0
+    # Not initialised, same stream for the write-back, block below mtp.
+    st = lambda dd, tt, s1, s2: _status(lambda: ess.ess_append_tokens(
+        dd, tt, P, P, P, P, P, stream=s1, d2h=s2))
+    assert st(d, t, 1, 2) == "invalid argument"
+    t.rows, t.block, t.first, t.n_ctx, t.start = P, 8, 100, 100, 100
+    t.events[0] = t.events[1] = P
+    assert st(d, t, 3, 3) == "invalid argument"
+    assert st(_d(mtp=2, idx_heads=16), ess.ess_tail(P, 1, 10, 10, 10, (P, P)), 1, 2) == "unsupported shape"
+    t.n_ctx = 4096                                                                 # full
+    assert st(d, t, 1, 2) == "invalid argument"
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, 5, 0)                      # tail_block 0
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
+                                               stream=0, side=1)) == "invalid argument"

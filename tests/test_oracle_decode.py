@@ -85,3 +85,40 @@ def test_page_overlap_ratio():
     # Fully hidden copy gives 1, fully exposed gives 0.
     assert footprint.overlap_ratio(10, 50, 50) == 1.0
     assert footprint.overlap_ratio(10, 50, 60) == 0.0
+
+
+def _small_growth(steps=6):
+    wl = get_workload("tiny-4k").with_(name="grow", mtp=2, ctx_len=600,
+                                       topk=700, pool_slots=1400, steps=steps)
+    return wl, 600 - 2 * steps - 3
+
+
+def test_growth_dense_sees_each_new_token():
+    # k above every visible length: step t token j selects exactly the
+    # positions 0 .. L0 + 2t + j (its own included), so each appended
+    # token is selected from the step that appends it; the pool holds every
+    # position seen so far, and each step's misses are its two new tokens
+    # (the fill covered token 0's view of the first L0 positions).
+    wl, L0 = _small_growth()
+    it = decode.run_workload_request(wl, 0, 0, grow_from=L0)
+    fill = next(it)
+    assert fill["n_miss"] == L0 - 1
+    for t, rec in enumerate(it):
+        for j in range(2):
+            n = L0 + 2 * t + 1 + j
+            assert rec["n_sel"][j] == n
+            assert sorted(rec["sel_pos"][j, :n].tolist()) == list(range(n))
+        # Step 0 also brings in L0 - 1, which the fill's token 0 did not see.
+        expect = [L0 - 1, L0, L0 + 1] if t == 0 else [L0 + 2 * t, L0 + 2 * t + 1]
+        assert rec["miss_pos"].tolist() == expect
+
+
+def test_growth_with_fixed_lengths_is_the_static_run():
+    # n_vis_fn returning the static lengths every step changes nothing.
+    wl = get_workload("tiny-4k").with_(steps=3)
+    a = list(decode.run_workload_request(wl, 0, 0))
+    fixed = [wl.n_vis(j) for j in range(wl.mtp)]
+    b = list(decode.run_workload_request(wl, 0, 0, n_vis_fn=lambda t: fixed))
+    for ra, rb in zip(a[1:], b[1:]):
+        for key in ("sel_pos", "n_sel", "miss_pos", "out", "lse"):
+            assert np.array_equal(ra[key], rb[key]), key
