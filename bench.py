@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the 128K and multi-layer prefetch measurements")
     p.add_argument("--extra-only", choices=["prefill_pipeline", "eviction_replay",
-                                            "fp8_entries"],
+                                            "fp8_entries", "growing_context"],
                    help="only run one extra measurement and print its JSON (for "
                         "profiling it alone)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -384,6 +384,82 @@ def fp8_entries(args, names=("32k-b16", "128k-b8-mtp2-r099")):
     return out
 
 
+def growing_context(args, name="32k-b16", block=64, K=32, W=8):
+    """Whole steps with the context growing by one token per request per
+    step (ess_append_tokens before each ess_decode_step, tail blocks of
+    `block` tokens written back to the host store on their own stream),
+    against the same steps over a fixed context: the cost of the append
+    and of reading the newest positions from the tail."""
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
+    from synth import gen, get_workload
+
+    dev = "cuda"
+    wl = get_workload(name).with_(steps=W + K)
+    d = dims_of(wl)
+    B, m, L = wl.batch, wl.mtp, wl.ctx_len
+    L0 = L - (W + K) * m
+    host = HostStore((B, L, 576))
+    gen.fill_latents(wl, 0, host.array)
+    T = W + K
+    # New tokens per step as contiguous [B][m][...] blocks: [T][B][m][...].
+    lat_new = torch.from_numpy(np.ascontiguousarray(
+        host.array[:, L0:].reshape(B, T, m, 576).transpose(1, 0, 2, 3)).view(np.int16)).to(dev)
+    lb = LayerBuffers(d, host)
+    kb = np.empty((B, L, wl.idx_dim), np.uint8)
+    gen.fill_index_keys(wl, 0, kb)
+    keys_new = torch.from_numpy(np.ascontiguousarray(
+        kb[:, L0:].reshape(B, T, m, wl.idx_dim).transpose(1, 0, 2, 3))).to(dev)
+    lb.k_idx.copy_(torch.from_numpy(kb))
+    del kb
+    qi, qa, w, _ = staged_inputs(wl, 0, dev)
+    lb.w_idx.copy_(torch.from_numpy(w))
+    n_vis = torch.empty((B, m), dtype=torch.int32, device=dev)
+    rows = torch.empty((B, 2 * block, 576), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    side, d2h = torch.cuda.Stream(), torch.cuda.Stream()
+    out = {}
+    for grow in (False, True):
+        n_vis.copy_(torch.tensor([[L0 - m + 1 + j for j in range(m)]] * B, dtype=torch.int32))
+        lb.reset(stream)
+        io = lb.io()
+        io.q_idx, io.q_abs = qi[0].data_ptr(), qa[0].data_ptr()
+        ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_FILL, stream)
+        tail = ess.ess_tail_init(rows, block, L0)
+        if not grow:        # the fixed context: every step sees L0 + 1 positions
+            n_vis.copy_(torch.tensor([[L0 + 1 + j for j in range(m)]] * B, dtype=torch.int32))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        misses = 0
+        for t in range(W + K):
+            if t == W:
+                torch.cuda.synchronize()
+                ev[0].record(stream)
+            if grow:
+                ess.ess_append_tokens(d, tail, keys_new[t], lat_new[t], lb.k_idx, n_vis,
+                                      host.host, stream, d2h)
+            io = lb.io()
+            io.q_idx, io.q_abs = qi[t].data_ptr(), qa[t].data_ptr()
+            if grow:
+                io.tail_rows, io.tail_start, io.tail_block = rows.data_ptr(), tail.start, block
+            ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_INLINE, stream, side)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        misses = int(lb.n_miss.sum())
+        ess.ess_tail_release(tail)
+        t_step = ev[0].elapsed_time(ev[1]) * 1e-3 / K
+        out["growing" if grow else "fixed"] = {
+            "us_per_step": t_step * 1e6, "query_tok_s": B * m / t_step,
+            "misses_last_step": misses}
+    out["block"] = block
+    out["written_back_per_block_mb"] = B * block * 1152 / 1e6
+    out["context_start"] = L0
+    host.free()
+    log(args, f"growing context {name}: {out}")
+    return out
+
+
 def replay_curves(args, name="128k-b8-mtp2-r095", T=32,
                   capacities=(8192, 12288, 16384, 24576)):
     """The pages' offline eviction-policy comparison on traces of our own
@@ -604,7 +680,8 @@ def main():
         import torch
         torch.cuda.set_device(0)
         fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves,
-              "fp8_entries": lambda a: fp8_entries(a, (a.workload,))}
+              "fp8_entries": lambda a: fp8_entries(a, (a.workload,)),
+              "growing_context": lambda a: growing_context(a, a.workload)}
         print(json.dumps({args.extra_only: fn[args.extra_only](args)}), flush=True)
         return 0
     if args.gpus != 1:
@@ -874,6 +951,7 @@ def main():
         res["extra"]["eviction_replay"] = replay_curves(args)
         res["extra"]["prefill_pipeline"] = prefill_pipeline(args)
         res["extra"]["fp8_entries"] = fp8_entries(args)
+        res["extra"]["growing_context"] = growing_context(args)
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)

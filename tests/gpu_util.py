@@ -70,11 +70,17 @@ def dims(**kw):
 def dequantized_latents(wl, layer):
     """(entries [B][L][656], their dequantized latents [B][L][576] as bf16
     bits) of a layer's generated latents."""
-    lat = np.empty((wl.batch, wl.ctx_len, 576), np.uint16)
-    gen.fill_latents(wl, layer, lat)
-    ent = gen.encode_entries(lat.reshape(-1, 576))
-    eff = gen.f32_to_bf16_bits(decode_entries(ent).astype(np.float32))
-    return ent.reshape(wl.batch, wl.ctx_len, 656), eff.reshape(lat.shape)
+    from concurrent.futures import ThreadPoolExecutor
+    B, L = wl.batch, wl.ctx_len
+    ent = np.empty((B, L, 656), np.uint8)
+    eff = np.empty((B, L, 576), np.uint16)
+
+    def one(b):
+        ent[b] = gen.encode_entries(gen.latents(wl, layer, b))
+        eff[b] = gen.f32_to_bf16_bits(decode_entries(ent[b]).astype(np.float32))
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(one, range(B)))
+    return ent, eff
 
 
 def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None,

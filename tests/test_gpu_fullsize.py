@@ -62,3 +62,25 @@ def test_64k_b32_two_layers_prefetch_full_size():
     # positions each), in the side-stream prefetch mode.
     wl = get_workload("64k-b32-16layer").with_(steps=3)
     _check(wl, requests=[0, 31], mode=ess.ESS_MODE_PREFETCH, layers=2)
+
+
+def test_32k_b16_fp8_entries_full_size():
+    # The host store as 656-byte fp8 entries at full size: the oracle runs
+    # on the dequantized latents.
+    from tests.gpu_util import dequantized_latents
+    wl = get_workload("32k-b16").with_(steps=3)
+    print(f"\n[fullsize] {wl.name} fp8 entries", flush=True)
+    recs = gpu_sequence(wl, store="entries")
+    _, eff = dequantized_latents(wl, 0)
+    compare_with_oracle(wl, recs, requests=[0, 15], host=eff)
+
+
+def test_32k_b16_growing_context_full_size():
+    # Four steps of growth that cross a 64-token block boundary (a block
+    # written back mid-run), at the full 32K x 16 shape.
+    from tests.test_gpu_growth import _grow
+    wl = get_workload("32k-b16").with_(steps=4)
+    L0 = 32702
+    print(f"\n[fullsize] {wl.name} growing from {L0}", flush=True)
+    recs, _ = _grow(wl, L0, 64, ess.ESS_MODE_INLINE, 4)
+    compare_with_oracle(wl, recs, requests=[0, 15], grow_from=L0)
