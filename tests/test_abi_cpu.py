@@ -181,3 +181,9 @@ def test_tail_argument_checks(L):
     io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, 5, 0)                      # tail_block 0
     assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
                                                stream=0, side=1)) == "invalid argument"
+
+
+def test_tail_with_entry_store_is_unsupported(L):
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, P, P, 5, 16)
+    assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_INLINE,
+                                               stream=0, side=1)) == "unsupported shape"
