@@ -62,8 +62,8 @@ __global__ __launch_bounds__(NT) void miss_copy_kernel(
 // ---- 656-byte fp8 entries ------------------------------------------------
 // The copy reads each entry once from host memory into LDS and writes the
 // pool row as bf16 (c_KV dequantized with its block's scale, k_R as stored).
-constexpr int kEntriesPerIter = 24;                       // per workgroup pass
-constexpr int kEntryLoads = (kEntriesPerIter * kEntryPieces + NT - 1) / NT;   // 4
+constexpr int kEntriesPerIter = 48;                       // per workgroup pass
+constexpr int kEntryLoads = (kEntriesPerIter * kEntryPieces + NT - 1) / NT;   // 8
 
 __global__ __launch_bounds__(NT) void entry_copy_kernel(
     int list_stride, const int32_t* __restrict__ miss_pos,
