@@ -354,6 +354,10 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
   if (io.host_entries && (reinterpret_cast<uintptr_t>(io.host_entries) & 15))
     return fail(ESS_ERR_INVALID, "%s: layer %d host_entries must be 16-byte aligned",
                 fn, l);
+  if (io.tail_rows && mode == ESS_MODE_FILL)
+    return fail(ESS_ERR_INVALID,
+                "%s: layer %d: the first fill reads the host store and precedes the tail",
+                fn, l);
   if (io.tail_rows && io.host_entries)
     return fail(ESS_ERR_UNSUPPORTED,
                 "%s: layer %d: tail blocks write back bf16 rows, not fp8 entries", fn, l);

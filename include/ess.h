@@ -282,7 +282,9 @@ typedef struct ess_layer_io {
   int32_t tail_start;         /* ess_tail.start after the step's append:
                                  positions from here on are read from
                                  tail_rows instead of host memory */
-  int32_t tail_block;         /* ess_tail.block.  A tail needs the bf16
+  int32_t tail_block;         /* ess_tail.block.  ESS_MODE_FILL takes no
+                                 tail (it reads every row from the host
+                                 store).  A tail needs the bf16
                                  store (host_entries NULL): its blocks are
                                  written back as bf16 rows; with entries,
                                  ESS_ERR_UNSUPPORTED. */

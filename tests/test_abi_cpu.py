@@ -187,3 +187,9 @@ def test_tail_with_entry_store_is_unsupported(L):
     io = ess.ess_layer_io(*([P] * 22), 1 << 30, P, P, 5, 16)
     assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_INLINE,
                                                stream=0, side=1)) == "unsupported shape"
+
+
+def test_fill_takes_no_tail(L):
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, 5, 16)
+    assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_FILL,
+                                               stream=0, side=1)) == "invalid argument"
