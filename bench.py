@@ -454,6 +454,11 @@ def growing_context(args, name="32k-b16", block=64, K=32, W=8):
             "misses_last_step": misses}
     out["block"] = block
     out["written_back_per_block_mb"] = B * block * 1152 / 1e6
+    # Device-resident latent bytes of the layer against a fully resident
+    # cache: B (C + 2b) 1152 against B L 1152 (the K/V term of M_decode).
+    out["device_latent_mb"] = B * (wl.pool_slots + 2 * block) * 1152 / 1e6
+    out["full_resident_latent_mb"] = B * L * 1152 / 1e6
+    out["resident_fraction"] = (wl.pool_slots + 2 * block) / L
     out["context_start"] = L0
     host.free()
     log(args, f"growing context {name}: {out}")
