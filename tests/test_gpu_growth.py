@@ -20,69 +20,85 @@ pytestmark = pytest.mark.gpu
 NAN_BF16 = 0x7FC0
 
 
-def _grow(wl, L0, block, mode, steps):
+def _grow(wl, L0, block, mode, steps, layers=1):
     B, m, L, k = wl.batch, wl.mtp, wl.ctx_len, wl.topk
     d = dims_of(wl)
-    lat = np.empty((B, L, 576), np.uint16)
-    gen.fill_latents(wl, 0, lat)
-    keys = np.empty((B, L, wl.idx_dim), np.uint8)
-    gen.fill_index_keys(wl, 0, keys)
-    host = HostStore((B, L, 576))
-    host.array[:] = NAN_BF16
-    host.array[:, :L0] = lat[:, :L0]
-    run = DecodeRunner(d, [host])
-    lb = run.layers[0]
-    ins = LayerInputs(wl, 0)
-    ins.upload_static(lb, None, keys=False, latents=False)
-    k0 = np.zeros_like(keys)
-    k0[:, :L0] = keys[:, :L0]
-    lb.k_idx.copy_(torch.from_numpy(k0))
+    lats, keys, hosts = [], [], []
+    for l in range(layers):
+        lat = np.empty((B, L, 576), np.uint16)
+        gen.fill_latents(wl, l, lat)
+        kb = np.empty((B, L, wl.idx_dim), np.uint8)
+        gen.fill_index_keys(wl, l, kb)
+        host = HostStore((B, L, 576))
+        host.array[:] = NAN_BF16
+        host.array[:, :L0] = lat[:, :L0]
+        lats.append(lat); keys.append(kb); hosts.append(host)
+    run = DecodeRunner(d, hosts)
+    ins = [LayerInputs(wl, l) for l in range(layers)]
+    for l, lb in enumerate(run.layers):
+        ins[l].upload_static(lb, None, keys=False, latents=False)
+        k0 = np.zeros_like(keys[l])
+        k0[:, :L0] = keys[l][:, :L0]
+        lb.k_idx.copy_(torch.from_numpy(k0))
+        ins[l].upload_step(lb, 0)
     run.set_n_vis([[L0 - m + 1 + j for j in range(m)]] * B)
     run.reset()
-    ins.upload_step(lb, 0)
     run.fill()
     sync()
     recs = {"fill": [dict(n_miss=h(lb.n_miss), miss_pos=h(lb.lists(lb.miss_pos, wl.pool_slots)),
-                          miss_slot=h(lb.lists(lb.miss_slot, wl.pool_slots)))], "steps": []}
-    rows = torch.full((B, 2 * block, 576), NAN_BF16, dtype=torch.int16, device="cuda")
-    tail = ess.ess_tail_init(rows, block, L0)
+                          miss_slot=h(lb.lists(lb.miss_slot, wl.pool_slots)))
+                     for lb in run.layers], "steps": []}
     stream = torch.cuda.current_stream()
     d2h = torch.cuda.Stream()
-    new_keys = torch.from_numpy(np.ascontiguousarray(keys[:, L0:L0 + steps * m])).cuda()
-    new_lat = torch.from_numpy(np.ascontiguousarray(lat[:, L0:L0 + steps * m]).view(np.int16)).cuda()
+    rows, tails, new_keys, new_lat = [], [], [], []
+    for l in range(layers):
+        rows.append(torch.full((B, 2 * block, 576), NAN_BF16, dtype=torch.int16, device="cuda"))
+        tails.append(ess.ess_tail_init(rows[l], block, L0))
+        new_keys.append(torch.from_numpy(np.ascontiguousarray(keys[l][:, L0:L0 + steps * m])).cuda())
+        new_lat.append(torch.from_numpy(
+            np.ascontiguousarray(lats[l][:, L0:L0 + steps * m]).view(np.int16)).cuda())
+    # Every layer's n_vis is the same; each layer's append writes it again.
     from_tail = 0
     for t in range(steps):
-        ins.upload_step(lb, t)
-        ess.ess_append_tokens(d, tail, new_keys[:, t * m:(t + 1) * m].contiguous(),
-                              new_lat[:, t * m:(t + 1) * m].contiguous(), lb.k_idx,
-                              run.n_vis, host.host, stream, d2h)
-        io = lb.io()
-        io.tail_rows, io.tail_start, io.tail_block = rows.data_ptr(), tail.start, block
-        ess.ess_decode_step(d, [io], run.n_vis, mode, stream, run.side)
+        ios = []
+        for l, lb in enumerate(run.layers):
+            ins[l].upload_step(lb, t)
+            ess.ess_append_tokens(d, tails[l], new_keys[l][:, t * m:(t + 1) * m].contiguous(),
+                                  new_lat[l][:, t * m:(t + 1) * m].contiguous(), lb.k_idx,
+                                  run.n_vis, hosts[l].host, stream, d2h)
+            io = lb.io()
+            io.tail_rows, io.tail_start, io.tail_block = rows[l].data_ptr(), tails[l].start, block
+            ios.append(io)
+        ess.ess_decode_step(d, ios, run.n_vis, mode, stream, run.side)
         sync()
-        nm = h(lb.n_miss)
-        mp = h(lb.lists(lb.miss_pos, m * k))
-        from_tail += sum(int((mp[b, :nm[b]] >= tail.start).sum()) for b in range(B))
-        recs["steps"].append([dict(
-            sel_pos=h(lb.rows(lb.sel_pos, k, m)), sel_slot=h(lb.rows(lb.sel_slot, k, m)),
-            n_sel=h(lb.n_sel), row_dst=h(lb.rows(lb.row_dst, k, m)),
-            sel_slot_post=h(lb.rows(lb.sel_slot_post, k, m)),
-            miss_pos=mp, miss_slot=h(lb.lists(lb.miss_slot, m * k)),
-            n_miss=nm, n_evict=h(lb.n_evict), out=h(lb.out), lse=h(lb.lse))])
+        per = []
+        for l, lb in enumerate(run.layers):
+            nm = h(lb.n_miss)
+            mp = h(lb.lists(lb.miss_pos, m * k))
+            from_tail += sum(int((mp[b, :nm[b]] >= tails[l].start).sum()) for b in range(B))
+            per.append(dict(
+                sel_pos=h(lb.rows(lb.sel_pos, k, m)), sel_slot=h(lb.rows(lb.sel_slot, k, m)),
+                n_sel=h(lb.n_sel), row_dst=h(lb.rows(lb.row_dst, k, m)),
+                sel_slot_post=h(lb.rows(lb.sel_slot_post, k, m)),
+                miss_pos=mp, miss_slot=h(lb.lists(lb.miss_slot, m * k)),
+                n_miss=nm, n_evict=h(lb.n_evict), out=h(lb.out), lse=h(lb.lse)))
+        recs["steps"].append(per)
     torch.cuda.synchronize()
     n_ctx = L0 + steps * m
-    assert tail.n_ctx == n_ctx
-    # Written back: every full block from L0 on; beyond it the host store is untouched.
     done = (n_ctx // block) * block
-    assert np.array_equal(host.array[:, :done], lat[:, :done])
-    assert np.all(host.array[:, max(done, L0):] == NAN_BF16)
-    # Every resident slot holds its latent, wherever it came from.
-    cs, pool = h(lb.cache_slots), h(lb.pool)
-    for b in range(B):
-        res = np.nonzero(cs[b] >= 0)[0]
-        assert np.array_equal(pool[b, cs[b, res]], lat[b, res]), b
-    ess.ess_tail_release(tail)
-    host.free()
+    for l, lb in enumerate(run.layers):
+        assert tails[l].n_ctx == n_ctx
+        # Written back: every full block from L0 on; beyond it the host
+        # store is untouched.
+        assert np.array_equal(hosts[l].array[:, :done], lats[l][:, :done])
+        assert np.all(hosts[l].array[:, max(done, L0):] == NAN_BF16)
+        # Every resident slot holds its latent, wherever it came from.
+        cs, pool = h(lb.cache_slots), h(lb.pool)
+        for b in range(B):
+            res = np.nonzero(cs[b] >= 0)[0]
+            assert np.array_equal(pool[b, cs[b, res]], lats[l][b, res]), (l, b)
+        ess.ess_tail_release(tails[l])
+        hosts[l].free()
     return recs, from_tail
 
 
@@ -97,3 +113,18 @@ def test_growth_matches_oracle(mode, m, block):
     recs, from_tail = _grow(wl, L0, block, mode, steps)
     assert from_tail > 0               # some misses were served from the tail
     compare_with_oracle(wl, recs, grow_from=L0)
+
+
+def test_growth_two_layers_prefetch():
+    # Two layers, each with its own tail and host store, selected ahead on
+    # the side stream: every layer against the oracle.
+    steps, m, block = 12, 2, 8
+    wl = get_workload("tiny-4k").with_(name="grow2", batch=2, mtp=m, ctx_len=2048,
+                                       topk=256, pool_slots=1024, steps=steps, rho=0.9,
+                                       layers=2)
+    L0 = 2048 - steps * m - 3
+    print(f"growth two layers m={m} block={block} L0={L0}", flush=True)
+    recs, from_tail = _grow(wl, L0, block, ess.ESS_MODE_PREFETCH, steps, layers=2)
+    assert from_tail > 0
+    for layer in range(2):
+        compare_with_oracle(wl, recs, layer=layer, grow_from=L0)
