@@ -418,6 +418,7 @@ def growing_context(args, name="32k-b16", block=64, K=32, W=8):
     lb.w_idx.copy_(torch.from_numpy(w))
     n_vis = torch.empty((B, m), dtype=torch.int32, device=dev)
     rows = torch.empty((B, 2 * block, 576), dtype=torch.int16, device=dev)
+    state = torch.empty(3 * B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     side, d2h = torch.cuda.Stream(), torch.cuda.Stream()
     out = {}
@@ -427,7 +428,7 @@ def growing_context(args, name="32k-b16", block=64, K=32, W=8):
         io = lb.io()
         io.q_idx, io.q_abs = qi[0].data_ptr(), qa[0].data_ptr()
         ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_FILL, stream)
-        tail = ess.ess_tail_init(rows, block, L0)
+        tail = ess.ess_tail_init(d, rows, block, [L0] * B, state, stream)
         if not grow:        # the fixed context: every step sees L0 + 1 positions
             n_vis.copy_(torch.tensor([[L0 + 1 + j for j in range(m)]] * B, dtype=torch.int32))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -442,7 +443,7 @@ def growing_context(args, name="32k-b16", block=64, K=32, W=8):
             io = lb.io()
             io.q_idx, io.q_abs = qi[t].data_ptr(), qa[t].data_ptr()
             if grow:
-                io.tail_rows, io.tail_start, io.tail_block = rows.data_ptr(), tail.start, block
+                io.tail_rows, io.tail_start, io.tail_block = rows.data_ptr(), tail.start_dev, block
             ess.ess_decode_step(d, [io], n_vis, ess.ESS_MODE_INLINE, stream, side)
         ev[1].record(stream)
         torch.cuda.synchronize()

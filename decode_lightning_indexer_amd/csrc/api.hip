@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -361,8 +362,8 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
   if (io.tail_rows && io.host_entries)
     return fail(ESS_ERR_UNSUPPORTED,
                 "%s: layer %d: tail blocks write back bf16 rows, not fp8 entries", fn, l);
-  if (io.tail_rows && (io.tail_block < 1 || io.tail_start < 0))
-    return fail(ESS_ERR_INVALID, "%s: layer %d tail_block must be >= 1 and tail_start >= 0",
+  if (io.tail_rows && (io.tail_block < 1 || !io.tail_start))
+    return fail(ESS_ERR_INVALID, "%s: layer %d: tail_block must be >= 1 and tail_start set",
                 fn, l);
   if (io.ws && (reinterpret_cast<uintptr_t>(io.ws) & 15))
     return fail(ESS_ERR_INVALID, "%s: layer %d workspace must be 16-byte aligned",
@@ -404,7 +405,7 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
 // under the attention's own work.
 static hipError_t enqueue_attention(const ess_dims& d, const ess_layer_io& io,
                                     hipStream_t st) {
-  const ess::TailView tail{io.tail_rows, io.tail_start,
+  const ess::TailView tail{io.tail_rows, io.tail_rows ? io.tail_start : nullptr,
                           io.tail_rows ? io.tail_block : 1};
   return ess::launch_sparse_mla(d, io.q_abs, io.sel_pos, io.sel_slot,
                                 io.row_dst, io.n_sel, io.pool,
@@ -498,37 +499,69 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
 }
 
-ess_status ess_tail_init(ess_tail* t, uint16_t* rows, int32_t block,
-                         int32_t n_ctx) {
+ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
+                         int32_t block, const int32_t* n_ctx,
+                         int32_t* state_dev, hipStream_t stream) {
   const char* fn = "ess_tail_init";
   ESS_NONNULL(t);
+  t->rows = nullptr;
+  t->host = nullptr;
+  t->events = nullptr;
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
   ESS_NONNULL(rows);
-  if (block < 1 || n_ctx < 0)
-    return fail(ESS_ERR_INVALID, "%s: block must be >= 1 and n_ctx >= 0", fn);
+  ESS_NONNULL(n_ctx);
+  ESS_NONNULL(state_dev);
+  const int B = d->batch;
+  if (block < 1) return fail(ESS_ERR_INVALID, "%s: block must be >= 1", fn);
+  for (int b = 0; b < B; ++b)
+    if (n_ctx[b] < 1 || n_ctx[b] > d->ctx_len)
+      return fail(ESS_ERR_INVALID, "%s: n_ctx[%d] = %d outside [1, ctx_len]", fn, b,
+                  n_ctx[b]);
+  int32_t* host = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * 3 * B));
+  void** events = static_cast<void**>(std::calloc(2 * (size_t)B, sizeof(void*)));
+  if (!host || !events) {
+    std::free(host);
+    std::free(events);
+    return fail(ESS_ERR_NOMEM, "%s: host allocation failed", fn);
+  }
+  for (int b = 0; b < B; ++b) host[b] = host[B + b] = host[2 * B + b] = n_ctx[b];
   t->rows = rows;
   t->block = block;
-  t->first = n_ctx;
-  t->n_ctx = n_ctx;
-  t->start = n_ctx;
-  t->events[0] = t->events[1] = nullptr;
-  for (int i = 0; i < 2; ++i) {
-    hipEvent_t e;
-    const hipError_t he = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-    if (he != hipSuccess) {
-      ess_tail_release(t);
-      return hip_fail(he, fn);
-    }
-    t->events[i] = e;
+  t->batch = B;
+  t->host = host;
+  t->state_dev = state_dev;
+  t->events = events;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 2 * B && e == hipSuccess; ++i) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) events[i] = ev;
+  }
+  // The device copy of (first, n_ctx, start): the append kernel advances it,
+  // the attention reads start.  Copied from the library's host array, which
+  // stays alive until ess_tail_release, after a wait for the copy.
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(state_dev, host, sizeof(int32_t) * 3 * B,
+                       hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    ess_tail_release(t);
+    return hip_fail(e, fn);
   }
   return ESS_OK;
 }
 
 ess_status ess_tail_release(ess_tail* t) {
   if (!t) return ESS_OK;
-  for (int i = 0; i < 2; ++i) {
-    if (t->events[i]) hipEventDestroy(static_cast<hipEvent_t>(t->events[i]));
-    t->events[i] = nullptr;
-  }
+  if (t->events)
+    for (int i = 0; i < 2 * t->batch; ++i)
+      if (t->events[i]) hipEventDestroy(static_cast<hipEvent_t>(t->events[i]));
+  std::free(t->events);
+  std::free(t->host);
+  t->events = nullptr;
+  t->host = nullptr;
+  t->rows = nullptr;
   return ESS_OK;
 }
 
@@ -546,50 +579,64 @@ ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
   ESS_NONNULL(k_idx);
   ESS_NONNULL(n_vis);
   ESS_NONNULL(host_kv);
-  if (!t->rows || !t->events[0] || !t->events[1])
+  if (!t->rows || !t->host || !t->events || !t->state_dev)
     return fail(ESS_ERR_INVALID, "%s: tail is not initialised (ess_tail_init)", fn);
+  if (t->batch != d->batch)
+    return fail(ESS_ERR_INVALID, "%s: tail of %d requests, dims of %d", fn,
+                t->batch, d->batch);
   if (stream == d2h)
     return fail(ESS_ERR_INVALID, "%s: the write-back needs a stream of its own", fn);
   const int m = d->mtp, B = d->batch, L = d->ctx_len, blk = t->block;
   if (blk < m)
     return fail(ESS_ERR_UNSUPPORTED, "%s: tail block of %d tokens < mtp %d", fn, blk, m);
-  const int n0 = t->n_ctx, n1 = n0 + m;
-  if (n1 > L)
-    return fail(ESS_ERR_INVALID, "%s: context of %d + %d tokens exceeds ctx_len %d",
-                fn, n0, m, L);
+  int32_t* first = t->host;
+  int32_t* ctx = t->host + B;
+  int32_t* start = t->host + 2 * B;
+  for (int b = 0; b < B; ++b)
+    if (ctx[b] + m > L)
+      return fail(ESS_ERR_INVALID, "%s: request %d: context of %d + %d tokens exceeds ctx_len %d",
+                  fn, b, ctx[b], m, L);
   hipEvent_t* ev;
   if ((s = get_events(1, &ev)) != ESS_OK) return s;
   hipError_t e = hipSuccess;
   // A block's buffer last held the block two before it: that block's
   // write-back must finish before its rows are overwritten.
-  for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c)
-    if (c * blk >= n0 && c >= 2 && (c - 1) * blk - 1 >= t->first)
-      e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(t->events[c & 1]), 0);
+  for (int b = 0; b < B && e == hipSuccess; ++b) {
+    const int n0 = ctx[b], n1 = n0 + m;
+    for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c)
+      if (c * blk >= n0 && c >= 2 && (c - 1) * blk - 1 >= first[b])
+        e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(t->events[2 * b + (c & 1)]), 0);
+  }
   if (e == hipSuccess)
-    e = ess::launch_append_tokens(*d, m, n0, blk, new_keys, new_lat, k_idx,
-                                  t->rows, n_vis, stream);
+    e = ess::launch_append_tokens(*d, blk, new_keys, new_lat, k_idx, t->rows,
+                                  n_vis, t->state_dev, stream);
   // Blocks filled by this append go back to the host store on d2h.
   bool recorded = false;
-  for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c) {
-    const int last = (c + 1) * blk - 1;
-    if (last < n0 || last >= n1) continue;
-    if (!recorded) {
-      e = hipEventRecord(ev[0], stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(d2h, ev[0], 0);
-      recorded = true;
-    }
-    const int p0 = std::max(t->first, c * blk);
-    const size_t bytes = (size_t)(last + 1 - p0) * ess::kLat * sizeof(uint16_t);
-    for (int b = 0; b < B && e == hipSuccess; ++b)
+  for (int b = 0; b < B && e == hipSuccess; ++b) {
+    const int n0 = ctx[b], n1 = n0 + m;
+    for (int c = n0 / blk; c <= (n1 - 1) / blk && e == hipSuccess; ++c) {
+      const int last = (c + 1) * blk - 1;
+      if (last < n0 || last >= n1) continue;
+      if (!recorded) {
+        e = hipEventRecord(ev[0], stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(d2h, ev[0], 0);
+        recorded = true;
+        if (e != hipSuccess) break;
+      }
+      const int p0 = std::max(first[b], c * blk);
       e = hipMemcpyAsync(host_kv + ((size_t)b * L + p0) * ess::kLat,
                          t->rows + ((size_t)b * 2 * blk + (c & 1) * blk + p0 % blk) * ess::kLat,
-                         bytes, hipMemcpyDeviceToHost, d2h);
-    if (e == hipSuccess)
-      e = hipEventRecord(static_cast<hipEvent_t>(t->events[c & 1]), d2h);
+                         (size_t)(last + 1 - p0) * ess::kLat * sizeof(uint16_t),
+                         hipMemcpyDeviceToHost, d2h);
+      if (e == hipSuccess)
+        e = hipEventRecord(static_cast<hipEvent_t>(t->events[2 * b + (c & 1)]), d2h);
+    }
   }
   if (e != hipSuccess) return hip_fail(e, fn);
-  t->n_ctx = n1;
-  t->start = std::max(t->first, ((n1 - 1) / blk - 1) * blk);
+  for (int b = 0; b < B; ++b) {
+    ctx[b] += m;
+    start[b] = std::max(first[b], ((ctx[b] - 1) / blk - 1) * blk);
+  }
   return ESS_OK;
 }
 

@@ -93,11 +93,11 @@ struct MlaPlan {
 MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs = 0);
 size_t sparse_mla_ws_bytes(const ess_dims& d, int target_wgs = 0);
 // Device tail blocks of growing context: rows [B][2 * block][576] bf16;
-// position p >= start is held in row ((p / block) & 1) * block + p % block.
-// rows == nullptr: no tail.
+// position p >= start[b] of request b is held in row ((p / block) & 1) *
+// block + p % block.  rows == nullptr: no tail.
 struct TailView {
   const uint16_t* rows;
-  int start;
+  const int32_t* start;   // device [B]
   int block;
 };
 
@@ -108,7 +108,7 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                              float* out, float* lse, void* ws,
                              hipStream_t s, int target_wgs = 0,
                              const uint8_t* entries = nullptr,
-                             TailView tail = TailView{nullptr, 0, 1});
+                             TailView tail = TailView{nullptr, nullptr, 1});
 // (entries non-null: misses are read from 656-byte fp8 entries [B][L][656]
 // instead of host, and dequantized in the tile.)
 
@@ -124,13 +124,16 @@ hipError_t launch_entry_copy(const ess_dims& d, int list_stride,
                              uint16_t* pool, hipStream_t s);
 
 // ---- growing context ----------------------------------------------------
-// Append n_new tokens at positions n_ctx.. of every request: keys into k_idx
-// [B][L][d_I], latents into the tail rows [B][2*block][576], n_vis [B][m] =
-// n_ctx + 1 + j.
-hipError_t launch_append_tokens(const ess_dims& d, int n_new, int n_ctx,
-                                int block, const uint8_t* new_keys,
+// Append mtp tokens to every request b at positions state[B + b] ..: keys
+// into k_idx [B][L][d_I], latents into the tail rows [B][2*block][576],
+// n_vis [B][m] = n_ctx + 1 + j; then state[B + b] += m and state[2B + b] =
+// the new first tail position.  state = device (first[B], n_ctx[B],
+// start[B]).
+hipError_t launch_append_tokens(const ess_dims& d, int block,
+                                const uint8_t* new_keys,
                                 const uint16_t* new_lat, uint8_t* k_idx,
-                                uint16_t* tail, int32_t* n_vis, hipStream_t s);
+                                uint16_t* tail, int32_t* n_vis,
+                                int32_t* state, hipStream_t s);
 
 // ---- prefill pipeline ---------------------------------------------------
 // Per-block partial sums of the stand-in layer compute for `rows` rows.

@@ -52,9 +52,9 @@
 // Softmax runs in the log2 domain with a running max and sum per head.
 //
 // With growing context the newest positions sit in two tail blocks in device
-// memory until written back to the host store; a selected position from
-// tail.start on is loaded from its tail row like a pool row (and, as a miss
-// with a writer slot, still written to that slot from the tile).
+// memory until written back to the host store; a selected position from its
+// request's tail.start on is loaded from its tail row like a pool row (and,
+// as a miss with a writer slot, still written to that slot from the tile).
 //
 // With a host store of 656-byte fp8 entries (c_KV in e4m3 with one
 // power-of-two scale per 128 values, k_R in bf16) a miss crosses the host
@@ -190,9 +190,10 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   // Misses come from bf16 rows (host) or, with kEnt, from fp8 entries.
   const uint16_t* host_b = kEnt ? nullptr : host + (size_t)b * L * kLat;
   const unsigned char* ent_b = kEnt ? entries + (size_t)b * L * kEntryBytes : nullptr;
-  // Positions from tail.start on are read from the request's two tail blocks
+  // Positions from tail.start[b] on are read from the request's two tail blocks
   // in device memory (row code C + tail row) instead of host memory.
   const uint16_t* tail_b = tail.rows ? tail.rows + (size_t)b * 2 * tail.block * kLat : nullptr;
+  const int tail_start = tail.rows ? tail.start[b] : INT32_MAX;
 
   // Row sources of the chunk, once: hits read their slot, misses host
   // memory.  Given writer slots, the first head group stores each
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       if (src >= 0) {
         if (src < C) cd = src;
       } else if (pos >= 0 && pos < L) {
-        cd = tail_b && pos >= tail.start
+        cd = pos >= tail_start
                  ? C + ((pos / tail.block) & 1) * tail.block + pos % tail.block
                  : ~pos;
         if (writer_wg && dst >= 0 && dst < C) {

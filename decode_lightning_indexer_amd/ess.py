@@ -65,12 +65,36 @@ class ess_layer_io(ctypes.Structure):
         "sel_slot", "n_sel", "row_dst", "sel_slot_post", "miss_pos",
         "miss_slot", "n_miss", "n_evict", "out", "lse", "ws")] + [
         ("ws_bytes", _S), ("host_entries", _P), ("tail_rows", _P),
-        ("tail_start", _I), ("tail_block", _I)]
+        ("tail_start", _P), ("tail_block", _I)]
 
 
 class ess_tail(ctypes.Structure):
-    _fields_ = [("rows", _P), ("block", _I), ("first", _I), ("n_ctx", _I),
-                ("start", _I), ("events", _P * 2)]
+    _fields_ = [("rows", _P), ("block", _I), ("batch", _I),
+                ("host", ctypes.POINTER(ctypes.c_int32)), ("state_dev", _P),
+                ("events", _P)]
+
+    def _host(self, i):
+        B = self.batch
+        return [self.host[i * B + b] for b in range(B)]
+
+    @property
+    def first(self):
+        return self._host(0)
+
+    @property
+    def n_ctx(self):
+        return self._host(1)
+
+    @property
+    def start(self):
+        """Host copy of every request's first tail position."""
+        return self._host(2)
+
+    @property
+    def start_dev(self):
+        """Device address of the per-request start array (for
+        ess_layer_io.tail_start)."""
+        return self.state_dev + 2 * self.batch * 4
 
 
 _lib = None
@@ -103,7 +127,7 @@ def lib():
             "ess_decode_step": (_I, [D, _I, ctypes.POINTER(ess_layer_io), _P,
                                      _I, _P, _P]),
             "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
-            "ess_tail_init": (_I, [ctypes.POINTER(ess_tail), _P, _I, _I]),
+            "ess_tail_init": (_I, [ctypes.POINTER(ess_tail), D, _P, _I, _P, _P, _P]),
             "ess_tail_release": (_I, [ctypes.POINTER(ess_tail)]),
             "ess_append_tokens": (_I, [D, ctypes.POINTER(ess_tail), _P, _P, _P, _P,
                                        _P, _P, _P]),
@@ -232,10 +256,15 @@ def ess_decode_step(d, layers, n_vis, mode, stream=None, side=None):
         _stream(stream), _stream(side) if side is not None else None))
 
 
-def ess_tail_init(rows, block, n_ctx):
-    """A new ess_tail over the device tail rows [B][2*block][576]."""
+def ess_tail_init(d, rows, block, n_ctx, state_dev, stream=None):
+    """A new ess_tail over the device tail rows [B][2*block][576]; n_ctx:
+    every request's length (sequence of B ints); state_dev: device int32
+    [3*B]."""
     t = ess_tail()
-    _check("ess_tail_init", lib().ess_tail_init(ctypes.byref(t), _ptr(rows), block, n_ctx))
+    arr = (ctypes.c_int32 * d.batch)(*[int(x) for x in n_ctx])
+    _check("ess_tail_init", lib().ess_tail_init(
+        ctypes.byref(t), ctypes.byref(d), _ptr(rows), block, arr, _ptr(state_dev),
+        _stream(stream)))
     return t
 
 

@@ -279,9 +279,9 @@ typedef struct ess_layer_io {
                                    fill copies with ess_miss_copy_entries. */
   const uint16_t* tail_rows;  /* growing context: the tail blocks
                                  (ess_tail.rows) or NULL */
-  int32_t tail_start;         /* ess_tail.start after the step's append:
-                                 positions from here on are read from
-                                 tail_rows instead of host memory */
+  const int32_t* tail_start;  /* device [B]: ess_tail.state_dev + 2*B; a
+                                 request's positions from its start on are
+                                 read from tail_rows instead of host memory */
   int32_t tail_block;         /* ess_tail.block.  ESS_MODE_FILL takes no
                                  tail (it reads every row from the host
                                  store).  A tail needs the bf16
@@ -317,44 +317,57 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
 /* Growing context (FlashOffloading analysis, architecture section and
  * Fig. 2: beside the C-slot hot cache the decode side keeps two tail blocks
  * of new KV; host memory holds the authoritative copy, written back by
- * block).  Each step appends its m tokens: their index keys go to the
- * resident index cache and their latents to the open tail block in device
- * memory.  When a block fills it is copied to the host store on a stream of
- * its own; its rows stay readable from the tail until the block after next
- * reuses its buffer, which first waits for that copy.  The pool's residency
- * rules do not change: a selected position from `start` on that misses the
- * pool is read from its tail row (device memory) instead of host memory,
- * and written to its slot as any miss.
+ * block).  Each step appends every request's m tokens: their index keys go
+ * to the resident index cache and their latents to the request's open tail
+ * block in device memory.  When a block fills it is copied to the host store
+ * on a stream of its own; its rows stay readable from the tail until the
+ * block after next reuses its buffer, which first waits for that copy.  The
+ * pool's residency rules do not change: a selected position from the
+ * request's `start` on that misses the pool is read from its tail row
+ * (device memory) instead of host memory, and written to its slot as any
+ * miss.  Requests may be at different lengths.
  *
- * State of one layer's tail: rows [B][2*block][576] bf16 device memory
- * (caller-owned); position p >= start lives in row ((p / block) % 2) * block
- * + p % block of its request.  first = the context length the tail started
- * at (positions below it are already in the host store); n_ctx = current
- * length; events: owned by the library between ess_tail_init and
- * ess_tail_release. */
+ * State of one layer's tail (fields owned by the library between
+ * ess_tail_init and ess_tail_release):
+ *   rows      [B][2*block][576] bf16 device memory (caller-owned); position
+ *             p >= start[b] of request b lives in its row
+ *             ((p / block) % 2) * block + p % block
+ *   host      [3][B] int32 host copy of (first, n_ctx, start): first = the
+ *             length the tail started at (positions below it are already
+ *             in the host store), n_ctx = current length, start = first
+ *             position read from the tail
+ *   state_dev [3][B] int32 device memory (caller-owned): the same, kept
+ *             current on the stream by ess_append_tokens; the attention
+ *             reads start from it (ess_layer_io.tail_start = state_dev + 2B)
+ *   events    2B write-back events */
 typedef struct ess_tail {
   uint16_t* rows;
-  int32_t block, first, n_ctx, start;
-  void* events[2];
+  int32_t block, batch;
+  int32_t* host;
+  int32_t* state_dev;
+  void** events;
 } ess_tail;
 
-/* Start a tail at context length n_ctx (block >= 1 tokens per tail block).
- * Creates the two write-back events; ESS_ERR_HIP if that fails. */
-ess_status ess_tail_init(ess_tail* t, uint16_t* rows, int32_t block,
-                         int32_t n_ctx);
-/* Destroy the tail's events (its copies must have completed). */
+/* Start a tail for d->batch requests at lengths n_ctx[B] (host array, each
+ * in [1, ctx_len]) with blocks of `block` >= 1 tokens.  Allocates the host
+ * arrays and creates the events; writes state_dev and waits for that copy
+ * on `stream`.  ESS_ERR_NOMEM / ESS_ERR_HIP if that fails. */
+ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
+                         int32_t block, const int32_t* n_ctx,
+                         int32_t* state_dev, hipStream_t stream);
+/* Free the tail's host arrays and events (its copies must have completed). */
 ess_status ess_tail_release(ess_tail* t);
 
-/* Append the step's m = d->mtp tokens of every request at positions
- * t->n_ctx .. t->n_ctx + m - 1:
+/* Append the step's m = d->mtp tokens of every request b at positions
+ * n_ctx[b] .. n_ctx[b] + m - 1:
  *   k_idx[b][n_ctx + j] = new_keys[b][j]      ([B][m][d_I] fp8 -> [B][L][d_I])
  *   tail row of n_ctx + j = new_lat[b][j]     ([B][m][576] bf16)
  *   n_vis[b][j] = n_ctx + 1 + j               (token j sees up to itself)
- * on `stream`; every tail block this fills is copied to
- * host_kv[b][p] (the host store's CPU address, [B][L][576]) for its
- * positions p >= first, on `d2h` (a different stream).  Then t->n_ctx += m
- * and t->start = max(first, start of the block before the newest one).
- * Requires m <= block and n_ctx + m <= ctx_len. */
+ * on `stream`; every tail block this fills is copied to host_kv[b][p] (the
+ * host store's CPU address, [B][L][576]) for its positions p >= first[b], on
+ * `d2h` (a different stream).  Then n_ctx[b] += m and start[b] = max(first,
+ * start of the block before the newest one), in both copies of the state.
+ * Requires m <= block and n_ctx[b] + m <= ctx_len. */
 ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
                              const uint8_t* new_keys, const uint16_t* new_lat,
                              uint8_t* k_idx, int32_t* n_vis, uint16_t* host_kv,

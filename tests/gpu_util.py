@@ -158,14 +158,15 @@ def compare_with_oracle(wl, recs, layer=0, requests=None, steps=None,
                         host=None, grow_from=None):
     """host: the layer's latents [B][L][576] when they are not the generated
     ones (a store of fp8 entries: their dequantized rows); grow_from: the
-    initial context length of a growing run."""
+    initial context length of a growing run (one per request, or one for
+    all)."""
     requests = range(wl.batch) if requests is None else requests
     steps = len(recs["steps"]) if steps is None else steps
     worst = 0.0
     for b in requests:
         it = odecode.run_workload_request(
             wl, layer, b, steps=steps, host=None if host is None else host[b],
-            grow_from=grow_from)
+            grow_from=grow_from[b] if isinstance(grow_from, (list, tuple)) else grow_from)
         fill = next(it)
         g = recs["fill"][layer]
         n = int(g["n_miss"][b])

@@ -165,31 +165,37 @@ def test_entry_copy_argument_checks(L):
 
 def test_tail_argument_checks(L):
     d = _d()
-    t = ess.ess_tail()
-    assert _status(lambda: ess.ess_tail_init(0, 8, 100)) == "invalid argument"      # no rows
-    assert _status(lambda: ess.ess_tail_init(P, 0, 100)) == "invalid argument"      # block 0
-    # Not initialised, same stream for the write-back, block below mtp.
+    B = d.batch
+    assert _status(lambda: ess.ess_tail_init(d, 0, 8, [100] * B, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_tail_init(d, P, 0, [100] * B, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_tail_init(d, P, 8, [0] * B, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_tail_init(d, P, 8, [5000] * B, P, stream=0)) == "invalid argument"
     st = lambda dd, tt, s1, s2: _status(lambda: ess.ess_append_tokens(
         dd, tt, P, P, P, P, P, stream=s1, d2h=s2))
+    assert st(d, ess.ess_tail(), 1, 2) == "invalid argument"          # not initialised
+    lens = (ctypes.c_int32 * (3 * B))(*([100] * B + [100] * B + [100] * B))
+    t = ess.ess_tail(P, 8, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
+    assert st(d, t, 3, 3) == "invalid argument"                       # one stream for both
+    assert st(_d(batch=3), t, 1, 2) == "invalid argument"             # batch differs
+    t1 = ess.ess_tail(P, 1, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
+    assert st(_d(mtp=2, idx_heads=16), t1, 1, 2) == "unsupported shape"   # block < mtp
+    lens[B + 1] = 4096                                                # request 1 is full
     assert st(d, t, 1, 2) == "invalid argument"
-    t.rows, t.block, t.first, t.n_ctx, t.start = P, 8, 100, 100, 100
-    t.events[0] = t.events[1] = P
-    assert st(d, t, 3, 3) == "invalid argument"
-    assert st(_d(mtp=2, idx_heads=16), ess.ess_tail(P, 1, 10, 10, 10, (P, P)), 1, 2) == "unsupported shape"
-    t.n_ctx = 4096                                                                 # full
-    assert st(d, t, 1, 2) == "invalid argument"
-    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, 5, 0)                      # tail_block 0
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, P, 0)         # tail_block 0
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
+                                               stream=0, side=1)) == "invalid argument"
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, None, 16)     # no tail_start
     assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE,
                                                stream=0, side=1)) == "invalid argument"
 
 
 def test_tail_with_entry_store_is_unsupported(L):
-    io = ess.ess_layer_io(*([P] * 22), 1 << 30, P, P, 5, 16)
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, P, P, P, 16)
     assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_INLINE,
                                                stream=0, side=1)) == "unsupported shape"
 
 
 def test_fill_takes_no_tail(L):
-    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, 5, 16)
+    io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, P, 16)
     assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_FILL,
                                                stream=0, side=1)) == "invalid argument"

@@ -21,8 +21,10 @@ NAN_BF16 = 0x7FC0
 
 
 def _grow(wl, L0, block, mode, steps, layers=1):
+    """L0: the initial length, one per request or one for all."""
     B, m, L, k = wl.batch, wl.mtp, wl.ctx_len, wl.topk
     d = dims_of(wl)
+    L0 = list(L0) if isinstance(L0, (list, tuple)) else [L0] * B
     lats, keys, hosts = [], [], []
     for l in range(layers):
         lat = np.empty((B, L, 576), np.uint16)
@@ -31,17 +33,19 @@ def _grow(wl, L0, block, mode, steps, layers=1):
         gen.fill_index_keys(wl, l, kb)
         host = HostStore((B, L, 576))
         host.array[:] = NAN_BF16
-        host.array[:, :L0] = lat[:, :L0]
+        for b in range(B):
+            host.array[b, :L0[b]] = lat[b, :L0[b]]
         lats.append(lat); keys.append(kb); hosts.append(host)
     run = DecodeRunner(d, hosts)
     ins = [LayerInputs(wl, l) for l in range(layers)]
     for l, lb in enumerate(run.layers):
         ins[l].upload_static(lb, None, keys=False, latents=False)
         k0 = np.zeros_like(keys[l])
-        k0[:, :L0] = keys[l][:, :L0]
+        for b in range(B):
+            k0[b, :L0[b]] = keys[l][b, :L0[b]]
         lb.k_idx.copy_(torch.from_numpy(k0))
         ins[l].upload_step(lb, 0)
-    run.set_n_vis([[L0 - m + 1 + j for j in range(m)]] * B)
+    run.set_n_vis([[L0[b] - m + 1 + j for j in range(m)] for b in range(B)])
     run.reset()
     run.fill()
     sync()
@@ -50,24 +54,28 @@ def _grow(wl, L0, block, mode, steps, layers=1):
                      for lb in run.layers], "steps": []}
     stream = torch.cuda.current_stream()
     d2h = torch.cuda.Stream()
-    rows, tails, new_keys, new_lat = [], [], [], []
+    rows, states, tails, new_keys, new_lat = [], [], [], [], []
     for l in range(layers):
         rows.append(torch.full((B, 2 * block, 576), NAN_BF16, dtype=torch.int16, device="cuda"))
-        tails.append(ess.ess_tail_init(rows[l], block, L0))
-        new_keys.append(torch.from_numpy(np.ascontiguousarray(keys[l][:, L0:L0 + steps * m])).cuda())
-        new_lat.append(torch.from_numpy(
-            np.ascontiguousarray(lats[l][:, L0:L0 + steps * m]).view(np.int16)).cuda())
+        states.append(torch.empty(3 * B, dtype=torch.int32, device="cuda"))
+        tails.append(ess.ess_tail_init(d, rows[l], block, L0, states[l], stream))
+        # Each request's new tokens, [steps][B][m][...].
+        new_keys.append(torch.from_numpy(np.ascontiguousarray(np.stack(
+            [keys[l][b, L0[b]:L0[b] + steps * m].reshape(steps, m, -1) for b in range(B)], 1))).cuda())
+        new_lat.append(torch.from_numpy(np.ascontiguousarray(np.stack(
+            [lats[l][b, L0[b]:L0[b] + steps * m].reshape(steps, m, 576) for b in range(B)],
+            1)).view(np.int16)).cuda())
     # Every layer's n_vis is the same; each layer's append writes it again.
     from_tail = 0
     for t in range(steps):
         ios = []
         for l, lb in enumerate(run.layers):
             ins[l].upload_step(lb, t)
-            ess.ess_append_tokens(d, tails[l], new_keys[l][:, t * m:(t + 1) * m].contiguous(),
-                                  new_lat[l][:, t * m:(t + 1) * m].contiguous(), lb.k_idx,
+            ess.ess_append_tokens(d, tails[l], new_keys[l][t], new_lat[l][t], lb.k_idx,
                                   run.n_vis, hosts[l].host, stream, d2h)
             io = lb.io()
-            io.tail_rows, io.tail_start, io.tail_block = rows[l].data_ptr(), tails[l].start, block
+            io.tail_rows, io.tail_start, io.tail_block = (rows[l].data_ptr(), tails[l].start_dev,
+                                                          block)
             ios.append(io)
         ess.ess_decode_step(d, ios, run.n_vis, mode, stream, run.side)
         sync()
@@ -75,7 +83,9 @@ def _grow(wl, L0, block, mode, steps, layers=1):
         for l, lb in enumerate(run.layers):
             nm = h(lb.n_miss)
             mp = h(lb.lists(lb.miss_pos, m * k))
-            from_tail += sum(int((mp[b, :nm[b]] >= tails[l].start).sum()) for b in range(B))
+            st = tails[l].start
+            assert h(states[l]).tolist() == tails[l].first + tails[l].n_ctx + st
+            from_tail += sum(int((mp[b, :nm[b]] >= st[b]).sum()) for b in range(B))
             per.append(dict(
                 sel_pos=h(lb.rows(lb.sel_pos, k, m)), sel_slot=h(lb.rows(lb.sel_slot, k, m)),
                 n_sel=h(lb.n_sel), row_dst=h(lb.rows(lb.row_dst, k, m)),
@@ -84,14 +94,14 @@ def _grow(wl, L0, block, mode, steps, layers=1):
                 n_miss=nm, n_evict=h(lb.n_evict), out=h(lb.out), lse=h(lb.lse)))
         recs["steps"].append(per)
     torch.cuda.synchronize()
-    n_ctx = L0 + steps * m
-    done = (n_ctx // block) * block
     for l, lb in enumerate(run.layers):
-        assert tails[l].n_ctx == n_ctx
-        # Written back: every full block from L0 on; beyond it the host
-        # store is untouched.
-        assert np.array_equal(hosts[l].array[:, :done], lats[l][:, :done])
-        assert np.all(hosts[l].array[:, max(done, L0):] == NAN_BF16)
+        assert tails[l].n_ctx == [L0[b] + steps * m for b in range(B)]
+        for b in range(B):
+            # Written back: every full block from L0 on; beyond it the host
+            # store is untouched.
+            done = ((L0[b] + steps * m) // block) * block
+            assert np.array_equal(hosts[l].array[b, :done], lats[l][b, :done]), (l, b)
+            assert np.all(hosts[l].array[b, max(done, L0[b]):] == NAN_BF16), (l, b)
         # Every resident slot holds its latent, wherever it came from.
         cs, pool = h(lb.cache_slots), h(lb.pool)
         for b in range(B):
@@ -128,3 +138,16 @@ def test_growth_two_layers_prefetch():
     assert from_tail > 0
     for layer in range(2):
         compare_with_oracle(wl, recs, layer=layer, grow_from=L0)
+
+
+def test_growth_requests_at_different_lengths():
+    # Four requests starting at different lengths (block boundaries, and so
+    # write-backs, fall on different steps for each).
+    steps, m, block = 20, 2, 8
+    wl = get_workload("tiny-4k").with_(name="grow-ragged", batch=4, mtp=m, ctx_len=2048,
+                                       topk=256, pool_slots=1024, steps=steps, rho=0.9)
+    L0 = [1500, 1733, 2048 - steps * m, 901]
+    print(f"growth ragged lengths {L0} m={m} block={block}", flush=True)
+    recs, from_tail = _grow(wl, L0, block, ess.ESS_MODE_INLINE, steps)
+    assert from_tail > 0
+    compare_with_oracle(wl, recs, grow_from=L0)
