@@ -12,9 +12,11 @@
  *      in device memory, misses straight from mapped host
  *      memory - and absorbed-MLA attention over them         (ess_sparse_mla_decode)
  * plus a standalone host->pool copy of a miss list (ess_miss_copy, and
- * ess_miss_copy_entries from 656-byte fp8 entries) and a
- * whole-step entry point over several layers with side-stream prefetch
- * (ess_decode_step).
+ * ess_miss_copy_entries from 656-byte fp8 entries), a whole-step entry point
+ * over several layers with side-stream prefetch (ess_decode_step), a growing
+ * context with device tail blocks (ess_tail_init, ess_append_tokens), the
+ * prefill four-buffer pipeline (ess_prefill_layers) and an offline replay of
+ * the pool under other eviction policies (ess_replay_evictions).
  *
  * Sources: the ESS concept page ("ESS: Latent-Cache Offload", tables "dual
  * cache" and "core mechanism") and the FlashOffloading analysis
