@@ -11,6 +11,7 @@
 
 #include "ess_host.h"
 #include "ess_internal.h"
+#include "fp8_entry.h"
 
 namespace {
 
@@ -359,9 +360,6 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
     return fail(ESS_ERR_INVALID,
                 "%s: layer %d: the first fill reads the host store and precedes the tail",
                 fn, l);
-  if (io.tail_rows && io.host_entries)
-    return fail(ESS_ERR_UNSUPPORTED,
-                "%s: layer %d: tail blocks write back bf16 rows, not fp8 entries", fn, l);
   if (io.tail_rows && (io.tail_block < 1 || !io.tail_start))
     return fail(ESS_ERR_INVALID, "%s: layer %d: tail_block must be >= 1 and tail_start set",
                 fn, l);
@@ -500,11 +498,12 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
 }
 
 ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
-                         int32_t block, const int32_t* n_ctx,
+                         uint8_t* entries, int32_t block, const int32_t* n_ctx,
                          int32_t* state_dev, hipStream_t stream) {
   const char* fn = "ess_tail_init";
   ESS_NONNULL(t);
   t->rows = nullptr;
+  t->entries = nullptr;
   t->host = nullptr;
   t->events = nullptr;
   ess_status s = check_dims(d, fn);
@@ -514,6 +513,8 @@ ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
   ESS_NONNULL(state_dev);
   const int B = d->batch;
   if (block < 1) return fail(ESS_ERR_INVALID, "%s: block must be >= 1", fn);
+  if (entries && (reinterpret_cast<uintptr_t>(entries) & 15))
+    return fail(ESS_ERR_INVALID, "%s: entries must be 16-byte aligned", fn);
   for (int b = 0; b < B; ++b)
     if (n_ctx[b] < 1 || n_ctx[b] > d->ctx_len)
       return fail(ESS_ERR_INVALID, "%s: n_ctx[%d] = %d outside [1, ctx_len]", fn, b,
@@ -527,6 +528,7 @@ ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
   }
   for (int b = 0; b < B; ++b) host[b] = host[B + b] = host[2 * B + b] = n_ctx[b];
   t->rows = rows;
+  t->entries = entries;
   t->block = block;
   t->batch = B;
   t->host = host;
@@ -562,12 +564,13 @@ ess_status ess_tail_release(ess_tail* t) {
   t->events = nullptr;
   t->host = nullptr;
   t->rows = nullptr;
+  t->entries = nullptr;
   return ESS_OK;
 }
 
 ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
                              const uint8_t* new_keys, const uint16_t* new_lat,
-                             uint8_t* k_idx, int32_t* n_vis, uint16_t* host_kv,
+                             uint8_t* k_idx, int32_t* n_vis, void* host_store,
                              hipStream_t stream, hipStream_t d2h) {
   const char* fn = "ess_append_tokens";
   ess_status s = check_dims(d, fn);
@@ -578,7 +581,7 @@ ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
   ESS_NONNULL(new_lat);
   ESS_NONNULL(k_idx);
   ESS_NONNULL(n_vis);
-  ESS_NONNULL(host_kv);
+  ESS_NONNULL(host_store);
   if (!t->rows || !t->host || !t->events || !t->state_dev)
     return fail(ESS_ERR_INVALID, "%s: tail is not initialised (ess_tail_init)", fn);
   if (t->batch != d->batch)
@@ -609,7 +612,7 @@ ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
   }
   if (e == hipSuccess)
     e = ess::launch_append_tokens(*d, blk, new_keys, new_lat, k_idx, t->rows,
-                                  n_vis, t->state_dev, stream);
+                                  t->entries, n_vis, t->state_dev, stream);
   // Blocks filled by this append go back to the host store on d2h.
   bool recorded = false;
   for (int b = 0; b < B && e == hipSuccess; ++b) {
@@ -623,11 +626,15 @@ ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
         recorded = true;
         if (e != hipSuccess) break;
       }
+      // Rows of the block as the host store holds them: bf16 rows, or the
+      // entries quantized at append.
       const int p0 = std::max(first[b], c * blk);
-      e = hipMemcpyAsync(host_kv + ((size_t)b * L + p0) * ess::kLat,
-                         t->rows + ((size_t)b * 2 * blk + (c & 1) * blk + p0 % blk) * ess::kLat,
-                         (size_t)(last + 1 - p0) * ess::kLat * sizeof(uint16_t),
-                         hipMemcpyDeviceToHost, d2h);
+      const size_t unit = t->entries ? ess::kEntryBytes : ess::kLat * sizeof(uint16_t);
+      const char* src = t->entries ? reinterpret_cast<const char*>(t->entries)
+                                   : reinterpret_cast<const char*>(t->rows);
+      e = hipMemcpyAsync(static_cast<char*>(host_store) + ((size_t)b * L + p0) * unit,
+                         src + ((size_t)b * 2 * blk + (c & 1) * blk + p0 % blk) * unit,
+                         (size_t)(last + 1 - p0) * unit, hipMemcpyDeviceToHost, d2h);
       if (e == hipSuccess)
         e = hipEventRecord(static_cast<hipEvent_t>(t->events[2 * b + (c & 1)]), d2h);
     }

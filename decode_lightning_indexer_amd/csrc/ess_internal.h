@@ -128,12 +128,14 @@ hipError_t launch_entry_copy(const ess_dims& d, int list_stride,
 // into k_idx [B][L][d_I], latents into the tail rows [B][2*block][576],
 // n_vis [B][m] = n_ctx + 1 + j; then state[B + b] += m and state[2B + b] =
 // the new first tail position.  state = device (first[B], n_ctx[B],
-// start[B]).
+// start[B]).  tail_ent non-null ([B][2*block][656]): the latents are
+// quantized into 656-byte entries there and the tail rows get them
+// dequantized.
 hipError_t launch_append_tokens(const ess_dims& d, int block,
                                 const uint8_t* new_keys,
                                 const uint16_t* new_lat, uint8_t* k_idx,
-                                uint16_t* tail, int32_t* n_vis,
-                                int32_t* state, hipStream_t s);
+                                uint16_t* tail, uint8_t* tail_ent,
+                                int32_t* n_vis, int32_t* state, hipStream_t s);
 
 // ---- prefill pipeline ---------------------------------------------------
 // Per-block partial sums of the stand-in layer compute for `rows` rows.

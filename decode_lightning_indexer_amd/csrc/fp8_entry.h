@@ -49,3 +49,32 @@ __device__ __forceinline__ entry_v4u dequant8(unsigned lo, unsigned hi, float sc
 }
 
 }  // namespace ess
+
+namespace ess {
+
+// Quantizing a bf16 latent into an entry: the block scale is the smallest
+// power of two s with max|x| <= 448 s (1 for an all-zero block), and each
+// c_KV value x becomes the e4m3fn code nearest x / s (ties to the even code,
+// |x / s| <= 448 by the choice of s; -0 becomes +0).
+__device__ __forceinline__ int entry_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int t = ilogbf(amax) - 9;                  // 448 * 2^t < amax here
+  while (amax > 448.f * ldexpf(1.f, t)) ++t;
+  return t;
+}
+
+__device__ __forceinline__ unsigned f32_to_e4m3fn_rne(float x) {
+  const float v = fabsf(x);
+  unsigned code;
+  if (v < 0x1p-6f) {
+    code = (unsigned)rintf(v * 512.f);       // subnormal steps of 2^-9
+  } else {
+    const int e = ilogbf(v);
+    const unsigned m = (unsigned)rintf((ldexpf(v, -e) - 1.f) * 8.f);
+    code = ((unsigned)(e + 7) << 3) + m;     // m == 8 carries into the exponent
+  }
+  if (code > 0x7Eu) code = 0x7Eu;
+  return (x < 0.f && code != 0u) ? (code | 0x80u) : code;
+}
+
+}  // namespace ess

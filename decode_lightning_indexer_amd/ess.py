@@ -69,7 +69,7 @@ class ess_layer_io(ctypes.Structure):
 
 
 class ess_tail(ctypes.Structure):
-    _fields_ = [("rows", _P), ("block", _I), ("batch", _I),
+    _fields_ = [("rows", _P), ("entries", _P), ("block", _I), ("batch", _I),
                 ("host", ctypes.POINTER(ctypes.c_int32)), ("state_dev", _P),
                 ("events", _P)]
 
@@ -127,7 +127,7 @@ def lib():
             "ess_decode_step": (_I, [D, _I, ctypes.POINTER(ess_layer_io), _P,
                                      _I, _P, _P]),
             "ess_host_alloc": (_I, [_S, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
-            "ess_tail_init": (_I, [ctypes.POINTER(ess_tail), D, _P, _I, _P, _P, _P]),
+            "ess_tail_init": (_I, [ctypes.POINTER(ess_tail), D, _P, _P, _I, _P, _P, _P]),
             "ess_tail_release": (_I, [ctypes.POINTER(ess_tail)]),
             "ess_append_tokens": (_I, [D, ctypes.POINTER(ess_tail), _P, _P, _P, _P,
                                        _P, _P, _P]),
@@ -256,15 +256,15 @@ def ess_decode_step(d, layers, n_vis, mode, stream=None, side=None):
         _stream(stream), _stream(side) if side is not None else None))
 
 
-def ess_tail_init(d, rows, block, n_ctx, state_dev, stream=None):
+def ess_tail_init(d, rows, block, n_ctx, state_dev, stream=None, entries=None):
     """A new ess_tail over the device tail rows [B][2*block][576]; n_ctx:
     every request's length (sequence of B ints); state_dev: device int32
-    [3*B]."""
+    [3*B]; entries: device [B][2*block][656] for a store of fp8 entries."""
     t = ess_tail()
     arr = (ctypes.c_int32 * d.batch)(*[int(x) for x in n_ctx])
     _check("ess_tail_init", lib().ess_tail_init(
-        ctypes.byref(t), ctypes.byref(d), _ptr(rows), block, arr, _ptr(state_dev),
-        _stream(stream)))
+        ctypes.byref(t), ctypes.byref(d), _ptr(rows), _ptr(entries), block, arr,
+        _ptr(state_dev), _stream(stream)))
     return t
 
 
@@ -274,7 +274,8 @@ def ess_tail_release(t):
 
 def ess_append_tokens(d, t, new_keys, new_lat, k_idx, n_vis, host_kv, stream=None,
                       d2h=None):
-    """host_kv: the host store's CPU address (HostStore.host)."""
+    """host_kv: the host store's CPU address (HostStore.host): bf16 rows, or
+    656-byte entries when the tail has entries."""
     _check("ess_append_tokens", lib().ess_append_tokens(
         ctypes.byref(d), ctypes.byref(t), _ptr(new_keys), _ptr(new_lat),
         _ptr(k_idx), _ptr(n_vis), _ptr(host_kv), _stream(stream),

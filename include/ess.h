@@ -286,10 +286,8 @@ typedef struct ess_layer_io {
                                  read from tail_rows instead of host memory */
   int32_t tail_block;         /* ess_tail.block.  ESS_MODE_FILL takes no
                                  tail (it reads every row from the host
-                                 store).  A tail needs the bf16
-                                 store (host_entries NULL): its blocks are
-                                 written back as bf16 rows; with entries,
-                                 ESS_ERR_UNSUPPORTED. */
+                                 store).  With host_entries the tail must
+                                 have entries too. */
 } ess_layer_io;
 
 enum {
@@ -334,6 +332,14 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
  *   rows      [B][2*block][576] bf16 device memory (caller-owned); position
  *             p >= start[b] of request b lives in its row
  *             ((p / block) % 2) * block + p % block
+ *   entries   NULL for a host store of bf16 rows; for a store of 656-byte
+ *             fp8 entries, [B][2*block][656] device memory (caller-owned,
+ *             16-byte aligned): each appended latent is quantized there
+ *             (block scale = the smallest power of two s with
+ *             max|c_KV| <= 448 s, 1 for an all-zero block; codes = the
+ *             nearest e4m3fn value of x / s, ties to the even code; k_R
+ *             as is), its tail row holds the entry dequantized, and the
+ *             write-back copies entries
  *   host      [3][B] int32 host copy of (first, n_ctx, start): first = the
  *             length the tail started at (positions below it are already
  *             in the host store), n_ctx = current length, start = first
@@ -344,6 +350,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
  *   events    2B write-back events */
 typedef struct ess_tail {
   uint16_t* rows;
+  uint8_t* entries;
   int32_t block, batch;
   int32_t* host;
   int32_t* state_dev;
@@ -355,7 +362,7 @@ typedef struct ess_tail {
  * arrays and creates the events; writes state_dev and waits for that copy
  * on `stream`.  ESS_ERR_NOMEM / ESS_ERR_HIP if that fails. */
 ess_status ess_tail_init(ess_tail* t, const ess_dims* d, uint16_t* rows,
-                         int32_t block, const int32_t* n_ctx,
+                         uint8_t* entries, int32_t block, const int32_t* n_ctx,
                          int32_t* state_dev, hipStream_t stream);
 /* Free the tail's host arrays and events (its copies must have completed). */
 ess_status ess_tail_release(ess_tail* t);
@@ -365,14 +372,15 @@ ess_status ess_tail_release(ess_tail* t);
  *   k_idx[b][n_ctx + j] = new_keys[b][j]      ([B][m][d_I] fp8 -> [B][L][d_I])
  *   tail row of n_ctx + j = new_lat[b][j]     ([B][m][576] bf16)
  *   n_vis[b][j] = n_ctx + 1 + j               (token j sees up to itself)
- * on `stream`; every tail block this fills is copied to host_kv[b][p] (the
- * host store's CPU address, [B][L][576]) for its positions p >= first[b], on
- * `d2h` (a different stream).  Then n_ctx[b] += m and start[b] = max(first,
+ * on `stream`; every tail block this fills is copied to host_store[b][p]
+ * (the host store's CPU address: [B][L][576] bf16, or [B][L][656] entries
+ * when the tail has entries) for its positions p >= first[b], on `d2h` (a
+ * different stream).  Then n_ctx[b] += m and start[b] = max(first,
  * start of the block before the newest one), in both copies of the state.
  * Requires m <= block and n_ctx[b] + m <= ctx_len. */
 ess_status ess_append_tokens(const ess_dims* d, ess_tail* t,
                              const uint8_t* new_keys, const uint16_t* new_lat,
-                             uint8_t* k_idx, int32_t* n_vis, uint16_t* host_kv,
+                             uint8_t* k_idx, int32_t* n_vis, void* host_store,
                              hipStream_t stream, hipStream_t d2h);
 
 /* Pinned host memory mapped into the device address space (write-combined

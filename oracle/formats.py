@@ -58,3 +58,42 @@ def decode_entries(entries: np.ndarray) -> np.ndarray:
     out[:, :512] = (vals * scale[:, :, None]).reshape(n, 512)
     out[:, 512:] = decode_bf16(np.ascontiguousarray(e[:, 528:656]).view(np.uint16))
     return out
+
+
+def encode_entries(bf16_rows: np.ndarray) -> np.ndarray:
+    """bf16 latents [n][576] (uint16 bits) -> 656-byte entries [n][656], by
+    the definition: per 128-value block of c_KV the scale is the smallest
+    power of two s with max|x| <= 448 s (1 for an all-zero block), found by
+    stepping the exponent; each value takes the finite e4m3fn code whose
+    value is nearest x / s, a tie going to the even code, and -0 encodes as
+    +0; k_R is copied.  Brute force over every code (slow; small inputs
+    only).  Parity unpinned against the pages, which give only the entry's
+    size: this is the library's reading of the 656-byte block."""
+    rows = np.asarray(bf16_rows, dtype=np.uint16).reshape(-1, 576)
+    n = rows.shape[0]
+    x = decode_bf16(rows[:, :512]).reshape(n, 4, 128)
+    out = np.zeros((n, 656), np.uint8)
+    finite = np.array([c for c in range(256) if not np.isnan(E4M3FN_TABLE[c])])
+    vals = E4M3FN_TABLE[finite]
+    for i in range(n):
+        for blk in range(4):
+            amax = float(np.abs(x[i, blk]).max())
+            t = 0
+            if amax > 0:
+                t = -160
+                while amax > 448.0 * 2.0 ** t:
+                    t += 1
+            s = 2.0 ** t
+            for c in range(128):
+                v = x[i, blk, c] / s
+                d = np.abs(vals - v)
+                best = finite[d == d.min()]
+                if len(best) > 1:          # a tie: the even code (signed zeros aside)
+                    best = best[best % 2 == 0] if np.any(best % 2 == 0) else best
+                code = int(best.min())
+                if code == 0x80:
+                    code = 0
+                out[i, blk * 128 + c] = code
+            out[i, 512 + 4 * blk:516 + 4 * blk] = np.frombuffer(np.float32(s).tobytes(), np.uint8)
+    out[:, 528:] = np.ascontiguousarray(rows[:, 512:]).view(np.uint8).reshape(n, 128)
+    return out

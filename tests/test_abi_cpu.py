@@ -174,10 +174,10 @@ def test_tail_argument_checks(L):
         dd, tt, P, P, P, P, P, stream=s1, d2h=s2))
     assert st(d, ess.ess_tail(), 1, 2) == "invalid argument"          # not initialised
     lens = (ctypes.c_int32 * (3 * B))(*([100] * B + [100] * B + [100] * B))
-    t = ess.ess_tail(P, 8, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
+    t = ess.ess_tail(P, None, 8, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
     assert st(d, t, 3, 3) == "invalid argument"                       # one stream for both
     assert st(_d(batch=3), t, 1, 2) == "invalid argument"             # batch differs
-    t1 = ess.ess_tail(P, 1, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
+    t1 = ess.ess_tail(P, None, 1, B, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), P, P)
     assert st(_d(mtp=2, idx_heads=16), t1, 1, 2) == "unsupported shape"   # block < mtp
     lens[B + 1] = 4096                                                # request 1 is full
     assert st(d, t, 1, 2) == "invalid argument"
@@ -189,10 +189,10 @@ def test_tail_argument_checks(L):
                                                stream=0, side=1)) == "invalid argument"
 
 
-def test_tail_with_entry_store_is_unsupported(L):
-    io = ess.ess_layer_io(*([P] * 22), 1 << 30, P, P, P, 16)
-    assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_INLINE,
-                                               stream=0, side=1)) == "unsupported shape"
+def test_tail_entries_must_be_aligned(L):
+    d = _d()
+    assert _status(lambda: ess.ess_tail_init(d, P, 8, [100] * d.batch, P, stream=0,
+                                             entries=P + 8)) == "invalid argument"
 
 
 def test_fill_takes_no_tail(L):

@@ -13,30 +13,46 @@ from decode_lightning_indexer_amd.runner import DecodeRunner
 from decode_lightning_indexer_amd.session import HostStore, dims_of
 from synth import gen, get_workload
 from synth.device import LayerInputs
-from tests.gpu_util import compare_with_oracle, h, sync
+from oracle.formats import encode_entries as oracle_encode_entries
+from tests.gpu_util import compare_with_oracle, dequantized_latents, h, sync
 
 pytestmark = pytest.mark.gpu
 
 NAN_BF16 = 0x7FC0
 
 
-def _grow(wl, L0, block, mode, steps, layers=1):
-    """L0: the initial length, one per request or one for all."""
+def _grow(wl, L0, block, mode, steps, layers=1, store="bf16"):
+    """L0: the initial length, one per request or one for all.  store:
+    "bf16" rows or 656-byte fp8 "entries" (then every latent the path sees
+    is the dequantized entry, and the oracle runs on those)."""
     B, m, L, k = wl.batch, wl.mtp, wl.ctx_len, wl.topk
     d = dims_of(wl)
     L0 = list(L0) if isinstance(L0, (list, tuple)) else [L0] * B
-    lats, keys, hosts = [], [], []
+    lats, keys, hosts, ents, effs = [], [], [], [], []
     for l in range(layers):
         lat = np.empty((B, L, 576), np.uint16)
         gen.fill_latents(wl, l, lat)
         kb = np.empty((B, L, wl.idx_dim), np.uint8)
         gen.fill_index_keys(wl, l, kb)
-        host = HostStore((B, L, 576))
-        host.array[:] = NAN_BF16
-        for b in range(B):
-            host.array[b, :L0[b]] = lat[b, :L0[b]]
+        if store == "bf16":
+            host = HostStore((B, L, 576))
+            host.array[:] = NAN_BF16
+            for b in range(B):
+                host.array[b, :L0[b]] = lat[b, :L0[b]]
+            effs.append(lat)
+        else:
+            ent, eff = dequantized_latents(wl, l)
+            host = HostStore((B, L, 656), np.uint8)
+            host.array[:] = 0x7F                     # NaN codes and NaN scales
+            for b in range(B):
+                host.array[b, :L0[b]] = ent[b, :L0[b]]
+            ents.append(ent)
+            effs.append(eff)
         lats.append(lat); keys.append(kb); hosts.append(host)
-    run = DecodeRunner(d, hosts)
+    if store == "bf16":
+        run = DecodeRunner(d, hosts)
+    else:
+        run = DecodeRunner(d, [None] * layers, entries=hosts)
     ins = [LayerInputs(wl, l) for l in range(layers)]
     for l, lb in enumerate(run.layers):
         ins[l].upload_static(lb, None, keys=False, latents=False)
@@ -54,11 +70,14 @@ def _grow(wl, L0, block, mode, steps, layers=1):
                      for lb in run.layers], "steps": []}
     stream = torch.cuda.current_stream()
     d2h = torch.cuda.Stream()
-    rows, states, tails, new_keys, new_lat = [], [], [], [], []
+    rows, states, tails, new_keys, new_lat, tail_ents = [], [], [], [], [], []
     for l in range(layers):
         rows.append(torch.full((B, 2 * block, 576), NAN_BF16, dtype=torch.int16, device="cuda"))
         states.append(torch.empty(3 * B, dtype=torch.int32, device="cuda"))
-        tails.append(ess.ess_tail_init(d, rows[l], block, L0, states[l], stream))
+        tail_ents.append(None if store == "bf16" else
+                         torch.full((B, 2 * block, 656), 0x7F, dtype=torch.uint8, device="cuda"))
+        tails.append(ess.ess_tail_init(d, rows[l], block, L0, states[l], stream,
+                                       entries=tail_ents[l]))
         # Each request's new tokens, [steps][B][m][...].
         new_keys.append(torch.from_numpy(np.ascontiguousarray(np.stack(
             [keys[l][b, L0[b]:L0[b] + steps * m].reshape(steps, m, -1) for b in range(B)], 1))).cuda())
@@ -98,17 +117,26 @@ def _grow(wl, L0, block, mode, steps, layers=1):
         assert tails[l].n_ctx == [L0[b] + steps * m for b in range(B)]
         for b in range(B):
             # Written back: every full block from L0 on; beyond it the host
-            # store is untouched.
+            # store is untouched.  Entries written back are the oracle's
+            # quantization of the latents.
             done = ((L0[b] + steps * m) // block) * block
-            assert np.array_equal(hosts[l].array[b, :done], lats[l][b, :done]), (l, b)
-            assert np.all(hosts[l].array[b, max(done, L0[b]):] == NAN_BF16), (l, b)
+            if store == "bf16":
+                assert np.array_equal(hosts[l].array[b, :done], lats[l][b, :done]), (l, b)
+                assert np.all(hosts[l].array[b, max(done, L0[b]):] == NAN_BF16), (l, b)
+            else:
+                assert np.array_equal(hosts[l].array[b, :L0[b]], ents[l][b, :L0[b]]), (l, b)
+                assert np.array_equal(hosts[l].array[b, L0[b]:done],
+                                      oracle_encode_entries(lats[l][b, L0[b]:done])), (l, b)
+                assert np.all(hosts[l].array[b, max(done, L0[b]):] == 0x7F), (l, b)
         # Every resident slot holds its latent, wherever it came from.
         cs, pool = h(lb.cache_slots), h(lb.pool)
         for b in range(B):
             res = np.nonzero(cs[b] >= 0)[0]
-            assert np.array_equal(pool[b, cs[b, res]], lats[l][b, res]), (l, b)
+            assert np.array_equal(pool[b, cs[b, res]], effs[l][b, res]), (l, b)
         ess.ess_tail_release(tails[l])
         hosts[l].free()
+    if store != "bf16":
+        recs["effective"] = effs
     return recs, from_tail
 
 
@@ -151,3 +179,19 @@ def test_growth_requests_at_different_lengths():
     recs, from_tail = _grow(wl, L0, block, ess.ESS_MODE_INLINE, steps)
     assert from_tail > 0
     compare_with_oracle(wl, recs, grow_from=L0)
+
+
+@pytest.mark.parametrize("mode", [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH])
+def test_growth_over_fp8_entries(mode):
+    # A host store of fp8 entries: appended tokens are quantized on the GPU,
+    # written back as entries (bit-exact against the oracle's quantizer) and
+    # read from the tail as the dequantized entry; requests at different
+    # lengths, blocks of 6 tokens.
+    steps, m, block = 16, 2, 6
+    wl = get_workload("tiny-4k").with_(name="grow-fp8", batch=3, mtp=m, ctx_len=2048,
+                                       topk=256, pool_slots=1024, steps=steps, rho=0.9)
+    L0 = [1990, 1601, 1777]
+    print(f"growth over entries mode={mode} lengths {L0} block={block}", flush=True)
+    recs, from_tail = _grow(wl, L0, block, mode, steps, store="entries")
+    assert from_tail > 0
+    compare_with_oracle(wl, recs, grow_from=L0, host=recs["effective"][0])

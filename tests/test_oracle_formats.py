@@ -115,3 +115,37 @@ def test_656_byte_entries_round_trip_the_generator():
     assert np.array_equal(got[:, 512:], ref[:, 512:])
     assert np.array_equal(decode_bf16(gen.f32_to_bf16_bits(got.astype(np.float32))), got)
     assert np.all(got[7, :128] == 0.0)
+
+
+def test_oracle_entry_encoder_by_hand():
+    # Block 0: 1.0 and 448 (scale 1), the midpoint 1.0625 of codes 0x38 and
+    # 0x39 (tie -> even 0x38), 1.1875 between 0x39 and 0x3A (tie -> 0x3A),
+    # -0 -> +0; block 1: max 450 needs scale 2 (450 / 2 = 225 -> 224, 0x76);
+    # block 2 all zero: scale 1; block 3: max 0.5 -> scale 2^-9 (0.5 / 2^-9
+    # = 256 -> 0x78).
+    from oracle.formats import decode_entries, encode_entries
+    x = np.zeros(576, np.float32)
+    x[0], x[1], x[2], x[3], x[4] = 1.0, 448.0, 1.0625, 1.1875, -0.0
+    x[128] = 450.0
+    x[384] = 0.5
+    x[512], x[575] = 1.5, -3.0
+    e = encode_entries(gen.f32_to_bf16_bits(x)[None])[0]
+    assert e[:5].tolist() == [0x38, 0x7E, 0x38, 0x3A, 0x00]
+    assert e[128] == 0x76
+    assert e[384] == 0x78
+    sc = e[512:528].view(np.float32).tolist()
+    assert sc == [1.0, 2.0, 1.0, 2.0 ** -9]
+    d = decode_entries(e[None])[0]
+    assert d[1] == 448.0 and d[128] == 448.0 and d[384] == 0.5
+    assert d[512] == 1.5 and d[575] == -3.0
+
+
+def test_oracle_entry_encoder_agrees_with_the_generator():
+    # Two separate implementations of the same quantization (the generator's
+    # vectorised one and the oracle's brute-force one) agree bit for bit.
+    from oracle.formats import encode_entries
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((24, 576)).astype(np.float32) * rng.choice([1e-3, 0.5, 30.0], (24, 1)).astype(np.float32)
+    x[3, 128:256] = 0.0
+    rows = gen.f32_to_bf16_bits(x)
+    assert np.array_equal(encode_entries(rows), gen.encode_entries(rows))
