@@ -580,14 +580,22 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
 MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs) {
   MlaPlan p;
   const int H = d.mla_heads;
-  p.heads_per_wg = (H % 64 == 0) ? 64 : (H % 48 == 0) ? 48 : (H % 32 == 0) ? 32 : 16;
-  p.head_groups = H / p.heads_per_wg;
   // One workgroup per compute unit (each holds nearly all of a CU's LDS);
   // more chunks would also mean more partial traffic.
   const int target = target_wgs > 0 ? target_wgs : 256;
-  const int base = d.batch * d.mtp * p.head_groups;
   // A chunk is a whole number of tile pairs (one tile per sub-group).
   const int max_chunks = (d.topk + 2 * kTile - 1) / (2 * kTile);
+  // The most heads per workgroup (each head group reads the chunk's rows
+  // again) that still gives the target number of workgroups; with few
+  // requests the heads split further so more workgroups share the rows.
+  p.heads_per_wg = 16;
+  for (const int c : {64, 48, 32, 16}) {
+    if (H % c) continue;
+    p.heads_per_wg = c;
+    if ((long)d.batch * d.mtp * (H / c) * max_chunks >= target) break;
+  }
+  p.head_groups = H / p.heads_per_wg;
+  const int base = d.batch * d.mtp * p.head_groups;
   int nchunk = (target + base - 1) / base;
   const int min_chunks = (d.topk + kMaxChunkRows - 1) / kMaxChunkRows;
   if (nchunk < min_chunks) nchunk = min_chunks;   // miss list fits in LDS
