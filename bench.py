@@ -43,8 +43,10 @@ def parse():
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the 128K and multi-layer prefetch measurements")
+    p.add_argument("--layers", type=int, default=16,
+                   help="layers of the 16-layer configuration to run (16 = all)")
     p.add_argument("--extra-only", choices=["prefill_pipeline", "eviction_replay",
-                                            "fp8_entries", "growing_context"],
+                                            "fp8_entries", "growing_context", "multilayer"],
                    help="only run one extra measurement and print its JSON (for "
                         "profiling it alone)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -311,11 +313,46 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
     return res, n_miss, t_copy, wl
 
 
+def multilayer(args, n_layers=16, K=16, W=4):
+    """The 16-layer configuration (64K context, 32 requests per layer) over
+    n_layers layers: inline against side-stream prefetch, the host link's
+    busy share, and the multi-layer overlap of the miss transfer."""
+    from decode_lightning_indexer_amd import ess
+    t0 = time.perf_counter()
+    name = "64k-b32-16layer"
+    res, n_miss, t_copy, wl = run_steps(
+        args, name, n_layers, [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH], K, W,
+        resident=True)
+    ti, tp = res[ess.ESS_MODE_INLINE], res[ess.ESS_MODE_PREFETCH]
+    t_res = res["resident"]
+    # Prefetch hides the next layer's selection under this layer's copy and
+    # attention: the share of the step's non-copy work that disappears, and
+    # how much of each step the host link is busy.
+    res_out = {"layers_timed": n_layers,
+               "inline_us_per_step": ti * 1e6, "prefetch_us_per_step": tp * 1e6,
+               "query_tok_s_prefetch": wl.batch * wl.mtp / tp,
+               "misses_last_step": n_miss,
+               "miss_copy_us_last_step": t_copy * 1e6,
+               "link_busy_inline": t_copy / ti, "link_busy_prefetch": t_copy / tp,
+               # The multi-layer overlap of the miss transfer: (sum of the
+               # step's copies + the step with every row resident - the
+               # pipelined step) / the copies, with its bound.
+               "resident_us_per_step": t_res * 1e6,
+               "resident_step_misses": res["resident_misses"],
+               "overlap_prefetch": (t_copy + t_res - tp) / t_copy,
+               "overlap_inline": (t_copy + t_res - ti) / t_copy,
+               "overlap_bound": min(1.0, t_res / t_copy),
+               "hidden_noncopy_fraction": (ti - tp) / (ti - t_copy) if ti > t_copy else None}
+    res_out["wall_s"] = time.perf_counter() - t0
+    log(args, f"{name} over {n_layers} layers: {res_out}")
+    return res_out
+
+
 def extra_measurements(args):
     """The 128K / MTP=2 configuration at its three query-drift rates, the
     1M-token single request at both pool sizes, and the 16-layer
-    configuration's per-layer shape over 4 layers with and without
-    side-stream prefetch."""
+    configuration (all of its layers unless --layers says fewer) with and
+    without side-stream prefetch."""
     from decode_lightning_indexer_amd import ess
     out = {}
     K, W = 16, 4
@@ -328,31 +365,7 @@ def extra_measurements(args):
                      "misses_last_step": n_miss,
                      "miss_rate_last_step": n_miss / (wl.batch * wl.mtp * wl.topk),
                      "miss_copy_us_last_step": t_copy * 1e6}
-    name = "64k-b32-16layer"
-    n_layers = 4
-    res, n_miss, t_copy, wl = run_steps(
-        args, name, n_layers, [ess.ESS_MODE_INLINE, ess.ESS_MODE_PREFETCH], K, W,
-        resident=True)
-    ti, tp = res[ess.ESS_MODE_INLINE], res[ess.ESS_MODE_PREFETCH]
-    t_res = res["resident"]
-    # Prefetch hides the next layer's selection under this layer's copy and
-    # attention: the share of the step's non-copy work that disappears, and
-    # how much of each step the host link is busy.
-    out[name] = {"layers_timed": n_layers,
-                 "inline_us_per_step": ti * 1e6, "prefetch_us_per_step": tp * 1e6,
-                 "query_tok_s_prefetch": wl.batch * wl.mtp / tp,
-                 "misses_last_step": n_miss,
-                 "miss_copy_us_last_step": t_copy * 1e6,
-                 "link_busy_inline": t_copy / ti, "link_busy_prefetch": t_copy / tp,
-                 # The multi-layer overlap of the miss transfer: (sum of the
-                 # step's copies + the step with every row resident - the
-                 # pipelined step) / the copies, with its bound.
-                 "resident_us_per_step": t_res * 1e6,
-                 "resident_step_misses": res["resident_misses"],
-                 "overlap_prefetch": (t_copy + t_res - tp) / t_copy,
-                 "overlap_inline": (t_copy + t_res - ti) / t_copy,
-                 "overlap_bound": min(1.0, t_res / t_copy),
-                 "hidden_noncopy_fraction": (ti - tp) / (ti - t_copy) if ti > t_copy else None}
+    out["64k-b32-16layer"] = multilayer(args, n_layers=args.layers)
     return out
 
 
@@ -687,7 +700,8 @@ def main():
         torch.cuda.set_device(0)
         fn = {"prefill_pipeline": prefill_pipeline, "eviction_replay": replay_curves,
               "fp8_entries": lambda a: fp8_entries(a, (a.workload,)),
-              "growing_context": lambda a: growing_context(a, a.workload)}
+              "growing_context": lambda a: growing_context(a, a.workload),
+              "multilayer": lambda a: multilayer(a, a.layers)}
         print(json.dumps({args.extra_only: fn[args.extra_only](args)}), flush=True)
         return 0
     if args.gpus != 1:
