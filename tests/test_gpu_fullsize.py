@@ -14,12 +14,12 @@ from tests.gpu_util import compare_with_oracle, gpu_sequence
 pytestmark = pytest.mark.gpu
 
 
-def _check(wl, requests, mode=ess.ESS_MODE_INLINE, layers=None):
+def _check(wl, requests, mode=ess.ESS_MODE_INLINE, layers=None, check_layers=None):
     print(f"\n[fullsize] {wl.name}: B={wl.batch} m={wl.mtp} L={wl.ctx_len} "
           f"k={wl.topk} C={wl.pool_slots} steps={wl.steps} mode={mode}", flush=True)
     recs = gpu_sequence(wl, mode=mode, layers=layers)
     n_layers = wl.layers if layers is None else layers
-    for layer in range(n_layers):
+    for layer in (range(n_layers) if check_layers is None else check_layers):
         compare_with_oracle(wl, recs, layer=layer, requests=requests)
     misses = sum(int(s[0]["n_miss"].sum()) for s in recs["steps"][1:])
     assert misses > 0, "drift should produce misses after the first step"
@@ -62,6 +62,14 @@ def test_64k_b32_two_layers_prefetch_full_size():
     # positions each), in the side-stream prefetch mode.
     wl = get_workload("64k-b32-16layer").with_(steps=3)
     _check(wl, requests=[0, 31], mode=ess.ESS_MODE_PREFETCH, layers=2)
+
+
+def test_64k_b32_sixteen_layers_prefetch_full_size():
+    # All sixteen layers (38.7 GB of host latents, each layer its own pool and
+    # seeds) selected ahead on the side stream; the first, a middle and the
+    # last layer against the oracle on one request.
+    wl = get_workload("64k-b32-16layer").with_(steps=2)
+    _check(wl, requests=[5], mode=ess.ESS_MODE_PREFETCH, check_layers=[0, 7, 15])
 
 
 def test_32k_b16_fp8_entries_full_size():
