@@ -199,3 +199,31 @@ def test_fill_takes_no_tail(L):
     io = ess.ess_layer_io(*([P] * 22), 1 << 30, None, P, P, 16)
     assert _status(lambda: ess.ess_decode_step(_d(), [io], P, ess.ESS_MODE_FILL,
                                                stream=0, side=1)) == "invalid argument"
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # The ctypes mirrors of the ABI structs have the sizes and field offsets
+    # a C compiler gives the declarations in include/ess.h.
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs gcc and the HIP headers")
+    fields = {"ess_dims": ess.ess_dims, "ess_layer_io": ess.ess_layer_io, "ess_tail": ess.ess_tail}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ess.h"', "int main(void) {"]
+    for name, cls in fields.items():
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for name, cls in fields.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)
