@@ -227,3 +227,50 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(got[name]) == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)
+
+
+def test_a_c_program_calls_the_library(tmp_path):
+    # The library used from C with nothing but include/ess.h: a host-only
+    # call (the eviction replay) on a small recorded run gives what the
+    # Python binding gives, and the status strings come back.
+    import shutil
+    import subprocess
+    import numpy as np
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs gcc and the HIP headers")
+    T, m, Lc, k, C = 3, 1, 12, 4, 6
+    rng = np.random.default_rng(4)
+    scores = rng.standard_normal((T, m, Lc)).astype(np.float32)
+    sel = np.argsort(-scores, axis=2, kind="stable")[:, :, :k].astype(np.int32)
+    n_sel = np.full((T, m), k, np.int32)
+    want_miss, want_ev = ess.ess_replay_evictions(ess.ESS_EVICT_LRU, C, scores, sel, n_sel)
+    arr = lambda a, t: "{" + ", ".join(f"{x}{t}" for x in a.ravel().tolist()) + "}"
+    src = tmp_path / "use.c"
+    src.write_text(f"""#include <stdio.h>
+#include "ess.h"
+int main(void) {{
+  const float scores[] = {arr(scores, "f")};
+  const int32_t sel[] = {arr(sel, "")};
+  const int32_t n_sel[] = {arr(n_sel, "")};
+  int32_t n_miss[{T}], n_evict[{T}];
+  ess_status s = ess_replay_evictions(ESS_EVICT_LRU, {Lc}, {C}, {T}, {m}, {k}, scores, sel,
+                                      n_sel, 0, 0, n_miss, n_evict);
+  printf("%s\\n", ess_status_string(s));
+  for (int t = 0; t < {T}; ++t) printf("%d %d\\n", n_miss[t], n_evict[t]);
+  s = ess_replay_evictions(ESS_EVICT_LRU, {Lc}, 1, {T}, {m}, {k}, scores, sel, n_sel, 0, 0,
+                           n_miss, n_evict);
+  printf("%s\\n", ess_status_string(s));
+  return 0;
+}}
+""")
+    libdir = os.path.join(ROOT, "decode_lightning_indexer_amd")
+    exe = tmp_path / "use"
+    subprocess.run([gcc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-L", libdir, "-less",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    assert out[0] == "ok"
+    for t in range(T):
+        assert out[1 + t].split() == [str(want_miss[t]), str(want_ev[t])]
+    assert out[1 + T] != "ok"            # a pool smaller than k is refused
