@@ -570,7 +570,6 @@ def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.
     load time.  Exposed time = pipelined - compute only, against the pages'
     per-layer bound max(0, tau_H2D - d_on tau_compute) (d_on = 2 layers for
     the default prefetch) and the serial-link bound."""
-    import ctypes
     import numpy as np
     import torch
     from decode_lightning_indexer_amd import ess
@@ -595,9 +594,6 @@ def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.
     ws = torch.empty(ess.ess_prefill_ws_bytes(rows), dtype=torch.uint8, device=dev)
     sc, sh, sd = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                   ctypes.c_int, ctypes.c_void_p]
     row_b = 576 * 2
 
     def timed(stream, fn, reps=3):
@@ -611,13 +607,14 @@ def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.
         stream.synchronize()
         return ev[0].elapsed_time(ev[1]) / reps * 1e-3
 
+    # The per-layer transfers alone, through the library's copy call (one
+    # HIP runtime in the process).
     def h2d():
-        hip.hipMemcpyAsync(bufs[1].data_ptr(), store.host + row_b * rows, n_hist * row_b,
-                           1, sh.cuda_stream)
+        ess.ess_copy_async(bufs[1].data_ptr(), store.host + row_b * rows, n_hist * row_b, sh)
 
     def d2h():
-        hip.hipMemcpyAsync(store.host + row_b * (rows + n_hist), bufs[1][n_hist:].data_ptr(),
-                           n_new * row_b, 2, sd.cuda_stream)
+        ess.ess_copy_async(store.host + row_b * (rows + n_hist), bufs[1][n_hist:].data_ptr(),
+                           n_new * row_b, sd)
 
     def call(n_layers, reps):
         with torch.cuda.stream(sc):

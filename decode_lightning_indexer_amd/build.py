@@ -52,9 +52,16 @@ HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
               "-x", "c++"]
 
 
-def _compile(src, cc, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    extra = EXTRA.get(os.path.basename(src), [])
+# Host-code sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for a
+# checking build of the library's host paths: every flag applies to the host
+# compilation only (-Xarch_host), the GPU code is built as usual.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src, cc, verbose, out_dir=BUILD, extra_flags=()):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    extra = EXTRA.get(os.path.basename(src), []) + list(extra_flags)
     flags = HOST_FLAGS if src.endswith(".cpp") else FLAGS
     cmd = [cc, *flags, *extra, "-I", os.path.join(ROOT, "include"),
            "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
@@ -82,6 +89,44 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with its host code under ASan + UBSan, for the CPU tests
+    of the host paths (argument checks, the host replay).  It resolves the
+    sanitizer runtime at load time: load it with that runtime preloaded
+    (sanitizer_runtime()).  Returns the library's path (in _build/)."""
+    cc = hipcc()
+    out = os.path.join(BUILD, "asan")
+    os.makedirs(out, exist_ok=True)
+    srcs = sources()
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, cc, verbose, out, SANITIZE), srcs))
+    lib = os.path.join(out, "libess_asan.so")
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(lib + ".tmp", lib)
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too)."""
+    cc = hipcc()
+    r = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "llvm",
+                                     "bin", "clang"), "--print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return hits[-1]
 
 
 if __name__ == "__main__":

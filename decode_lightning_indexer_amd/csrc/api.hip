@@ -6,7 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "ess_host.h"
@@ -37,6 +40,22 @@ ess_status ess::host_fail(ess_status s, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return s;
+}
+
+// The largest dynamic LDS size set so far for each (kernel, device): the
+// attribute call runs only when a launch needs more.
+hipError_t ess::ensure_dyn_lds(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> set;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  int& have = set[{fn, dev}];
+  if (bytes <= have) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 namespace {
@@ -164,6 +183,38 @@ ess_status ess_pool_reset(const ess_dims* d, int32_t* cache_slots,
   hipError_t e = ess::launch_pool_reset(*d, cache_slots, slot_pos, lru_state,
                                         stream);
   return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_pool_status(const ess_dims* d, const void* lru_state,
+                           int32_t* status, hipStream_t stream) {
+  const char* fn = "ess_pool_status";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  ESS_NONNULL(lru_state);
+  ESS_NONNULL(status);
+  hipError_t e = ess::launch_pool_status(*d, lru_state, status, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_copy_async(void* dst, const void* src, size_t bytes,
+                          hipStream_t stream) {
+  const char* fn = "ess_copy_async";
+  ESS_NONNULL(dst);
+  ESS_NONNULL(src);
+  if (bytes == 0) return ESS_OK;
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
+ess_status ess_thread_release(void) {
+  hipError_t first = hipSuccess;
+  for (hipEvent_t e : g_events) {
+    const hipError_t r = hipEventDestroy(e);
+    if (first == hipSuccess) first = r;
+  }
+  g_events.clear();
+  g_events.shrink_to_fit();
+  return first == hipSuccess ? ESS_OK : hip_fail(first, "ess_thread_release");
 }
 
 ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,

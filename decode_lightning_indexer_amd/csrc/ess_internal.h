@@ -50,8 +50,10 @@ struct LruHeader {
   int32_t free_head;  // slots [free_head, C) have never been used
   int32_t epoch;      // stamp of the next update
   int32_t cap;        // ring capacity in entries
-  int32_t err;        // nonzero: victim scan ran dry (state inconsistent)
-  int32_t pad[2];
+  int32_t err;        // 0 ok; 1 the victim scan ran dry (state inconsistent);
+                      // 2 a selected position was outside [0, L)
+  int32_t compactions;  // times the ring was compacted since the reset
+  int32_t pad;
 };
 __host__ __device__ inline int lru_ring_cap(int C) { return 4 * C; }
 inline size_t lru_bytes_per_req(int C) {
@@ -62,6 +64,11 @@ inline size_t lru_bytes_per_req(int C) {
 
 hipError_t launch_pool_reset(const ess_dims& d, int32_t* cache_slots,
                              int32_t* slot_pos, void* lru, hipStream_t s);
+// status[b][0..4) = (err, compactions, epoch, live ring entries) of request b.
+hipError_t launch_pool_status(const ess_dims& d, const void* lru,
+                              int32_t* status, hipStream_t s);
+// hipFuncSetAttribute(MaxDynamicSharedMemorySize) once per kernel and device.
+hipError_t ensure_dyn_lds(const void* fn, int bytes);
 // Top-k and residency update of one query token per request in one kernel
 // (select_update_fits tells when it applies).
 bool select_update_fits(const ess_dims& d, int k, int n_tok);

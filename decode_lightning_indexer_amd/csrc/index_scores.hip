@@ -130,9 +130,12 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 #pragma unroll
   for (int j = 0; j < MT; ++j) nv[j] = n_vis[b * MT + j];
 
-  const uint8_t* kb = keys + (size_t)b * L * DI;
   const int span0 = blockIdx.x * kSpan;
   const int span1 = min(L, span0 + kSpan);
+  // The staging loads take a 64-bit base at this workgroup's first row and
+  // a 32-bit lane offset below kSpan * DI bytes, so no offset wraps however
+  // long the context is.
+  const uint8_t* kb = keys + ((size_t)b * L + span0) * DI;
 
   // Copy rows [p, p + kRows) into buffer `which`: load j writes slots
   // 64 j .. 64 j + 63, i.e. rows 64 j / kSlots + lane / kSlots, slot
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     for (int j = 0; j < S::kLoads; ++j) {
       const int r = j * (64 / S::kSlots) + lr;           // row in the buffer
       const int pc = S::slot(r, ls);                     // piece in that slot
-      const int row = min(p + r, L - 1);
+      const int row = min(p + r, L - 1) - span0;
       const uint32_t off = (uint32_t)row * DI + pc * 16;
       load_lds16(kb, off, buf + j * 1024);
     }
@@ -231,9 +234,7 @@ hipError_t launch_t(const ess_dims& d, const uint8_t* q, const float* w,
                     hipStream_t s) {
   dim3 grid((d.ctx_len + kSpan - 1) / kSpan, d.batch);
   const size_t lds = (size_t)(kThreads / 64) * 2 * Stage<DI>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)index_scores_kernel<DI, NT, MT>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = ensure_dyn_lds((const void*)index_scores_kernel<DI, NT, MT>, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((index_scores_kernel<DI, NT, MT>), grid, dim3(kThreads),
                      lds, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads);

@@ -47,7 +47,21 @@ __global__ __launch_bounds__(NT) void pool_reset_kernel(
     h->epoch = 0;
     h->cap = lru_ring_cap(C);
     h->err = 0;
+    h->compactions = 0;
+    h->pad = 0;
   }
+}
+
+__global__ void pool_status_kernel(const void* lru, size_t stride, int B,
+                                   int32_t* __restrict__ status) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const LruHeader* h = reinterpret_cast<const LruHeader*>(
+      static_cast<const char*>(lru) + stride * b);
+  status[4 * b + 0] = h->err;
+  status[4 * b + 1] = h->compactions;
+  status[4 * b + 2] = h->epoch;
+  status[4 * b + 3] = h->tail - h->head;
 }
 
 // One 1024-thread workgroup per request.
@@ -70,6 +84,14 @@ hipError_t launch_pool_reset(const ess_dims& d, int32_t* cache_slots,
   return hipGetLastError();
 }
 
+hipError_t launch_pool_status(const ess_dims& d, const void* lru,
+                              int32_t* status, hipStream_t s) {
+  const size_t stride = lru_bytes_per_req(d.pool_slots);
+  hipLaunchKernelGGL(pool_status_kernel, dim3((d.batch + 255) / 256), dim3(256), 0,
+                     s, lru, stride, d.batch, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               const int32_t* sel_pos, const int32_t* n_sel,
                               int32_t* cache_slots, int32_t* slot_pos,
@@ -86,9 +108,7 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
   int bits = 0;
   while ((1 << bits) < d.ctx_len) ++bits;
   const int pos_shift = bits > 11 ? bits - 11 : 0;
-  hipError_t e = hipFuncSetAttribute((const void*)pool_update_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)(kMaxTopk * sizeof(uint64_t)));
+  hipError_t e = ensure_dyn_lds((const void*)pool_update_kernel, (int)(kMaxTopk * sizeof(uint64_t)));
   if (e != hipSuccess) return e;
   const pool::Args a{sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
                      miss_pos, miss_slot, n_miss, n_evict, row_dst,

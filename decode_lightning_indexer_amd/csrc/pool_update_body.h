@@ -283,6 +283,7 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
     }
     head = 0;
     tail = dst;
+    if (tid == 0) h->compactions += 1;
   }
 
   // 6. Push the union in ascending position order with current slots, and
@@ -309,8 +310,10 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
     h->tail = tail + (int)n_u;
     h->free_head = free_head + use_free;
     h->epoch = epoch + 1;
-    a.n_miss_out[b] = (int)n_miss;
-    a.n_evict_out[b] = n_ev;
+    // A dry victim scan (flagged) leaves misses unpaired: the copy list and
+    // the counts hold the paired ones only.
+    a.n_miss_out[b] = use_free + found;
+    a.n_evict_out[b] = found;
   }
 }
 

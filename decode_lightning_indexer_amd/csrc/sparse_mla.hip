@@ -37,8 +37,11 @@
 // with one workgroup barrier per tile and no registers held for staging.
 // Padding and unusable rows load a zero row.  At the end the second
 // sub-group's running state is merged into the first's through LDS, and the
-// chunk's partial is written normalised, in fp16, with its running max and
-// sum in fp32.
+// chunk's partial is written normalised, in fp16 scaled by a power of two per
+// (head, half of the value columns) so that the half's largest magnitude
+// lies in [0.5, 1): the stored values keep fp16's 11 significant bits
+// whatever the latents' range (no overflow above 65504, no subnormals for
+// small latents).  The running max and sum and the two scales are fp32.
 //   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
 //                                           rows from LDS, B = Q in registers
 //   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T, B = P in registers
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ host, const unsigned char* __restrict__ entries,
     TailView tail, _Float16* __restrict__ part_acc,
-    float2* __restrict__ part_ml, int L, int C, int m, int H, int k,
+    float4* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
   constexpr int NT = 2 * WPS * 64;
@@ -477,16 +480,19 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   }
   const float wm = sg == 0 ? w0 : w1, wo = sg == 0 ? w1 : w0;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c.
+  // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c, this
+  // sub-group's half of the columns.  The half's largest magnitude (over the
+  // four lane groups that hold the head) sets a power-of-two scale 2^e with
+  // amax * 2^-e in [0.5, 1); multiplying by 2^-e is exact.
   _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal +
                  sg * (kVal / 2) + g * 4;
   const v4f* theirs = ostage + (size_t)((1 - sg) * WPS + wv) * kHalf * 64 + lane;
+  v4f fin[kHalf];
 #define ESS_MLA_FINISH(BASE)                                                   \
   _Pragma("unroll") for (int u = 0; u < kHalf; ++u) {                          \
     v4f o = oacc[(BASE) + u] * wm;                                             \
     if (wo != 0.f) o += theirs[u * 64] * wo;                                   \
-    o *= inv;                                                                  \
-    *reinterpret_cast<v4h*>(pa + u * 16) = __builtin_convertvector(o, v4h);    \
+    fin[u] = o * inv;                                                          \
   }
   if (sg == 0) {
     ESS_MLA_FINISH(0)
@@ -494,30 +500,51 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     ESS_MLA_FINISH(kHalf)
   }
 #undef ESS_MLA_FINISH
-  if (sg == 0 && g == 0)
-    part_ml[((size_t)bj * nchunk + chunk) * H + h0 + c] = make_float2(M, l);
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < kHalf; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(fin[u][r]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int ex = 0;
+  if (amax > 0.f && amax <= 3.0e38f) (void)frexpf(amax, &ex);
+  const float down = ldexpf(1.f, -ex);
+#pragma unroll
+  for (int u = 0; u < kHalf; ++u)
+    *reinterpret_cast<v4h*>(pa + u * 16) = __builtin_convertvector(fin[u] * down, v4h);
+  float* ml = reinterpret_cast<float*>(part_ml + ((size_t)bj * nchunk + chunk) * H + h0 + c);
+  if (g == 0) {
+    if (sg == 0) {
+      ml[0] = M;
+      ml[1] = l;
+    }
+    ml[2 + sg] = ldexpf(1.f, ex);
+  }
 }
 
 // Merge the chunk partials of one (request, token, head) in chunk order;
-// each partial is normalised, so its weight is 2^(m - M) times its sum.
-// 64 threads per head, 8 values each (16-byte fp16 loads), 4 heads per
-// workgroup.  Chunks go in groups of 8 whose loads are all in flight
-// together, folded in with a running maximum (fixed order).
+// each partial is normalised, so its weight is 2^(m - M) times its sum, and
+// its stored values are multiplied back by their half's scale.  64 threads
+// per head, 8 values each (16-byte fp16 loads), 4 heads per workgroup.
+// Chunks go in groups of 8 whose loads are all in flight together, folded
+// in with a running maximum (fixed order).
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 constexpr int kCombineHeads = 4;
 constexpr int kCombineGroup = 8;
 __global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
-    const _Float16* __restrict__ part_acc, const float2* __restrict__ part_ml,
+    const _Float16* __restrict__ part_acc, const float4* __restrict__ part_ml,
     float* __restrict__ out, float* __restrict__ lse, int H, int nchunk) {
   const int bj = blockIdx.y;
   const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
   const int t = threadIdx.x & 63;
-  const float2* ml = part_ml + (size_t)bj * nchunk * H + h;
+  const bool hi_half = t * 8 >= kVal / 2;      // this thread's columns' scale
+  const float4* ml = part_ml + (size_t)bj * nchunk * H + h;
   const _Float16* pp = part_acc + ((size_t)bj * nchunk * H + h) * kVal + t * 8;
   float M = -__builtin_inff(), den = 0.f;
   v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
   for (int c0 = 0; c0 < nchunk; c0 += kCombineGroup) {
-    float2 v[kCombineGroup];
+    float4 v[kCombineGroup];
     v8h x[kCombineGroup];
 #pragma unroll
     for (int u = 0; u < kCombineGroup; ++u) {
@@ -539,9 +566,10 @@ __global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
 #pragma unroll
     for (int u = 0; u < kCombineGroup; ++u) {
       const float w = v[u].y > 0.f ? exp2f(v[u].x - M) * v[u].y : 0.f;
+      const float ws = w * (hi_half ? v[u].w : v[u].z);
       den += w;
-      a0 += w * __builtin_convertvector(x[u].lo, v4f);
-      a1 += w * __builtin_convertvector(x[u].hi, v4f);
+      a0 += ws * __builtin_convertvector(x[u].lo, v4f);
+      a1 += ws * __builtin_convertvector(x[u].hi, v4f);
     }
   }
   const float inv = 1.f / den;
@@ -557,11 +585,9 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* row_dst, const int32_t* n_sel,
                     uint16_t* pool, const uint16_t* host,
                     const unsigned char* entries, TailView tail,
-                    _Float16* part_acc, float2* part_ml, hipStream_t s) {
+                    _Float16* part_acc, float4* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<WPS, kEnt>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kMlaLds);
+  hipError_t e = ensure_dyn_lds((const void*)sparse_mla_kernel<WPS, kEnt>, (int)kMlaLds);
   if (e != hipSuccess) return e;
   // 1-D grid over (group, token, head group) in whole rounds of 8 XCDs.
   const int groups = d.batch * p.nchunk;
@@ -611,7 +637,7 @@ size_t sparse_mla_ws_bytes(const ess_dims& d, int target_wgs) {
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   return align_up(parts * kVal * sizeof(_Float16), 256) +
-         align_up(parts * sizeof(float2), 256);
+         align_up(parts * sizeof(float4), 256);
 }
 
 hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
@@ -624,7 +650,7 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
   const MlaPlan p = plan_sparse_mla(d, target_wgs);
   const size_t parts = (size_t)d.batch * d.mtp * p.nchunk * d.mla_heads;
   _Float16* part_acc = static_cast<_Float16*>(ws);
-  float2* part_ml = reinterpret_cast<float2*>(
+  float4* part_ml = reinterpret_cast<float4*>(
       static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
 #define ESS_MLA_CASE(W)                                                        \

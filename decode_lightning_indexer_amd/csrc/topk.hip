@@ -721,8 +721,7 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
     const int32_t* fp;
     hipError_t e = enqueue_levels(d, k, n_tok, nl, scores, n_vis, ws, &fk, &fp, s);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)topk_final_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = ensure_dyn_lds((const void*)topk_final_kernel, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_final_kernel, dim3(d.batch * n_tok), dim3(NT), lds, s,
                        fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
@@ -732,8 +731,7 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
   // Rows of at most one chunk stay in registers for all passes.
   const bool res = d.ctx_len <= CHUNK;
   const void* fn = res ? (const void*)topk_kernel<true> : (const void*)topk_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = ensure_dyn_lds(fn, (int)lds);
   if (e != hipSuccess) return e;
   if (res)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
@@ -779,8 +777,7 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
   const void* fn = nl > 0 ? (const void*)select_update_kernel<true, true>
                    : res  ? (const void*)select_update_kernel<true, false>
                           : (const void*)select_update_kernel<false, false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = ensure_dyn_lds(fn, (int)lds);
   if (e != hipSuccess) return e;
   if (nl > 0) {
     e = enqueue_levels(d, k, 1, nl, scores, n_vis, ws, &fk, &fp, s);

@@ -8,7 +8,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libess.so")
+# ESS_LIB names another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree libess.so.
+LIB_PATH = os.environ.get("ESS_LIB") or os.path.join(HERE, "libess.so")
 
 ESS_OK = 0
 ESS_ERR_INVALID = -1
@@ -34,6 +36,7 @@ EXPORTED = (
     "ess_host_alloc", "ess_host_free", "ess_replay_evictions",
     "ess_tail_init", "ess_tail_release", "ess_append_tokens",
     "ess_prefill_ws_bytes", "ess_prefill_layers",
+    "ess_pool_status", "ess_copy_async", "ess_thread_release",
     "ess_status_string", "ess_last_error",
 )
 
@@ -137,6 +140,9 @@ def lib():
             "ess_prefill_ws_bytes": (_S, [_I]),
             "ess_prefill_layers": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _S,
                                         _P, _P, _I, _I, _P, _P, _P]),
+            "ess_pool_status": (_I, [D, _P, _P, _P]),
+            "ess_copy_async": (_I, [_P, _P, _S, _P]),
+            "ess_thread_release": (_I, []),
             "ess_status_string": (ctypes.c_char_p, [_I]),
             "ess_last_error": (ctypes.c_char_p, []),
         }
@@ -145,7 +151,16 @@ def lib():
             f.restype = res
             f.argtypes = args
         _lib = L
+        # Before the interpreter exits (and so before the HIP runtime's
+        # static destructors run): the main thread's stream-ordering events.
+        import atexit
+        atexit.register(_release_at_exit)
     return _lib
+
+
+def _release_at_exit():
+    if _lib is not None:
+        _lib.ess_thread_release()
 
 
 def _ptr(t):
@@ -191,6 +206,23 @@ def ess_pool_reset(d, cache_slots, slot_pos, lru_state, stream=None):
     _check("ess_pool_reset", lib().ess_pool_reset(
         ctypes.byref(d), _ptr(cache_slots), _ptr(slot_pos), _ptr(lru_state),
         _stream(stream)))
+
+
+def ess_pool_status(d, lru_state, status, stream=None):
+    """status: device int32 [B][4] <- (err, compactions, updates, ring entries)."""
+    _check("ess_pool_status", lib().ess_pool_status(
+        ctypes.byref(d), _ptr(lru_state), _ptr(status), _stream(stream)))
+
+
+def ess_copy_async(dst, src, nbytes, stream=None):
+    """Copy nbytes between device memory and pinned host memory (addresses or
+    tensors) on the stream."""
+    _check("ess_copy_async", lib().ess_copy_async(_ptr(dst), _ptr(src), nbytes,
+                                                  _stream(stream)))
+
+
+def ess_thread_release():
+    _check("ess_thread_release", lib().ess_thread_release())
 
 
 def ess_index_scores(d, q_fp8, w, k_fp8, n_vis, scores, stream=None):

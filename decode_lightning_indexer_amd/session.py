@@ -6,6 +6,7 @@ a NumPy array over the host address, so it can be filled in place.  Nothing
 here computes any step of the path.
 """
 import ctypes
+import weakref
 
 import numpy as np
 import torch
@@ -23,18 +24,15 @@ class HostStore:
         self.host, self.dev = ess.ess_host_alloc(self.nbytes)
         buf = (ctypes.c_uint8 * self.nbytes).from_address(self.host)
         self.array = np.frombuffer(buf, dtype=self.dtype).reshape(self.shape)
+        # Freed by free(), when the object is collected, or at the latest by
+        # the interpreter's exit handlers, before the HIP runtime is torn down.
+        self._fin = weakref.finalize(self, ess.ess_host_free, self.host)
 
     def free(self):
         if self.host:
             self.array = None
-            ess.ess_host_free(self.host)
+            self._fin()
             self.host = self.dev = 0
-
-    def __del__(self):
-        try:
-            self.free()
-        except Exception:
-            pass
 
 
 def dims_of(wl, **over) -> ess.ess_dims:

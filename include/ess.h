@@ -55,8 +55,10 @@ extern "C" {
 
 /* Problem shape of one layer.
  *   batch      B  requests
- *   mtp        m  query tokens per step per request (MTP ways sharing a pool)
- *   ctx_len    L  cached positions per request
+ *   mtp        m  query tokens per step per request (MTP ways sharing a pool;
+ *                 1 .. 4)
+ *   ctx_len    L  cached positions per request (1 .. 2^28; offsets into
+ *                 every [B][L][...] array are 64-bit)
  *   idx_heads  H_I indexer heads (multiple of 16; mtp*idx_heads <= 128)
  *   idx_dim    d_I indexer dimension (64 or 128)
  *   mla_heads  H  absorbed-MLA query heads (16, 32, 48, ... 128)
@@ -95,6 +97,21 @@ size_t ess_lru_state_bytes(const ess_dims* d);
 ess_status ess_pool_reset(const ess_dims* d, int32_t* cache_slots,
                           int32_t* slot_pos, void* lru_state,
                           hipStream_t stream);
+
+/* Health of the pool state after the updates so far, per request, for
+ * diagnosing caller errors (FlashOffloading analysis, "five steps and the MTP
+ * union": every miss is paired with one victim, so the pool size stays C).
+ * Writes status [B][4] int32 (device memory) on the stream:
+ *   [0] err: 0 consistent; 1 an update found fewer victims than misses
+ *       (the state was corrupted, e.g. by a foreign write): its unpaired
+ *       misses are left out of the copy list, n_miss counts the paired
+ *       ones only, and those rows stay unresident; 2 a selected position was
+ *       outside [0, ctx_len) (it was dropped);
+ *   [1] times the recency ring was compacted since ess_pool_reset;
+ *   [2] updates applied since ess_pool_reset (the first fill included);
+ *   [3] entries on the recency ring (live and dead). */
+ess_status ess_pool_status(const ess_dims* d, const void* lru_state,
+                           int32_t* status, hipStream_t stream);
 
 /* Indexer scores (the indexer scores all L positions every step: ESS concept
  * page, "dual cache" table; score form: the DSA lightning indexer):
@@ -470,6 +487,20 @@ ess_status ess_replay_evictions(int32_t policy, int32_t ctx_len,
                                 const int32_t* n_sel, uint64_t seed,
                                 int32_t request, int32_t* n_miss,
                                 int32_t* n_evict);
+
+/* Asynchronous copy of `bytes` bytes on the stream between any two of
+ * device memory and pinned host memory (hipMemcpyDefault: the direction
+ * follows from the addresses); for callers that stage data without a HIP
+ * runtime handle of their own.  0 bytes: nothing is enqueued. */
+ess_status ess_copy_async(void* dst, const void* src, size_t bytes,
+                          hipStream_t stream);
+
+/* Destroy the stream-ordering events the calling thread's calls created
+ * (they are otherwise kept for the thread's later calls).  Call it once the
+ * thread's work has completed and before the HIP runtime is torn down
+ * (e.g. at process exit, before static destructors run); a later call on
+ * the thread creates new ones. */
+ess_status ess_thread_release(void);
 
 const char* ess_status_string(ess_status s);
 /* Message of the last failing call on this thread ("" if none). */

@@ -84,11 +84,15 @@ def dequantized_latents(wl, layer):
 
 
 def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None,
-                 store="bf16"):
+                 store="bf16", keep=None, keep_layers=None, score_requests=()):
     """Fill + steps on the GPU; per step and layer, every output as numpy.
     store: "bf16" (generated latents as bf16 rows), "entries" (656-byte fp8
     entries of them) or "dequantized" (bf16 rows of the dequantized
-    entries)."""
+    entries).  keep: the requests whose outputs are recorded (all if None;
+    arrays keep the request axis, other requests' rows are zero);
+    keep_layers: the layers recorded (all if None); score_requests: requests
+    whose whole score rows are recorded every step.  recs["status"][l] is
+    the layer's ess_pool_status after the last step."""
     steps = wl.steps if steps is None else steps
     layers = wl.layers if layers is None else layers
     d = dims_of(wl)
@@ -123,25 +127,44 @@ def gpu_sequence(wl, steps=None, mode=ess.ESS_MODE_INLINE, layers=None,
         ins[l].upload_step(run.layers[l], 0)
     run.fill()
     sync()
-    recs = {"fill": [], "steps": []}
+    recs = {"fill": [], "steps": [], "status": []}
     for l, lb in enumerate(run.layers):
         nm = h(lb.n_miss)
         mp = h(lb.lists(lb.miss_pos, C))
         recs["fill"].append(dict(n_miss=nm, miss_pos=mp, miss_slot=h(lb.lists(lb.miss_slot, C))))
+    kept = list(range(B)) if keep is None else list(keep)
+    kl = set(range(layers)) if keep_layers is None else set(keep_layers)
+
+    def rec(x):
+        a = h(x)
+        if keep is None:
+            return a
+        r = np.zeros_like(a)
+        r[kept] = a[kept]
+        return r
     for t in range(steps):
         for l in range(layers):
             ins[l].upload_step(run.layers[l], t)
         run.step(mode)
         sync()
         per = []
-        for lb in run.layers:
+        for l, lb in enumerate(run.layers):
+            if l not in kl:
+                per.append(None)
+                continue
             per.append(dict(
-                sel_pos=h(lb.rows(lb.sel_pos, k, m)), sel_slot=h(lb.rows(lb.sel_slot, k, m)),
-                n_sel=h(lb.n_sel), row_dst=h(lb.rows(lb.row_dst, k, m)),
-                sel_slot_post=h(lb.rows(lb.sel_slot_post, k, m)),
-                miss_pos=h(lb.lists(lb.miss_pos, m * k)), miss_slot=h(lb.lists(lb.miss_slot, m * k)),
-                n_miss=h(lb.n_miss), n_evict=h(lb.n_evict), out=h(lb.out), lse=h(lb.lse)))
+                sel_pos=rec(lb.rows(lb.sel_pos, k, m)), sel_slot=rec(lb.rows(lb.sel_slot, k, m)),
+                n_sel=h(lb.n_sel), row_dst=rec(lb.rows(lb.row_dst, k, m)),
+                sel_slot_post=rec(lb.rows(lb.sel_slot_post, k, m)),
+                miss_pos=rec(lb.lists(lb.miss_pos, m * k)), miss_slot=rec(lb.lists(lb.miss_slot, m * k)),
+                n_miss=h(lb.n_miss), n_evict=h(lb.n_evict), out=rec(lb.out), lse=rec(lb.lse),
+                scores={b: h(lb.scores[b]) for b in score_requests}))
         recs["steps"].append(per)
+    for lb in run.layers:
+        st = torch.empty((B, 4), dtype=torch.int32, device=DEV)
+        ess.ess_pool_status(d, lb.lru, st)
+        sync()
+        recs["status"].append(h(st))
     # Every resident slot holds its host row.
     for l, lb in enumerate(run.layers):
         cs, pool = h(lb.cache_slots), h(lb.pool)
@@ -164,9 +187,11 @@ def compare_with_oracle(wl, recs, layer=0, requests=None, steps=None,
     steps = len(recs["steps"]) if steps is None else steps
     worst = 0.0
     for b in requests:
+        want_scores = b in recs["steps"][0][layer].get("scores", {})
         it = odecode.run_workload_request(
             wl, layer, b, steps=steps, host=None if host is None else host[b],
-            grow_from=grow_from[b] if isinstance(grow_from, (list, tuple)) else grow_from)
+            grow_from=grow_from[b] if isinstance(grow_from, (list, tuple)) else grow_from,
+            keep_scores=want_scores)
         fill = next(it)
         g = recs["fill"][layer]
         n = int(g["n_miss"][b])
@@ -175,6 +200,9 @@ def compare_with_oracle(wl, recs, layer=0, requests=None, steps=None,
         assert np.array_equal(g["miss_slot"][b, :n], fill["miss_slot"])
         for t, ref in enumerate(it):
             g = recs["steps"][t][layer]
+            if want_scores:
+                # Whole score rows, bit for bit (-inf past n_vis included).
+                assert np.array_equal(g["scores"][b].astype(np.float64), ref["scores"]), (b, t)
             for key in ("sel_pos", "sel_slot", "n_sel", "row_dst", "sel_slot_post"):
                 assert np.array_equal(g[key][b], ref[key]), (key, b, t)
             n = int(g["n_miss"][b])

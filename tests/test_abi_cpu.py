@@ -267,10 +267,42 @@ int main(void) {{
     libdir = os.path.join(ROOT, "decode_lightning_indexer_amd")
     exe = tmp_path / "use"
     subprocess.run([gcc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
-                    "-I", "/opt/rocm/include", str(src), "-L", libdir, "-less",
-                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+                    "-I", "/opt/rocm/include", str(src), ess.LIB_PATH,
+                    f"-Wl,-rpath,{libdir}", "-Wl,--allow-shlib-undefined", "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
     assert out[0] == "ok"
     for t in range(T):
         assert out[1 + t].split() == [str(want_miss[t]), str(want_ev[t])]
     assert out[1 + T] != "ok"            # a pool smaller than k is refused
+
+
+def test_pool_status_copy_and_release_checks(L):
+    d = _d()
+    assert _status(lambda: ess.ess_pool_status(d, 0, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_pool_status(d, P, 0, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_pool_status(_d(batch=0), P, P, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_copy_async(0, P, 16, stream=0)) == "invalid argument"
+    assert _status(lambda: ess.ess_copy_async(P, 0, 16, stream=0)) == "invalid argument"
+    # Zero bytes enqueue nothing; a thread that created no events releases
+    # nothing.  Neither touches the GPU.
+    ess.ess_copy_async(P, P, 0, stream=0)
+    ess.ess_thread_release()
+
+
+def test_lru_header_layout(L):
+    # Per request: a 32-byte header (head, tail, free_head, epoch, cap, err,
+    # compactions, pad), C int32 stamps and a ring of 4C (slot, stamp) pairs,
+    # rounded up to 256 bytes; ess_pool_status reads the header fields.
+    for C in (1024, 1000, 8192):
+        d = _d(pool_slots=C)
+        per = -(-(32 + 4 * C + 8 * 4 * C) // 256) * 256
+        assert ess.ess_lru_state_bytes(d) == 2 * per
+
+
+def test_long_context_is_accepted_up_to_2_28(L):
+    # Contexts up to 2^28 positions pass the host checks (the kernels use
+    # 64-bit offsets into every [B][L][...] array); beyond, unsupported.
+    big = _d(ctx_len=(1 << 28), idx_dim=128)
+    assert _status(lambda: ess.ess_index_scores(big, 0, P, P, P, P, stream=0)) == "invalid argument"
+    over = _d(ctx_len=(1 << 28) + 1, idx_dim=128)
+    assert _status(lambda: ess.ess_index_scores(over, P, P, P, P, P, stream=0)) == "unsupported shape"

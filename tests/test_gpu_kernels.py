@@ -49,6 +49,33 @@ def test_index_scores_bit_exact(B, m, L, HI, dI, ragged):
         assert np.array_equal(got[b].astype(np.float64), ref), b
 
 
+def test_index_scores_long_context_offsets():
+    # A context past 2^25 positions of 128-byte keys: byte offsets into the
+    # index cache pass 2^32.  Every key is zero except the last 12288 rows
+    # (seeded), so a wrapped offset would read a zero row; the last 8192
+    # scores, on both sides of position 2^25, must equal the oracle's.
+    L, HI, dI, tail = (1 << 25) + 4096, 16, 128, 12288
+    print(f"\n[indexer] L={L} d_I={dI}", flush=True)
+    rng = np.random.default_rng(1 << 25)
+    qi = rng.integers(-7, 8, (1, 1, HI, dI))
+    ki = rng.integers(-7, 8, (tail, dI))
+    ki[rng.random(tail) < 0.05] = 0        # a few zero rows: scores of 0
+    w = rng.integers(1, 5, (1, 1, HI)).astype(np.float32)
+    q8, k8 = gen.encode_e4m3_int(qi), gen.encode_e4m3_int(ki)
+    keys = torch.zeros((1, L, dI), dtype=torch.uint8, device="cuda")
+    keys[0, L - tail:] = torch.from_numpy(k8).to("cuda")
+    n_vis = np.array([[L]], np.int32)
+    d = dims(batch=1, mtp=1, ctx_len=L, idx_heads=HI, idx_dim=dI)
+    scores = torch.empty((1, 1, L), dtype=torch.float32, device="cuda")
+    ess.ess_index_scores(d, t(q8), t(w), keys, t(n_vis), scores)
+    sync()
+    got = h(scores[0, 0, L - 8192:])
+    ref = index_scores(q8[0], w[0], k8[tail - 8192:], [8192])[0]
+    assert np.array_equal(got.astype(np.float64), ref)
+    assert float(scores[0, 0, :L - tail].abs().max()) == 0.0
+    del keys, scores
+
+
 # --------------------------------------------------------------- top-k --
 
 def _scores(kind, rng, shape):
@@ -184,6 +211,51 @@ def test_pool_update_bit_exact(B, m, L, C, k, steps, ragged):
                 sel[b, j, :n] = ways[j][:n]
                 nsel[b, j] = n
         run(k, m, sel, nsel)
+    # The pool status: consistent, one update per call, and the ring
+    # compacted in the long run (60 updates of 16 on a ring of 4 * 64).
+    st = torch.empty((B, 4), dtype=torch.int32, device="cuda")
+    ess.ess_pool_status(d, lru, st)
+    sync()
+    st = h(st)
+    assert (st[:, 0] == 0).all() and (st[:, 2] == steps + 1).all(), st
+    if (C, k, steps) == (64, 16, 60):
+        assert (st[:, 1] >= 1).all(), st
+
+
+def test_pool_status_flags_a_corrupted_ring():
+    # A foreign write kills every recency entry (all slot stamps overwritten)
+    # after the fill: the next update's victim scan runs dry.  The update
+    # flags it, pairs no miss, and reports only paired misses (none), so no
+    # stale copy-list entry is ever handed on.
+    B, L, C, k = 1, 600, 64, 16
+    d = dims(batch=B, ctx_len=L, topk=k, pool_slots=C)
+    cs = torch.empty((B, L), dtype=torch.int32, device="cuda")
+    sp = torch.empty((B, C), dtype=torch.int32, device="cuda")
+    lru = torch.empty(ess.ess_lru_state_bytes(d), dtype=torch.uint8, device="cuda")
+    ess.ess_pool_reset(d, cs, sp, lru)
+    mp = torch.full((B * C,), 7, dtype=torch.int32, device="cuda")
+    ms, rd, post = torch.full_like(mp, 7), torch.empty_like(mp), torch.empty_like(mp)
+    nm = torch.empty(B, dtype=torch.int32, device="cuda")
+    ne = torch.empty_like(nm)
+    fill = np.arange(C, dtype=np.int32)[None, None, :]
+    ess.ess_pool_update(d, C, 1, t(fill), t(np.array([[C]], np.int32)), cs, sp, lru,
+                        mp, ms, nm, ne, rd, post)
+    sync()
+    st = torch.empty((B, 4), dtype=torch.int32, device="cuda")
+    ess.ess_pool_status(d, lru, st)
+    sync()
+    assert h(st)[0].tolist() == [0, 0, 1, C]
+    # Header (8 int32), then the C slot stamps: overwrite the stamps.
+    lru.view(torch.int32)[8:8 + C] = -5
+    sel = np.arange(C, C + k, dtype=np.int32)[None, None, :]     # k misses
+    ess.ess_pool_update(d, k, 1, t(sel), t(np.array([[k]], np.int32)), cs, sp, lru,
+                        mp, ms, nm, ne, rd, post)
+    ess.ess_pool_status(d, lru, st)
+    sync()
+    assert h(st)[0, 0] == 1                 # victim scan ran dry
+    assert int(h(nm)[0]) == 0 and int(h(ne)[0]) == 0
+    assert (h(cs)[0, C:C + k] == -1).all()  # the misses stay unresident
+    assert (h(post)[:k] == -1).all()
 
 
 def test_pool_update_rejects_capacity():
@@ -212,10 +284,23 @@ def _bf16(rng, shape, std):
     (8, 2, 128, 6000, 2048, 4200, True, 0.7),
 ])
 def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
+    _mla_case(B, m, H, L, k, C, ragged, p_hit)
+
+
+@pytest.mark.parametrize("lat_std", [0.5e-4, 0.5e4, 0.5e5])
+def test_sparse_mla_latent_scales(lat_std):
+    # Latents far from unit scale: tiny values (whose partial outputs would
+    # be fp16 subnormals unscaled) and values whose weighted means pass
+    # fp16's largest finite value (65504).
+    print(f"\n[mla] latent std {lat_std}", flush=True)
+    _mla_case(2, 1, 64, 3000, 512, 1024, True, 0.5, lat_std=lat_std)
+
+
+def _mla_case(B, m, H, L, k, C, ragged, p_hit, lat_std=0.5, q_std=0.1):
     rng = np.random.default_rng(H * 7 + k)
     host = HostStore((B, L, 576))
-    host.array[:] = _bf16(rng, (B, L, 576), 0.5)
-    qa = _bf16(rng, (B, m, H, 576), 0.1)
+    host.array[:] = _bf16(rng, (B, L, 576), lat_std)
+    qa = _bf16(rng, (B, m, H, 576), q_std)
     n_sel = np.zeros((B, m), np.int32)
     sel = np.full((B, m, k), -1, np.int32)
     src = np.full((B, m, k), -1, np.int32)
