@@ -339,6 +339,36 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
                          host_view, nullptr, out, lse, ws, ws_bytes, stream);
 }
 
+ess_status ess_sparse_mla_decode_noalloc(const ess_dims* d, const uint16_t* q_abs,
+                                         const int32_t* sel_pos,
+                                         const int32_t* sel_src,
+                                         const int32_t* row_dst,
+                                         const int32_t* n_sel, uint16_t* pool,
+                                         const uint16_t* host_view, float* out,
+                                         float* lse, hipStream_t stream) {
+  const char* fn = "ess_sparse_mla_decode_noalloc";
+  ess_status s = check_dims(d, fn);
+  if (s != ESS_OK) return s;
+  if ((s = check_mla(d, fn)) != ESS_OK) return s;
+  ESS_NONNULL(q_abs);
+  ESS_NONNULL(sel_pos);
+  ESS_NONNULL(sel_src);
+  ESS_NONNULL(n_sel);
+  ESS_NONNULL(pool);
+  ESS_NONNULL(host_view);
+  ESS_NONNULL(out);
+  const size_t need = ess::sparse_mla_ws_bytes(*d);
+  if (need > ess::kNoAllocScratchBytes)
+    return fail(ESS_ERR_NOMEM,
+                "%s: these dims need %zu bytes of scratch; the fixed scratch "
+                "array holds %zu (use ess_sparse_mla_decode with a workspace)",
+                fn, need, ess::kNoAllocScratchBytes);
+  hipError_t e = ess::launch_sparse_mla_noalloc(*d, q_abs, sel_pos, sel_src, row_dst,
+                                                n_sel, pool, host_view, out, lse,
+                                                stream);
+  return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
+}
+
 ess_status ess_sparse_mla_decode_entries(
     const ess_dims* d, const uint16_t* q_abs, const int32_t* sel_pos,
     const int32_t* sel_src, const int32_t* row_dst, const int32_t* n_sel,
@@ -609,7 +639,7 @@ ess_status ess_tail_release(ess_tail* t) {
   if (!t) return ESS_OK;
   if (t->events)
     for (int i = 0; i < 2 * t->batch; ++i)
-      if (t->events[i]) hipEventDestroy(static_cast<hipEvent_t>(t->events[i]));
+      if (t->events[i]) (void)hipEventDestroy(static_cast<hipEvent_t>(t->events[i]));
   std::free(t->events);
   std::free(t->host);
   t->events = nullptr;

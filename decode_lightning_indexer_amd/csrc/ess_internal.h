@@ -119,6 +119,16 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
 // (entries non-null: misses are read from 656-byte fp8 entries [B][L][656]
 // instead of host, and dequantized in the tile.)
 
+// The same gather + attention with its partials in the library's fixed
+// per-device scratch array (kNoAllocScratchBytes) instead of a workspace;
+// the caller checks sparse_mla_ws_bytes(d) <= kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)24 << 20;
+hipError_t launch_sparse_mla_noalloc(const ess_dims& d, const uint16_t* q_abs,
+                                     const int32_t* sel_pos, const int32_t* sel_src,
+                                     const int32_t* row_dst, const int32_t* n_sel,
+                                     uint16_t* pool, const uint16_t* host,
+                                     float* out, float* lse, hipStream_t s);
+
 // ---- miss copy ----------------------------------------------------------
 hipError_t launch_miss_copy(const ess_dims& d, int list_stride,
                             const int32_t* miss_pos, const int32_t* miss_slot,

@@ -65,6 +65,8 @@
 // entry into the last 41 slots of its tile row, and after the tile has
 // landed one wave per miss row expands it in place to the 576 bf16 values
 // the MFMAs and the pool write-back read (a second barrier per tile).
+#include <mutex>
+
 #include "ess_internal.h"
 #include "fp8_entry.h"
 
@@ -671,6 +673,50 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
                      dim3(64 * kCombineHeads), 0, s, part_acc, part_ml, out, lse,
                      d.mla_heads, p.nchunk);
   return hipGetLastError();
+}
+
+// ---- a fixed scratch array for callers that cannot allocate -------------
+//
+// The attention's split-row partials in a file-scope device array instead of
+// a caller workspace.  Each device the library runs on holds its own copy
+// (from module load to process exit); its device address is looked up once
+// per device with that device current and kept.  The array's host-side name
+// is only a stand-in for the symbol: kernels get the looked-up address.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_sparse_mla_noalloc(const ess_dims& d, const uint16_t* q_abs,
+                                     const int32_t* sel_pos, const int32_t* sel_src,
+                                     const int32_t* row_dst, const int32_t* n_sel,
+                                     uint16_t* pool, const uint16_t* host,
+                                     float* out, float* lse, hipStream_t s) {
+  void* ws = nullptr;
+  hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_sparse_mla(d, q_abs, sel_pos, sel_src, row_dst, n_sel, pool, host,
+                           out, lse, ws, s);
 }
 
 }  // namespace ess

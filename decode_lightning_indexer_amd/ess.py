@@ -37,6 +37,7 @@ EXPORTED = (
     "ess_tail_init", "ess_tail_release", "ess_append_tokens",
     "ess_prefill_ws_bytes", "ess_prefill_layers",
     "ess_pool_status", "ess_copy_async", "ess_thread_release",
+    "ess_sparse_mla_decode_noalloc",
     "ess_status_string", "ess_last_error",
 )
 
@@ -141,6 +142,8 @@ def lib():
             "ess_prefill_layers": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _S,
                                         _P, _P, _I, _I, _P, _P, _P]),
             "ess_pool_status": (_I, [D, _P, _P, _P]),
+            "ess_sparse_mla_decode_noalloc": (_I, [D, _P, _P, _P, _P, _P, _P, _P,
+                                                   _P, _P, _P]),
             "ess_copy_async": (_I, [_P, _P, _S, _P]),
             "ess_thread_release": (_I, []),
             "ess_status_string": (ctypes.c_char_p, [_I]),
@@ -255,6 +258,14 @@ def ess_sparse_mla_decode(d, q_abs, sel_pos, sel_src, row_dst, n_sel, pool,
         ctypes.byref(d), _ptr(q_abs), _ptr(sel_pos), _ptr(sel_src),
         _ptr(row_dst), _ptr(n_sel), _ptr(pool), _ptr(host_view), _ptr(out),
         _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ess_sparse_mla_decode_noalloc(d, q_abs, sel_pos, sel_src, row_dst, n_sel,
+                                  pool, host_view, out, lse, stream=None):
+    _check("ess_sparse_mla_decode_noalloc", lib().ess_sparse_mla_decode_noalloc(
+        ctypes.byref(d), _ptr(q_abs), _ptr(sel_pos), _ptr(sel_src),
+        _ptr(row_dst), _ptr(n_sel), _ptr(pool), _ptr(host_view), _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def ess_sparse_mla_decode_entries(d, q_abs, sel_pos, sel_src, row_dst, n_sel,

@@ -213,6 +213,26 @@ ess_status ess_sparse_mla_decode(const ess_dims* d, const uint16_t* q_abs,
                                  float* out, float* lse, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* ess_sparse_mla_decode for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and result, with
+ * the split-row partials in a fixed scratch array of 24 MiB that the library
+ * holds on each device it runs on, from its first use there until the
+ * process ends.  No allocation happens in the call.  Dims whose partials
+ * exceed it (ess_workspace_bytes's attention part: 2 * 512 + 16 bytes per
+ * request, token, head and row chunk) are refused with ESS_ERR_NOMEM before
+ * anything is enqueued.  Every call on one device shares that device's
+ * array: calls that overlap on one device (on different streams or host
+ * threads) race and give wrong results; order them.  Other arguments and
+ * errors as in ess_sparse_mla_decode. */
+ess_status ess_sparse_mla_decode_noalloc(const ess_dims* d, const uint16_t* q_abs,
+                                         const int32_t* sel_pos,
+                                         const int32_t* sel_src,
+                                         const int32_t* row_dst,
+                                         const int32_t* n_sel, uint16_t* pool,
+                                         const uint16_t* host_view, float* out,
+                                         float* lse, hipStream_t stream);
+
 /* The same with a host store of 656-byte fp8 latent entries (layout under
  * ess_miss_copy_entries): every miss row (sel_src[i] < 0) is read from
  * entry_view[b][sel_pos[i]] (656 bytes over the host link) and dequantized in

@@ -306,3 +306,15 @@ def test_long_context_is_accepted_up_to_2_28(L):
     assert _status(lambda: ess.ess_index_scores(big, 0, P, P, P, P, stream=0)) == "invalid argument"
     over = _d(ctx_len=(1 << 28) + 1, idx_dim=128)
     assert _status(lambda: ess.ess_index_scores(over, P, P, P, P, P, stream=0)) == "unsupported shape"
+
+
+def test_noalloc_refuses_dims_beyond_its_array(L):
+    # The no-allocation attention holds 24 MiB of partials per device: dims
+    # needing more are refused on the host, anything smaller passes the size
+    # check (and here fails on a NULL pointer instead).
+    big = _d(batch=64, mla_heads=128, topk=2048, pool_slots=4096)
+    st = _status(lambda: ess.ess_sparse_mla_decode_noalloc(big, P, P, P, P, P, P, P, P, P, stream=0))
+    assert st == "out of memory" and "scratch" in L.ess_last_error().decode()
+    small = _d(batch=16, mla_heads=128, topk=2048, pool_slots=8192)
+    st = _status(lambda: ess.ess_sparse_mla_decode_noalloc(small, P, P, P, P, P, P, 0, P, P, stream=0))
+    assert st == "invalid argument"
