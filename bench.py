@@ -66,35 +66,66 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle, as is, on the same workload: requests 0, 1, ... each run
-    from its fill through its steps, until about `seconds` of step time
-    (fill and input generation excluded) have been spent."""
+def host_machine():
+    """The host the oracle runs on: logical CPUs, the ones this process may
+    use, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+
+
+def cpu_baseline(wl, seconds, requests=None, layers=1):
+    """The oracle, as is, on the same workload: (layer, request) sequences in
+    order - layers 0.. of requests 0, 1, ... (or the given requests) - each
+    run from its fill through its steps, until about `seconds` of step time
+    (fill and input generation excluded) have been spent.  A workload step
+    is B * layers request-layer-steps of oracle work for B * m query
+    tokens, so query-tok/s = m * (request-layer-steps per second) / layers;
+    with sampled requests or layers the figure is extrapolated that way."""
     from oracle import decode as odecode
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    n, spent, reqs = 0, 0.0, 0
-    for b in range(wl.batch):
-        it = odecode.run_workload_request(wl, 0, b, check_pool=False)
-        next(it)                                  # the fill (untimed)
-        reqs += 1
-        while spent < seconds:
-            t0 = time.perf_counter()
-            try:
-                next(it)
-            except StopIteration:
+    requests = list(range(wl.batch)) if requests is None else list(requests)
+    n, spent, seqs = 0, 0.0, []
+    for b in requests:
+        for layer in range(layers):
+            it = odecode.run_workload_request(wl, layer, b, check_pool=False)
+            next(it)                              # the fill (untimed)
+            seqs.append((layer, b))
+            while spent < seconds:
+                t0 = time.perf_counter()
+                try:
+                    next(it)
+                except StopIteration:
+                    break
+                spent += time.perf_counter() - t0
+                n += 1
+            if spent >= seconds:
                 break
-            spent += time.perf_counter() - t0
-            n += 1
         if spent >= seconds:
             break
-    return {"value": n * wl.mtp / spent, "unit": "query-tok/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} request-steps of {wl.name} (requests 0..{reqs - 1}, "
-                      f"fill excluded), {spent:.1f} s of step time"}
+    sampled = layers > 1 or len(seqs) < wl.batch * layers
+    return {"value": wl.mtp * n / spent / layers, "unit": "query-tok/s",
+            "cores": int(cores), "kind": "oracle",
+            "steps_per_s": n / spent / (wl.batch * layers),
+            "extrapolated": sampled,
+            "sample": f"{n} request-layer-steps of {wl.name} over (layer, request) "
+                      f"{seqs[0]}..{seqs[-1]} ({len(seqs)} sequences, fills excluded), "
+                      f"{spent:.1f} s of step time"
+                      + (f"; one step = {wl.batch} requests x {layers} layers, "
+                         "scaled from the sample" if sampled else "")}
 
 
 # Kernels whose counters give roofline.traffic, with the source each is
@@ -269,18 +300,35 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
 
     steps = [ios(t) for t in range(W + K)]
     res = {}
+    n_miss_steps = torch.zeros(K, dtype=torch.int64, device=dev)
     for mode in modes:
         for lb in lbs:
             lb.reset(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
         ess.ess_decode_step(d, steps[0], n_vis, ess.ESS_MODE_FILL, stream)
+        ev[1].record(stream)
         for t in range(W):
             ess.ess_decode_step(d, steps[t], n_vis, mode, stream, side)
         torch.cuda.synchronize()
+        res.setdefault("fill", ev[0].elapsed_time(ev[1]) * 1e-3)
         t1 = time.perf_counter()
         for i in range(K):
             ess.ess_decode_step(d, steps[W + i], n_vis, mode, stream, side)
         torch.cuda.synchronize()
         res[mode] = (time.perf_counter() - t1) / K
+        if mode == modes[0]:
+            # Misses per timed step (the same steps again, counted: the
+            # timed pass records nothing between its calls).
+            for lb in lbs:
+                lb.reset(stream)
+            ess.ess_decode_step(d, steps[0], n_vis, ess.ESS_MODE_FILL, stream)
+            for t in range(W + K):
+                ess.ess_decode_step(d, steps[t], n_vis, mode, stream, side)
+                if t >= W:
+                    n_miss_steps[t - W] = sum(lb.n_miss.sum() for lb in lbs)
+            torch.cuda.synchronize()
+            res["misses_per_step"] = float(n_miss_steps.double().mean())
     n_miss = sum(int(lb.n_miss.sum()) for lb in lbs)
     # The last step's miss lists copied again, alone: host-link time of a step.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -313,7 +361,138 @@ def run_steps(args, name, n_layers, modes, K, W, resident=False, store="bf16"):
     return res, n_miss, t_copy, wl
 
 
-def multilayer(args, n_layers=16, K=16, W=4):
+def overlap_split(d, lb, qi, qa, n_vis, ts, stream, host_dev):
+    """The pages' OverlapRatio (FlashOffloading analysis, "numbers: 1.03x to
+    1.27x") on steps ts, each selected through the per-stage calls, then its
+    gather + attention timed three ways with HIP events on the launch
+    stream: T_fused = the call with per-row writer slots (the misses read
+    from host memory inside the attention kernel and written to their
+    slots), T_copy = the step's miss list copied host -> pool alone, T_attn
+    = the attention with every row read from the pool.  Returns the mean
+    times (us), the ratio (T_copy + T_attn - T_fused) / T_copy, its physical
+    bound min(1, T_attn / T_copy) and the misses per step."""
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    m, k = d.mtp, d.topk
+    sel_pos, sel_slot = lb.rows(lb.sel_pos, k, m), lb.rows(lb.sel_slot, k, m)
+    row_dst, post = lb.rows(lb.row_dst, k, m), lb.rows(lb.sel_slot_post, k, m)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in ts]
+    n_miss = torch.zeros(len(ts), dtype=torch.int64, device=lb.n_miss.device)
+    for i, t in enumerate(ts):
+        ess.ess_index_scores(d, qi[t], lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
+        ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos, sel_slot,
+                            lb.n_sel, lb.ws, lb.ws_bytes, stream)
+        ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos, lb.lru,
+                            lb.miss_pos, lb.miss_slot, lb.n_miss, lb.n_evict, row_dst, post,
+                            stream)
+        e = evs[i]
+        e[0].record(stream)
+        ess.ess_sparse_mla_decode(d, qa[t], sel_pos, sel_slot, row_dst, lb.n_sel, lb.pool,
+                                  host_dev, lb.out, lb.lse, lb.ws, lb.ws_bytes, stream)
+        e[1].record(stream)
+        ess.ess_miss_copy(d, m * k, lb.miss_pos, lb.miss_slot, lb.n_miss, host_dev,
+                          lb.pool, stream)
+        e[2].record(stream)
+        ess.ess_sparse_mla_decode(d, qa[t], sel_pos, post, None, lb.n_sel, lb.pool,
+                                  host_dev, lb.out, lb.lse, lb.ws, lb.ws_bytes, stream)
+        e[3].record(stream)
+        n_miss[i] = lb.n_miss.sum()
+    torch.cuda.synchronize()
+    tt = np.zeros(3)
+    for e in evs:
+        tt += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+    t_fused, t_copy, t_attn = tt / len(ts) * 1e3
+    return {"t_copy_us": t_copy, "t_attn_us": t_attn, "t_fused_us": t_fused,
+            "ratio": (t_copy + t_attn - t_fused) / t_copy if t_copy > 0 else None,
+            "bound": min(1.0, t_attn / t_copy) if t_copy > 0 else None,
+            "misses_per_step": float(n_miss.double().mean())}
+
+
+def single_layer_config(args, name, K=16, burn=16, n_ov=8, index_flush=False):
+    """One single-layer workload through ess_decode_step: the first fill
+    (event-timed), `burn` untimed steps, K timed steps (misses counted per
+    step), then n_ov further steps split for the OverlapRatio; optionally
+    the indexer alone over rotating copies of the index cache (from HBM).
+    Steps/s are reported without and with the fill over the workload's own
+    step count."""
+    import numpy as np
+    import torch
+    from decode_lightning_indexer_amd import ess
+    from decode_lightning_indexer_amd.session import HostStore, LayerBuffers, dims_of
+    from synth import gen, get_workload
+
+    dev = "cuda"
+    base = get_workload(name)
+    wl = base.with_(steps=burn + K + n_ov)
+    d = dims_of(wl)
+    B, m, L, k = wl.batch, wl.mtp, wl.ctx_len, wl.topk
+    t0 = time.perf_counter()
+    host = HostStore((B, L, 576))
+    gen.fill_latents(wl, 0, host.array)
+    lb = LayerBuffers(d, host)
+    kb = np.empty((B, L, wl.idx_dim), np.uint8)
+    gen.fill_index_keys(wl, 0, kb)
+    lb.k_idx.copy_(torch.from_numpy(kb))
+    del kb
+    qi, qa, w, nv = staged_inputs(wl, 0, dev)
+    lb.w_idx.copy_(torch.from_numpy(w))
+    n_vis = torch.from_numpy(nv).to(dev)
+    torch.cuda.synchronize()
+    log(args, f"{name}: ready in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    n_miss_all = torch.zeros((wl.steps, B), dtype=torch.int32, device=dev)
+
+    def io(t):
+        x = lb.io()
+        x.q_idx, x.q_abs = qi[t].data_ptr(), qa[t].data_ptr()
+        x.n_miss = n_miss_all[t].data_ptr()
+        return [x]
+    ios = [io(t) for t in range(wl.steps)]
+    lb.reset(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    ess.ess_decode_step(d, ios[0], n_vis, ess.ESS_MODE_FILL, stream)
+    ev[1].record(stream)
+    for t in range(burn):
+        ess.ess_decode_step(d, ios[t], n_vis, ess.ESS_MODE_INLINE, stream)
+    torch.cuda.synchronize()
+    t_fill = ev[0].elapsed_time(ev[1]) * 1e-3
+    t1 = time.perf_counter()
+    for i in range(K):
+        ess.ess_decode_step(d, ios[burn + i], n_vis, ess.ESS_MODE_INLINE, stream)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t1) / K
+    misses = n_miss_all[burn:burn + K].double().sum(dim=1)
+    T = base.steps
+    out = {"steps_per_s": 1 / t_step, "query_tok_s": B * m / t_step,
+           "us_per_step": t_step * 1e6, "rho": wl.rho,
+           "burn_in_steps": burn, "timed_steps": K,
+           "fill_us": t_fill * 1e6,
+           "steps_per_s_incl_fill": T / (t_fill + T * t_step),
+           "query_tok_s_incl_fill": B * m * T / (t_fill + T * t_step),
+           "workload_steps": T,
+           "misses_per_step": float(misses.mean()),
+           "miss_rate": float(misses.mean()) / (B * m * k)}
+    if n_ov > 0:
+        out["overlap"] = overlap_split(d, lb, qi, qa, n_vis,
+                                       range(burn + K, burn + K + n_ov), stream, host.dev)
+    if index_flush:
+        cold, warm, n_copies = indexer_alone(d, lb, qi[burn + K - 1], n_vis, stream)
+        idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
+        out["indexer"] = {"bytes_per_launch": idx_bytes, "us_from_hbm": cold * 1e6,
+                          "gbps_from_hbm": idx_bytes / cold / 1e9,
+                          "frac_of_hbm_peak": idx_bytes / cold / 1e9 / HBM_PEAK_GBPS,
+                          "index_cache_copies": n_copies,
+                          "same_cache_back_to_back_gbps": idx_bytes / warm / 1e9}
+    host.free()
+    del lb, qi, qa
+    torch.cuda.empty_cache()
+    log(args, f"{name}: {out}")
+    return out
+
+
+def multilayer(args, n_layers=16, K=16, W=16):
     """The 16-layer configuration (64K context, 32 requests per layer) over
     n_layers layers: inline against side-stream prefetch, the host link's
     busy share, and the multi-layer overlap of the miss transfer."""
@@ -328,9 +507,16 @@ def multilayer(args, n_layers=16, K=16, W=4):
     # Prefetch hides the next layer's selection under this layer's copy and
     # attention: the share of the step's non-copy work that disappears, and
     # how much of each step the host link is busy.
-    res_out = {"layers_timed": n_layers,
+    T = 16
+    res_out = {"layers_timed": n_layers, "burn_in_steps": W, "timed_steps": K,
                "inline_us_per_step": ti * 1e6, "prefetch_us_per_step": tp * 1e6,
+               "steps_per_s": 1 / tp, "query_tok_s": wl.batch * wl.mtp / tp,
                "query_tok_s_prefetch": wl.batch * wl.mtp / tp,
+               "query_tok_s_inline": wl.batch * wl.mtp / ti,
+               "fill_us": res["fill"] * 1e6,
+               "steps_per_s_incl_fill": T / (res["fill"] + T * tp),
+               "misses_per_step": res["misses_per_step"],
+               "miss_rate": res["misses_per_step"] / (n_layers * wl.batch * wl.mtp * wl.topk),
                "misses_last_step": n_miss,
                "miss_copy_us_last_step": t_copy * 1e6,
                "link_busy_inline": t_copy / ti, "link_busy_prefetch": t_copy / tp,
@@ -348,23 +534,18 @@ def multilayer(args, n_layers=16, K=16, W=4):
     return res_out
 
 
-def extra_measurements(args):
-    """The 128K / MTP=2 configuration at its three query-drift rates, the
-    1M-token single request at both pool sizes, and the 16-layer
-    configuration (all of its layers unless --layers says fewer) with and
-    without side-stream prefetch."""
-    from decode_lightning_indexer_amd import ess
+def config_measurements(args):
+    """Every workload other than the headline one: the 4K oracle-sized
+    decode, the 128K / MTP=2 configuration at its three query-drift rates
+    (each with its OverlapRatio), the 1M-token single request at both pool
+    sizes, and the 16-layer configuration (all of its layers unless
+    --layers says fewer) with and without side-stream prefetch.  The
+    indexer alone from HBM at 128K and 1M."""
     out = {}
-    K, W = 16, 4
-    for name in ("128k-b8-mtp2-r099", "128k-b8-mtp2-r095", "128k-b8-mtp2-r080",
-                 "1m-b1-c8k", "1m-b1-c16k"):
-        res, n_miss, t_copy, wl = run_steps(args, name, 1, [ess.ESS_MODE_INLINE], K, W)
-        t = res[ess.ESS_MODE_INLINE]
-        out[name] = {"steps_per_s": 1 / t, "query_tok_s": wl.batch * wl.mtp / t,
-                     "us_per_step": t * 1e6, "rho": wl.rho,
-                     "misses_last_step": n_miss,
-                     "miss_rate_last_step": n_miss / (wl.batch * wl.mtp * wl.topk),
-                     "miss_copy_us_last_step": t_copy * 1e6}
+    for name, flush in (("tiny-4k", False), ("128k-b8-mtp2-r099", False),
+                        ("128k-b8-mtp2-r095", True), ("128k-b8-mtp2-r080", False),
+                        ("1m-b1-c8k", False), ("1m-b1-c16k", True)):
+        out[name] = single_layer_config(args, name, index_flush=flush)
     out["64k-b32-16layer"] = multilayer(args, n_layers=args.layers)
     return out
 
@@ -726,9 +907,13 @@ def main():
 
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
+    # Untimed steps after the first fill: at least 16 whatever --warmup is,
+    # so that the timed steps see the pool's steady state (misses per step
+    # grow over the first steps after the fill).
+    burn = max(16, W)
     n_ov = min(8, K)                       # extra steps for the overlap split
     base = get_workload(args.workload)
-    wl = base.with_(steps=W + K + n_ov)
+    wl = base.with_(steps=burn + K + n_ov)
     B, m, L, k, C, H = wl.batch, wl.mtp, wl.ctx_len, wl.topk, wl.pool_slots, wl.mla_heads
     d = dims_of(wl)
     dev = "cuda"
@@ -792,7 +977,7 @@ def main():
     ess.ess_decode_step(d, [lb.io()], n_vis, ess.ESS_MODE_FILL, stream)
     torch.cuda.synchronize()
 
-    for t in range(W):
+    for t in range(burn):
         step(t)
     torch.cuda.synchronize()
 
@@ -800,7 +985,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(W + i, evs[i])
+        step(burn + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -809,64 +994,40 @@ def main():
         for s in range(n_st):
             stage_ms[s] += e[s].elapsed_time(e[s + 1])
     stage_us = stage_ms / K * 1e3
-    n_miss_tot = int(n_miss_all[W:].sum())
+    n_miss_tot = int(n_miss_all[burn:burn + K].sum())
 
     # The same steps without the per-stage events, as one ess_decode_step
-    # call per step: the headline figure.
-    lb.reset(stream)
-    lb.q_idx.copy_(q_idx[0])
-    ess.ess_decode_step(d, [lb.io()], n_vis, ess.ESS_MODE_FILL, stream)
+    # call per step: the headline figure.  Each step's miss counts go to a
+    # buffer of their own (no work added between the calls).
+    n_miss_plain = torch.zeros((wl.steps, B), dtype=torch.int32, device=dev)
     ios = []
-    for t in range(W + K):
+    for t in range(burn + K):
         io = lb.io()
         io.q_idx = q_idx[t].data_ptr()
         io.q_abs = q_abs[t].data_ptr()
+        io.n_miss = n_miss_plain[t].data_ptr()
         ios.append([io])
-    for t in range(W):
+    lb.reset(stream)
+    ev_fill = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_fill[0].record(stream)
+    ess.ess_decode_step(d, ios[0], n_vis, ess.ESS_MODE_FILL, stream)
+    ev_fill[1].record(stream)
+    for t in range(burn):
         ess.ess_decode_step(d, ios[t], n_vis, ess.ESS_MODE_INLINE, stream)
     torch.cuda.synchronize()
+    t_fill = ev_fill[0].elapsed_time(ev_fill[1]) * 1e-3
     t1 = time.perf_counter()
     for i in range(K):
-        ess.ess_decode_step(d, ios[W + i], n_vis, ess.ESS_MODE_INLINE, stream)
+        ess.ess_decode_step(d, ios[burn + i], n_vis, ess.ESS_MODE_INLINE, stream)
     torch.cuda.synchronize()
     wall_plain = time.perf_counter() - t1
+    miss_plain = n_miss_plain[burn:burn + K].double().sum(dim=1)
 
-    # Overlap on the same steps' miss lists (the pages' OverlapRatio):
-    # T_fused = the gather call with per-row writer slots (misses read from
-    # host inside the attention kernel, written to their slots from the tile),
-    # T_copy  = the miss list copied host -> pool alone,
-    # T_attn  = attention with every row read from the pool.
-    ev_ov = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ov)]
-    t_ov = np.zeros(3)
-    miss_ov = 0
-    for i in range(n_ov):
-        t = W + K + i
-        ess.ess_index_scores(d, q_idx[t], lb.w_idx, lb.k_idx, n_vis, lb.scores, stream)
-        ess.ess_topk_lookup(d, k, m, lb.scores, n_vis, lb.cache_slots, sel_pos,
-                            sel_slot, lb.n_sel, lb.ws, lb.ws_bytes, stream)
-        ess.ess_pool_update(d, k, m, sel_pos, lb.n_sel, lb.cache_slots, lb.slot_pos,
-                            lb.lru, lb.miss_pos, lb.miss_slot, lb.n_miss, lb.n_evict,
-                            row_dst, post, stream)
-        e = ev_ov[i]
-        e[0].record(stream)
-        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, sel_slot, row_dst, lb.n_sel,
-                                  lb.pool, host.dev, lb.out, lb.lse, lb.ws,
-                                  lb.ws_bytes, stream)
-        e[1].record(stream)
-        ess.ess_miss_copy(d, lists, lb.miss_pos, lb.miss_slot, lb.n_miss, host.dev,
-                          lb.pool, stream)
-        e[2].record(stream)
-        ess.ess_sparse_mla_decode(d, q_abs[t], sel_pos, post, None, lb.n_sel,
-                                  lb.pool, host.dev, lb.out, lb.lse, lb.ws,
-                                  lb.ws_bytes, stream)
-        e[3].record(stream)
-        miss_ov += int(lb.n_miss.sum())
-    torch.cuda.synchronize()
-    for e in ev_ov:
-        t_ov += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-    t_fused, t_copy, t_attn = t_ov / n_ov * 1e3          # us
-    overlap = (t_copy + t_attn - t_fused) / t_copy if t_copy > 0 else None
-    overlap_bound = min(1.0, t_attn / t_copy) if t_copy > 0 else None
+    # Overlap on further steps (the pages' OverlapRatio): T_fused, T_copy
+    # and T_attn of each step's gather + attention.
+    ov = overlap_split(d, lb, q_idx, q_abs, n_vis, range(burn + K, burn + K + n_ov),
+                       stream, host.dev)
+    t_fused, t_copy, t_attn = ov["t_fused_us"], ov["t_copy_us"], ov["t_attn_us"]
 
     # Host-link ceiling: the copy kernel over every row of the pool.
     ev_h = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -878,7 +1039,7 @@ def main():
     torch.cuda.synchronize()
     host_gbps = B * C * 1152 / (ev_h[0].elapsed_time(ev_h[1]) * 1e-3) / 1e9
 
-    t_idx_cold, t_idx_warm, n_idx_copies = indexer_alone(d, lb, q_idx[W + K - 1], n_vis, stream)
+    t_idx_cold, t_idx_warm, n_idx_copies = indexer_alone(d, lb, q_idx[burn + K - 1], n_vis, stream)
 
     # Algorithmic bytes / flops per launch.
     idx_bytes = B * L * wl.idx_dim + B * m * L * 4 + B * m * wl.idx_heads * (wl.idx_dim + 4)
@@ -944,6 +1105,12 @@ def main():
                    "pool_slots": C, "rho": wl.rho,
                    "miss_mode": "in-kernel"},
         "steps_per_s": K / wall_plain,
+        "burn_in_steps": burn,
+        "misses_per_step_timed": float(miss_plain.mean()),
+        "miss_rate_timed": float(miss_plain.mean()) / (B * m * k),
+        "fill_us": t_fill * 1e6,
+        "steps_per_s_incl_fill": base.steps / (t_fill + base.steps * wall_plain / K),
+        "query_tok_s_incl_fill": B * m * base.steps / (t_fill + base.steps * wall_plain / K),
         "steps_per_s_staged": K / wall,
         "stage_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
         "indexer_gbps": idx_bytes / t_idx_cold / 1e9,
@@ -954,9 +1121,7 @@ def main():
         "miss_fetch_gbps": miss_bytes / (t_gather * 1e3),
         "gather_us": t_gather,
         "host_link_gbps_measured": host_gbps,
-        "overlap": {"t_copy_us": t_copy, "t_attn_us": t_attn, "t_fused_us": t_fused,
-                    "ratio": overlap, "bound": overlap_bound,
-                    "misses_per_step": miss_ov / n_ov},
+        "overlap": ov,
         "roofline": roof,
         "rooflines": roofs,
     }
@@ -964,7 +1129,8 @@ def main():
     del lb, q_idx, q_abs
     torch.cuda.empty_cache()
     if not args.no_extra:
-        res["extra"] = extra_measurements(args)
+        res["configs"] = config_measurements(args)
+        res["extra"] = {}
         res["extra"]["eviction_replay"] = replay_curves(args)
         res["extra"]["prefill_pipeline"] = prefill_pipeline(args)
         res["extra"]["fp8_entries"] = fp8_entries(args)
@@ -972,6 +1138,19 @@ def main():
     if args.cpu_seconds > 0:
         log(args, "timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+        res["cpu_baseline"]["machine"] = host_machine()
+        if not args.no_extra:
+            # Every other workload, a shorter sample each; the 16-layer one
+            # on its first and last requests over all its layers.
+            short = max(1.0, args.cpu_seconds / 4)
+            per = {}
+            for name in ("tiny-4k", "128k-b8-mtp2-r099", "128k-b8-mtp2-r095",
+                         "128k-b8-mtp2-r080", "1m-b1-c8k", "1m-b1-c16k"):
+                per[name] = cpu_baseline(get_workload(name), short)
+            w16 = get_workload("64k-b32-16layer")
+            per[w16.name] = cpu_baseline(w16, short, requests=[0, w16.batch - 1],
+                                         layers=w16.layers)
+            res["cpu_baselines"] = per
     print(json.dumps(res), flush=True)
     return 0
 
