@@ -133,7 +133,7 @@ __device__ void bitonic_sort_u64(uint64_t* a, int n) {
 // go through LDS.  DESC: largest first.  Ends with the sorted keys back in
 // `a` and a barrier.
 template <int NT, bool DESC, int E>
-__device__ void block_sort_u64(uint64_t* a) {
+__device__ __forceinline__ void block_sort_u64(uint64_t* a) {
   constexpr int n = NT * E;
   const int t = threadIdx.x;
   uint64_t v[E];
@@ -151,15 +151,21 @@ __device__ void block_sort_u64(uint64_t* a) {
 #pragma unroll 1
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride >= NT) {
-        const int rs = stride / NT;
+        // Partners in the same thread: register index r ^ rs.  rs takes
+        // each power of two below E as a compile-time constant, so v stays
+        // in registers (a runtime index would put it in scratch memory).
 #pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if (r & rs) continue;
-          const int i = r * NT + t;
-          const uint64_t x = v[r], y = v[r ^ rs];
-          const bool wm = want_max(i, i ^ stride, size);
-          v[r] = wm ? (x > y ? x : y) : (x < y ? x : y);
-          v[r ^ rs] = wm ? (x > y ? y : x) : (x < y ? y : x);
+        for (int rs = 1; rs < E; rs <<= 1) {
+          if (stride != rs * NT) continue;
+#pragma unroll
+          for (int r = 0; r < E; ++r) {
+            if (r & rs) continue;
+            const int i = r * NT + t;
+            const uint64_t x = v[r], y = v[r ^ rs];
+            const bool wm = want_max(i, i ^ stride, size);
+            v[r] = wm ? (x > y ? x : y) : (x < y ? x : y);
+            v[r ^ rs] = wm ? (x > y ? y : x) : (x < y ? y : x);
+          }
         }
       } else if (stride >= 64) {
 #pragma unroll
@@ -193,7 +199,7 @@ __device__ void block_sort_u64(uint64_t* a) {
 
 // block_sort_u64 for any power-of-two n in [NT, 16 NT].
 template <int NT, bool DESC>
-__device__ void block_sort_u64_n(uint64_t* a, int n) {
+__device__ __forceinline__ void block_sort_u64_n(uint64_t* a, int n) {
   switch (n / NT) {
     case 1: block_sort_u64<NT, DESC, 1>(a); break;
     case 2: block_sort_u64<NT, DESC, 2>(a); break;

@@ -64,11 +64,16 @@ struct Args {
 // entries of LDS (twice that when two_buffers).  PRESEL: one query token
 // whose n_pre selected positions and their cache_slots values (read before
 // this update) are already in LDS (pre_pos, pre_slot); otherwise the
-// selections of every token are read from sel_pos / n_sel.
-template <bool PRESEL>
-__device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
+// selections of every token are read from sel_pos / n_sel.  SORTED (with
+// PRESEL): the selection is already in ascending position order in LDS -
+// pw[i] holds entry i's full selection key (its low word ~position),
+// pre_pos[i] its rank and pre_slot[i] its slot - so the entries are built
+// in order and not sorted.
+template <bool PRESEL, bool SORTED = false>
+__device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* smem_ent,
                                const int32_t* pre_pos, const int32_t* pre_slot,
-                               int n_pre) {
+                               int n_pre, const uint64_t* pw = nullptr) {
+  static_assert(!SORTED || PRESEL, "a sorted selection comes from the fused top-k");
   __shared__ uint32_t tmp[NT / 64 + 1];
   __shared__ uint32_t bcnt[kSortBuckets];
   __shared__ int s_head_new;
@@ -112,6 +117,24 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
   // positions are dropped (they sort last and end the scan).
   bool bad = false;
   constexpr int kU = 4;   // entries per thread whose reads are in flight together
+  if constexpr (SORTED) {
+    // Positions come from the selection over [0, n_vis), so all are valid
+    // (an invalid one would end the list here, flagged).
+    for (int e = tid; e < epow2; e += NT) {
+      uint64_t key = kNoEntry;
+      if (e < n_e) {
+        const int pos = (int)(~(uint32_t)pw[e]);
+        if (pos >= 0 && pos < L) {
+          key = make_entry(pos, 0, pre_pos[e]);
+          const int sl = pre_slot[e];
+          if (sl >= 0 && sl < C) key = with_slot(key, sl);
+        } else {
+          bad = true;
+        }
+      }
+      ent[e] = key;
+    }
+  } else
   for (int eb = tid; eb < epow2; eb += kU * NT) {
     int pos[kU], row[kU], tok[kU], slot[kU], given[kU];
 #pragma unroll
@@ -158,7 +181,7 @@ __device__ void update_request(const Args& a, int b, uint64_t* smem_ent,
   // spread over the context, so buckets hold a few entries each), ordered
   // within a bucket on the whole entry; a full sort if the buckets come out
   // uneven or there is no room for a second buffer.
-  {
+  if (!SORTED) {
     bool done = false;
     if (a.two_buffers) {
       const int shift = a.pos_shift;

@@ -51,6 +51,9 @@ constexpr int kSmall = 64;       // candidates sorted by one wave
 constexpr int kMaxBucket = 256;  // larger winner buckets take the full sort
 constexpr int kFusedMaxK = 4096;  // top-k + update in one workgroup up to this k
 constexpr int kLevelMaxK = 4096;  // multi-level selection up to this k (>= 8x per level)
+// Rank order by sorting the winners (two kpow2-word LDS buffers) up to this
+// power of two; above, the winner buckets rank them (one buffer).
+constexpr int kSortRankMax = 4096;
 
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -58,13 +61,28 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t full_key(uint32_t ok, int pos) {
-  return ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)pos);
+// Comparisons as 0/1 register values from min / max / subtract, for tests
+// made on every held key.  The keys go through pin() first: an empty asm
+// that the compiler cannot look through, so the tests of one key are made
+// where they are used, not all at once (with 32 keys per thread the
+// compiler otherwise computes every key's lane masks and write values up
+// front and spills them).
+__device__ __forceinline__ uint32_t pin(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t gt_u32(uint32_t a, uint32_t b) {
+  return min(max(a, b) - b, 1u);             // 1 iff a > b
+}
+__device__ __forceinline__ uint32_t ge_u32(uint32_t a, uint32_t b) {
+  return 1u - min(max(a, b) - a, 1u);        // 1 iff a >= b
+}
+__device__ __forceinline__ uint32_t eq_u32(uint32_t a, uint32_t b) {
+  return 1u - min(a ^ b, 1u);
 }
 
-__device__ __forceinline__ bool in_fixed(uint32_t key, uint32_t prefix,
-                                         int lo_fixed) {
-  return ((uint64_t)key >> lo_fixed) == ((uint64_t)prefix >> lo_fixed);
+__device__ __forceinline__ uint64_t full_key(uint32_t ok, int pos) {
+  return ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)pos);
 }
 
 // Keys are read in chunks of NT * 32: thread t holds positions
@@ -102,16 +120,23 @@ struct RowOut {
   int32_t* opos;       // POSORD
   int32_t* rpos;       // FUSE
   int32_t* rslot;      // FUSE
+  // Rank order from a compact list (BYSORT, rows in registers): kpow2 + NT
+  // words of LDS that receive the winners' full keys in input order (and
+  // one dump word per thread); `grp` then holds them grouped by rank
+  // bucket.  With FUSE, rpos / rslot are indexed by that input (= position)
+  // order: each winner's rank and slot.
+  uint64_t* pw;
 };
 
 // Top-k of one input by a 1024-thread workgroup; returns the number
 // selected.  grp: kpow2 winners of LDS (rank order only).  FUSE: the
 // outputs are also left in LDS (rpos, rslot) for the residency update that
 // follows in the same workgroup.
-template <bool RES, bool FUSE, bool EXPL, bool POSORD, int TVX = 0>
-__device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
+template <bool RES, bool FUSE, bool EXPL, bool POSORD, int TVX = 0, bool BYSORT = false>
+__device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
                         uint64_t* grp) {
   static_assert(!POSORD || RES, "position-order output needs the row in registers");
+  static_assert(!BYSORT || (RES && !POSORD), "rank order by sort needs the row in registers");
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t cand[kSmall];
   __shared__ uint32_t tmp[2 * (NT / 64) + 1];
@@ -244,6 +269,9 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       const int nb = 1 << (hi - lo + 1);
       for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
+      // Keys in the current bin share the bits at and above lo_fixed
+      // (32-bit test; lo_fixed = 32 lets every key through).
+      const uint32_t fixed_mask = lo_fixed >= 32 ? 0u : (~0u << lo_fixed);
       for (int c = 0; c < nchunks; ++c) {
         const int base = c * TC;
         if (!RES) ESS_TOPK_LOAD(base);
@@ -251,8 +279,8 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
         for (int v = 0; v < TV; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t key = kr[4 * v + e];
-            if (pos_of(base, v, e) < n && in_fixed(key, prefix, lo_fixed))
+            const uint32_t key = pin(kr[4 * v + e]);
+            if (pos_of(base, v, e) < n && ((key ^ prefix) & fixed_mask) == 0u)
               atomicAdd(&hist[(key >> lo) & (nb - 1)], 1u);
           }
       }
@@ -289,7 +317,17 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
   const bool small_bin = need > 0 && cnt <= (uint32_t)kSmall;
   const bool ordered = need > 0 && !small_bin;   // a run of equal keys
 
-  if constexpr (POSORD) {
+  constexpr bool by_sort = BYSORT;
+  if constexpr (by_sort) {
+    // Every slot the emission below does not write reads as "no winner".
+    for (int i = tid; i < kpow2; i += NT) out.pw[i] = 0ull;
+    __syncthreads();
+  }
+  // 32-bit forms of the bin bounds: keys above the bin are >= win32 (none
+  // when win_lo = 2^32), keys in it are >= bin32.
+  const bool win_any = win_lo <= 0xFFFFFFFFull;
+  const uint32_t win32 = (uint32_t)win_lo, bin32 = (uint32_t)bin_lo;
+  if constexpr (POSORD || by_sort) {
     // The selected pairs in input order: keys above the bin; of a small bin
     // the `need` largest full keys (one wave sorts the bin, the need-th
     // becomes a threshold); of a run of equal keys the first `need`.
@@ -303,9 +341,8 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
         for (int v = 0; v < TV; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t key = kr[4 * v + e];
-            if (pos_of(base, v, e) < n && (uint64_t)key >= bin_lo &&
-                (uint64_t)key < win_lo) {
+            const uint32_t key = pin(kr[4 * v + e]);
+            if (pos_of(base, v, e) < n && key >= bin32 && (!win_any || key < win32)) {
               const uint32_t at = atomicAdd(&s_nc, 1u);
               if (at < (uint32_t)kSmall) cand[at] = full_key(key, real_pos(base, v, e));
             }
@@ -321,6 +358,7 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
       __syncthreads();
     }
     const uint64_t thr = small_bin ? s_thr : 0ull;
+    const uint32_t thr_key = (uint32_t)(thr >> 32), thr_npos = (uint32_t)thr;
     // Index order is group-major (v, then thread, then e): the counts of a
     // thread's groups go through packed scans, 16 bits per group, four
     // groups per 64-bit word.
@@ -343,7 +381,7 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
           uint64_t n_eq = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (pos_of(base, v, e) < n && (uint64_t)kr[4 * v + e] == bin_lo) ++n_eq;
+            n_eq += (pos_of(base, v, e) < n && kr[4 * v + e] == bin32) ? 1u : 0u;
           pk[v >> 2] |= n_eq << (16 * (v & 3));
         }
 #pragma unroll
@@ -356,52 +394,166 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
         }
         // (equal keys of earlier chunks precede; a single chunk here)
       }
+      // Selection flags without divergent branches (small_bin and ordered
+      // are uniform): of a small bin the full keys from the threshold up
+      // (every key above the bin is larger), of a run of equal keys the
+      // first `need`, otherwise the keys above the bin.
       uint32_t selm = 0;
       uint64_t sk[NW], pre[NW], tot[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) sk[w] = 0;
+      // One loop per case, so no case's tests are evaluated for another's.
+      // Keys above the bin: none when win_lo = 2^32 (win32 = 0 then, and
+      // win_mul = 0 cancels the test).
+      const uint32_t win_mul = win_any ? 1u : 0u;
+#define ESS_SEL_LOOP(TEST)                                                     \
+  _Pragma("unroll") for (int v = 0; v < TV; ++v) {                             \
+    uint32_t cv = 0;                                                           \
+    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                            \
+      const uint32_t key = pin(kr[4 * v + e]);                                 \
+      const uint32_t inr = gt_u32((uint32_t)n, (uint32_t)pos_of(base, v, e));  \
+      const uint32_t t = inr & (TEST);                                         \
+      selm |= t << (4 * v + e);                                                \
+      cv += t;                                                                 \
+    }                                                                          \
+    sk[v >> 2] |= (uint64_t)cv << (16 * (v & 3));                              \
+  }
+      if (small_bin) {
+        ESS_SEL_LOOP(gt_u32(key, thr_key) |
+                     (eq_u32(key, thr_key) & ge_u32(~(uint32_t)real_pos(base, v, e), thr_npos)))
+      } else if (ordered) {
 #pragma unroll
-      for (int v = 0; v < TV; ++v) {
-        uint64_t cv = 0;
+        for (int v = 0; v < TV; ++v) {
+          uint32_t cv = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = kr[4 * v + e];
-          bool t = false;
-          if (pos_of(base, v, e) < n) {
-            if ((uint64_t)key >= win_lo) {
-              t = true;
-            } else if (small_bin) {
-              t = (uint64_t)key >= bin_lo && full_key(key, real_pos(base, v, e)) >= thr;
-            } else if (ordered && (uint64_t)key == bin_lo) {
-              t = eqr[v] < need;
-              ++eqr[v];
-            }
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = pin(kr[4 * v + e]);
+            const uint32_t inr = gt_u32((uint32_t)n, (uint32_t)pos_of(base, v, e));
+            const uint32_t eq = inr & eq_u32(key, bin32);
+            const uint32_t t = (inr & win_mul & ge_u32(key, win32)) |
+                               (eq & gt_u32(need, eqr[v]));
+            eqr[v] += eq;
+            selm |= t << (4 * v + e);
+            cv += t;
           }
-          selm |= (uint32_t)t << (4 * v + e);
-          cv += t;
+          sk[v >> 2] |= (uint64_t)cv << (16 * (v & 3));
         }
-        sk[v >> 2] |= cv << (16 * (v & 3));
+      } else {
+        ESS_SEL_LOOP(win_mul & ge_u32(key, win32))
       }
+#undef ESS_SEL_LOOP
 #pragma unroll
       for (int w = 0; w < NW; ++w) pre[w] = block_exscan_u64<NT>(sk[w], tmp64, &tot[w]);
 #pragma unroll
       for (int v = 0; v < TV; ++v) {
         uint32_t o = at + ESS_FIELD(pre, v);
+        if constexpr (POSORD) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((selm >> (4 * v + e)) & 1u) {
-            if (o < (uint32_t)keff) {   // exactly keff are selected
-              out.okey[o] = kr[4 * v + e];
-              out.opos[o] = real_pos(base, v, e);
+          for (int e = 0; e < 4; ++e)
+            if ((selm >> (4 * v + e)) & 1u) {
+              if (o < (uint32_t)keff) {   // exactly keff are selected
+                out.okey[o] = kr[4 * v + e];
+                out.opos[o] = real_pos(base, v, e);
+              }
+              ++o;
             }
-            ++o;
+        } else {
+          // Every key is written, without a branch: a winner at its place,
+          // the others to this thread's own slot past the list.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = pin(kr[4 * v + e]);
+            const uint32_t sel = (selm >> (4 * v + e)) & 1u;
+            const uint32_t dst = sel && o < (uint32_t)keff ? o : (uint32_t)(kpow2 + tid);
+            out.pw[dst] = full_key(key, real_pos(base, v, e));
+            o += sel;
           }
+        }
         at += ESS_FIELD(tot, v);
       }
     }
 #undef ESS_FIELD
+    if constexpr (POSORD) return keff;
+  }
+  if constexpr (by_sort) {
+    // Rank order of the compact list (input order = ascending position):
+    // buckets of equal key width over the winners' key range, larger keys
+    // first; a counting pass, a scan, a scatter grouped by bucket, then
+    // each winner's rank is its bucket's start plus the number of larger
+    // full keys in its bucket (full keys are unique).  A bucket over
+    // kMaxBucket keys (long runs of near-equal scores) sorts the whole list
+    // instead.  Each rank's slot is read from cache_slots; with FUSE each
+    // winner's rank and slot are also left at its input-order index (a
+    // binary search over the positions), for the update that follows.
+    __syncthreads();
+    const uint64_t* pw = out.pw;
+    const uint32_t klo = max(need > 0 ? (uint32_t)bin_lo : (uint32_t)min(win_lo, (uint64_t)mx), mn);
+    const uint32_t krange = mx - klo;
+    const int kshift = krange < (uint32_t)kBins ? 0 : (32 - __clz(krange)) - 11;
+#define rank_bucket(FK) min((int)((mx - (uint32_t)((FK) >> 32)) >> kshift), kBins - 1)
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < keff; i += NT) atomicAdd(&hist[rank_bucket(pw[i])], 1u);
+    __syncthreads();
+    bool big;
+    {
+      const uint32_t c0 = hist[2 * tid], c1 = hist[2 * tid + 1];
+      uint32_t total;
+      const uint32_t off = block_exscan<NT>(c0 + c1, tmp, &total);
+      big = __syncthreads_or(max(c0, c1) > (uint32_t)kMaxBucket);
+      hist[2 * tid] = off;
+      hist[2 * tid + 1] = off + c0;
+    }
+    __syncthreads();
+    // pidx[j]: the input-order index of grp[j] (FUSE), so each rank finds
+    // its winner's place in the position-ordered list directly.
+    uint32_t* pidx = reinterpret_cast<uint32_t*>(out.pw + kpow2 + NT);
+    auto emit_rank = [&](int r, uint64_t x, int i) {
+      const int pos = (int)(~(uint32_t)x);     // -1 only for "no winner"
+      const int32_t sl = pos >= 0 ? cs[pos] : -1;
+      op[r] = pos;
+      os[r] = sl;
+      if (FUSE) {
+        if (i < 0) {                           // (the full sort: search)
+          int lo = 0, hi = keff - 1;           // pw ascends in position
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)(~(uint32_t)pw[mid]) < pos) lo = mid + 1;
+            else hi = mid;
+          }
+          i = lo;
+        }
+        out.rpos[i] = r;
+        out.rslot[i] = sl;
+      }
+    };
+    if (!big) {
+      for (int i = tid; i < keff; i += NT) {
+        const uint64_t x = pw[i];
+        const uint32_t at = atomicAdd(&hist[rank_bucket(x)], 1u);
+        grp[at] = x;
+        if (FUSE) pidx[at] = (uint32_t)i;
+      }
+      __syncthreads();
+      // hist[b] is now the end of bucket b: bucket b spans [hist[b-1], hist[b]).
+      for (int j = tid; j < keff; j += NT) {
+        const uint64_t x = grp[j];
+        const int bk = rank_bucket(x);
+        const int lo = bk == 0 ? 0 : (int)hist[bk - 1];
+        const int hi = (int)hist[bk];
+        int r = lo;
+        for (int q = lo; q < hi; ++q) r += grp[q] > x;
+        emit_rank(r, x, FUSE ? (int)pidx[j] : -1);
+      }
+    } else {
+      for (int i = tid; i < kpow2; i += NT) grp[i] = i < keff ? pw[i] : 0ull;
+      __syncthreads();
+      block_sort_u64_n<NT, true>(grp, kpow2);
+      for (int r = tid; r < keff; r += NT) emit_rank(r, grp[r], -1);
+    }
+#undef rank_bucket
     return keff;
-  } else {
+  } else if constexpr (!POSORD) {
 
   // Winner buckets of equal width over [max(win_lo, mn), mx], larger keys
   // first.
@@ -531,6 +683,7 @@ __device__ int topk_row(const RowIn& in, int k, int kpow2, const RowOut& out,
 #undef ESS_TOPK_LOAD
   return keff;
   }
+  return keff;   // (position-order output returned above)
 }
 
 // Candidates a level leaves of n entries: k per full chunk and min(k, rest)
@@ -553,20 +706,23 @@ __device__ __forceinline__ int visible(const int32_t* n_vis, int b, int m, int j
   return n < 0 ? 0 : (n > L ? L : n);
 }
 
-template <bool RES>
+template <bool RES, bool BYSORT>
 __global__ __launch_bounds__(NT) void topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
     int n_tok, int k, int kpow2) {
-  extern __shared__ uint64_t grp[];  // kpow2: winners grouped by bucket
+  // kpow2 words: winners grouped by bucket, or (rank order by sort) the sort
+  // buffer followed by kpow2 words for the winners in position order.
+  extern __shared__ uint64_t grp[];
   const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
   const size_t o = ((size_t)b * n_tok + j) * k;
   const RowIn in{scores + ((size_t)b * m + j) * L, nullptr, nullptr,
                  visible(n_vis, b, m, j, L), (L & 3) == 0, 0};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
-                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr};
-  topk_row<RES, false, false, false>(in, k, kpow2, out, grp);
+                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr,
+                   BYSORT ? grp + kpow2 : nullptr};
+  topk_row<RES, false, false, false, 0, BYSORT>(in, k, kpow2, out, grp);
 }
 
 // One level of a long row's reduction: workgroup (s, row) writes the exact
@@ -595,12 +751,13 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(
                (L & 3) == 0, base};
   const size_t ob = rb + (size_t)blockIdx.x * k;
   const RowOut out{nullptr, nullptr, nullptr, nullptr, okey + ob, opos + ob,
-                   nullptr, nullptr};
+                   nullptr, nullptr, nullptr};
   topk_row<true, false, EXPL, true, VPT_E>(in, k, 0, out, nullptr);
 }
 
 // The final selection of a long row from its candidate list after `levels`
 // levels: rank order with slots.
+template <bool BYSORT>
 __global__ __launch_bounds__(NT) void topk_final_kernel(
     const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cpos,
     size_t cap, const int32_t* __restrict__ n_vis,
@@ -614,8 +771,9 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   const size_t rb = (size_t)row * cap, o = ((size_t)b * n_tok + j) * k;
   const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
-                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr};
-  topk_row<true, false, true, false>(in, k, kpow2, out, grp);
+                   n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr,
+                   BYSORT ? grp + kpow2 : nullptr};
+  topk_row<true, false, true, false, 0, BYSORT>(in, k, kpow2, out, grp);
 }
 
 // One query token per request: the top-k and the residency update of a
@@ -631,26 +789,45 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
     int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_slot,
     int32_t* __restrict__ n_sel, int L, int m, int k, int kpow2, int levels,
     pool::Args pa, int rank_off) {
-  extern __shared__ uint64_t dyn[];  // top-k winners, then the update's entries
+  // Top-k: the sort buffer, then the winners in position order (kpow2 words
+  // each); then the update's entries over the sort buffer.  rpos / rslot:
+  // per winner its rank and slot (in position order after a sort, in rank
+  // order otherwise).
+  extern __shared__ uint64_t dyn[];
   int32_t* rpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dyn) + rank_off);
   int32_t* rslot = rpos + k;
   const int b = blockIdx.x;
   int n = visible(n_vis, b, m, 0, L);
   const size_t o = (size_t)b * k;
+  // Rows held in registers rank their winners by a sort and hand the update
+  // a position-ordered selection (it then sorts nothing).
+  constexpr bool kSorted = RES;
+  uint64_t* pw = kSorted ? dyn + kpow2 : nullptr;
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L, n_sel + b,
-                   nullptr, nullptr, rpos, rslot};
+                   nullptr, nullptr, rpos, rslot, pw};
   int keff;
   if constexpr (EXPL) {
     for (int l = 1; l <= levels; ++l) n = level_count(n, k, l);
     const size_t rb = (size_t)b * cap;
     const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
-    keff = topk_row<true, true, true, false>(in, k, kpow2, out, dyn);
+    keff = topk_row<true, true, true, false, 0, kSorted>(in, k, kpow2, out, dyn);
   } else {
     const RowIn in{scores + (size_t)b * m * L, nullptr, nullptr, n, (L & 3) == 0, 0};
-    keff = topk_row<RES, true, false, false>(in, k, kpow2, out, dyn);
+    keff = topk_row<RES, true, false, false, 0, kSorted>(in, k, kpow2, out, dyn);
   }
-  __syncthreads();   // ranked selections complete; the winners' buffer is free
-  pool::update_request<true>(pa, b, dyn, rpos, rslot, keff);
+  __syncthreads();   // selections complete; the sort buffer is free
+  if constexpr (kSorted)
+    pool::update_request<true, true>(pa, b, dyn, rpos, rslot, keff, pw);
+  else
+    pool::update_request<true>(pa, b, dyn, rpos, rslot, keff);
+}
+
+// Dynamic LDS of the rank-order-by-list path: the scatter buffer (kpow2
+// words), then the winners in position order (kpow2 words), one dump word
+// per thread for the keys that are not winners, and the input-order index
+// of each scattered winner (kpow2 32-bit words).
+size_t rank_lds_bytes(int kpow2) {
+  return (size_t)(2 * kpow2 + NT) * sizeof(uint64_t) + (size_t)kpow2 * sizeof(uint32_t);
 }
 
 // Levels a row of L entries needs before one workgroup holds its candidate
@@ -712,35 +889,54 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, void* ws,
                        hipStream_t s) {
-  // The fallback sort needs a power of two of at least one key per thread.
+  // The sorts need a power of two of at least one key per thread.  Rows
+  // held in registers (and candidate lists) rank their winners by a sort
+  // over a second kpow2-word buffer up to kSortRankMax.
   const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
-  const size_t lds = (size_t)kpow2 * sizeof(uint64_t);
+  const size_t lds1 = (size_t)kpow2 * sizeof(uint64_t);
+  const size_t lds2 = kpow2 <= kSortRankMax ? rank_lds_bytes(kpow2) : lds1;
   const int nl = ws ? n_levels(d.ctx_len, k) : 0;
+  size_t lds = lds2;
   if (nl > 0) {
     const uint32_t* fk;
     const int32_t* fp;
     hipError_t e = enqueue_levels(d, k, n_tok, nl, scores, n_vis, ws, &fk, &fp, s);
     if (e != hipSuccess) return e;
-    e = ensure_dyn_lds((const void*)topk_final_kernel, (int)lds);
+    const bool bys = kpow2 <= kSortRankMax;
+    const void* ff = bys ? (const void*)topk_final_kernel<true>
+                         : (const void*)topk_final_kernel<false>;
+    e = ensure_dyn_lds(ff, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(d.batch * n_tok), dim3(NT), lds, s,
-                       fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
-                       sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
+    if (bys)
+      hipLaunchKernelGGL(topk_final_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                         fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
+                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
+    else
+      hipLaunchKernelGGL(topk_final_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
+                         fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
+                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
     return hipGetLastError();
   }
   // Rows of at most one chunk stay in registers for all passes.
   const bool res = d.ctx_len <= CHUNK;
-  const void* fn = res ? (const void*)topk_kernel<true> : (const void*)topk_kernel<false>;
+  const bool bys = res && kpow2 <= kSortRankMax;
+  lds = bys ? lds2 : lds1;
+  const void* fn = bys ? (const void*)topk_kernel<true, true>
+                   : res ? (const void*)topk_kernel<true, false>
+                         : (const void*)topk_kernel<false, false>;
   hipError_t e = ensure_dyn_lds(fn, (int)lds);
   if (e != hipSuccess) return e;
-  if (res)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
-                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, n_tok, k, kpow2);
+#define ESS_TOPK_LAUNCH(R, S)                                                  \
+  hipLaunchKernelGGL((topk_kernel<R, S>), dim3(d.batch * n_tok), dim3(NT), lds, s, \
+                     scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,       \
+                     d.ctx_len, d.mtp, n_tok, k, kpow2)
+  if (bys)
+    ESS_TOPK_LAUNCH(true, true);
+  else if (res)
+    ESS_TOPK_LAUNCH(true, false);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
-                       scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,
-                       d.ctx_len, d.mtp, n_tok, k, kpow2);
+    ESS_TOPK_LAUNCH(false, false);
+#undef ESS_TOPK_LAUNCH
   return hipGetLastError();
 }
 
@@ -766,14 +962,19 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
                       lru_bytes_per_req(d.pool_slots), miss_pos, miss_slot,
                       n_miss, n_evict, row_dst, sel_slot_post, d.ctx_len,
                       d.pool_slots, k, 1, epow2, two, pos_shift};
-  const size_t topk_bytes = (size_t)kpow2 * sizeof(uint64_t);
-  const size_t upd_bytes = (size_t)epow2 * sizeof(uint64_t) * (two ? 2 : 1);
+  const int nl = ws ? n_levels(d.ctx_len, k) : 0;
+  const bool res = d.ctx_len <= CHUNK;
+  // Register-resident rows and candidate lists rank by a sort: the sort
+  // buffer and the position-ordered winners (the update then sorts
+  // nothing); streamed rows use winner buckets and the update sorts.
+  const bool sorted = res || nl > 0;
+  const size_t topk_bytes = sorted ? rank_lds_bytes(kpow2) : (size_t)kpow2 * sizeof(uint64_t);
+  const size_t upd_bytes = sorted ? (size_t)epow2 * sizeof(uint64_t)
+                                  : (size_t)epow2 * sizeof(uint64_t) * (two ? 2 : 1);
   const size_t rank_off = align_up(topk_bytes > upd_bytes ? topk_bytes : upd_bytes, 16);
   const size_t lds = rank_off + 2 * (size_t)k * sizeof(int32_t);
-  const int nl = ws ? n_levels(d.ctx_len, k) : 0;
   const uint32_t* fk = nullptr;
   const int32_t* fp = nullptr;
-  const bool res = d.ctx_len <= CHUNK;
   const void* fn = nl > 0 ? (const void*)select_update_kernel<true, true>
                    : res  ? (const void*)select_update_kernel<true, false>
                           : (const void*)select_update_kernel<false, false>;
