@@ -130,10 +130,16 @@ def cpu_baseline(wl, seconds, requests=None, layers=1):
 
 # Kernels whose counters give roofline.traffic, with the source each is
 # built from; a recorded figure only counts while that source is unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_32k-b16.txt")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+
+
 KERNEL_SOURCES = {
     "index_scores_kernel": "index_scores.hip",
     "topk_kernel": "topk.hip",
+    "topk_level_kernel": "topk.hip",
+    "topk_final_kernel": "topk.hip",
+    "select_update_kernel": "topk.hip",
     "pool_update_kernel": "pool_update.hip",
     "miss_copy_kernel": "miss_copy.hip",
     "sparse_mla_kernel": "sparse_mla.hip",
@@ -149,12 +155,12 @@ def source_digest(kernel):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
-    there is none or the kernel's source has changed since."""
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy),
+    or None when there is none or the kernel's source has changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             for line in f:
                 w = line.split()
                 if len(w) == 4 and w[0] == "traffic" and w[1] == kernel:
@@ -1086,7 +1092,7 @@ def main():
     roof = dict(roofs.get(names[dom], {"kernel": names[dom], "bound": "alu",
                                         "achieved": None, "peak": None,
                                         "unit": "us", "frac": None}))
-    parts = [recorded_traffic(kn) for kn in roof["kernel"].split("+")
+    parts = [recorded_traffic(kn, base.name) for kn in roof["kernel"].split("+")
              if kn in KERNEL_SOURCES]
     roof["traffic"] = (sum(parts) if parts and all(x is not None for x in parts)
                        and len(parts) == len(roof["kernel"].split("+")) else None)
