@@ -147,14 +147,22 @@ ess_status get_events(size_t n, hipEvent_t** out) {
 }
 
 // Workspace layout: the attention's partials, then the top-k levels' lists
-// (sized for the step's top-k and for the first fill's top-C).
+// (sized for the step's top-k and for the first fill's top-C), then each
+// token's selection in position order (position, rank, slot) for the
+// residency update of a step with several query tokens.
 size_t attn_region(const ess_dims& d) {
   return ess::align_up(ess::sparse_mla_ws_bytes(d), 256);
 }
 size_t topk_region(const ess_dims& d) {
   const size_t a = ess::topk_ws_bytes(d, d.topk, d.mtp);
   const size_t b = ess::topk_ws_bytes(d, d.pool_slots, 1);
-  return a > b ? a : b;
+  return ess::align_up(a > b ? a : b, 256);
+}
+size_t lists_region(const ess_dims& d) {
+  return ess::align_up((size_t)d.batch * d.mtp * d.topk * 3 * sizeof(int32_t), 256);
+}
+size_t ws_total(const ess_dims& d) {
+  return attn_region(d) + topk_region(d) + lists_region(d);
 }
 
 }  // namespace
@@ -163,7 +171,7 @@ extern "C" {
 
 size_t ess_workspace_bytes(const ess_dims* d) {
   if (check_dims(d, "ess_workspace_bytes") != ESS_OK) return 0;
-  return attn_region(*d) + topk_region(*d);
+  return ws_total(*d);
 }
 
 size_t ess_lru_state_bytes(const ess_dims* d) {
@@ -451,10 +459,11 @@ static ess_status check_layer(const ess_layer_io& io, int mode, int l) {
 }
 
 // Scores, top-k and pool update of one layer on one stream; tws: the
-// layer's top-k region of its workspace (nullptr: one workgroup per row).
+// layer's top-k region of its workspace (nullptr: one workgroup per row);
+// lws: its position-list region (nullptr: none).
 static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                  const int32_t* n_vis, int k, int n_tok,
-                                 void* tws, hipStream_t st) {
+                                 void* tws, void* lws, hipStream_t st) {
   hipError_t e = ess::launch_index_scores(d, io.q_idx, io.w_idx, io.k_idx,
                                           n_vis, io.scores, st);
   if (e != hipSuccess) return e;
@@ -464,15 +473,25 @@ static hipError_t enqueue_select(const ess_dims& d, const ess_layer_io& io,
                                      io.slot_pos, io.lru_state, io.miss_pos,
                                      io.miss_slot, io.n_miss, io.n_evict,
                                      io.row_dst, io.sel_slot_post, tws, st);
+  // Several tokens: the top-k leaves each token's winners in position order
+  // (when it ranks them from a compact list) and the update merges those
+  // lists instead of sorting the union.
+  ess::PosLists pl{nullptr, nullptr, nullptr};
+  if (lws && (size_t)n_tok * k <= (size_t)d.mtp * d.topk &&
+      ess::topk_pos_lists_fit(d, k, tws != nullptr)) {
+    int32_t* base = static_cast<int32_t*>(lws);
+    const size_t n = (size_t)d.batch * n_tok * k;
+    pl = ess::PosLists{base, base + n, base + 2 * n};
+  }
   e = ess::launch_topk(d, k, n_tok, io.scores, n_vis, io.cache_slots,
-                       io.sel_pos, io.sel_slot, io.n_sel, tws, st);
+                       io.sel_pos, io.sel_slot, io.n_sel, tws, st, pl);
   if (e != hipSuccess) return e;
   // The update takes each row's pre-update slot from the top-k's lookup.
   return ess::launch_pool_update(d, k, n_tok, io.sel_pos, io.n_sel,
                                  io.cache_slots, io.slot_pos, io.lru_state,
                                  io.miss_pos, io.miss_slot, io.n_miss,
                                  io.n_evict, io.row_dst, io.sel_slot_post, st,
-                                 io.sel_slot);
+                                 io.sel_slot, pl);
 }
 
 // Gather + attention of one selected layer: the attention reads each miss
@@ -515,12 +534,17 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   }
   if (mode == ESS_MODE_PREFETCH && (side == stream))
     return fail(ESS_ERR_INVALID, "%s: prefetch needs a second stream", fn);
-  const size_t ws_need = attn_region(*d) + topk_region(*d);
-  // The top-k region of a layer's workspace (the first fill uses it only
-  // when the layer brings a full workspace; it is not required there).
+  const size_t ws_need = ws_total(*d);
+  // The top-k and position-list regions of a layer's workspace (the first
+  // fill uses them only when the layer brings a full workspace; it is not
+  // required there).
   auto tws = [&](const ess_layer_io& io) -> void* {
     if (!io.ws || io.ws_bytes < ws_need || topk_region(*d) == 0) return nullptr;
     return static_cast<char*>(io.ws) + attn_region(*d);
+  };
+  auto lws = [&](const ess_layer_io& io) -> void* {
+    if (!io.ws || io.ws_bytes < ws_need) return nullptr;
+    return static_cast<char*>(io.ws) + attn_region(*d) + topk_region(*d);
   };
   for (int l = 0; l < n_layers; ++l) {
     if ((s = check_layer(layers[l], mode, l)) != ESS_OK) return s;
@@ -534,7 +558,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
     const int C = d->pool_slots;
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
-      e = enqueue_select(*d, io, n_vis, C, 1, tws(io), stream);
+      e = enqueue_select(*d, io, n_vis, C, 1, tws(io), lws(io), stream);
       if (e == hipSuccess)
         e = io.host_entries
                 ? ess::launch_entry_copy(*d, C, io.miss_pos, io.miss_slot,
@@ -549,7 +573,7 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   if (mode == ESS_MODE_INLINE) {
     for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
       const ess_layer_io& io = layers[l];
-      e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, tws(io), stream);
+      e = enqueue_select(*d, io, n_vis, d->topk, d->mtp, tws(io), lws(io), stream);
       if (e == hipSuccess) e = enqueue_attention(*d, io, stream);
     }
     return e == hipSuccess ? ESS_OK : hip_fail(e, fn);
@@ -567,7 +591,8 @@ ess_status ess_decode_step(const ess_dims* d, int32_t n_layers,
   e = hipEventRecord(ev[n_layers], stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[n_layers], 0);
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
-    e = enqueue_select(*d, layers[l], n_vis, d->topk, d->mtp, tws(layers[l]), side);
+    e = enqueue_select(*d, layers[l], n_vis, d->topk, d->mtp, tws(layers[l]), lws(layers[l]),
+                       side);
     if (e == hipSuccess) e = hipEventRecord(ev[l], side);
   }
   for (int l = 0; l < n_layers && e == hipSuccess; ++l) {

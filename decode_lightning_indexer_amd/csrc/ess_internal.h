@@ -36,11 +36,22 @@ hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
 // (0 when it does not apply: short rows, or k > 4096).  With ws == nullptr
 // the top-k runs one workgroup per row over the whole row.
 size_t topk_ws_bytes(const ess_dims& d, int k, int n_tok);
+// Each row's winners in ascending position order: position, rank and slot
+// before the update, [B][n_tok][k] each (for the residency update that
+// follows; pos == nullptr: none).
+struct PosLists {
+  int32_t* pos;
+  int32_t* rank;
+  int32_t* slot;
+};
+// Whether launch_topk can fill position lists for this k (ranked from a
+// compact winner list: rows of at most 32768 keys, or levels when `levels`).
+bool topk_pos_lists_fit(const ess_dims& d, int k, bool levels);
 hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, void* ws,
-                       hipStream_t s);
+                       hipStream_t s, PosLists pl = PosLists{nullptr, nullptr, nullptr});
 
 // ---- pool ---------------------------------------------------------------
 // Per-request LRU state: header, slot stamps [C], ring of (slot, stamp).
@@ -87,7 +98,8 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               int32_t* miss_slot, int32_t* n_miss,
                               int32_t* n_evict, int32_t* row_dst,
                               int32_t* sel_slot_post, hipStream_t s,
-                              const int32_t* sel_slot_pre = nullptr);
+                              const int32_t* sel_slot_pre = nullptr,
+                              PosLists lists = PosLists{nullptr, nullptr, nullptr});
 
 // ---- attention ----------------------------------------------------------
 struct MlaPlan {

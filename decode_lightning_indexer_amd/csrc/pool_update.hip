@@ -64,10 +64,12 @@ __global__ void pool_status_kernel(const void* lru, size_t stride, int B,
   status[4 * b + 3] = h->tail - h->head;
 }
 
-// One 1024-thread workgroup per request.
+// One 1024-thread workgroup per request.  MERGE: the selections come as
+// position-ordered lists per token and are merged, not sorted.
+template <bool MERGE>
 __global__ __launch_bounds__(NT) void pool_update_kernel(pool::Args a) {
   extern __shared__ uint64_t smem_ent[];       // epow2 entries (x2: sort target)
-  pool::update_request<false>(a, blockIdx.x, smem_ent, nullptr, nullptr, 0);
+  pool::update_request<false, false, MERGE>(a, blockIdx.x, smem_ent, nullptr, nullptr, 0);
 }
 
 }  // namespace
@@ -99,7 +101,7 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               int32_t* miss_slot, int32_t* n_miss,
                               int32_t* n_evict, int32_t* row_dst,
                               int32_t* sel_slot_post, hipStream_t s,
-                              const int32_t* sel_slot_pre) {
+                              const int32_t* sel_slot_pre, PosLists lists) {
   const size_t stride = lru_bytes_per_req(d.pool_slots);
   // The sort buffer holds at least one entry per thread.
   const int epow2 = pow2_at_least(n_tok * k) < NT ? NT : pow2_at_least(n_tok * k);
@@ -108,13 +110,22 @@ hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
   int bits = 0;
   while ((1 << bits) < d.ctx_len) ++bits;
   const int pos_shift = bits > 11 ? bits - 11 : 0;
-  hipError_t e = ensure_dyn_lds((const void*)pool_update_kernel, (int)(kMaxTopk * sizeof(uint64_t)));
+  // Position-ordered lists are merged in place of the sort (the lists'
+  // positions take the second buffer).
+  const bool merge = lists.pos != nullptr && two;
+  const void* fn = merge ? (const void*)pool_update_kernel<true>
+                         : (const void*)pool_update_kernel<false>;
+  hipError_t e = ensure_dyn_lds(fn, (int)(kMaxTopk * sizeof(uint64_t)));
   if (e != hipSuccess) return e;
   const pool::Args a{sel_pos, n_sel, cache_slots, slot_pos, lru, stride,
                      miss_pos, miss_slot, n_miss, n_evict, row_dst,
                      sel_slot_post, d.ctx_len, d.pool_slots, k, n_tok, epow2,
-                     two, pos_shift, sel_slot_pre};
-  hipLaunchKernelGGL(pool_update_kernel, dim3(d.batch), dim3(NT), lds, s, a);
+                     two, pos_shift, sel_slot_pre,
+                     merge ? lists : PosLists{nullptr, nullptr, nullptr}};
+  if (merge)
+    hipLaunchKernelGGL(pool_update_kernel<true>, dim3(d.batch), dim3(NT), lds, s, a);
+  else
+    hipLaunchKernelGGL(pool_update_kernel<false>, dim3(d.batch), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 

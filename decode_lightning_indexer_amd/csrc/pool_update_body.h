@@ -58,6 +58,9 @@ struct Args {
   // (cache_slots at sel_pos); read next to sel_pos instead of looking
   // cache_slots up at each position after sel_pos arrives.
   const int32_t* sel_slot_pre;
+  // Optional (MERGE): each token's selection in ascending position order
+  // with its rank and slot, from the top-k.
+  PosLists lists;
 };
 
 // The update of request b by a 1024-thread workgroup.  smem_ent: epow2
@@ -69,11 +72,17 @@ struct Args {
 // pw[i] holds entry i's full selection key (its low word ~position),
 // pre_pos[i] its rank and pre_slot[i] its slot - so the entries are built
 // in order and not sorted.
-template <bool PRESEL, bool SORTED = false>
+//   MERGE (without PRESEL): every token's selection comes in ascending
+// position order (a.lists); the entries are placed by merging those lists
+// (each entry's place: its index in its own list plus, for every other
+// token, the entries before it there - equal positions: smaller token
+// first), so nothing is sorted.  Needs a second epow2-entry LDS buffer.
+template <bool PRESEL, bool SORTED = false, bool MERGE = false>
 __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* smem_ent,
                                const int32_t* pre_pos, const int32_t* pre_slot,
                                int n_pre, const uint64_t* pw = nullptr) {
   static_assert(!SORTED || PRESEL, "a sorted selection comes from the fused top-k");
+  static_assert(!MERGE || !PRESEL, "merged lists come from the top-k's outputs");
   __shared__ uint32_t tmp[NT / 64 + 1];
   __shared__ uint32_t bcnt[kSortBuckets];
   __shared__ int s_head_new;
@@ -117,7 +126,49 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   // positions are dropped (they sort last and end the scan).
   bool bad = false;
   constexpr int kU = 4;   // entries per thread whose reads are in flight together
-  if constexpr (SORTED) {
+  if constexpr (MERGE) {
+    // The lists' positions into the second buffer, then each entry finds
+    // its merged place by binary searches in the other tokens' lists.
+    int32_t* lp = reinterpret_cast<int32_t*>(smem_ent + epow2);
+    for (int e = tid; e < n_e; e += NT) {
+      int j = 0;
+      while (e >= off[j + 1]) ++j;
+      lp[e] = a.lists.pos[rows0 + (size_t)j * k + (e - off[j])];
+    }
+    // (every place starts empty: an entry that could not be placed leaves
+    // a kNoEntry, which ends the scans below, never a stale entry)
+    for (int e = tid; e < epow2; e += NT) ent[e] = kNoEntry;
+    __syncthreads();
+    for (int e = tid; e < n_e; e += NT) {
+      int j = 0;
+      while (e >= off[j + 1]) ++j;
+      const int i = e - off[j];
+      const int pos = lp[e];
+      if (pos < 0 || pos >= L) {            // cannot come from the top-k
+        bad = true;
+        continue;
+      }
+      int at = i;
+      for (int j2 = 0; j2 < n_tok; ++j2) {
+        if (j2 == j) continue;
+        // Entries of list j2 before this one: positions below pos, and pos
+        // itself when j2 < j.
+        const int32_t* l2 = lp + off[j2];
+        int lo = 0, hi = off[j2 + 1] - off[j2];
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (l2[mid] < pos || (j2 < j && l2[mid] == pos)) lo = mid + 1;
+          else hi = mid;
+        }
+        at += lo;
+      }
+      const size_t li = rows0 + (size_t)j * k + i;
+      uint64_t key = make_entry(pos, j, a.lists.rank[li]);
+      const int sl = a.lists.slot[li];
+      if (sl >= 0 && sl < C) key = with_slot(key, sl);
+      ent[at] = key;
+    }
+  } else if constexpr (SORTED) {
     // Positions come from the selection over [0, n_vis), so all are valid
     // (an invalid one would end the list here, flagged).
     for (int e = tid; e < epow2; e += NT) {
@@ -181,7 +232,7 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   // spread over the context, so buckets hold a few entries each), ordered
   // within a bucket on the whole entry; a full sort if the buckets come out
   // uneven or there is no room for a second buffer.
-  if (!SORTED) {
+  if (!SORTED && !MERGE) {
     bool done = false;
     if (a.two_buffers) {
       const int shift = a.pos_shift;

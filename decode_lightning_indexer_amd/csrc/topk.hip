@@ -126,6 +126,11 @@ struct RowOut {
   // bucket.  With FUSE, rpos / rslot are indexed by that input (= position)
   // order: each winner's rank and slot.
   uint64_t* pw;
+  // Optional (BYSORT, not FUSE): the winners in position order for a later
+  // residency update - position, rank and slot of each ([k] each).
+  int32_t* lpos;
+  int32_t* lrank;
+  int32_t* lslot;
 };
 
 // Top-k of one input by a 1024-thread workgroup; returns the number
@@ -505,15 +510,17 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
       hist[2 * tid + 1] = off + c0;
     }
     __syncthreads();
-    // pidx[j]: the input-order index of grp[j] (FUSE), so each rank finds
-    // its winner's place in the position-ordered list directly.
+    // pidx[j]: the input-order index of grp[j] (FUSE or position lists), so
+    // each rank finds its winner's place in the position-ordered list
+    // directly.
+    const bool lists = FUSE || out.lpos != nullptr;
     uint32_t* pidx = reinterpret_cast<uint32_t*>(out.pw + kpow2 + NT);
     auto emit_rank = [&](int r, uint64_t x, int i) {
       const int pos = (int)(~(uint32_t)x);     // -1 only for "no winner"
       const int32_t sl = pos >= 0 ? cs[pos] : -1;
       op[r] = pos;
       os[r] = sl;
-      if (FUSE) {
+      if (lists) {
         if (i < 0) {                           // (the full sort: search)
           int lo = 0, hi = keff - 1;           // pw ascends in position
           while (lo < hi) {
@@ -523,8 +530,14 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
           }
           i = lo;
         }
-        out.rpos[i] = r;
-        out.rslot[i] = sl;
+        if (FUSE) {
+          out.rpos[i] = r;
+          out.rslot[i] = sl;
+        } else {
+          out.lpos[i] = pos;
+          out.lrank[i] = r;
+          out.lslot[i] = sl;
+        }
       }
     };
     if (!big) {
@@ -532,7 +545,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
         const uint64_t x = pw[i];
         const uint32_t at = atomicAdd(&hist[rank_bucket(x)], 1u);
         grp[at] = x;
-        if (FUSE) pidx[at] = (uint32_t)i;
+        if (lists) pidx[at] = (uint32_t)i;
       }
       __syncthreads();
       // hist[b] is now the end of bucket b: bucket b spans [hist[b-1], hist[b]).
@@ -543,7 +556,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
         const int hi = (int)hist[bk];
         int r = lo;
         for (int q = lo; q < hi; ++q) r += grp[q] > x;
-        emit_rank(r, x, FUSE ? (int)pidx[j] : -1);
+        emit_rank(r, x, lists ? (int)pidx[j] : -1);
       }
     } else {
       for (int i = tid; i < kpow2; i += NT) grp[i] = i < keff ? pw[i] : 0ull;
@@ -711,7 +724,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int n_tok, int k, int kpow2) {
+    int n_tok, int k, int kpow2, PosLists pl) {
   // kpow2 words: winners grouped by bucket, or (rank order by sort) the sort
   // buffer followed by kpow2 words for the winners in position order.
   extern __shared__ uint64_t grp[];
@@ -721,7 +734,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(
                  visible(n_vis, b, m, j, L), (L & 3) == 0, 0};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
                    n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr,
-                   BYSORT ? grp + kpow2 : nullptr};
+                   BYSORT ? grp + kpow2 : nullptr,
+                   pl.pos ? pl.pos + o : nullptr, pl.pos ? pl.rank + o : nullptr,
+                   pl.pos ? pl.slot + o : nullptr};
   topk_row<RES, false, false, false, 0, BYSORT>(in, k, kpow2, out, grp);
 }
 
@@ -751,7 +766,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(
                (L & 3) == 0, base};
   const size_t ob = rb + (size_t)blockIdx.x * k;
   const RowOut out{nullptr, nullptr, nullptr, nullptr, okey + ob, opos + ob,
-                   nullptr, nullptr, nullptr};
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   topk_row<true, false, EXPL, true, VPT_E>(in, k, 0, out, nullptr);
 }
 
@@ -763,7 +778,7 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
     size_t cap, const int32_t* __restrict__ n_vis,
     const int32_t* __restrict__ cache_slots, int32_t* __restrict__ sel_pos,
     int32_t* __restrict__ sel_slot, int32_t* __restrict__ n_sel, int L, int m,
-    int n_tok, int k, int kpow2, int levels) {
+    int n_tok, int k, int kpow2, int levels, PosLists pl) {
   extern __shared__ uint64_t grp[];
   const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
   int n = visible(n_vis, b, m, j, L);
@@ -772,7 +787,9 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
                    n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr,
-                   BYSORT ? grp + kpow2 : nullptr};
+                   BYSORT ? grp + kpow2 : nullptr,
+                   pl.pos ? pl.pos + o : nullptr, pl.pos ? pl.rank + o : nullptr,
+                   pl.pos ? pl.slot + o : nullptr};
   topk_row<true, false, true, false, 0, BYSORT>(in, k, kpow2, out, grp);
 }
 
@@ -804,7 +821,7 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
   constexpr bool kSorted = RES;
   uint64_t* pw = kSorted ? dyn + kpow2 : nullptr;
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L, n_sel + b,
-                   nullptr, nullptr, rpos, rslot, pw};
+                   nullptr, nullptr, rpos, rslot, pw, nullptr, nullptr, nullptr};
   int keff;
   if constexpr (EXPL) {
     for (int l = 1; l <= levels; ++l) n = level_count(n, k, l);
@@ -884,11 +901,17 @@ size_t topk_ws_bytes(const ess_dims& d, int k, int n_tok) {
   return 4 * level_half((size_t)d.batch * n_tok, level_cap(d.ctx_len, k));
 }
 
+bool topk_pos_lists_fit(const ess_dims& d, int k, bool levels) {
+  const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
+  const bool nl = levels && n_levels(d.ctx_len, k) > 0;
+  return kpow2 <= kSortRankMax && (d.ctx_len <= CHUNK || nl);
+}
+
 hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, PosLists pl) {
   // The sorts need a power of two of at least one key per thread.  Rows
   // held in registers (and candidate lists) rank their winners by a sort
   // over a second kpow2-word buffer up to kSortRankMax.
@@ -910,11 +933,12 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
     if (bys)
       hipLaunchKernelGGL(topk_final_kernel<true>, dim3(d.batch * n_tok), dim3(NT), lds, s,
                          fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
-                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
+                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl, pl);
     else
       hipLaunchKernelGGL(topk_final_kernel<false>, dim3(d.batch * n_tok), dim3(NT), lds, s,
                          fk, fp, level_cap(d.ctx_len, k), n_vis, cache_slots, sel_pos,
-                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl);
+                         sel_slot, n_sel, d.ctx_len, d.mtp, n_tok, k, kpow2, nl,
+                         PosLists{nullptr, nullptr, nullptr});
     return hipGetLastError();
   }
   // Rows of at most one chunk stay in registers for all passes.
@@ -926,16 +950,17 @@ hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                          : (const void*)topk_kernel<false, false>;
   hipError_t e = ensure_dyn_lds(fn, (int)lds);
   if (e != hipSuccess) return e;
-#define ESS_TOPK_LAUNCH(R, S)                                                  \
+#define ESS_TOPK_LAUNCH(R, S, PL)                                              \
   hipLaunchKernelGGL((topk_kernel<R, S>), dim3(d.batch * n_tok), dim3(NT), lds, s, \
                      scores, n_vis, cache_slots, sel_pos, sel_slot, n_sel,       \
-                     d.ctx_len, d.mtp, n_tok, k, kpow2)
+                     d.ctx_len, d.mtp, n_tok, k, kpow2, PL)
+  const PosLists none{nullptr, nullptr, nullptr};
   if (bys)
-    ESS_TOPK_LAUNCH(true, true);
+    ESS_TOPK_LAUNCH(true, true, pl);
   else if (res)
-    ESS_TOPK_LAUNCH(true, false);
+    ESS_TOPK_LAUNCH(true, false, none);
   else
-    ESS_TOPK_LAUNCH(false, false);
+    ESS_TOPK_LAUNCH(false, false, none);
 #undef ESS_TOPK_LAUNCH
   return hipGetLastError();
 }

@@ -84,11 +84,21 @@ def test_capacity(L):
 
 
 def test_workspace_too_small(L):
+    # The attention needs its partials' part of the workspace (2 * 512 + 16
+    # bytes per request, token, head and row chunk): one byte short is
+    # refused.  The whole-step call needs all of ess_workspace_bytes.
     d = _d()
     need = ess.ess_workspace_bytes(d)
-    st = _status(lambda: ess.ess_sparse_mla_decode(d, P, P, P, P, P, P, P, P, P, P, need - 1, stream=0))
+    st = _status(lambda: ess.ess_sparse_mla_decode(d, P, P, P, P, P, P, P, P, P, P, 1024, stream=0))
     assert st == "out of memory"
-    assert "workspace" in L.ess_last_error().decode()
+    msg = L.ess_last_error().decode()
+    assert "workspace" in msg
+    attn_need = int(msg.split("need ")[1].split()[0])
+    assert attn_need <= need
+    st = _status(lambda: ess.ess_sparse_mla_decode(d, P, P, P, P, P, P, P, P, P, P, attn_need - 1, stream=0))
+    assert st == "out of memory"
+    io = ess.ess_layer_io(*([P] * 22), need - 1)
+    assert _status(lambda: ess.ess_decode_step(d, [io], P, ess.ESS_MODE_INLINE, stream=0, side=1)) == "out of memory"
 
 
 def test_decode_step_argument_checks(L):
