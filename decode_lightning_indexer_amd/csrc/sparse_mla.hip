@@ -200,6 +200,16 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const uint16_t* tail_b = tail.rows ? tail.rows + (size_t)b * 2 * tail.block * kLat : nullptr;
   const int tail_start = tail.rows ? tail.start[b] : INT32_MAX;
 
+  // Q fragments first (they do not depend on the row table, so their
+  // latency overlaps the table's): lane holds Q[h0 + c][32 kk + 8 g .. + 8].
+  bf16x8 qf[kLat / 32];
+  {
+    const uint16_t* qrow = q_abs + ((size_t)bj * H + h0 + c) * kLat + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < kLat / 32; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32);
+  }
+
   // Row sources of the chunk, once: hits read their slot, misses host
   // memory.  Given writer slots, the first head group stores each
   // designated-writer miss from the tile to its slot (wdst, and one bit per
@@ -235,15 +245,6 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
         wmask[((i0 - r0) >> 5) + 1] = (unsigned)(bal >> 32);
       }
     }
-  }
-
-  // Q fragments: lane holds Q[h0 + c][32 kk + 8 g .. + 8].
-  bf16x8 qf[kLat / 32];
-  {
-    const uint16_t* qrow = q_abs + ((size_t)bj * H + h0 + c) * kLat + g * 8;
-#pragma unroll
-    for (int kk = 0; kk < kLat / 32; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32);
   }
 
   const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
@@ -528,32 +529,40 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
 // Merge the chunk partials of one (request, token, head) in chunk order;
 // each partial is normalised, so its weight is 2^(m - M) times its sum, and
 // its stored values are multiplied back by their half's scale.  64 threads
-// per head, 8 values each (16-byte fp16 loads), 4 heads per workgroup.
-// Chunks go in groups of 8 whose loads are all in flight together, folded
-// in with a running maximum (fixed order).
+// per head and wave, 8 values each (16-byte fp16 loads).  With WPH waves per
+// head (many chunks, few heads) wave w folds chunks [w n / WPH, (w + 1) n /
+// WPH) and wave 0 then folds the waves' states in wave order; with one wave
+// per head a workgroup holds 4 heads.  Chunks go in groups of 8 whose loads
+// are all in flight together, folded in with a running maximum.  The order
+// of every fold depends only on the shape, never on the data's placement.
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-constexpr int kCombineHeads = 4;
+constexpr int kCombineThreads = 256;
 constexpr int kCombineGroup = 8;
-__global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
+template <int WPH>
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
     const _Float16* __restrict__ part_acc, const float4* __restrict__ part_ml,
     float* __restrict__ out, float* __restrict__ lse, int H, int nchunk) {
+  constexpr int kHeads = kCombineThreads / 64 / WPH;   // heads per workgroup
   const int bj = blockIdx.y;
-  const int h = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int hl = wave / WPH, w = wave % WPH;
+  const int h = blockIdx.x * kHeads + hl;
   const int t = threadIdx.x & 63;
   const bool hi_half = t * 8 >= kVal / 2;      // this thread's columns' scale
   const float4* ml = part_ml + (size_t)bj * nchunk * H + h;
   const _Float16* pp = part_acc + ((size_t)bj * nchunk * H + h) * kVal + t * 8;
+  const int cb = w * nchunk / WPH, ce = (w + 1) * nchunk / WPH;
   float M = -__builtin_inff(), den = 0.f;
   v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  for (int c0 = 0; c0 < nchunk; c0 += kCombineGroup) {
+  for (int c0 = cb; c0 < ce; c0 += kCombineGroup) {
     float4 v[kCombineGroup];
     v8h x[kCombineGroup];
 #pragma unroll
     for (int u = 0; u < kCombineGroup; ++u) {
-      const int ci = min(c0 + u, nchunk - 1);
+      const int ci = min(c0 + u, ce - 1);
       v[u] = ml[(size_t)ci * H];
       x[u] = *reinterpret_cast<const v8h*>(pp + (size_t)ci * H * kVal);
-      if (c0 + u >= nchunk) v[u].y = 0.f;          // past the last chunk
+      if (c0 + u >= ce) v[u].y = 0.f;              // past this wave's chunks
     }
     float mg = M;
 #pragma unroll
@@ -567,11 +576,33 @@ __global__ __launch_bounds__(64 * kCombineHeads) void mla_combine_kernel(
     M = mg;
 #pragma unroll
     for (int u = 0; u < kCombineGroup; ++u) {
-      const float w = v[u].y > 0.f ? exp2f(v[u].x - M) * v[u].y : 0.f;
-      const float ws = w * (hi_half ? v[u].w : v[u].z);
-      den += w;
+      const float wgt = v[u].y > 0.f ? exp2f(v[u].x - M) * v[u].y : 0.f;
+      const float ws = wgt * (hi_half ? v[u].w : v[u].z);
+      den += wgt;
       a0 += ws * __builtin_convertvector(x[u].lo, v4f);
       a1 += ws * __builtin_convertvector(x[u].hi, v4f);
+    }
+  }
+  if constexpr (WPH > 1) {
+    // The waves' states through LDS; wave 0 of the head folds them in order.
+    __shared__ float st_m[kHeads][WPH][64], st_d[kHeads][WPH][64];
+    __shared__ v4f st_a[kHeads][WPH][2][64];
+    st_m[hl][w][t] = M;
+    st_d[hl][w][t] = den;
+    st_a[hl][w][0][t] = a0;
+    st_a[hl][w][1][t] = a1;
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int q = 1; q < WPH; ++q) {
+      const float mq = st_m[hl][q][t], dq = st_d[hl][q][t];
+      if (!(dq > 0.f)) continue;
+      const float mg = fmaxf(M, mq);
+      const float s0 = exp2f(M - mg), s1 = exp2f(mq - mg);   // s0 = 0 while M is -inf
+      den = den * s0 + dq * s1;
+      a0 = a0 * s0 + st_a[hl][q][0][t] * s1;
+      a1 = a1 * s0 + st_a[hl][q][1][t] * s1;
+      M = mg;
     }
   }
   const float inv = 1.f / den;
@@ -668,10 +699,23 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
   }
 #undef ESS_MLA_CASE
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel,
-                     dim3(d.mla_heads / kCombineHeads, d.batch * d.mtp),
-                     dim3(64 * kCombineHeads), 0, s, part_acc, part_ml, out, lse,
-                     d.mla_heads, p.nchunk);
+  // Waves per head: enough that each folds about 8 chunks (one round of
+  // loads), when the grid would otherwise hold few workgroups.
+  const int bm = d.batch * d.mtp;
+  int wph = 1;
+  while (wph < 4 && p.nchunk >= 16 * wph && bm * d.mla_heads * wph < 4 * 1024) wph *= 2;
+#define ESS_COMBINE(W)                                                         \
+  hipLaunchKernelGGL(mla_combine_kernel<W>,                                    \
+                     dim3(d.mla_heads / (kCombineThreads / 64 / W), bm),       \
+                     dim3(kCombineThreads), 0, s, part_acc, part_ml, out, lse, \
+                     d.mla_heads, p.nchunk)
+  if (wph == 4)
+    ESS_COMBINE(4);
+  else if (wph == 2)
+    ESS_COMBINE(2);
+  else
+    ESS_COMBINE(1);
+#undef ESS_COMBINE
   return hipGetLastError();
 }
 

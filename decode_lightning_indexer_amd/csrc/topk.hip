@@ -748,7 +748,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_vis,
     const uint32_t* __restrict__ ikey, const int32_t* __restrict__ ipos,
     uint32_t* __restrict__ okey, int32_t* __restrict__ opos, size_t cap, int L,
-    int m, int n_tok, int k, int level) {
+    int m, int n_tok, int k, int kpow2, int level) {
   const int row = blockIdx.y, b = row / n_tok, j = row % n_tok;
   int n = visible(n_vis, b, m, j, L);
   for (int l = 1; l < level; ++l) n = level_count(n, k, l);
@@ -765,9 +765,11 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(
     in = RowIn{scores + ((size_t)b * m + j) * L + base, nullptr, nullptr, ns,
                (L & 3) == 0, base};
   const size_t ob = rb + (size_t)blockIdx.x * k;
+  // (Staging this output in LDS to write it without a branch per key was
+  // measured slower: 13.4 -> 14.0 us and 13.9 -> 15.8 us per level at 1M.)
   const RowOut out{nullptr, nullptr, nullptr, nullptr, okey + ob, opos + ob,
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  topk_row<true, false, EXPL, true, VPT_E>(in, k, 0, out, nullptr);
+  topk_row<true, false, EXPL, true, VPT_E>(in, k, kpow2, out, nullptr);
 }
 
 // The final selection of a long row from its candidate list after `levels`
@@ -874,17 +876,18 @@ hipError_t enqueue_levels(const ess_dims& d, int k, int n_tok, int nl,
   uint32_t* key[2] = {reinterpret_cast<uint32_t*>(w), reinterpret_cast<uint32_t*>(w + 2 * half)};
   int32_t* pos[2] = {reinterpret_cast<int32_t*>(w + half), reinterpret_cast<int32_t*>(w + 3 * half)};
   int n = d.ctx_len;
+  const int kpow2 = pow2_at_least(k) < NT ? NT : pow2_at_least(k);
   for (int l = 1; l <= nl; ++l) {
     const int chunks = (n + level_chunk(l) - 1) / level_chunk(l);
     const int ob = (l - 1) & 1, ib = ob ^ 1;
     if (l == 1)
       hipLaunchKernelGGL(topk_level_kernel<false>, dim3(chunks, rows), dim3(NT), 0, s,
                          scores, n_vis, nullptr, nullptr, key[ob], pos[ob], cap,
-                         d.ctx_len, d.mtp, n_tok, k, l);
+                         d.ctx_len, d.mtp, n_tok, k, kpow2, l);
     else
       hipLaunchKernelGGL(topk_level_kernel<true>, dim3(chunks, rows), dim3(NT), 0, s,
                          scores, n_vis, key[ib], pos[ib], key[ob], pos[ob], cap,
-                         d.ctx_len, d.mtp, n_tok, k, l);
+                         d.ctx_len, d.mtp, n_tok, k, kpow2, l);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     n = level_count(n, k, l);

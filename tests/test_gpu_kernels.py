@@ -282,6 +282,10 @@ def _bf16(rng, shape, std):
     # 8 requests x 2 tokens x 2 head groups: 8 chunks of 256 of the 2048
     # rows, the chunk plan of the 128K workload.
     (8, 2, 128, 6000, 2048, 4200, True, 0.7),
+    # One request: 32 chunks of 64 rows, combined by 4 waves per head (the
+    # 1M workload's plan), and 16 chunks by 2 waves per head.
+    (1, 1, 64, 20000, 2048, 4096, False, 0.6),
+    (1, 2, 128, 9000, 1024, 2500, True, 0.5),
 ])
 def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
     _mla_case(B, m, H, L, k, C, ragged, p_hit)
