@@ -26,10 +26,18 @@ inline int pow2_at_least(int x) {
 }
 
 // ---- indexer ------------------------------------------------------------
+// Words the indexer clears before it scores, for a selection that follows
+// on the same stream (rows of `words` 32-bit words, `stride_words` apart).
+struct ClearSpec {
+  uint32_t* base;
+  size_t stride_words;
+  int words;
+  int rows;
+};
 hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
                                const float* w, const uint8_t* k,
                                const int32_t* n_vis, float* scores,
-                               hipStream_t s);
+                               hipStream_t s, ClearSpec clr = ClearSpec{nullptr, 0, 0, 0});
 
 // ---- top-k --------------------------------------------------------------
 // Workspace of the multi-level selection of rows longer than 32768 keys
@@ -47,11 +55,22 @@ struct PosLists {
 // Whether launch_topk can fill position lists for this k (ranked from a
 // compact winner list: rows of at most 32768 keys, or levels when `levels`).
 bool topk_pos_lists_fit(const ess_dims& d, int k, bool levels);
+// Rows longer than 32768 keys (k <= 4096, and few enough rows) select with
+// several workgroups per row that exchange counts through the workspace
+// (unless `split` is false: then they select in levels, whose workgroups
+// never wait for one another - the choice for a selection that runs beside
+// other kernels); its control words must be zero when the selection
+// starts.  split_clear tells whether a selection of (k, n_tok) over `ws`
+// takes that path and which words to clear; a launch with `cleared` set
+// trusts that they were (by the indexer on the same stream), otherwise it
+// clears them itself.
+bool split_clear(const ess_dims& d, int k, int n_tok, void* ws, ClearSpec* c);
 hipError_t launch_topk(const ess_dims& d, int k, int n_tok,
                        const float* scores, const int32_t* n_vis,
                        const int32_t* cache_slots, int32_t* sel_pos,
                        int32_t* sel_slot, int32_t* n_sel, void* ws,
-                       hipStream_t s, PosLists pl = PosLists{nullptr, nullptr, nullptr});
+                       hipStream_t s, PosLists pl = PosLists{nullptr, nullptr, nullptr},
+                       bool cleared = false, bool split = true);
 
 // ---- pool ---------------------------------------------------------------
 // Per-request LRU state: header, slot stamps [C], ring of (slot, stamp).
@@ -90,7 +109,8 @@ hipError_t launch_select_update(const ess_dims& d, int k, const float* scores,
                                 int32_t* miss_pos, int32_t* miss_slot,
                                 int32_t* n_miss, int32_t* n_evict,
                                 int32_t* row_dst, int32_t* sel_slot_post,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, bool cleared = false,
+                                bool split = true);
 hipError_t launch_pool_update(const ess_dims& d, int k, int n_tok,
                               const int32_t* sel_pos, const int32_t* n_sel,
                               int32_t* cache_slots, int32_t* slot_pos,

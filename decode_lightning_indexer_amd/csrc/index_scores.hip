@@ -104,8 +104,16 @@ template <int DI, int NT, int MT>
 __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const int32_t* __restrict__ n_vis,
-    float* __restrict__ scores, int L, int HI) {
+    float* __restrict__ scores, int L, int HI, ClearSpec clr) {
   using S = Stage<DI>;
+  if (clr.base) {
+    // Zero the following selection's control words, spread over the grid.
+    const size_t total = (size_t)clr.rows * clr.words;
+    const size_t step = (size_t)gridDim.x * gridDim.y * kThreads;
+    for (size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+         i < total; i += step)
+      clr.base[(i / clr.words) * clr.stride_words + i % clr.words] = 0u;
+  }
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -231,13 +239,13 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 template <int DI, int NT, int MT>
 hipError_t launch_t(const ess_dims& d, const uint8_t* q, const float* w,
                     const uint8_t* k, const int32_t* n_vis, float* scores,
-                    hipStream_t s) {
+                    hipStream_t s, ClearSpec clr) {
   dim3 grid((d.ctx_len + kSpan - 1) / kSpan, d.batch);
   const size_t lds = (size_t)(kThreads / 64) * 2 * Stage<DI>::kBytes;
   hipError_t e = ensure_dyn_lds((const void*)index_scores_kernel<DI, NT, MT>, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((index_scores_kernel<DI, NT, MT>), grid, dim3(kThreads),
-                     lds, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads);
+                     lds, s, q, w, k, n_vis, scores, d.ctx_len, d.idx_heads, clr);
   return hipGetLastError();
 }
 
@@ -246,13 +254,13 @@ hipError_t launch_t(const ess_dims& d, const uint8_t* q, const float* w,
 hipError_t launch_index_scores(const ess_dims& d, const uint8_t* q,
                                const float* w, const uint8_t* k,
                                const int32_t* n_vis, float* scores,
-                               hipStream_t s) {
+                               hipStream_t s, ClearSpec clr) {
   // Shapes checked by the caller: DI in {64, 128}, H_I % 16 == 0,
   // m * H_I <= 128.
   const int rows = d.mtp * d.idx_heads;
 #define ESS_IDX_CASE(DI_, NT_, MT_)                                          \
   if (d.idx_dim == DI_ && rows == NT_ * 16 && d.mtp == MT_)                 \
-    return launch_t<DI_, NT_, MT_>(d, q, w, k, n_vis, scores, s);
+    return launch_t<DI_, NT_, MT_>(d, q, w, k, n_vis, scores, s, clr);
 #define ESS_IDX_ROWS(DI_)                                                    \
   ESS_IDX_CASE(DI_, 1, 1) ESS_IDX_CASE(DI_, 2, 1) ESS_IDX_CASE(DI_, 3, 1)    \
   ESS_IDX_CASE(DI_, 4, 1) ESS_IDX_CASE(DI_, 5, 1) ESS_IDX_CASE(DI_, 6, 1)    \

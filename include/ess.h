@@ -84,8 +84,10 @@ typedef enum ess_status {
 
 /* Bytes of workspace the calls below need for these dims: the attention's
  * split-row partials, then (ctx_len > 32768 with topk or pool_slots <= 4096)
- * the candidate lists of the top-k's levels.  One workspace serves one
- * stream at a time; it must be 16-byte aligned. */
+ * the top-k's exchange area for rows split over several workgroups or the
+ * candidate lists of its levels, whichever is larger, then each token's
+ * winners in position order for a step with several tokens.  One workspace
+ * serves one stream at a time; it must be 16-byte aligned. */
 size_t ess_workspace_bytes(const ess_dims* d);
 
 /* Bytes of the opaque per-layer LRU state (B requests): per request a header,
@@ -142,11 +144,18 @@ ess_status ess_index_scores(const ess_dims* d, const uint8_t* q_fp8,
  * sel_pos, sel_slot [B][n_tok][k] and n_sel [B][n_tok].  1 <= n_tok <= m,
  * 1 <= k <= 16384.  Scores must not be NaN.  Rows of at most 32768 keys,
  * and any k > 4096, select in on-chip memory (ws and ws_bytes are not used;
- * NULL and 0 are fine).  Longer rows with k <= 4096 select in levels: each
+ * NULL and 0 are fine).  Longer rows with k <= 4096 use ws: each row is
+ * split over workgroups of 16384 keys that select together, exchanging
+ * counts and winners through ws (when B * n_tok * ceil(L / 16384) is at most
+ * half the device's compute units), or else is reduced in levels - each
  * 16384-key chunk's top-k is written to ws as candidates until one
- * workgroup holds the row's list; ws must then hold ess_workspace_bytes(d)
- * bytes (enough for k = d->topk with n_tok <= d->mtp, and for
- * k = d->pool_slots with n_tok = 1), else ESS_ERR_NOMEM. */
+ * workgroup holds the row's list.  ws must then hold
+ * ess_workspace_bytes(d) bytes (enough for k = d->topk with n_tok <=
+ * d->mtp, and for k = d->pool_slots with n_tok = 1), else ESS_ERR_NOMEM.
+ * The split selection needs all workgroups of a row resident at once; its
+ * waits are bounded, and a row whose wait ran out (only possible when other
+ * work holds the compute units for seconds) is returned with n_sel = 0 and
+ * no selection. */
 ess_status ess_topk_lookup(const ess_dims* d, int32_t k, int32_t n_tok,
                            const float* scores, const int32_t* n_vis,
                            const int32_t* cache_slots, int32_t* sel_pos,

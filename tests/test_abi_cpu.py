@@ -116,23 +116,41 @@ def test_status_strings(L):
         assert L.ess_status_string(code).decode() == text
 
 
+def _split_row_bytes(spans, k):
+    # Control words (512 B) and four 2048-bin histograms, two counts per
+    # span (128-byte aligned), 64 candidate keys, k winners; 256-aligned.
+    win = 512 + 4 * 2048 * 4 + -(-spans * 8 // 128) * 128 + 64 * 8
+    return -(-(win + 8 * k) // 256) * 256
+
+
 def test_long_rows_need_a_topk_workspace(L):
-    # Rows over 32768 keys with k <= 4096 select in levels whose candidate
-    # lists (two buffers of keys and positions, k per 16384-key chunk and
-    # row) sit after the attention's partials; the first fill's top-C
-    # (n_tok = 1) is covered too.
+    # Rows over 32768 keys with k <= 4096 select either split over
+    # workgroups that exchange counts and winners through the workspace, or
+    # in levels whose candidate lists (two buffers of keys and positions, k
+    # per 16384-key chunk and row) sit there; the region after the
+    # attention's partials holds the larger of the two, for the step's top-k
+    # and for the first fill's top-C (n_tok = 1).
     short = _d(topk=2048, pool_slots=4096)
     long_ = _d(ctx_len=100000, topk=2048, pool_slots=4096)
     chunks = -(-100000 // 16384)
     step = 4 * (2 * 1) * chunks * 2048 * 4       # B=2 rows, k=2048
     fill = 4 * (2 * 1) * chunks * 4096 * 4       # k=C=4096
-    assert ess.ess_workspace_bytes(long_) - ess.ess_workspace_bytes(short) == max(step, fill)
+    split = 2 * _split_row_bytes(chunks, 4096)
+    assert ess.ess_workspace_bytes(long_) - ess.ess_workspace_bytes(short) == max(step, fill, split)
+    # Few candidates per chunk: the split selection's exchange area is larger.
+    few = _d(batch=1, ctx_len=40000, topk=64, pool_slots=64)
+    few_short = _d(batch=1, topk=64, pool_slots=64)
+    lv = 4 * 1 * 3 * 64 * 4
+    sp = _split_row_bytes(3, 64)
+    assert sp > lv
+    assert ess.ess_workspace_bytes(few) - ess.ess_workspace_bytes(few_short) == \
+        -(-sp // 256) * 256
     # k > 4096 never uses levels.
     assert ess.ess_workspace_bytes(_d(ctx_len=100000, topk=8192, pool_slots=16384)) == \
         ess.ess_workspace_bytes(_d(topk=8192, pool_slots=16384))
     st = _status(lambda: ess.ess_topk_lookup(long_, 2048, 1, P, P, P, P, P, P, stream=0))
     assert st == "out of memory"
-    assert "levels" in L.ess_last_error().decode()
+    assert "workspace" in L.ess_last_error().decode()
     st = _status(lambda: ess.ess_topk_lookup(long_, 2048, 1, P, P, P, P, P, P, P + 4, 1 << 30, stream=0))
     assert st == "invalid argument"
 

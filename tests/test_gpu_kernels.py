@@ -108,7 +108,8 @@ def _scores(kind, rng, shape):
     ("indexer_like", 1, 2, 1, 30000, 16384, False),  # fill-size k, token 0 only
     ("int_ties", 3, 1, 1, 1, 1, False),
     ("float", 1, 3, 3, 2049, 7, True),
-    # Rows longer than 32768 keys select in levels (k <= 4096).
+    # Rows longer than 32768 keys (k <= 4096) are split over workgroups of
+    # 16384 keys that select together.
     ("int_ties", 2, 1, 1, 70000, 1000, True),
     ("equal", 1, 1, 1, 100000, 2048, False),      # one run of equal keys
     ("zeros", 1, 1, 1, 50000, 513, False),        # +-0, k not a multiple of 4
@@ -118,6 +119,9 @@ def _scores(kind, rng, shape):
     ("float", 1, 1, 1, 300000, 7, True),
     ("float", 1, 1, 1, 40000, 5000, False),       # k > 4096: one workgroup
     ("float", 2, 3, 1, 40000, 100, True),         # n_tok < m on long rows
+    # 10 rows x 14 spans: more workgroups than the split selection takes in
+    # one launch, so these rows select in levels.
+    ("indexer_like", 5, 2, 2, 220000, 1024, True),
 ])
 def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
     rng = np.random.default_rng(zlib.crc32(f"{kind}-{L}-{k}".encode()))
@@ -400,6 +404,34 @@ def test_miss_copy():
         untouched = np.setdiff1d(np.arange(C), ms[b, :nm[b]])
         assert not gp[b, untouched].any()
     host.free()
+
+
+@pytest.mark.parametrize("kind", ["int_ties", "equal", "indexer_like"])
+def test_topk_split_rows_at_the_edges(kind):
+    # Rows of 70000 keys are split over five workgroups; visible lengths of
+    # 0, 1, k - 1, k, k + 1, one span and all of them, so some rows select
+    # everything, some spans see nothing, and ties cross span boundaries.
+    L, k = 70000, 2048
+    n_vis = np.array([[0], [1], [k - 1], [k], [k + 1], [16384], [16385], [L]], np.int32)
+    B = n_vis.shape[0]
+    rng = np.random.default_rng(zlib.crc32(f"split-{kind}".encode()))
+    s = _scores(kind, rng, (B, 1, L))
+    cs = np.where(rng.random((B, L)) < 0.5, rng.integers(0, 8192, (B, L)), -1).astype(np.int32)
+    d = dims(batch=B, mtp=1, ctx_len=L, topk=k, pool_slots=8192)
+    sp = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    ss = torch.empty_like(sp)
+    ns = torch.empty((B, 1), dtype=torch.int32, device="cuda")
+    wsb = ess.ess_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    for rep in range(2):      # the workspace's counters start from what the last call left
+        ess.ess_topk_lookup(d, k, 1, t(s), t(n_vis), t(cs), sp, ss, ns, ws, wsb)
+        sync()
+        for b in range(B):
+            rp, rs, rn = topk_lookup(s[b, :1].astype(np.float64), n_vis[b, :1], k, cs[b])
+            where = (kind, rep, b, int(n_vis[b, 0]))
+            assert np.array_equal(h(ns)[b], rn), where
+            assert np.array_equal(h(sp)[b], rp), where
+            assert np.array_equal(h(ss)[b], rs), where
 
 
 def test_topk_random_shapes_around_the_level_boundary():
