@@ -139,20 +139,34 @@ KERNEL_SOURCES = {
     "topk_kernel": "topk.hip",
     "topk_level_kernel": "topk.hip",
     "topk_final_kernel": "topk.hip",
+    "topk_split_kernel": "topk.hip",
+    "split_clear_kernel": "topk.hip",
     "select_update_kernel": "topk.hip",
     "pool_update_kernel": "pool_update.hip",
+    "pool_reset_kernel": "pool_update.hip",
+    "pool_status_kernel": "pool_update.hip",
     "miss_copy_kernel": "miss_copy.hip",
+    "entry_copy_kernel": "miss_copy.hip",
+    "append_tokens_kernel": "tail.hip",
     "sparse_mla_kernel": "sparse_mla.hip",
     "mla_combine_kernel": "sparse_mla.hip",
+    "append_rows_kernel": "prefill.hip",
+    "column_sums_kernel": "prefill.hip",
+    "column_sums_reduce_kernel": "prefill.hip",
 }
 
 
 def source_digest(kernel):
+    """Digest of the kernel's source file together with every header of the
+    kernel sources (any of which it may include)."""
+    import glob
     import hashlib
-    src = os.path.join(ROOT, "decode_lightning_indexer_amd", "csrc",
-                       KERNEL_SOURCES[kernel])
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "decode_lightning_indexer_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(csrc, KERNEL_SOURCES[kernel])] + sorted(glob.glob(os.path.join(csrc, "*.h"))):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel, workload):
@@ -558,8 +572,8 @@ def config_measurements(args):
 
 def fp8_entries(args, names=("32k-b16", "128k-b8-mtp2-r099")):
     """The same steps with the host store holding 656-byte fp8 entries: the
-    misses cross the host link as entries and are dequantized into their
-    slots before the attention, which then reads every row from the pool.
+    misses cross the host link as entries, read inside the attention kernel,
+    which dequantizes each in its tile and writes the bf16 row to its slot.
     Step time and the last step's entry copy replayed alone, beside the
     bf16 store's figures (bytes per miss 656 against 1152)."""
     from decode_lightning_indexer_amd import ess
