@@ -928,7 +928,7 @@ inline SplitLayout split_layout(int spans, int k) {
   SplitLayout l;
   l.hist = kCtlWords * 4;
   l.mm = l.hist + (size_t)(1 + kSplitPasses) * kSplitBins * 4;
-  l.clear_words = l.mm / 4;
+  l.clear_words = l.mm / 4;   // a multiple of four (the clear kernel's 16-byte stores)
   l.cand = l.mm + align_up((size_t)spans * 8, 128);
   l.win = l.cand + (size_t)kSmall * 8;
   l.row_bytes = align_up(l.win + (size_t)k * 8, 256);
@@ -978,10 +978,14 @@ __device__ __forceinline__ void row_barrier(uint32_t* ctl, uint32_t phase, int s
   __syncthreads();
 }
 
+// Zero the first `words` 32-bit words of every row (a multiple of four):
+// blockIdx.y = row, blockIdx.x = one of gridDim.x slices, 16-byte stores.
 __global__ __launch_bounds__(256) void split_clear_kernel(char* sws, size_t row_bytes,
                                                           int words) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(sws + (size_t)blockIdx.x * row_bytes);
-  for (int i = threadIdx.x; i < words; i += 256) p[i] = 0u;
+  uint4* p = reinterpret_cast<uint4*>(sws + (size_t)blockIdx.y * row_bytes);
+  const int n = words / 4;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 struct SplitArgs {
@@ -1435,7 +1439,7 @@ hipError_t enqueue_split(const ess_dims& d, int k, int n_tok, const float* score
   hipError_t e = ensure_dyn_lds((const void*)topk_split_kernel<FUSE>, (int)lds);
   if (e != hipSuccess) return e;
   if (!cleared) {
-    hipLaunchKernelGGL(split_clear_kernel, dim3(rows), dim3(256), 0, s,
+    hipLaunchKernelGGL(split_clear_kernel, dim3(8, rows), dim3(256), 0, s,
                        static_cast<char*>(ws), lay.row_bytes, (int)lay.clear_words);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
