@@ -12,6 +12,42 @@ __device__ __forceinline__ int pow2_at_least_dev(uint32_t x) {
   return x <= 1u ? 1 : (int)(1u << (32 - __clz(x - 1u)));
 }
 
+// Inclusive scans over the 64 lanes of a wave in registers, with gfx9's
+// DPP lane moves: row_shr 1, 2, 4, 8 within each row of 16 lanes, then
+// row_bcast:15 (the last lane of rows 0 and 2 into rows 1 and 3) and
+// row_bcast:31 (lane 31 into rows 2 and 3).  The whole wave must be active.
+// (A shuffle per step goes through the LDS crossbar, one round trip each;
+// these stay in the vector ALU.)  Lanes a move leaves without a source
+// take the operation's identity.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
+  constexpr uint32_t I = 0xFFFFFFFFu;
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x111, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x112, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x114, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x118, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x142, 0xA, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(I, x, 0x143, 0xC, 0xF, false));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));
+  return x;
+}
+
 // Exclusive prefix sum over the workgroup in thread order.  tmp needs
 // NT/64 + 1 words of LDS.  Returns this thread's exclusive prefix; *total
 // receives the sum over all threads.
@@ -20,22 +56,12 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* tmp,
                                                  uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) tmp[wv] = x;
   __syncthreads();
   if (wv == 0) {
-    uint32_t t = lane < NW ? tmp[lane] : 0u;
-    uint32_t ti = t;
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      uint32_t y = __shfl_up(ti, o);
-      if (lane >= o) ti += y;
-    }
+    const uint32_t t = lane < NW ? tmp[lane] : 0u;
+    const uint32_t ti = wave_incl_sum(t);
     if (lane < NW) tmp[lane] = ti - t;
     if (lane == NW - 1) tmp[NW] = ti;
   }
@@ -47,28 +73,22 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* tmp,
 }
 
 // The same over uint64 values; used with several 16-bit counts packed in
-// one word (each field's total must stay below 2^16).  tmp: NT/64 + 1 words.
+// one word (each field's total must stay below 2^16, so the low 32 bits
+// never carry into the high 32 and each half is scanned on its own).
+// tmp: NT/64 + 1 words.
 template <int NT>
 __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, uint64_t* tmp,
                                                      uint64_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint64_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint64_t x = ((uint64_t)wave_incl_sum((uint32_t)(v >> 32)) << 32) |
+                     wave_incl_sum((uint32_t)v);
   if (lane == 63) tmp[wv] = x;
   __syncthreads();
   if (wv == 0) {
     const uint64_t t = lane < NW ? tmp[lane] : 0ull;
-    uint64_t ti = t;
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      const uint64_t y = __shfl_up(ti, o);
-      if (lane >= o) ti += y;
-    }
+    const uint64_t ti = ((uint64_t)wave_incl_sum((uint32_t)(t >> 32)) << 32) |
+                        wave_incl_sum((uint32_t)t);
     if (lane < NW) tmp[lane] = ti - t;
     if (lane == NW - 1) tmp[NW] = ti;
   }
@@ -85,11 +105,8 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx,
                                              uint32_t* tmp) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor(mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor(mx, o));
-  }
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_min(mn), 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(mx), 63);
   if (lane == 0) {
     tmp[wv] = mn;
     tmp[NW + wv] = mx;
