@@ -127,46 +127,96 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   bool bad = false;
   constexpr int kU = 4;   // entries per thread whose reads are in flight together
   if constexpr (MERGE) {
-    // The lists' positions into the second buffer, then each entry finds
-    // its merged place by binary searches in the other tokens' lists.
+    // Every entry's position, rank and slot are read first, all of a
+    // thread's reads in flight together (the merge runs with two buffers,
+    // so n_e <= kTwoBufferMax = kU * NT); the positions go to the second
+    // buffer, then each entry finds its merged place by binary searches in
+    // the other tokens' lists.
+    static_assert(kTwoBufferMax <= kU * NT, "one read per entry slot below");
     int32_t* lp = reinterpret_cast<int32_t*>(smem_ent + epow2);
-    for (int e = tid; e < n_e; e += NT) {
-      int j = 0;
-      while (e >= off[j + 1]) ++j;
-      lp[e] = a.lists.pos[rows0 + (size_t)j * k + (e - off[j])];
+    int pos[kU], rk[kU], sl[kU], tok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = tid + u * NT;
+      pos[u] = -1;
+      rk[u] = 0;
+      sl[u] = -1;
+      tok[u] = 0;
+      if (e < n_e) {
+        int j = 0;
+        while (e >= off[j + 1]) ++j;
+        const size_t li = rows0 + (size_t)j * k + (e - off[j]);
+        tok[u] = j;
+        pos[u] = a.lists.pos[li];
+        rk[u] = a.lists.rank[li];
+        sl[u] = a.lists.slot[li];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = tid + u * NT;
+      if (e < n_e) lp[e] = pos[u];
     }
     // (every place starts empty: an entry that could not be placed leaves
     // a kNoEntry, which ends the scans below, never a stale entry)
     for (int e = tid; e < epow2; e += NT) ent[e] = kNoEntry;
     __syncthreads();
-    for (int e = tid; e < n_e; e += NT) {
-      int j = 0;
-      while (e >= off[j + 1]) ++j;
-      const int i = e - off[j];
-      const int pos = lp[e];
-      if (pos < 0 || pos >= L) {            // cannot come from the top-k
+    // Place = index in its own list + the entries before it in every other
+    // list (positions below it, and its own position when that list's token
+    // is smaller).  Round d searches list (token + d) mod n_tok for each of
+    // a thread's entries, in lockstep with the same power-of-two steps
+    // (uniform over the workgroup, sized for the longest list), so their
+    // LDS reads are in flight together.
+    int at[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) at[u] = tid + u * NT - off[tok[u]];
+    int len_max = 0;
+    for (int j = 0; j < n_tok; ++j) len_max = max(len_max, off[j + 1] - off[j]);
+    // steps S, S/2, ..., 1 reach up to index 2S - 2 >= len_max - 1
+    const int s0 = pow2_at_least_dev((uint32_t)len_max + 1u) >> 1;
+    for (int d = 1; d < n_tok; ++d) {
+      const int32_t* l2[kU];
+      int len[kU], last[kU];
+      bool before[kU];                      // equal positions of list j2 come first
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        int j2 = tok[u] + d;
+        if (j2 >= n_tok) j2 -= n_tok;
+        l2[u] = lp + off[j2];
+        len[u] = off[j2 + 1] - off[j2];
+        before[u] = j2 < tok[u];
+        last[u] = -1;
+      }
+      for (int step = s0; step >= 1; step >>= 1) {
+        // Every load is made (at a clamped index inside the list region),
+        // so none waits behind a branch; a probe past the list's end
+        // compares as above every position.
+        int32_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          v[u] = l2[u][min(last[u] + step, max(len[u] - 1, 0))];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int cand = last[u] + step;
+          const bool take = (cand < len[u]) & ((v[u] < pos[u]) | (before[u] & (v[u] == pos[u])));
+          last[u] = take ? cand : last[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) at[u] += last[u] + 1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = tid + u * NT;
+      if (e >= n_e) break;
+      const int p = pos[u];
+      if (p < 0 || p >= L) {                // cannot come from the top-k
         bad = true;
         continue;
       }
-      int at = i;
-      for (int j2 = 0; j2 < n_tok; ++j2) {
-        if (j2 == j) continue;
-        // Entries of list j2 before this one: positions below pos, and pos
-        // itself when j2 < j.
-        const int32_t* l2 = lp + off[j2];
-        int lo = 0, hi = off[j2 + 1] - off[j2];
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (l2[mid] < pos || (j2 < j && l2[mid] == pos)) lo = mid + 1;
-          else hi = mid;
-        }
-        at += lo;
-      }
-      const size_t li = rows0 + (size_t)j * k + i;
-      uint64_t key = make_entry(pos, j, a.lists.rank[li]);
-      const int sl = a.lists.slot[li];
-      if (sl >= 0 && sl < C) key = with_slot(key, sl);
-      ent[at] = key;
+      uint64_t key = make_entry(p, tok[u], rk[u]);
+      if (sl[u] >= 0 && sl[u] < C) key = with_slot(key, sl[u]);
+      ent[min(at[u], n_e - 1)] = key;
     }
   } else if constexpr (SORTED) {
     // Positions come from the selection over [0, n_vis), so all are valid
