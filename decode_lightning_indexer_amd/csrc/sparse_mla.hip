@@ -28,20 +28,25 @@
 // another token writes is read from host memory too, never from the slot
 // being written.
 //
-// Per workgroup: one (request, token), 16 heads per wave, one chunk of rows
-// split between two sub-groups of waves that take alternate 32-row tiles
-// (each sub-group holds the same heads).  Tiles go from memory straight into
-// LDS (gfx950's 16-byte global-to-LDS load, one 1 KB block per wave
-// instruction), row-major with a 32-byte pad per row; each sub-group has
-// two tile buffers, so one tile is in flight while the other is computed,
-// with one workgroup barrier per tile and no registers held for staging.
-// Padding and unusable rows load a zero row.  At the end the second
-// sub-group's running state is merged into the first's through LDS, and the
-// chunk's partial is written normalised, in fp16 scaled by a power of two per
-// (head, half of the value columns) so that the half's largest magnitude
-// lies in [0.5, 1): the stored values keep fp16's 11 significant bits
-// whatever the latents' range (no overflow above 65504, no subnormals for
-// small latents).  The running max and sum and the two scales are fp32.
+// Per workgroup: one (request, token), one group of heads, one chunk of rows.
+// Each wave takes 16 heads and one half of the 512 value columns; the two
+// waves of a head block compute the same scores (so no state is merged
+// between waves) and accumulate disjoint columns.  Tiles of 32 rows go from
+// memory straight into LDS (gfx950's 16-byte global-to-LDS load, one 1 KB
+// block per wave instruction), row-major with a 32-byte pad per row, into a
+// ring of four buffers: three tiles are in flight while every wave reads
+// the fourth, with one workgroup barrier per tile.  The waves of the first
+// column half issue every tile load and store nothing, so the count of
+// their loads in flight says which tiles have landed; the waves of the
+// second half store the miss rows to their pool slots.  The queries of the
+// workgroup's heads also come through LDS (two ring buffers, before the
+// third and fourth tiles are issued).  Padding and unusable rows load a zero
+// row.  At the end each wave writes its half of the chunk's partial
+// normalised, in fp16 scaled by a power of two per (head, half of the value
+// columns) so that the half's largest magnitude lies in [0.5, 1): the stored
+// values keep fp16's 11 significant bits whatever the latents' range (no
+// overflow above 65504, no subnormals for small latents).  The running max
+// and sum and the two scales are fp32.
 //   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
 //                                           rows from LDS, B = Q in registers
 //   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T, B = P in registers
@@ -91,14 +96,17 @@ constexpr int kKStride = kRowSlots * 8;         // bf16 per row-major row (1184 
 constexpr int kChunks16 = kLat / 8;             // 16-byte pieces per latent row (72)
 constexpr int kTileLoads = (kTile * kRowSlots + 63) / 64;   // wave loads per tile (37)
 constexpr int kTileSlots = kTileLoads * 64;     // slots per tile buffer (2368)
-constexpr int kStages = 2;                      // tile buffers per sub-group
+constexpr int kRing = 4;                        // tile buffers: three in flight, one read
 constexpr int kMaxChunkRows = 512;              // rows per chunk held in LDS tables
 constexpr int kMaxChunkTiles = kMaxChunkRows / kTile;
-// Tile rings, then the row table, the writer slots and the per-tile writer
-// masks.
-constexpr size_t kMlaLds = (size_t)2 * kStages * kTileSlots * 16 +
-                           (size_t)kMaxChunkRows * 4 * 2 + kMaxChunkTiles * 4;
-constexpr int kNoRow = INT32_MIN;    // row code: contributes zeros
+// Tile ring, then the rows' source addresses, the writer slots and the
+// per-tile writer and fp8-entry masks.
+constexpr size_t kMlaLds = (size_t)kRing * kTileSlots * 16 + (size_t)kMaxChunkRows * 8 +
+                           (size_t)kMaxChunkRows * 4 + kMaxChunkTiles * 4 * 2;
+static_assert(kMlaLds <= 160 * 1024, "LDS of one compute unit");
+// The queries of up to 64 heads, rows laid out like tile rows, fill two
+// tile buffers.
+static_assert(64 * kRowSlots <= 2 * kTileSlots, "queries fit in two tile buffers");
 // A miss read from a 656-byte fp8 entry lands raw in the last 41 slots of
 // its tile row and is expanded in place to 576 bf16 before the tile is read.
 constexpr int kRawSlot0 = kRowSlots - kEntryPieces;   // 33
@@ -126,8 +134,47 @@ __device__ __forceinline__ void load_lds16(const void* src, const void* lds_bloc
                :: "s"(base), "v"(src) : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_vmem_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+// vmcnt(N): at most N of this wave's vector-memory operations still in
+// flight (expcnt, lgkmcnt unchanged).  N above the counter's 63 waits for 63,
+// which is more than asked, never less.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// This wave's loads of a group have landed, given that `after` further
+// groups of P loads each were issued since (loads land in issue order).
+template <int P>
+__device__ __forceinline__ void wait_loads(int after) {
+  if (after >= 3) wait_vmcnt<3 * P>();
+  else if (after == 2) wait_vmcnt<2 * P>();
+  else if (after == 1) wait_vmcnt<P>();
+  else wait_vmcnt<0>();
+}
+
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave (the
+// lanes that hold one head), with gfx950's lane swaps: VALU operations, so
+// they do not queue behind the tile reads in the LDS pipeline as lane
+// shuffles would.  permlane32_swap pairs lane l with l ^ 32, permlane16_swap
+// row 0 with row 1 and row 2 with row 3 (16 lanes a row); every lane ends
+// with the same value.
+__device__ __forceinline__ float head_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float head_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Expand the raw entry in slots kRawSlot0.. of a tile row into the row's
@@ -157,14 +204,27 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
   constexpr int NT = 2 * WPS * 64;
+  constexpr int NW = 2 * WPS;
+  // Loads per loading wave and tile: every loading wave issues the same
+  // number (repeating the tile's last block), so its count of loads in
+  // flight says how many tiles are still in flight.
+  constexpr int kLoadsPerWave = (kTileLoads + WPS - 1) / WPS;
+  constexpr int kQRows = WPS * 16;                               // the workgroup's heads
+  constexpr int kQLoads = (kQRows * kRowSlots + 63) / 64;        // wave loads of the queries
+  constexpr int kQPerWave = (kQLoads + NW - 1) / NW;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  int* code = reinterpret_cast<int*>(smem + (size_t)2 * kStages * kTileSlots * 8);
-  int* wdst = code + kMaxChunkRows;
+  // Row i of the chunk: its source address (bit 0 set for a miss read from
+  // an fp8 entry, the address then 33 pieces before the entry), its writer
+  // slot, and one bit per row in its tile's writer and entry masks.
+  uint64_t* raddr = reinterpret_cast<uint64_t*>(smem + (size_t)kRing * kTileSlots * 8);
+  int* wdst = reinterpret_cast<int*>(raddr + kMaxChunkRows);
   unsigned* wmask = reinterpret_cast<unsigned*>(wdst + kMaxChunkRows);
+  unsigned* emask = wmask + kMaxChunkTiles;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sg = wave / WPS, wv = wave - sg * WPS;
+  const int ch = wave / WPS, hb = wave - ch * WPS;   // value-column half, head block
+  const bool loader = ch == 0;
   const int g = lane >> 4, c = lane & 15;
   // Workgroup -> (token, head group, row chunk).  Consecutive workgroup ids
   // go to the 8 XCDs in turn, each with its own L2; the m * head_groups
@@ -186,7 +246,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const int bj = b * m + sub / head_groups;
   const int r0 = chunk * rows_per_chunk;
   const int rend = min(k, r0 + rows_per_chunk);    // rows the table covers
-  const int h0 = hg * (WPS * 16) + wv * 16;
+  const int h0 = hg * kQRows + hb * 16;
 
   const int32_t* rpos = sel_pos + (size_t)bj * k;
   const int32_t* rsrc = sel_src + (size_t)bj * k;
@@ -200,194 +260,244 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   const uint16_t* tail_b = tail.rows ? tail.rows + (size_t)b * 2 * tail.block * kLat : nullptr;
   const int tail_start = tail.rows ? tail.start[b] : INT32_MAX;
 
-  // Q fragments first (they do not depend on the row table, so their
-  // latency overlaps the table's): lane holds Q[h0 + c][32 kk + 8 g .. + 8].
+  // The zero row's address, once (not reloaded before every use).
+  const uint16_t* zrow = g_zero_row;
+  asm volatile("" : "+s"(zrow));
+
+  // Row sources of the chunk, once: a hit reads its slot, a miss host
+  // memory (or its tail row), a row past n_sel or with an out-of-range
+  // value (caller error) the zero row.  Given writer slots, the first head
+  // group stores each designated-writer miss from the tile to its slot
+  // (wdst, and one bit per row in its tile's mask).  The row loads are
+  // issued for the whole chunk up to k, together with the n_sel load.
+  // Each wave fills 64 consecutive rows (two whole tiles, as r0 and the
+  // chunk length are multiples of 64).
+  const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
+  const int ntile = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
+  const bool writer_wg = rdst != nullptr && hg == 0;
+  for (int i0 = r0 + wave * 64; i0 < r0 + rows_per_chunk; i0 += NT) {
+    const int i = i0 + lane;
+    bool wr = false, ent = false;
+    uintptr_t addr = (uintptr_t)zrow;
+    if (i < rend) {
+      const int src = rsrc[i], pos = rpos[i];
+      const int dst = rdst ? rdst[i] : -1;
+      if (i < r1) {
+        if (src >= 0) {
+          if (src < C) addr = (uintptr_t)(pool_b + (size_t)src * kLat);
+        } else if (pos >= 0 && pos < L) {
+          if (pos >= tail_start) {
+            addr = (uintptr_t)(tail_b + ((size_t)((pos / tail.block) & 1) * tail.block +
+                                         pos % tail.block) * kLat);
+          } else if constexpr (kEnt) {
+            addr = ((uintptr_t)(ent_b + (size_t)pos * kEntryBytes) - kRawSlot0 * 16) | 1u;
+            ent = true;
+          } else {
+            addr = (uintptr_t)(host_b + (size_t)pos * kLat);
+          }
+          if (writer_wg && dst >= 0 && dst < C) {
+            wdst[i - r0] = dst;
+            wr = true;
+          }
+        }
+      }
+    }
+    raddr[i - r0] = addr;
+    const unsigned long long bw = __ballot(wr), be = __ballot(ent);
+    if (lane == 0) {
+      wmask[(i0 - r0) >> 5] = (unsigned)bw;
+      wmask[((i0 - r0) >> 5) + 1] = (unsigned)(bw >> 32);
+      emask[(i0 - r0) >> 5] = (unsigned)be;
+      emask[((i0 - r0) >> 5) + 1] = (unsigned)(be >> 32);
+    }
+  }
+  // (every plain global load is consumed here, before the first load into
+  // LDS, so the compiler's own waits never count those)
+  asm volatile("" ::"v"(r1));
+
+  // Each of a loading wave's loads covers the same tile slots in every
+  // tile: slot q = 64 j + lane holds row q / kRowSlots, piece
+  // q % kRowSlots.  Kept packed per load: the row (5 bits), the piece a
+  // bf16 row reads (the pad pieces and slots past the tile repeat piece 0)
+  // and the piece an fp8-entry row reads, counted from 33 pieces before
+  // the entry (slots before its raw pieces take its first piece; the
+  // expansion overwrites them).
+  unsigned lslot[kLoadsPerWave];
+#pragma unroll
+  for (int u = 0; u < kLoadsPerWave; ++u) {
+    const int q = min(hb + u * WPS, kTileLoads - 1) * 64 + lane;
+    const int row = q / kRowSlots, piece = q - row * kRowSlots;
+    const int pr = row < kTile && piece < kChunks16 ? piece : 0;
+    const int pe = row < kTile ? max(piece, kRawSlot0) : kRawSlot0;
+    lslot[u] = (unsigned)min(row, kTile - 1) | (unsigned)pr << 5 | (unsigned)pe << 12;
+  }
+
+  // Issue the loads of tile tt into ring buffer tt % kRing (loading waves):
+  // each load's row address from the table plus its piece.  The table reads
+  // of all of a wave's loads are in flight together, then the loads.
+  auto issue = [&](int tt) {
+    uint16_t* buf = smem + (size_t)(tt & (kRing - 1)) * kTileSlots * 8;
+    const uint64_t* ta = raddr + tt * kTile;
+    uint64_t ra[kLoadsPerWave];
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) ra[u] = ta[lslot[u] & 31u];
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      const int j = min(hb + u * WPS, kTileLoads - 1);
+      uint64_t src;
+      if constexpr (kEnt) {
+        const unsigned piece = (ra[u] & 1u) ? lslot[u] >> 12 : (lslot[u] >> 5) & 127u;
+        src = (ra[u] & ~(uint64_t)1) + piece * 16u;
+      } else {
+        src = ra[u] + ((lslot[u] >> 5) & 127u) * 16u;
+      }
+      load_lds16((const void*)(uintptr_t)src, buf + (size_t)j * 64 * 8);
+    }
+  };
+
+  __syncthreads();            // row table visible to every wave
+  // The workgroup's queries into ring buffers 2 and 3 (row h at slot
+  // 74 h, like a tile row), every wave a share; then tiles 0 and 1.
+  uint16_t* qbuf = smem + (size_t)2 * kTileSlots * 8;
+  {
+    const uint16_t* qwg = q_abs + ((size_t)bj * H + hg * kQRows) * kLat;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int u = 0; u < kQPerWave; ++u) {
+      const int j = min(wave + u * NW, kQLoads - 1);
+      const int q = j * 64 + ln;
+      const int row = q / kRowSlots, piece = q - row * kRowSlots;
+      const int off = (piece < kChunks16 ? piece : 0) * 8;
+      load_lds16(qwg + (size_t)min(row, kQRows - 1) * kLat + off, qbuf + (size_t)j * 64 * 8);
+    }
+  }
+  if (loader) {
+    if (ntile > 0) issue(0);
+    if (ntile > 1) issue(1);
+    wait_loads<kLoadsPerWave>(min(ntile, 2));   // the queries (tiles 0, 1 may fly)
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();            // every wave's query loads have landed
+  // Lane holds Q[h0 + c][32 kk + 8 g .. + 8].
   bf16x8 qf[kLat / 32];
   {
-    const uint16_t* qrow = q_abs + ((size_t)bj * H + h0 + c) * kLat + g * 8;
+    const uint16_t* qrow = qbuf + (size_t)(hb * 16 + c) * kKStride + g * 8;
 #pragma unroll
     for (int kk = 0; kk < kLat / 32; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32);
   }
-
-  // Row sources of the chunk, once: hits read their slot, misses host
-  // memory.  Given writer slots, the first head group stores each
-  // designated-writer miss from the tile to its slot (wdst, and one bit per
-  // row in its tile's mask).  Out-of-range values (caller error) give zero
-  // rows.  The table covers the chunk up to k, so its loads do not wait for
-  // n_sel; entries at or past n_sel are never used.  Each wave fills 64
-  // consecutive rows (two whole tiles, as r0 is a multiple of 64).
-  const bool writer_wg = rdst != nullptr && hg == 0;
-  for (int i0 = r0 + wave * 64; i0 < rend; i0 += NT) {
-    const int i = i0 + lane;
-    bool wr = false;
-    if (i < rend) {
-      const int src = rsrc[i], pos = rpos[i];
-      const int dst = rdst ? rdst[i] : -1;
-      int cd = kNoRow;
-      if (src >= 0) {
-        if (src < C) cd = src;
-      } else if (pos >= 0 && pos < L) {
-        cd = pos >= tail_start
-                 ? C + ((pos / tail.block) & 1) * tail.block + pos % tail.block
-                 : ~pos;
-        if (writer_wg && dst >= 0 && dst < C) {
-          wdst[i - r0] = dst;
-          wr = true;
-        }
-      }
-      code[i - r0] = cd;
-    }
-    if (rdst) {
-      const unsigned long long bal = __ballot(wr);
-      if (lane == 0) {
-        wmask[(i0 - r0) >> 5] = (unsigned)bal;
-        wmask[((i0 - r0) >> 5) + 1] = (unsigned)(bal >> 32);
-      }
-    }
+  __syncthreads();            // queries read: buffers 2 and 3 are free
+  if (loader) {
+    if (ntile > 2) issue(2);
+    if (ntile > 3) issue(3);
   }
-
-  const int r1 = min(min(n_sel[bj], k), r0 + rows_per_chunk);
+  int issued = min(ntile, kRing) - 1;   // last tile issued (loading waves)
 
   float m_run = -__builtin_inff(), l_run = 0.f;
-  v4f oacc[kVal / 16];
+  constexpr int kHalf = kVal / 32;      // 16-column blocks per half
+  v4f oacc[kHalf];
 #pragma unroll
-  for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Tiles of the chunk: sub-group s takes tiles s, s + 2, ...; both run the
-  // same number of iterations (the barriers are workgroup-wide).
-  const int ntile = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
-  const int iters = (ntile + 1) / 2;
-  uint16_t* ring = smem + (size_t)sg * kStages * kTileSlots * 8;
-
-  // Issue the loads of this sub-group's tile of iteration `it` into buffer
-  // it % kStages: LDS slot q of the buffer holds row q / kRowSlots, piece
-  // q % kRowSlots (the pad pieces and any slots past the tile repeat a valid
-  // 16 bytes of the zero row or of the row).  Unrolled and branch-free, so
-  // the row-table reads of all of a wave's loads are in flight together.
-  auto issue = [&](int it) {
-    const int tt = 2 * it + sg;
-    if (tt >= ntile) return;
-    const int t0 = r0 + tt * kTile;
-    uint16_t* buf = ring + (size_t)(it % kStages) * kTileSlots * 8;
-    constexpr int kPerWave = (kTileLoads + WPS - 1) / WPS;
-    // Recomputed per tile (a few ALU ops per load) rather than hoisted out
-    // of the tile loop, where the compiler would keep them all live.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int u = 0; u < kPerWave; ++u) {
-      const int j = wv + u * WPS;
-      if (j < kTileLoads) {
-        const int q = j * 64 + ln;
-        const int row = q / kRowSlots, piece = q - row * kRowSlots;
-        const int rr = min(row, kTile - 1);
-        const int cd = code[t0 - r0 + rr];
-        const bool use = row < kTile && t0 + row < r1 && cd != kNoRow;
-        const int off = (piece < kChunks16 ? piece : 0) * 8;
-        if constexpr (kEnt) {
-          // A miss: its entry's 41 pieces into slots kRawSlot0.. of the row
-          // (the slots before them are overwritten by the expansion).
-          const int pe = cd < 0 ? ~cd : 0;
-          const void* src =
-              !use ? (const void*)(g_zero_row + off)
-              : cd >= C ? (const void*)(tail_b + (size_t)(cd - C) * kLat + off)
-              : cd >= 0 ? (const void*)(pool_b + (size_t)cd * kLat + off)
-              : piece >= kRawSlot0
-                  ? (const void*)(ent_b + (size_t)pe * kEntryBytes + (piece - kRawSlot0) * 16)
-                  : (const void*)g_zero_row;
-          load_lds16(src, buf + (size_t)j * 64 * 8);
-        } else {
-          const uint16_t* rowp = cd >= C ? tail_b + (size_t)(cd - C) * kLat
-                                 : cd >= 0 ? pool_b + (size_t)cd * kLat
-                                           : host_b + (size_t)(~cd) * kLat;
-          load_lds16((use ? rowp : g_zero_row) + off, buf + (size_t)j * 64 * 8);
-        }
-      }
-    }
-  };
+  for (int nt = 0; nt < kHalf; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Transposed-read address of this lane within a tile half: token
-  // 4 g + (c / 4), columns 4 (c % 4) .. of each 16-column group.
-  const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4;
+  // 4 g + (c / 4), columns 4 (c % 4) .. of each 16-column group, in this
+  // wave's half of the value columns.
+  const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4 + ch * (kVal / 2);
 
-  __syncthreads();            // row table visible to every wave
-  issue(0);
-  for (int it = 0; it < iters; ++it) {
-    wait_vmem_all();          // this wave's loads of tile `it` have landed
-    __syncthreads();          // ... and every wave's; tile it-1 consumed
-    issue(it + 1);
-    const int tt = 2 * it + sg;
+  for (int t = 0; t < ntile; ++t) {
+    if (loader) wait_loads<kLoadsPerWave>(issued - t);   // this wave's loads of tile t
+    __syncthreads();          // ... and every wave's; tile t - 1 read by every wave
+    if (loader && t + kRing - 1 < ntile && t + kRing - 1 > issued) {
+      issue(t + kRing - 1);   // into the buffer tile t - 1 used
+      issued = t + kRing - 1;
+    }
+    const int t0 = r0 + t * kTile;
+    uint16_t* krow_w = smem + (size_t)(t & (kRing - 1)) * kTileSlots * 8;
     if constexpr (kEnt) {
-      // Expand this tile's miss rows (the waves of the sub-group take them
-      // in turn), then make them visible to every wave.
-      if (tt < ntile) {
-        const int te = r0 + tt * kTile;
-        const int cd = code[te - r0 + min(lane, kTile - 1)];
-        const bool miss = lane < kTile && te + lane < r1 && cd < 0 && cd != kNoRow;
-        unsigned msk = (unsigned)__ballot(miss);
-        uint16_t* ebuf = ring + (size_t)(it % kStages) * kTileSlots * 8;
-        int n = 0;
-        while (msk) {
-          const int r = __builtin_ctz(msk);
-          msk &= msk - 1u;
-          if (n++ % WPS == wv) expand_entry_row(ebuf + (size_t)r * kKStride, lane);
-        }
+      // Expand this tile's miss rows (the waves take them in turn), then
+      // make them visible to every wave.
+      unsigned msk = __builtin_amdgcn_readfirstlane(emask[t]);
+      int n = 0;
+      while (msk) {
+        const int r = __builtin_ctz(msk);
+        msk &= msk - 1u;
+        if (n++ % NW == wave) expand_entry_row(krow_w + (size_t)r * kKStride, lane);
       }
       __syncthreads();
     }
-    if (tt >= ntile) continue;
-    const int t0 = r0 + tt * kTile;
-    const uint16_t* krow = ring + (size_t)(it % kStages) * kTileSlots * 8;
+    const uint16_t* krow = krow_w;
 
     // S^T for the two 16-token halves of the tile: the two accumulator
-    // chains interleaved, and each step's operand reads issued before the
-    // previous step's MFMAs, so LDS latency overlaps the matrix work.
+    // chains interleaved, and each step's operand reads issued kAhead steps
+    // before its MFMAs, so LDS latency overlaps the matrix work.
+    constexpr int kAhead = 3;
     v4f s[2];
     {
       const uint16_t* arow0 = &krow[c * kKStride + g * 8];
       const uint16_t* arow1 = arow0 + 16 * kKStride;
       v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(arow0);
-      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(arow1);
+      bf16x8 ka[kAhead][2];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        ka[i][0] = *reinterpret_cast<const bf16x8*>(arow0 + i * 32);
+        ka[i][1] = *reinterpret_cast<const bf16x8*>(arow1 + i * 32);
+      }
 #pragma unroll
       for (int kk = 0; kk < kLat / 32; ++kk) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (kk + 1 < kLat / 32) {
-          n0 = *reinterpret_cast<const bf16x8*>(arow0 + (kk + 1) * 32);
-          n1 = *reinterpret_cast<const bf16x8*>(arow1 + (kk + 1) * 32);
+        const bf16x8 a0 = ka[kk % kAhead][0], a1 = ka[kk % kAhead][1];
+        if (kk + kAhead < kLat / 32) {
+          ka[kk % kAhead][0] = *reinterpret_cast<const bf16x8*>(arow0 + (kk + kAhead) * 32);
+          ka[kk % kAhead][1] = *reinterpret_cast<const bf16x8*>(arow1 + (kk + kAhead) * 32);
         }
+        // (keeps the scheduler from moving the reads back next to their use)
+        __builtin_amdgcn_sched_barrier(0);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], acc1, 0, 0, 0);
-        a0 = n0;
-        a1 = n1;
       }
       s[0] = acc0;
       s[1] = acc1;
     }
+    // The first V^T reads do not depend on P: issue them before the softmax.
+    const uint16_t* vbase = &krow[tr_off];
+    v2u vlo[kAhead], vhi[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      vlo[i] = tr_read(vbase + i * 16);
+      vhi[i] = tr_read(vbase + i * 16 + 16 * kKStride);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // Online softmax for head h0 + c over this tile's tokens
-    // t0 + 16 mt + 4 g + r.
+    // t0 + 16 mt + 4 g + r (the same in both column halves).
     float z[8];
-    float mx = -__builtin_inff();
+    if (t0 + kTile <= r1) {       // a whole tile (wave-uniform)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = t0 + (e >> 2) * 16 + g * 4 + (e & 3);
-      z[e] = tok < r1 ? s[e >> 2][e & 3] * scale_log2 : -__builtin_inff();
-      mx = fmaxf(mx, z[e]);
+      for (int e = 0; e < 8; ++e) z[e] = s[e >> 2][e & 3] * scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = t0 + (e >> 2) * 16 + g * 4 + (e & 3);
+        z[e] = tok < r1 ? s[e >> 2][e & 3] * scale_log2 : -__builtin_inff();
+      }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = z[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+    mx = head_max(mx);
     // The running maximum moves only when some head of the wave sees a tile
     // maximum more than 2^8 above it (log2 domain); otherwise every
     // p = 2^(z - m_run) stays at most 256 and the accumulators keep their
-    // reference, so the 128 rescale multiplies are skipped (the sum and the
+    // reference, so the rescale multiplies are skipped (the sum and the
     // accumulators always share one reference, so the result is the same).
+    // (2^x below by the hardware's exp2 directly: x <= 8 here, and results
+    // under 2^-126 flush to zero, far below what the sums can resolve)
     if (__ballot(mx > m_run + 8.f) != 0ull) {   // wave-uniform
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int nt = 0; nt < kVal / 16; ++nt) oacc[nt] *= alpha;
+      for (int nt = 0; nt < kHalf; ++nt) oacc[nt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
@@ -395,46 +505,40 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = exp2f(z[e] - m_run);
+      const float p = __builtin_amdgcn_exp2f(z[e] - m_run);
       psum += p;
       pb[e] = (__bf16)p;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
+    l_run += head_sum(psum);
 
-    // O^T += V^T P^T over the tile; V^T read transposed from the tile rows:
-    // tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, column nt*16 + c.
-    // The next column block's reads are issued before this block's MFMA.
-    {
-      const uint16_t* vbase = &krow[tr_off];
-      v2u lo = tr_read(vbase), hi = tr_read(vbase + 16 * kKStride);
+    // O^T += V^T P^T over the tile for this wave's 256 value columns; V^T
+    // read transposed from the tile rows: tokens 4 g .. 4 g + 3 and
+    // 16 + 4 g .. 16 + 4 g + 3, column 256 ch + nt*16 + c.  Each column
+    // block's reads are issued kAhead blocks before its MFMA.
 #pragma unroll
-      for (int nt = 0; nt < kVal / 16; ++nt) {
-        v2u nlo = lo, nhi = hi;
-        if (nt + 1 < kVal / 16) {
-          nlo = tr_read(vbase + (nt + 1) * 16);
-          nhi = tr_read(vbase + (nt + 1) * 16 + 16 * kKStride);
-        }
-        const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
-        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt], 0, 0, 0);
-        lo = nlo;
-        hi = nhi;
+    for (int nt = 0; nt < kHalf; ++nt) {
+      const v2u lo = vlo[nt % kAhead], hi = vhi[nt % kAhead];
+      if (nt + kAhead < kHalf) {
+        vlo[nt % kAhead] = tr_read(vbase + (nt + kAhead) * 16);
+        vhi[nt % kAhead] = tr_read(vbase + (nt + kAhead) * 16 + 16 * kKStride);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      const v4u vv = {lo[0], lo[1], hi[0], hi[1]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[nt], 0, 0, 0);
     }
 
-    // Writer rows: this tile's designated-writer misses (read from host) go from
-    // the tile to their pool slots, one row per wave in turn.  Only rows
-    // below n_sel were loaded.
-    if (writer_wg) {
-      unsigned msk = __builtin_amdgcn_readfirstlane(wmask[tt]);
+    // Writer rows: this tile's designated-writer misses (read from host) go
+    // from the tile to their pool slots, one row per storing wave in turn.
+    // Only rows below n_sel were loaded.
+    if (!loader && writer_wg) {
+      unsigned msk = __builtin_amdgcn_readfirstlane(wmask[t]);
       if (r1 - t0 < kTile) msk &= (1u << (r1 - t0)) - 1u;
       int n = 0;
       while (msk) {
         const int r = __builtin_ctz(msk);
         msk &= msk - 1u;
-        if (n++ % WPS == wv) {
+        if (n++ % WPS == hb) {
           const int dst = __builtin_amdgcn_readfirstlane(wdst[t0 - r0 + r]);
           const v4u* srow = reinterpret_cast<const v4u*>(krow + r * kKStride);
           v4u* drow = reinterpret_cast<v4u*>(pool_b + (size_t)dst * kLat);
@@ -445,71 +549,22 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     }
   }
 
-  // Merge the two sub-groups (same heads, same lane layout) through LDS, in
-  // fixed order: each hands the other the half of its accumulator in the
-  // other's value columns (sub-group s finishes columns [256 s, 256 s + 256))
-  // and both write their half of the partial.
-  __syncthreads();            // every tile consumed; the ring is free
-  constexpr int kHalf = kVal / 32;                   // 16-column groups per half
-  v4f* ostage = reinterpret_cast<v4f*>(smem);        // [sg][wv][nt][lane]
-  float2* mlstage = reinterpret_cast<float2*>(smem + (size_t)2 * WPS * kHalf * 64 * 8);
-  // Register indices stay compile-time constants (one branch per half).
-  v4f* mystage = ostage + (size_t)(sg * WPS + wv) * kHalf * 64 + lane;
-  if (sg == 0) {
-#pragma unroll
-    for (int u = 0; u < kHalf; ++u) mystage[u * 64] = oacc[kHalf + u];
-  } else {
-#pragma unroll
-    for (int u = 0; u < kHalf; ++u) mystage[u * 64] = oacc[u];
-  }
-  mlstage[(sg * WPS + wv) * 64 + lane] = make_float2(m_run, l_run);
-  __syncthreads();
-  const float2 mine = make_float2(m_run, l_run);
-  const float2 other = mlstage[((1 - sg) * WPS + wv) * 64 + lane];
-  // Sub-group 0's state first, then sub-group 1's, on both sides.
-  const float2 s0 = sg == 0 ? mine : other, s1 = sg == 0 ? other : mine;
-  float w0 = 1.f, w1 = 0.f, M = s0.x, l = s0.y;
-  if (s1.y > 0.f) {
-    if (s0.y > 0.f) {
-      M = fmaxf(s0.x, s1.x);
-      w0 = exp2f(s0.x - M);
-      w1 = exp2f(s1.x - M);
-    } else {
-      w0 = 0.f;
-      w1 = 1.f;
-      M = s1.x;
-    }
-    l = w0 * s0.y + w1 * s1.y;
-  }
-  const float wm = sg == 0 ? w0 : w1, wo = sg == 0 ? w1 : w0;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
   // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c, this
-  // sub-group's half of the columns.  The half's largest magnitude (over the
+  // wave's half of the columns.  The half's largest magnitude (over the
   // four lane groups that hold the head) sets a power-of-two scale 2^e with
   // amax * 2^-e in [0.5, 1); multiplying by 2^-e is exact.
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal +
-                 sg * (kVal / 2) + g * 4;
-  const v4f* theirs = ostage + (size_t)((1 - sg) * WPS + wv) * kHalf * 64 + lane;
+                 ch * (kVal / 2) + g * 4;
   v4f fin[kHalf];
-#define ESS_MLA_FINISH(BASE)                                                   \
-  _Pragma("unroll") for (int u = 0; u < kHalf; ++u) {                          \
-    v4f o = oacc[(BASE) + u] * wm;                                             \
-    if (wo != 0.f) o += theirs[u * 64] * wo;                                   \
-    fin[u] = o * inv;                                                          \
-  }
-  if (sg == 0) {
-    ESS_MLA_FINISH(0)
-  } else {
-    ESS_MLA_FINISH(kHalf)
-  }
-#undef ESS_MLA_FINISH
+#pragma unroll
+  for (int u = 0; u < kHalf; ++u) fin[u] = oacc[u] * inv;
   float amax = 0.f;
 #pragma unroll
   for (int u = 0; u < kHalf; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(fin[u][r]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax = head_max(amax);
   int ex = 0;
   if (amax > 0.f && amax <= 3.0e38f) (void)frexpf(amax, &ex);
   const float down = ldexpf(1.f, -ex);
@@ -518,11 +573,11 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     *reinterpret_cast<v4h*>(pa + u * 16) = __builtin_convertvector(fin[u] * down, v4h);
   float* ml = reinterpret_cast<float*>(part_ml + ((size_t)bj * nchunk + chunk) * H + h0 + c);
   if (g == 0) {
-    if (sg == 0) {
-      ml[0] = M;
-      ml[1] = l;
+    if (ch == 0) {
+      ml[0] = m_run;
+      ml[1] = l_run;
     }
-    ml[2 + sg] = ldexpf(1.f, ex);
+    ml[2 + ch] = ldexpf(1.f, ex);
   }
 }
 
