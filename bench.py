@@ -767,8 +767,8 @@ def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.
     of n_hist history rows + n_new new rows of 576 bf16: per layer, the
     history load (H2D) and the new rows' write-back (D2H) timed alone on
     their streams, the stand-in compute timed alone (layer 0 resident), and
-    whole pipelined runs with the compute window set to about ratio x the
-    load time.  Exposed time = pipelined - compute only, against the pages'
+    whole pipelined passes (median of five, one at a time) with the compute
+    window set to about ratio x the load time.  Exposed time = pipelined - compute only, against the pages'
     per-layer bound max(0, tau_H2D - d_on tau_compute) (d_on = 2 layers for
     the default prefetch) and the serial-link bound."""
     import numpy as np
@@ -825,24 +825,31 @@ def prefill_pipeline(args, NL=16, n_hist=32768, n_new=2048, ratios=(0.5, 1.0, 2.
     t_h2d = timed(sh, h2d)
     t_d2h = timed(sd, d2h)
     # One layer (layer 0, resident): compute + its write-back; two rep counts
-    # give the time per rep of the stand-in compute.
+    # give the time per on-chip repetition of the stand-in compute and its
+    # fixed part (one pass over the buffer, the launches, the write-back).
     call(NL, 1)                              # first use: events, kernels loaded
     torch.cuda.synchronize()
-    ta = timed(sc, lambda: call(1, 4), reps=5)
-    tb = timed(sc, lambda: call(1, 24), reps=5)
-    per_rep = max(1e-6, (tb - ta) / 20)
+    ta = timed(sc, lambda: call(1, 64), reps=5)
+    tb = timed(sc, lambda: call(1, 1064), reps=5)
+    per_rep = max(1e-9, (tb - ta) / 1000)
+    fixed = max(0.0, ta - 64 * per_rep)
     # A discarded pass at the shortest window first: the first pipelined
     # runs in a process were up to 25 % slower (12-13.7 ms against
     # 10.7-10.9 ms at compute/load 0.56, with or without write-backs), so
     # the link and clocks are brought out of idle before anything is timed.
-    reps0 = max(1, int(round(min(ratios) * t_h2d / per_rep)))
-    timed(sc, lambda: call(NL, reps0), reps=3)
+    def reps_for(ratio):
+        return max(1, int(round((ratio * t_h2d + t_d2h - fixed) / per_rep)))
+    timed(sc, lambda: call(NL, reps_for(min(ratios))), reps=3)
     runs = []
     for ratio in ratios:
-        reps = max(1, int(round(ratio * t_h2d / per_rep)))
+        reps = reps_for(ratio)
         t_layer = timed(sc, lambda: call(1, reps))           # compute + write-back
         t_c = max(1e-9, t_layer - t_d2h)
-        t_pipe = timed(sc, lambda: call(NL, reps), reps=4)
+        # One prefill pass per timing (each after the previous has finished;
+        # passes issued back to back measured 1-1.6 ms slower each, the next
+        # pass's first loads waiting on the previous pass's last layers);
+        # the median of five.
+        t_pipe = float(np.median([timed(sc, lambda: call(NL, reps), reps=1) for _ in range(5)]))
         t_only = NL * t_c + t_d2h
         exposed = max(0.0, t_pipe - t_only)
         loads = (NL - 1) * t_h2d

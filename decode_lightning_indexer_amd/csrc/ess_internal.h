@@ -190,8 +190,9 @@ hipError_t launch_append_tokens(const ess_dims& d, int block,
 // Per-block partial sums of the stand-in layer compute for `rows` rows.
 size_t prefill_ws_bytes(int rows);
 // Stand-in compute of one layer on stream s: append n_new rows from
-// new_rows (device) after the n_hist history rows of buf, then `reps` times
-// reduce the n_hist + n_new rows to per-column sums in out[576].
+// new_rows (device) after the n_hist history rows of buf, then read the
+// n_hist + n_new rows once and `reps` times reduce them on chip to
+// per-column sums in out[576].
 hipError_t launch_prefill_compute(const uint16_t* new_rows, int n_new,
                                   uint16_t* buf, int n_hist, int reps,
                                   float* part, float* out, hipStream_t s);

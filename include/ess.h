@@ -436,7 +436,8 @@ ess_status ess_host_alloc(size_t bytes, void** host_ptr, void** dev_view);
 ess_status ess_host_free(void* host_ptr);
 
 /* Bytes of device workspace ess_prefill_layers needs for buffers of `rows`
- * rows (per-block partial sums of the stand-in compute); 0 if rows < 1. */
+ * rows (partial sums of the stand-in compute per block of 128 rows); 0 if
+ * rows < 1. */
 size_t ess_prefill_ws_bytes(int32_t rows);
 
 /* Prefill over n_layers layers with four full-layer device buffers
@@ -452,9 +453,10 @@ size_t ess_prefill_ws_bytes(int32_t rows);
  *   load   (stream h2d): host_kv[l][0:n_hist] -> buffer (layers >= 1);
  *   compute (stream compute, after the load): new_kv[l] appended at rows
  *          [n_hist, n_hist + n_new) of the buffer, then the stand-in
- *          consumer - per-column sums of all n_hist + n_new rows into
- *          layer_out[l][576], repeated compute_reps times (a knob for the
- *          compute window; the result is the same);
+ *          consumer - all n_hist + n_new rows read from the buffer once and
+ *          their per-column sums taken compute_reps times on chip into
+ *          layer_out[l][576] (a knob for the compute window, like a layer
+ *          whose work reads its KV once; the result is the same);
  *   write-back (stream d2h, after the compute): buffer rows
  *          [n_hist, n_hist + n_new) -> host_kv[l][n_hist:].
  *   host_kv   [n_layers][rows][576] bf16 in pinned host memory (the host

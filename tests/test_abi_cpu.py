@@ -172,7 +172,7 @@ def test_prefill_argument_checks(L):
     assert call(m=[-1, -1, -1, -1, -1, -1]) == "invalid argument"  # 4, 5 never loaded
     assert "not loaded" in L.ess_last_error().decode()
     assert ess.ess_prefill_ws_bytes(0) == 0
-    assert ess.ess_prefill_ws_bytes(512) == 576 * 4 and ess.ess_prefill_ws_bytes(513) == 2 * 576 * 4
+    assert ess.ess_prefill_ws_bytes(128) == 576 * 4 and ess.ess_prefill_ws_bytes(129) == 2 * 576 * 4
 
 
 def test_entry_copy_argument_checks(L):
