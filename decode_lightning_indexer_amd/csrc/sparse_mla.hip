@@ -697,7 +697,8 @@ MlaPlan plan_sparse_mla(const ess_dims& d, int target_wgs) {
   // One workgroup per compute unit (each holds nearly all of a CU's LDS);
   // more chunks would also mean more partial traffic.
   const int target = target_wgs > 0 ? target_wgs : 256;
-  // A chunk is a whole number of tile pairs (one tile per sub-group).
+  // A chunk is a whole number of 64-row groups (the row table is filled 64
+  // rows a wave, two tiles' writer masks at a time).
   const int max_chunks = (d.topk + 2 * kTile - 1) / (2 * kTile);
   // The most heads per workgroup (each head group reads the chunk's rows
   // again) that still gives the target number of workgroups; with few
