@@ -27,11 +27,15 @@ FLAGS = [
 ]
 
 
-# Per-source additions.  The indexer reads every MFMA result in its
-# epilogue: with the results in VGPRs (not accumulation registers) no copy
-# precedes each read (measured 8-12 % faster at 32K and 128K).
+# Per-source additions: MFMA results in VGPRs (not accumulation registers).
+# The indexer reads every MFMA result in its epilogue, so no copy precedes
+# each read (measured 8-12 % faster at 32K and 128K).  The attention
+# rescales its output accumulators under a branch; with them in
+# accumulation registers the compiler moved all of them to VGPRs and back
+# on every tile.
 EXTRA = {
     "index_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -29,24 +29,32 @@
 // being written.
 //
 // Per workgroup: one (request, token), one group of heads, one chunk of rows.
-// Each wave takes 16 heads and one half of the 512 value columns; the two
-// waves of a head block compute the same scores (so no state is merged
-// between waves) and accumulate disjoint columns.  Tiles of 32 rows go from
-// memory straight into LDS (gfx950's 16-byte global-to-LDS load, one 1 KB
-// block per wave instruction), row-major with a 32-byte pad per row, into a
-// ring of four buffers: three tiles are in flight while every wave reads
-// the fourth, with one workgroup barrier per tile.  The waves of the first
-// column half issue every tile load and store nothing, so the count of
-// their loads in flight says which tiles have landed; the waves of the
-// second half store the miss rows to their pool slots.  The queries of the
-// workgroup's heads also come through LDS (two ring buffers, before the
+// Each wave takes 16 heads.  With three or four head blocks (48 or 64
+// heads) a wave owns all 512 value columns of its heads: one wave per SIMD,
+// each scoring its heads once.  With fewer head blocks a wave owns one half
+// of the value columns and the two waves of a head block compute the same
+// scores (so no state is merged between waves, and the compute unit still
+// runs at least four waves).  Tiles of 32 rows go from memory straight into
+// LDS (gfx950's 16-byte global-to-LDS load, one 1 KB block per wave
+// instruction), row-major with a 32-byte pad per row, into a ring of four
+// buffers: three tiles are in flight while every wave reads the fourth,
+// with one workgroup barrier per tile.  One wave per head block issues the
+// tile loads; a wave waits until no more of its loads are in flight than it
+// issued after the tile's (loads land in issue order, so a store issued
+// between them can only make that wait longer, never end it early).  The
+// miss rows are stored to their pool slots by the waves of the second
+// column half, or by every wave when each owns all columns.  The queries of
+// the workgroup's heads also come through LDS (two ring buffers, before the
 // third and fourth tiles are issued).  Padding and unusable rows load a zero
-// row.  At the end each wave writes its half of the chunk's partial
+// row.  At the end each wave writes its columns of the chunk's partial
 // normalised, in fp16 scaled by a power of two per (head, half of the value
 // columns) so that the half's largest magnitude lies in [0.5, 1): the stored
 // values keep fp16's 11 significant bits whatever the latents' range (no
 // overflow above 65504, no subnormals for small latents).  The running max
-// and sum and the two scales are fp32.
+// and sum and the two scales are fp32.  The output accumulators stay in
+// VGPRs (MFMA results in VGPR form, set for this file at build time): in
+// accumulation registers the compiler moved all of them to VGPRs and back
+// around the rescale branch on every tile (~25 % of a tile's cycles).
 //   S^T[tok][h] = sum_d K[tok][d] Q[h][d]   mfma 16x16x32 bf16, A = K tile
 //                                           rows from LDS, B = Q in registers
 //   O^T[c][h]  += sum_tok V^T[c][tok] P[h][tok]   A = V^T, B = P in registers
@@ -193,8 +201,10 @@ __device__ __forceinline__ void expand_entry_row(uint16_t* row, int lane) {
   if (lane < 8) *reinterpret_cast<entry_v4u*>(row + (kVal / 8 + lane) * 8) = kr;
 }
 
-template <int WPS, bool kEnt>
-__global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
+// WPS head blocks of 16 heads; CH waves per head block, each with 512 / CH
+// value columns (CH = 1 or 2).
+template <int WPS, int CH, bool kEnt>
+__global__ __launch_bounds__(CH * WPS * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_src, const int32_t* __restrict__ row_dst,
     const int32_t* __restrict__ n_sel, uint16_t* __restrict__ pool,
@@ -203,8 +213,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     float4* __restrict__ part_ml, int L, int C, int m, int H, int k,
     int rows_per_chunk, int nchunk, int head_groups, int n_bj,
     float scale_log2) {
-  constexpr int NT = 2 * WPS * 64;
-  constexpr int NW = 2 * WPS;
+  static_assert(CH == 1 || CH == 2, "one or two column parts per head block");
+  constexpr int NW = CH * WPS;
+  constexpr int NT = NW * 64;
   // Loads per loading wave and tile: every loading wave issues the same
   // number (repeating the tile's last block), so its count of loads in
   // flight says how many tiles are still in flight.
@@ -223,8 +234,9 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ch = wave / WPS, hb = wave - ch * WPS;   // value-column half, head block
-  const bool loader = ch == 0;
+  const int ch = wave / WPS, hb = wave - ch * WPS;   // value-column part, head block
+  const bool loader = ch == 0;                       // issues tile loads
+  const bool storer = CH == 1 || ch == 1;            // stores miss rows
   const int g = lane >> 4, c = lane & 15;
   // Workgroup -> (token, head group, row chunk).  Consecutive workgroup ids
   // go to the 8 XCDs in turn, each with its own L2; the m * head_groups
@@ -396,15 +408,16 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   int issued = min(ntile, kRing) - 1;   // last tile issued (loading waves)
 
   float m_run = -__builtin_inff(), l_run = 0.f;
-  constexpr int kHalf = kVal / 32;      // 16-column blocks per half
-  v4f oacc[kHalf];
+  constexpr int kCols = kVal / CH;      // value columns of this wave
+  constexpr int kBlk = kCols / 16;      // 16-column blocks of this wave
+  v4f oacc[kBlk];
 #pragma unroll
-  for (int nt = 0; nt < kHalf; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < kBlk; ++nt) oacc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Transposed-read address of this lane within a tile half: token
   // 4 g + (c / 4), columns 4 (c % 4) .. of each 16-column group, in this
-  // wave's half of the value columns.
-  const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4 + ch * (kVal / 2);
+  // wave's part of the value columns.
+  const int tr_off = (g * 4 + (c >> 2)) * kKStride + (c & 3) * 4 + ch * kCols;
 
   for (int t = 0; t < ntile; ++t) {
     if (loader) wait_loads<kLoadsPerWave>(issued - t);   // this wave's loads of tile t
@@ -497,7 +510,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int nt = 0; nt < kHalf; ++nt) oacc[nt] *= alpha;
+      for (int nt = 0; nt < kBlk; ++nt) oacc[nt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
@@ -511,14 +524,14 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     }
     l_run += head_sum(psum);
 
-    // O^T += V^T P^T over the tile for this wave's 256 value columns; V^T
+    // O^T += V^T P^T over the tile for this wave's value columns; V^T
     // read transposed from the tile rows: tokens 4 g .. 4 g + 3 and
-    // 16 + 4 g .. 16 + 4 g + 3, column 256 ch + nt*16 + c.  Each column
+    // 16 + 4 g .. 16 + 4 g + 3, column ch kCols + nt*16 + c.  Each column
     // block's reads are issued kAhead blocks before its MFMA.
 #pragma unroll
-    for (int nt = 0; nt < kHalf; ++nt) {
+    for (int nt = 0; nt < kBlk; ++nt) {
       const v2u lo = vlo[nt % kAhead], hi = vhi[nt % kAhead];
-      if (nt + kAhead < kHalf) {
+      if (nt + kAhead < kBlk) {
         vlo[nt % kAhead] = tr_read(vbase + (nt + kAhead) * 16);
         vhi[nt % kAhead] = tr_read(vbase + (nt + kAhead) * 16 + 16 * kKStride);
       }
@@ -531,7 +544,7 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
     // Writer rows: this tile's designated-writer misses (read from host) go
     // from the tile to their pool slots, one row per storing wave in turn.
     // Only rows below n_sel were loaded.
-    if (!loader && writer_wg) {
+    if (storer && writer_wg) {
       unsigned msk = __builtin_amdgcn_readfirstlane(wmask[t]);
       if (r1 - t0 < kTile) msk &= (1u << (r1 - t0)) - 1u;
       int n = 0;
@@ -550,34 +563,38 @@ __global__ __launch_bounds__(2 * WPS * 64) void sparse_mla_kernel(
   }
 
   // Normalised partial: O^T rows 16 nt + 4 g + r of head h0 + c, this
-  // wave's half of the columns.  The half's largest magnitude (over the
-  // four lane groups that hold the head) sets a power-of-two scale 2^e with
-  // amax * 2^-e in [0.5, 1); multiplying by 2^-e is exact.
+  // wave's columns, one half of the value columns at a time.  The half's
+  // largest magnitude (over the four lane groups that hold the head) sets a
+  // power-of-two scale 2^e with amax * 2^-e in [0.5, 1); multiplying by
+  // 2^-e is exact.
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   _Float16* pa = part_acc + (((size_t)bj * nchunk + chunk) * H + h0 + c) * kVal +
-                 ch * (kVal / 2) + g * 4;
-  v4f fin[kHalf];
-#pragma unroll
-  for (int u = 0; u < kHalf; ++u) fin[u] = oacc[u] * inv;
-  float amax = 0.f;
-#pragma unroll
-  for (int u = 0; u < kHalf; ++u)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(fin[u][r]));
-  amax = head_max(amax);
-  int ex = 0;
-  if (amax > 0.f && amax <= 3.0e38f) (void)frexpf(amax, &ex);
-  const float down = ldexpf(1.f, -ex);
-#pragma unroll
-  for (int u = 0; u < kHalf; ++u)
-    *reinterpret_cast<v4h*>(pa + u * 16) = __builtin_convertvector(fin[u] * down, v4h);
+                 ch * kCols + g * 4;
   float* ml = reinterpret_cast<float*>(part_ml + ((size_t)bj * nchunk + chunk) * H + h0 + c);
-  if (g == 0) {
-    if (ch == 0) {
-      ml[0] = m_run;
-      ml[1] = l_run;
-    }
-    ml[2 + ch] = ldexpf(1.f, ex);
+  constexpr int kHalfBlk = kVal / 32;   // 16-column blocks per half
+#pragma unroll
+  for (int hh = 0; hh < kBlk / kHalfBlk; ++hh) {
+    v4f fin[kHalfBlk];
+#pragma unroll
+    for (int u = 0; u < kHalfBlk; ++u) fin[u] = oacc[hh * kHalfBlk + u] * inv;
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < kHalfBlk; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(fin[u][r]));
+    amax = head_max(amax);
+    int ex = 0;
+    if (amax > 0.f && amax <= 3.0e38f) (void)frexpf(amax, &ex);
+    const float down = ldexpf(1.f, -ex);
+#pragma unroll
+    for (int u = 0; u < kHalfBlk; ++u)
+      *reinterpret_cast<v4h*>(pa + (hh * kHalfBlk + u) * 16) =
+          __builtin_convertvector(fin[u] * down, v4h);
+    if (g == 0) ml[2 + ch + hh] = ldexpf(1.f, ex);
+  }
+  if (g == 0 && ch == 0) {
+    ml[0] = m_run;
+    ml[1] = l_run;
   }
 }
 
@@ -667,7 +684,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
   if (lse && t == 0) lse[(size_t)bj * H + h] = (M + log2f(den)) * 0.69314718055994531f;
 }
 
-template <int WPS, bool kEnt>
+template <int WPS, int CH, bool kEnt>
 hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const int32_t* sel_pos, const int32_t* sel_src,
                     const int32_t* row_dst, const int32_t* n_sel,
@@ -675,13 +692,13 @@ hipError_t launch_t(const ess_dims& d, const MlaPlan& p, const uint16_t* q,
                     const unsigned char* entries, TailView tail,
                     _Float16* part_acc, float4* part_ml, hipStream_t s) {
   const float scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  hipError_t e = ensure_dyn_lds((const void*)sparse_mla_kernel<WPS, kEnt>, (int)kMlaLds);
+  hipError_t e = ensure_dyn_lds((const void*)sparse_mla_kernel<WPS, CH, kEnt>, (int)kMlaLds);
   if (e != hipSuccess) return e;
   // 1-D grid over (group, token, head group) in whole rounds of 8 XCDs.
   const int groups = d.batch * p.nchunk;
   const int rounds = ((groups + 7) / 8) * d.mtp * p.head_groups;
   dim3 grid(rounds * 8);
-  hipLaunchKernelGGL((sparse_mla_kernel<WPS, kEnt>), grid, dim3(2 * WPS * 64), kMlaLds, s, q,
+  hipLaunchKernelGGL((sparse_mla_kernel<WPS, CH, kEnt>), grid, dim3(CH * WPS * 64), kMlaLds, s, q,
                      sel_pos, sel_src, row_dst, n_sel, pool, host, entries, tail, part_acc,
                      part_ml, d.ctx_len, d.pool_slots, d.mtp, d.mla_heads,
                      d.topk, p.rows_per_chunk, p.nchunk, p.head_groups,
@@ -742,16 +759,18 @@ hipError_t launch_sparse_mla(const ess_dims& d, const uint16_t* q_abs,
   float4* part_ml = reinterpret_cast<float4*>(
       static_cast<char*>(ws) + align_up(parts * kVal * sizeof(_Float16), 256));
   hipError_t e;
-#define ESS_MLA_CASE(W)                                                        \
-  e = entries ? launch_t<W, true>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel,  \
-                                  pool, host, entries, tail, part_acc, part_ml, s) \
-              : launch_t<W, false>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, \
-                                   pool, host, nullptr, tail, part_acc, part_ml, s)
+#define ESS_MLA_CASE(W, CH)                                                    \
+  e = entries ? launch_t<W, CH, true>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, \
+                                      pool, host, entries, tail, part_acc, part_ml, s) \
+              : launch_t<W, CH, false>(d, p, q_abs, sel_pos, sel_src, row_dst, n_sel, \
+                                       pool, host, nullptr, tail, part_acc, part_ml, s)
+  // Three or four head blocks: one wave per block with all columns; fewer:
+  // two waves per block (column halves), so at least four waves run.
   switch (p.heads_per_wg / 16) {
-    case 1: ESS_MLA_CASE(1); break;
-    case 2: ESS_MLA_CASE(2); break;
-    case 3: ESS_MLA_CASE(3); break;
-    default: ESS_MLA_CASE(4); break;
+    case 1: ESS_MLA_CASE(1, 2); break;
+    case 2: ESS_MLA_CASE(2, 2); break;
+    case 3: ESS_MLA_CASE(3, 1); break;
+    default: ESS_MLA_CASE(4, 1); break;
   }
 #undef ESS_MLA_CASE
   if (e != hipSuccess) return e;
