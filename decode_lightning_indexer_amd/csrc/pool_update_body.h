@@ -129,9 +129,9 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   if constexpr (MERGE) {
     // Every entry's position, rank and slot are read first, all of a
     // thread's reads in flight together (the merge runs with two buffers,
-    // so n_e <= kTwoBufferMax = kU * NT); the positions go to the second
-    // buffer, then each entry finds its merged place by binary searches in
-    // the other tokens' lists.
+    // so n_e <= kTwoBufferMax = kU * NT).  Two tokens: a merge path.  More:
+    // the positions go to the second buffer, then each entry finds its
+    // merged place by binary searches in the other tokens' lists.
     static_assert(kTwoBufferMax <= kU * NT, "one read per entry slot below");
     int32_t* lp = reinterpret_cast<int32_t*>(smem_ent + epow2);
     int pos[kU], rk[kU], sl[kU], tok[kU];
@@ -152,71 +152,117 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
         sl[u] = a.lists.slot[li];
       }
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int e = tid + u * NT;
-      if (e < n_e) lp[e] = pos[u];
-    }
-    // (every place starts empty: an entry that could not be placed leaves
-    // a kNoEntry, which ends the scans below, never a stale entry)
-    for (int e = tid; e < epow2; e += NT) ent[e] = kNoEntry;
-    __syncthreads();
-    // Place = index in its own list + the entries before it in every other
-    // list (positions below it, and its own position when that list's token
-    // is smaller).  Round d searches list (token + d) mod n_tok for each of
-    // a thread's entries, in lockstep with the same power-of-two steps
-    // (uniform over the workgroup, sized for the longest list), so their
-    // LDS reads are in flight together.
-    int at[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) at[u] = tid + u * NT - off[tok[u]];
-    int len_max = 0;
-    for (int j = 0; j < n_tok; ++j) len_max = max(len_max, off[j + 1] - off[j]);
-    // steps S, S/2, ..., 1 reach up to index 2S - 2 >= len_max - 1
-    const int s0 = pow2_at_least_dev((uint32_t)len_max + 1u) >> 1;
-    for (int d = 1; d < n_tok; ++d) {
-      const int32_t* l2[kU];
-      int len[kU], last[kU];
-      bool before[kU];                      // equal positions of list j2 come first
+    if (n_tok == 2) {
+      // Two lists: a merge path.  Every entry's whole key goes to the second
+      // buffer at its list index (list 0 then list 1, each ascending; a
+      // position both tokens selected orders token 0 first, as the keys
+      // do, and keys are unique).  Thread t then finds, by one binary
+      // search along the diagonal d = 4 t, how many of the first d merged
+      // entries come from list 0, and writes merged entries d .. d + 3.
+      // An out-of-range position (never from the top-k) is flagged and
+      // its key sorts last.
+      uint64_t* lk = smem_ent + epow2;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        int j2 = tok[u] + d;
-        if (j2 >= n_tok) j2 -= n_tok;
-        l2[u] = lp + off[j2];
-        len[u] = off[j2 + 1] - off[j2];
-        before[u] = j2 < tok[u];
-        last[u] = -1;
+        const int e = tid + u * NT;
+        if (e >= n_e) continue;
+        uint64_t key = kNoEntry;
+        if (pos[u] >= 0 && pos[u] < L) {
+          key = make_entry(pos[u], tok[u], rk[u]);
+          if (sl[u] >= 0 && sl[u] < C) key = with_slot(key, sl[u]);
+        } else {
+          bad = true;
+        }
+        lk[e] = key;
       }
-      for (int step = s0; step >= 1; step >>= 1) {
-        // Every load is made (at a clamped index inside the list region),
-        // so none waits behind a branch; a probe past the list's end
-        // compares as above every position.
-        int32_t v[kU];
+      for (int e = tid; e < epow2; e += NT) ent[e] = kNoEntry;   // places past n_e
+      __syncthreads();
+      const int nA = off[1], nB = off[2] - off[1];
+      const uint64_t* A = lk;
+      const uint64_t* B = lk + nA;
+      const int d0 = tid * kU;
+      if (d0 < n_e) {
+        int lo = max(0, d0 - nB), hi = min(d0, nA);
+        while (lo < hi) {   // A[mid] among the first d0 <=> it precedes B[d0 - mid - 1]
+          const int mid = (lo + hi) >> 1;
+          if (A[mid] < B[d0 - mid - 1]) lo = mid + 1;
+          else hi = mid;
+        }
+        int i = lo, j = d0 - lo;
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-          v[u] = l2[u][min(last[u] + step, max(len[u] - 1, 0))];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int cand = last[u] + step;
-          const bool take = (cand < len[u]) & ((v[u] < pos[u]) | (before[u] & (v[u] == pos[u])));
-          last[u] = take ? cand : last[u];
+        for (int q = 0; q < kU; ++q) {
+          if (d0 + q >= n_e) break;
+          const bool from_a = i < nA && (j >= nB || A[i] < B[j]);
+          ent[d0 + q] = from_a ? A[i++] : B[j++];
         }
       }
+    } else {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) at[u] += last[u] + 1;
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int e = tid + u * NT;
-      if (e >= n_e) break;
-      const int p = pos[u];
-      if (p < 0 || p >= L) {                // cannot come from the top-k
-        bad = true;
-        continue;
+      for (int u = 0; u < kU; ++u) {
+        const int e = tid + u * NT;
+        if (e < n_e) lp[e] = pos[u];
       }
-      uint64_t key = make_entry(p, tok[u], rk[u]);
-      if (sl[u] >= 0 && sl[u] < C) key = with_slot(key, sl[u]);
-      ent[min(at[u], n_e - 1)] = key;
+      // (every place starts empty: an entry that could not be placed leaves
+      // a kNoEntry, which ends the scans below, never a stale entry)
+      for (int e = tid; e < epow2; e += NT) ent[e] = kNoEntry;
+      __syncthreads();
+      // Place = index in its own list + the entries before it in every other
+      // list (positions below it, and its own position when that list's token
+      // is smaller).  Round d searches list (token + d) mod n_tok for each of
+      // a thread's entries, in lockstep with the same power-of-two steps
+      // (uniform over the workgroup, sized for the longest list), so their
+      // LDS reads are in flight together.
+      int at[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) at[u] = tid + u * NT - off[tok[u]];
+      int len_max = 0;
+      for (int j = 0; j < n_tok; ++j) len_max = max(len_max, off[j + 1] - off[j]);
+      // steps S, S/2, ..., 1 reach up to index 2S - 2 >= len_max - 1
+      const int s0 = pow2_at_least_dev((uint32_t)len_max + 1u) >> 1;
+      for (int d = 1; d < n_tok; ++d) {
+        const int32_t* l2[kU];
+        int len[kU], last[kU];
+        bool before[kU];                      // equal positions of list j2 come first
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          int j2 = tok[u] + d;
+          if (j2 >= n_tok) j2 -= n_tok;
+          l2[u] = lp + off[j2];
+          len[u] = off[j2 + 1] - off[j2];
+          before[u] = j2 < tok[u];
+          last[u] = -1;
+        }
+        for (int step = s0; step >= 1; step >>= 1) {
+          // Every load is made (at a clamped index inside the list region),
+          // so none waits behind a branch; a probe past the list's end
+          // compares as above every position.
+          int32_t v[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            v[u] = l2[u][min(last[u] + step, max(len[u] - 1, 0))];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int cand = last[u] + step;
+            const bool take = (cand < len[u]) & ((v[u] < pos[u]) | (before[u] & (v[u] == pos[u])));
+            last[u] = take ? cand : last[u];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) at[u] += last[u] + 1;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e = tid + u * NT;
+        if (e >= n_e) break;
+        const int p = pos[u];
+        if (p < 0 || p >= L) {                // cannot come from the top-k
+          bad = true;
+          continue;
+        }
+        uint64_t key = make_entry(p, tok[u], rk[u]);
+        if (sl[u] >= 0 && sl[u] < C) key = with_slot(key, sl[u]);
+        ent[min(at[u], n_e - 1)] = key;
+      }
     }
   } else if constexpr (SORTED) {
     // Positions come from the selection over [0, n_vis), so all are valid

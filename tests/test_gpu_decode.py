@@ -28,6 +28,18 @@ def test_mtp2_sequence_matches_oracle():
     compare_with_oracle(wl, recs)
 
 
+@pytest.mark.parametrize("m,k", [(3, 512), (4, 256)])
+def test_three_and_four_tokens_match_oracle(m, k):
+    # More than two query tokens per request: the residency update merges
+    # the tokens' position lists by searches in the other lists (two tokens
+    # take a merge path).
+    wl = get_workload("tiny-4k").with_(
+        name=f"mtp{m}-small", batch=2, mtp=m, ctx_len=8192, idx_heads=32,
+        idx_dim=128, mla_heads=32, topk=k, pool_slots=2048, steps=5, rho=0.9)
+    recs = gpu_sequence(wl)
+    compare_with_oracle(wl, recs)
+
+
 def test_placement_invariance_all_resident():
     wl = get_workload("tiny-4k").with_(steps=4)
     a = gpu_sequence(wl)
