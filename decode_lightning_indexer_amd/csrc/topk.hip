@@ -111,6 +111,9 @@ constexpr int CHUNK_E = NT * VPT_E * 4;   // 16384 candidates
 // One selection input: a run of a scores row (entry i is position pos0 + i)
 // or, with EXPL, a candidate list of order-preserving keys with explicit
 // positions in ascending order.  n entries; vec: 16-byte aligned start.
+// Optionally (a scores row held in registers) the entry count is read from
+// n_src instead, clamped to [0, cap], where cap entries of the row are
+// allocated: the row is then loaded before its count arrives.
 struct RowIn {
   const float* score;
   const uint32_t* key;
@@ -118,6 +121,8 @@ struct RowIn {
   int n;
   bool vec;
   int pos0;
+  int cap = 0;
+  const int32_t* n_src = nullptr;
 };
 
 // Rank-order outputs (with the slot of each winner) or, with POSORD, the
@@ -274,40 +279,17 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
   const uint32_t* krow = in.key;
   const int32_t* prow = in.pos;
   const int pos0 = in.pos0;
-  const int n = in.n;
-  const int keff = min(k, n);
   const bool vec = in.vec;
-  int32_t* op = out.op;
-  int32_t* os = out.os;
-  const int32_t* cs = out.cs;
-  if (!POSORD) {
-    for (int i = keff + tid; i < k; i += NT) {
-      op[i] = -1;
-      os[i] = -1;
-    }
-    if (tid == 0 && out.n_sel) *out.n_sel = keff;
-  }
-  if (keff == 0) return 0;
-  // Output row r: the selection and its slot.
-#define EMIT(R, POS, SLOT)                                                    \
-  do {                                                                        \
-    op[R] = (POS);                                                            \
-    os[R] = (SLOT);                                                           \
-    if (FUSE) {                                                               \
-      out.rpos[R] = (POS);                                                    \
-      out.rslot[R] = (SLOT);                                                  \
-    }                                                                         \
-  } while (0)
-
-  // Keys of one chunk for this thread.  A chunk wholly inside the visible
-  // row (the common case) takes eight unconditional 16-byte loads, all in
-  // flight together; a partial chunk takes bounds-checked scalar loads.
+  // Keys of one chunk for this thread, of the first LIM entries.  A chunk
+  // wholly inside them (the common case) takes eight unconditional 16-byte
+  // loads, all in flight together; a partial chunk takes bounds-checked
+  // scalar loads (zero past LIM).
   uint32_t kr[TK];
   int32_t pr[TK];   // positions of a candidate list's keys (EXPL only)
-#define ESS_TOPK_LOAD(BASE)                                                   \
+#define ESS_TOPK_LOAD(BASE, LIM)                                                   \
   do {                                                                        \
     const int base_ = (BASE);                                                 \
-    if (vec && base_ + TC <= n) {                                          \
+    if (vec && base_ + TC <= (LIM)) {                                          \
       if constexpr (EXPL) {                                                   \
         uint4 a_[TV];                                                         \
         int4 q_[TV];                                                          \
@@ -341,25 +323,66 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                       \
           const int p_ = base_ + (v * NT + tid) * 4 + e;                      \
           if constexpr (EXPL) {                                               \
-            kr[4 * v + e] = p_ < n ? krow[p_] : 0u;                           \
-            pr[4 * v + e] = p_ < n ? prow[p_] : 0;                            \
+            kr[4 * v + e] = p_ < (LIM) ? krow[p_] : 0u;                       \
+            pr[4 * v + e] = p_ < (LIM) ? prow[p_] : 0;                        \
           } else {                                                            \
-            kr[4 * v + e] = p_ < n ? ord_key(srow[p_]) : 0u;                  \
+            kr[4 * v + e] = p_ < (LIM) ? ord_key(srow[p_]) : 0u;              \
           }                                                                   \
         }                                                                     \
     }                                                                         \
   } while (0)
+  // A scores row held in registers whose entry count comes from memory:
+  // the count's load goes first, then the row's (bounded by the allocated
+  // cap), and only then is the count waited for, so the two round trips
+  // overlap; keys past the count are zeroed as the bounded loads leave them.
+  const bool early = RES && !EXPL && in.n_src != nullptr;
+  int n_in = in.n;
+  if (early) {
+    n_in = *in.n_src;
+    ESS_TOPK_LOAD(0, in.cap);
+  }
+  const int n = early ? min(max(n_in, 0), in.cap) : n_in;
+  if (early) {
+#pragma unroll
+    for (int v = 0; v < TV; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((v * NT + tid) * 4 + e >= n) kr[4 * v + e] = 0u;
+  }
+  const int keff = min(k, n);
+  int32_t* op = out.op;
+  int32_t* os = out.os;
+  const int32_t* cs = out.cs;
+  if (!POSORD) {
+    for (int i = keff + tid; i < k; i += NT) {
+      op[i] = -1;
+      os[i] = -1;
+    }
+    if (tid == 0 && out.n_sel) *out.n_sel = keff;
+  }
+  if (keff == 0) return 0;
+  // Output row r: the selection and its slot.
+#define EMIT(R, POS, SLOT)                                                    \
+  do {                                                                        \
+    op[R] = (POS);                                                            \
+    os[R] = (SLOT);                                                           \
+    if (FUSE) {                                                               \
+      out.rpos[R] = (POS);                                                    \
+      out.rslot[R] = (SLOT);                                                  \
+    }                                                                         \
+  } while (0)
+
   // Index of a held key in the input, and its position.
 #define pos_of(BASE, V, E) ((BASE) + ((V) * NT + tid) * 4 + (E))
 #define real_pos(BASE, V, E) (EXPL ? pr[4 * (V) + (E)] : pos0 + pos_of(BASE, V, E))
   const int nchunks = (n + TC - 1) / TC;
 
-  if (RES) ESS_TOPK_LOAD(0);
+  if (RES && !early) ESS_TOPK_LOAD(0, n);
   // 1. Range of the keys.
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int c = 0; c < nchunks; ++c) {
     const int base = c * TC;
-    if (!RES) ESS_TOPK_LOAD(base);
+    if (!RES) ESS_TOPK_LOAD(base, n);
 #pragma unroll
     for (int v = 0; v < TV; ++v)
 #pragma unroll
@@ -394,7 +417,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
       const uint32_t fixed_mask = lo_fixed >= 32 ? 0u : (~0u << lo_fixed);
       for (int c = 0; c < nchunks; ++c) {
         const int base = c * TC;
-        if (!RES) ESS_TOPK_LOAD(base);
+        if (!RES) ESS_TOPK_LOAD(base, n);
 #pragma unroll
         for (int v = 0; v < TV; ++v)
 #pragma unroll
@@ -456,7 +479,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
       __syncthreads();
       for (int c = 0; c < nchunks; ++c) {
         const int base = c * TC;
-        if (!RES) ESS_TOPK_LOAD(base);
+        if (!RES) ESS_TOPK_LOAD(base, n);
 #pragma unroll
         for (int v = 0; v < TV; ++v)
 #pragma unroll
@@ -487,7 +510,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
     uint32_t at = 0;   // uniform
     for (int c = 0; c < nchunks; ++c) {
       const int base = c * TC;
-      if (!RES) ESS_TOPK_LOAD(base);
+      if (!RES) ESS_TOPK_LOAD(base, n);
       // Ranks of equal keys in a run (first `need` in index order win).
       uint32_t eqr[TV];
 #pragma unroll
@@ -615,7 +638,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int base = c * TC;
-    if (!RES) ESS_TOPK_LOAD(base);
+    if (!RES) ESS_TOPK_LOAD(base, n);
 #pragma unroll
     for (int v = 0; v < TV; ++v)
 #pragma unroll
@@ -650,7 +673,7 @@ __device__ __forceinline__ int topk_row(const RowIn& in, int k, int kpow2, const
   uint32_t eq_taken = 0;
   for (int c = 0; c < nchunks; ++c) {
     const int base = c * TC;
-    if (!RES) ESS_TOPK_LOAD(base);
+    if (!RES) ESS_TOPK_LOAD(base, n);
 #pragma unroll
     for (int v = 0; v < TV; ++v)
 #pragma unroll
@@ -764,8 +787,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(
   extern __shared__ uint64_t grp[];
   const int row = blockIdx.x, b = row / n_tok, j = row % n_tok;
   const size_t o = ((size_t)b * n_tok + j) * k;
+  // (a row held in registers reads its visible count inside, with its loads
+  // already issued)
   const RowIn in{scores + ((size_t)b * m + j) * L, nullptr, nullptr,
-                 visible(n_vis, b, m, j, L), (L & 3) == 0, 0};
+                 RES ? 0 : visible(n_vis, b, m, j, L), (L & 3) == 0, 0,
+                 L, RES ? n_vis + b * m + j : nullptr};
   const RowOut out{sel_pos + o, sel_slot + o, cache_slots + (size_t)b * L,
                    n_sel + b * n_tok + j, nullptr, nullptr, nullptr, nullptr,
                    BYSORT ? grp + kpow2 : nullptr,
@@ -850,7 +876,6 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
   int32_t* rpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dyn) + rank_off);
   int32_t* rslot = rpos + k;
   const int b = blockIdx.x;
-  int n = visible(n_vis, b, m, 0, L);
   const size_t o = (size_t)b * k;
   // Rows held in registers rank their winners by a sort and hand the update
   // a position-ordered selection (it then sorts nothing).
@@ -860,12 +885,17 @@ __global__ __launch_bounds__(NT) void select_update_kernel(
                    nullptr, nullptr, rpos, rslot, pw, nullptr, nullptr, nullptr};
   int keff;
   if constexpr (EXPL) {
+    int n = visible(n_vis, b, m, 0, L);
     for (int l = 1; l <= levels; ++l) n = level_count(n, k, l);
     const size_t rb = (size_t)b * cap;
     const RowIn in{nullptr, ckey + rb, cpos + rb, n, (rb & 3) == 0, 0};
     keff = topk_row<true, true, true, false, 0, kSorted>(in, k, kpow2, out, dyn);
   } else {
-    const RowIn in{scores + (size_t)b * m * L, nullptr, nullptr, n, (L & 3) == 0, 0};
+    // (a row held in registers reads its visible count inside, with its
+    // loads already issued)
+    const RowIn in{scores + (size_t)b * m * L, nullptr, nullptr,
+                   RES ? 0 : visible(n_vis, b, m, 0, L), (L & 3) == 0, 0,
+                   L, RES ? n_vis + b * m : nullptr};
     keff = topk_row<RES, true, false, false, 0, kSorted>(in, k, kpow2, out, dyn);
   }
   __syncthreads();   // selections complete; the sort buffer is free
