@@ -290,6 +290,10 @@ def _bf16(rng, shape, std):
     # 1M workload's plan), and 16 chunks by 2 waves per head.
     (1, 1, 64, 20000, 2048, 4096, False, 0.6),
     (1, 2, 128, 9000, 1024, 2500, True, 0.5),
+    # Workgroups of 32 heads (two waves per head block, column halves) and
+    # of 48 heads (one wave per head block, all value columns).
+    (8, 1, 32, 2500, 2048, 2100, True, 0.6),
+    (4, 1, 96, 3000, 2048, 2100, True, 0.6),
 ])
 def test_sparse_mla_parity_and_writeback(B, m, H, L, k, C, ragged, p_hit):
     _mla_case(B, m, H, L, k, C, ragged, p_hit)
