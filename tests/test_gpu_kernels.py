@@ -98,6 +98,7 @@ def _scores(kind, rng, shape):
 @pytest.mark.parametrize("kind,B,m,n_tok,L,k,ragged", [
     ("int_ties", 2, 1, 1, 5000, 256, False),
     ("indexer_like", 4, 1, 1, 32768, 2048, False),
+    ("indexer_like", 4, 1, 1, 32768, 2048, True),   # row in registers, ragged counts
     ("indexer_like", 2, 2, 2, 40000, 2048, True),
     ("float", 2, 1, 1, 3000, 100, True),
     ("wide", 2, 1, 1, 20000, 1000, False),
