@@ -85,6 +85,7 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   static_assert(!MERGE || !PRESEL, "merged lists come from the top-k's outputs");
   __shared__ uint32_t tmp[NT / 64 + 1];
   __shared__ uint32_t bcnt[kSortBuckets];
+  __shared__ uint32_t rc[4 * 64 + 1];   // ring compaction: (row, wave) counts, then places
   __shared__ int s_head_new;
   uint64_t* ent = smem_ent;
   const int L = a.L, C = a.C, k = a.k, n_tok = a.n_tok, epow2 = a.epow2;
@@ -434,21 +435,65 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   __syncthreads();
 
   // 5. Make room on the ring: compact live entries to the front in order.
+  // A round takes kC rows of NT consecutive entries (entry src + q NT + t
+  // to thread t, so every read is coalesced), with all of a thread's ring
+  // reads and then its stamp reads in flight together: a 4C ring is a few
+  // rounds, not 4C / NT rounds of two memory round trips each.  An entry's
+  // place: the live entries of the round's earlier rows, of the earlier
+  // waves in its row (per-wave counts from ballots, scanned in (row, wave)
+  // order by one wave) and of the earlier lanes of its wave.  Every entry a
+  // round writes lies below the round's start (dst <= src), so none is
+  // overwritten before it is read.
   int tail = tail0;
   if (tail + (int)n_u > cap) {
+    constexpr int kC = 16;
+    constexpr int kWaves = NT / 64;
+    static_assert(kC * kWaves == 4 * 64, "one wave scans the (row, wave) counts, four each");
+    const int lane = tid & 63, wv = tid >> 6;
     int dst = 0;
-    for (int src = head; src < tail; src += NT) {
-      const int idx = src + tid;
-      Ring r = {0, 0};
-      bool live = false;
-      if (idx < tail) {
-        r = ring[idx];
-        live = r.slot >= 0 && r.slot < C && stamp[r.slot] == r.stamp;
+    for (int src = head; src < tail; src += NT * kC) {
+      Ring r[kC];
+#pragma unroll
+      for (int q = 0; q < kC; ++q) {
+        const int idx = src + q * NT + tid;
+        r[q] = idx < tail ? ring[idx] : Ring{-1, 0};
       }
-      uint32_t tot;
-      const uint32_t rank = block_exscan<NT>(live ? 1u : 0u, tmp, &tot);
-      if (live) ring[dst + rank] = r;
-      dst += (int)tot;
+      int32_t st[kC];
+#pragma unroll
+      for (int q = 0; q < kC; ++q)
+        st[q] = r[q].slot >= 0 && r[q].slot < C ? stamp[r[q].slot] : 0;
+      uint32_t live = 0, below[kC];
+#pragma unroll
+      for (int q = 0; q < kC; ++q) {
+        const bool l = r[q].slot >= 0 && r[q].slot < C && st[q] == r[q].stamp;
+        const uint64_t bq = __ballot(l);
+        below[q] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bq >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bq, 0u));
+        if (lane == 0) rc[q * kWaves + wv] = (uint32_t)__popcll(bq);
+        live |= (l ? 1u : 0u) << q;
+      }
+      __syncthreads();
+      if (wv == 0) {
+        uint32_t c4[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c4[j] = rc[lane * 4 + j];
+          sum += c4[j];
+        }
+        const uint32_t incl = wave_incl_sum(sum);
+        uint32_t run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rc[lane * 4 + j] = run;
+          run += c4[j];
+        }
+        if (lane == 63) rc[kC * kWaves] = incl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kC; ++q)
+        if ((live >> q) & 1u) ring[dst + (int)rc[q * kWaves + wv] + (int)below[q]] = r[q];
+      dst += (int)rc[kC * kWaves];
       __syncthreads();
     }
     head = 0;
