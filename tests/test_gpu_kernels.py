@@ -147,6 +147,34 @@ def test_topk_bit_exact(kind, B, m, n_tok, L, k, ragged):
         assert np.array_equal(h(ss)[b], rs), b
 
 
+@pytest.mark.parametrize("L", [3000, 32768, 40000])
+def test_topk_visible_counts_at_the_edges(L):
+    # Rows whose visible count is 0, 1, just below, at and just above k, and
+    # the whole row: a row of 32768 keys is held in registers and loaded
+    # before its count arrives, 3000 keys take the bounded scalar loads, and
+    # 40000 keys split over workgroups.
+    k = 2048
+    counts = [0, 1, k - 1, k, k + 1, L]
+    B = len(counts)
+    rng = np.random.default_rng(zlib.crc32(f"edges-{L}".encode()))
+    s = _scores("indexer_like", rng, (B, 1, L))
+    n_vis = np.array([[min(c, L)] for c in counts], np.int32)
+    cs = np.where(rng.random((B, L)) < 0.5, rng.integers(0, 1 << 20, (B, L)), -1).astype(np.int32)
+    d = dims(batch=B, mtp=1, ctx_len=L, topk=k, pool_slots=16384)
+    sp = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    ss = torch.empty_like(sp)
+    ns = torch.empty((B, 1), dtype=torch.int32, device="cuda")
+    wsb = ess.ess_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ess.ess_topk_lookup(d, k, 1, t(s), t(n_vis), t(cs), sp, ss, ns, ws, wsb)
+    sync()
+    for b in range(B):
+        rp, rs, rn = topk_lookup(s[b, :1].astype(np.float64), n_vis[b, :1], k, cs[b])
+        assert np.array_equal(h(ns)[b], rn), b
+        assert np.array_equal(h(sp)[b], rp), b
+        assert np.array_equal(h(ss)[b], rs), b
+
+
 # ---------------------------------------------------------------- pool --
 
 def _ways(rng, L, m, k, prev, keep=0.85):
