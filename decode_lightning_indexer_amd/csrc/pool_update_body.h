@@ -84,6 +84,7 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   static_assert(!SORTED || PRESEL, "a sorted selection comes from the fused top-k");
   static_assert(!MERGE || !PRESEL, "merged lists come from the top-k's outputs");
   __shared__ uint32_t tmp[NT / 64 + 1];
+  __shared__ uint64_t tmp64[NT / 64 + 1];
   __shared__ uint32_t bcnt[kSortBuckets];
   __shared__ uint32_t rc[4 * 64 + 1];   // ring compaction: (row, wave) counts, then places
   __shared__ int s_head_new;
@@ -361,9 +362,13 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
       else ++n_m_mine;
     }
   }
-  uint32_t n_u, n_miss;
-  const uint32_t u_base = block_exscan<NT>(n_u_mine, tmp, &n_u);
-  const uint32_t m_base = block_exscan<NT>(n_m_mine, tmp, &n_miss);
+  // Both counts in one scan: unique positions in the low half, misses in
+  // the high half (each total is at most n_e, so neither half carries).
+  uint64_t um_tot;
+  const uint64_t um_base =
+      block_exscan_u64<NT>(((uint64_t)n_m_mine << 32) | n_u_mine, tmp64, &um_tot);
+  const uint32_t u_base = (uint32_t)um_base, m_base = (uint32_t)(um_base >> 32);
+  const uint32_t n_u = (uint32_t)um_tot, n_miss = (uint32_t)(um_tot >> 32);
 
   // 3. Victims: never-used slots first, then the ring from its head.
   const int n_free = C - free_head;
@@ -441,9 +446,11 @@ __device__ __forceinline__ void update_request(const Args& a, int b, uint64_t* s
   // rounds, not 4C / NT rounds of two memory round trips each.  An entry's
   // place: the live entries of the round's earlier rows, of the earlier
   // waves in its row (per-wave counts from ballots, scanned in (row, wave)
-  // order by one wave) and of the earlier lanes of its wave.  Every entry a
-  // round writes lies below the round's start (dst <= src), so none is
-  // overwritten before it is read.
+  // order by one wave) and of the earlier lanes of its wave.  A round reads
+  // all of its entries before it writes any (a barrier between), and it
+  // writes only below the next round's start: dst counts the live entries
+  // of the earlier rounds, so dst <= src, and a round has at most NT kC live
+  // entries.  No entry is overwritten before it is read.
   int tail = tail0;
   if (tail + (int)n_u > cap) {
     constexpr int kC = 16;
