@@ -752,7 +752,9 @@ def replay_curves(args, name="128k-b8-mtp2-r095", T=32,
     lo, hi = min(capacities), 16384
     return {
         "workload": name, "steps": T, "requests": B,
-        "lru_replay_equals_gpu_pool": True,
+        # (per request and step; the pool's contents are compared with the
+        # oracle, step by step, by the full-size parity tests)
+        "lru_replay_miss_counts_equal_gpu_pool": True,
         "misses_per_request_step": {p: {str(c): v / per for c, v in d_.items()}
                                     for p, d_ in misses.items()},
         f"miss_cut_{lo}_to_{hi}": {p: 1 - misses[p][hi] / misses[p][lo] for p in codes},
